@@ -1,0 +1,154 @@
+/*
+ * flash_attn.h — C ABI of a fused, exact scaled-dot-product attention library for AMD MI355X
+ * (gfx950), in the FlashAttention-2 style: forward with an online softmax that never writes
+ * the T x T score matrix and stores one log-sum-exp per query row; backward that recomputes
+ * the probabilities tile by tile from that log-sum-exp.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [forge]     "flash_attention.metal" (forge, S.-P. Boucher): header comment (what is stored,
+ *               the online-softmax update, m starting at -FLT_MAX), FlashParams, the forward
+ *               kernel flash_attn_fwd and the backward kernels flash_attn_bwd_dq / _dv / _dk.
+ *   [ipu]       "flash_attention_qkv_packed.cpp" (Graphcore flash-attention-ipu):
+ *               flashAttentionQKVPackedWithStash (forward with stored log-sum-exp),
+ *               flashAttentionQKVPackedGrad (backward), getTriuOffsetSequence (causal masks
+ *               of non-square blocks).
+ *   [teeny]     "flash_attn2.rs" (teeny-kernels 0.2.0): forward, backward_dq, backward_dkv
+ *               doc comments.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Layouts (row-major, contiguous, as in [forge] forward kernel's address arithmetic):
+ *    Q, O, dO, dQ : [B, T, H,   D]      K, V, dK, dV : [B, T, HKV, D]
+ *    L, Dvec      : [B, H, T]  float32
+ *  GQA: query head h reads KV head h / (H / HKV) ([forge] forward kernel); H % HKV == 0.
+ *  scale multiplies q.k ([forge] flash_attn_fwd, [teeny] forward); must be finite and > 0.
+ *  causal != 0 keeps keys j <= i (diagonal kept).  window > 0 keeps keys j >= i - window + 1
+ *  (window counts keys including self; 0 = off; without causal it is a lower bound only),
+ *  as in [forge] FlashParams and the per-row bounds of its kernels.
+ *  L = m + ln(l) in natural-log units ([ipu] forward epilogue, [forge] forward epilogue);
+ *  a row with no visible key gets O = 0 and L = 0 ([forge] forward epilogue guard).
+ *  dtype selects the element type of Q, K, V, O and dO: FA_DTYPE_F32 (float) or
+ *  FA_DTYPE_BF16 (bfloat16, fp32 accumulation).  L, Dvec, dQ, dK, dV are float32 in both.
+ *
+ *  Pointers are DEVICE pointers (HIP device memory of the current device), 16-byte aligned.
+ *  The caller owns every buffer; the library keeps no pointer after a call returns.  Calls
+ *  are asynchronous on `stream` (0 = the null stream): they return after enqueueing, and
+ *  errors raised while the kernels run surface at the caller's next synchronisation.
+ *  Every output is overwritten (never accumulated into).
+ *
+ *  Errors: arguments are validated on the host before anything is enqueued.
+ *    FA_ERR_INVALID_ARG  null pointer, B/T/H/HKV/D < 1, H % HKV != 0, window < 0,
+ *                        scale not finite or <= 0, misaligned pointer, size overflow,
+ *                        tile sizes that are not supported values;
+ *    FA_ERR_UNSUPPORTED  a valid request this build has no kernel for (head dim);
+ *    FA_ERR_HIP          a HIP runtime error while enqueueing (hipGetLastError).
+ *  No C++ exception crosses this interface.
+ *
+ *  Supported head dims: FA_DTYPE_F32: D a multiple of 8 in [8, 128];
+ *                       FA_DTYPE_BF16: D in {64, 128}.
+ */
+#ifndef FLASH_ATTN_H
+#define FLASH_ATTN_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = 1,
+    FA_ERR_UNSUPPORTED = 2,
+    FA_ERR_HIP = 3
+} fa_status_t;
+
+typedef enum { FA_DTYPE_F32 = 0, FA_DTYPE_BF16 = 1 } fa_dtype_t;
+
+/* Forward ([forge] flash_attn_fwd; [ipu] flashAttentionQKVPackedWithStash; [teeny] forward):
+ * O = softmax(scale * Q K^T, masked) V per (b, h), and L = row log-sum-exp of the masked,
+ * scaled scores.  Inputs Q, K, V (dtype); outputs O (dtype) and L (float32). */
+fa_status_t flash_attn_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
+                           int B, int T, int H, int HKV, int D, float scale, int causal,
+                           int window, fa_dtype_t dtype, hipStream_t stream);
+
+/* Backward of the loss sum(O * dO) ([forge] backward kernels; [ipu]
+ * flashAttentionQKVPackedGrad; [teeny] backward_dq / backward_dkv):
+ *   Dvec_i = dO_i . O_i;  P = exp(scale * Q K^T - L) on visible entries;  dP = dO V^T;
+ *   dS = P * (dP - Dvec);  dQ = scale dS K;  dK = scale dS^T Q;  dV = P^T dO,
+ * dK and dV summed over the H/HKV query heads of each KV head.  O and L must be the forward's
+ * outputs for the same inputs.  Outputs dQ, dK, dV are float32.  Runs the three stages below
+ * in order on `stream`; the Dvec workspace (B*H*T floats) is allocated stream-ordered
+ * (hipMallocAsync) and released the same way. */
+fa_status_t flash_attn_bwd(const void* Q, const void* K, const void* V, const void* O,
+                           const float* L, const void* dO, float* dQ, float* dK, float* dV,
+                           int B, int T, int H, int HKV, int D, float scale, int causal,
+                           int window, fa_dtype_t dtype, hipStream_t stream);
+
+/* As flash_attn_fwd / flash_attn_bwd, with the block tiling forced: bq query rows by bk keys
+ * per block (0, 0 = the library's choice).  FA_DTYPE_F32 accepts bq in {32, 64} and
+ * bk in {16, 32, 64}; FA_DTYPE_BF16 accepts only (0, 0).  The tiling decides which blocks
+ * are skipped, computed without a mask, or masked (causal diagonal, window edge, ragged T);
+ * results agree with the automatic tiling up to rounding order. */
+fa_status_t flash_attn_fwd_ex(const void* Q, const void* K, const void* V, void* O, float* L,
+                              int B, int T, int H, int HKV, int D, float scale, int causal,
+                              int window, fa_dtype_t dtype, hipStream_t stream, int bq, int bk);
+fa_status_t flash_attn_bwd_ex(const void* Q, const void* K, const void* V, const void* O,
+                              const float* L, const void* dO, float* dQ, float* dK, float* dV,
+                              int B, int T, int H, int HKV, int D, float scale, int causal,
+                              int window, fa_dtype_t dtype, hipStream_t stream, int bq, int bk);
+
+/* Backward stage 1 ([ipu] flashAttentionQKVPackedGrad, its D = rowsum(O * grad) step;
+ * [forge] backward section comment; [teeny] backward_dq): Dvec[b,h,i] = sum_d dO[b,i,h,d] *
+ * O[b,i,h,d], accumulated in float32.  Dvec is a caller-owned [B,H,T] float32 buffer. */
+fa_status_t flash_attn_bwd_preprocess(const void* O, const void* dO, float* Dvec, int B, int T,
+                                      int H, int D, fa_dtype_t dtype, hipStream_t stream);
+
+/* Backward stage 2 ([forge] flash_attn_bwd_dv / flash_attn_bwd_dk; [teeny] backward_dkv;
+ * [ipu] flashAttentionQKVPackedGrad outer loop over key chunks): dK and dV, each key block
+ * owned by one workgroup that loops over the query heads of its group and the query blocks
+ * that see it, so every element is written once, without atomics.  Dvec from stage 1. */
+fa_status_t flash_attn_bwd_dkdv(const void* Q, const void* K, const void* V, const void* dO,
+                                const float* L, const float* Dvec, float* dK, float* dV, int B,
+                                int T, int H, int HKV, int D, float scale, int causal,
+                                int window, fa_dtype_t dtype, hipStream_t stream, int bq,
+                                int bk);
+
+/* Backward stage 3 ([forge] flash_attn_bwd_dq; [teeny] backward_dq): dQ, one query block per
+ * workgroup looping over the key blocks it sees.  Dvec from stage 1. */
+fa_status_t flash_attn_bwd_dq(const void* Q, const void* K, const void* V, const void* dO,
+                              const float* L, const float* Dvec, float* dQ, int B, int T,
+                              int H, int HKV, int D, float scale, int causal, int window,
+                              fa_dtype_t dtype, hipStream_t stream, int bq, int bk);
+
+/* ---- host-only helpers (no GPU needed) ---- */
+
+/* Human-readable name of a status code (static string). */
+const char* flash_attn_status_string(fa_status_t s);
+
+/* Class of block (i, j) — query rows [i*bq, i*bq+bq) by keys [j*bk, j*bk+bk) of a T x T
+ * problem — exactly as the kernels decide it: 0 = skipped (nothing visible), 1 = computed
+ * without a mask (every in-range element visible), 2 = computed with the element mask
+ * (causal diagonal, window edge, or keys past T).  *off receives i*bq - j*bk, from which the
+ * kernels rebuild the mask (keep c <= r + off, c >= r + off - window + 1); this is the
+ * quantity whose cycle [ipu] getTriuOffsetSequence enumerates (as off + 1).
+ * Returns -1 on invalid arguments. */
+int flash_attn_block_class(int T, int bq, int bk, int causal, int window, int i, int j,
+                           int* off);
+
+/* Key-block range [*j_lo, *j_hi) a query tile i loops over (same rule as the kernels). */
+fa_status_t flash_attn_kv_block_range(int T, int bq, int bk, int causal, int window, int i,
+                                      int* j_lo, int* j_hi);
+
+/* Tiling the library picks for a dtype / head dim: pass 0 = forward, 1 = dK/dV, 2 = dQ.
+ * *bq, *bk are the query and key block sizes of that pass. */
+fa_status_t flash_attn_default_tiles(fa_dtype_t dtype, int D, int pass, int* bq, int* bk);
+
+/* Library ABI version (major * 100 + minor). */
+int flash_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASH_ATTN_H */

@@ -1,0 +1,62 @@
+"""ctypes loader for libflashattn.so (built in-tree by online_softmax_fwd_flash_amd.build).
+
+There is no fallback: if the library is missing or fails to load, every entry point raises.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("FLASHATTN_LIB", os.path.join(_HERE, "libflashattn.so"))
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_DTYPE_F32, FA_DTYPE_BF16 = 0, 1
+
+EXPORTS = [
+    "flash_attn_fwd", "flash_attn_bwd", "flash_attn_fwd_ex", "flash_attn_bwd_ex",
+    "flash_attn_bwd_preprocess", "flash_attn_bwd_dkdv", "flash_attn_bwd_dq",
+    "flash_attn_status_string", "flash_attn_block_class", "flash_attn_kv_block_range",
+    "flash_attn_default_tiles", "flash_attn_version",
+]
+
+_lib = None
+
+P = ctypes.c_void_p
+I = ctypes.c_int
+F = ctypes.c_float
+_DIMS = [I, I, I, I, I, F, I, I, I, P]          # B T H HKV D scale causal window dtype stream
+
+
+def _declare(lib):
+    sig = {
+        "flash_attn_fwd": [P, P, P, P, P] + _DIMS,
+        "flash_attn_fwd_ex": [P, P, P, P, P] + _DIMS + [I, I],
+        "flash_attn_bwd": [P] * 9 + _DIMS,
+        "flash_attn_bwd_ex": [P] * 9 + _DIMS + [I, I],
+        "flash_attn_bwd_preprocess": [P, P, P, I, I, I, I, I, P],
+        "flash_attn_bwd_dkdv": [P] * 8 + _DIMS + [I, I],
+        "flash_attn_bwd_dq": [P] * 7 + _DIMS + [I, I],
+        "flash_attn_block_class": [I, I, I, I, I, I, I, ctypes.POINTER(I)],
+        "flash_attn_kv_block_range": [I, I, I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)],
+        "flash_attn_default_tiles": [I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)],
+        "flash_attn_version": [],
+        "flash_attn_status_string": [I],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_char_p if name == "flash_attn_status_string" else I
+    return lib
+
+
+def lib():
+    """The loaded library (raises OSError with a build hint if it is absent)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise OSError(f"{LIB_PATH} is not built; run `python -m online_softmax_fwd_flash_amd.build`")
+        _lib = _declare(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def status_string(code):
+    return lib().flash_attn_status_string(code).decode()

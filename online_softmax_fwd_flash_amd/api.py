@@ -1,0 +1,170 @@
+"""Thin Python binding of the C ABI in include/flash_attn.h.
+
+Functions carry the C names and only marshal arguments: they check tensor metadata, allocate
+output tensors with torch when the caller passes none, and hand raw device pointers plus the
+current HIP stream to the library.  Every arithmetic step runs in the library's kernels.
+"""
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float32: _lib.FA_DTYPE_F32, torch.bfloat16: _lib.FA_DTYPE_BF16}
+
+
+class FlashAttnError(RuntimeError):
+    def __init__(self, fn, code):
+        super().__init__(f"{fn} failed: {_lib.status_string(code)}")
+        self.code = code
+
+
+def _check(fn, code):
+    if code != _lib.FA_OK:
+        raise FlashAttnError(fn, code)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dims(q, k):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("expected q [B,T,H,D] and k/v [B,T,HKV,D]")
+    B, T, H, D = q.shape
+    HKV = k.shape[2]
+    return B, T, H, HKV, D
+
+
+def _want(t, shape, dtype, name):
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name}: expected contiguous {dtype} cuda tensor of shape {tuple(shape)}")
+
+
+def _scale(scale, D):
+    return 1.0 / math.sqrt(D) if scale is None else float(scale)
+
+
+def flash_attn_fwd(q, k, v, causal=True, window=0, scale=None, out=None, lse=None, tiles=(0, 0),
+                   stream=None):
+    """O [B,T,H,D] (q.dtype) and L [B,H,T] (float32) for q [B,T,H,D], k, v [B,T,HKV,D]."""
+    B, T, H, HKV, D = _dims(q, k)
+    dt = _DT[q.dtype]
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _want(t, t.shape, q.dtype, name)
+    _want(v, k.shape, q.dtype, "v")
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty(B, H, T, device=q.device, dtype=torch.float32) if lse is None else lse
+    _want(out, q.shape, q.dtype, "out")
+    _want(lse, (B, H, T), torch.float32, "lse")
+    code = _lib.lib().flash_attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, T, H,
+                                        HKV, D, _scale(scale, D), int(bool(causal)), int(window),
+                                        dt, _stream(stream), int(tiles[0]), int(tiles[1]))
+    _check("flash_attn_fwd", code)
+    return out, lse
+
+
+def flash_attn_bwd_preprocess(o, do, dvec=None, stream=None):
+    B, T, H, D = o.shape
+    _want(do, o.shape, o.dtype, "do")
+    dvec = torch.empty(B, H, T, device=o.device, dtype=torch.float32) if dvec is None else dvec
+    _want(dvec, (B, H, T), torch.float32, "dvec")
+    code = _lib.lib().flash_attn_bwd_preprocess(_ptr(o), _ptr(do), _ptr(dvec), B, T, H, D,
+                                                _DT[o.dtype], _stream(stream))
+    _check("flash_attn_bwd_preprocess", code)
+    return dvec
+
+
+def _grads(q, k, dq, dk, dv):
+    f = torch.float32
+    dq = torch.empty(q.shape, device=q.device, dtype=f) if dq is None else dq
+    dk = torch.empty(k.shape, device=q.device, dtype=f) if dk is None else dk
+    dv = torch.empty(k.shape, device=q.device, dtype=f) if dv is None else dv
+    _want(dq, q.shape, f, "dq")
+    _want(dk, k.shape, f, "dk")
+    _want(dv, k.shape, f, "dv")
+    return dq, dk, dv
+
+
+def flash_attn_bwd_dkdv(q, k, v, do, lse, dvec, causal=True, window=0, scale=None, dk=None,
+                        dv=None, tiles=(0, 0), stream=None):
+    B, T, H, HKV, D = _dims(q, k)
+    f = torch.float32
+    dk = torch.empty(k.shape, device=q.device, dtype=f) if dk is None else dk
+    dv = torch.empty(k.shape, device=q.device, dtype=f) if dv is None else dv
+    _want(dk, k.shape, f, "dk")
+    _want(dv, k.shape, f, "dv")
+    code = _lib.lib().flash_attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse),
+                                          _ptr(dvec), _ptr(dk), _ptr(dv), B, T, H, HKV, D,
+                                          _scale(scale, D), int(bool(causal)), int(window),
+                                          _DT[q.dtype], _stream(stream), int(tiles[0]),
+                                          int(tiles[1]))
+    _check("flash_attn_bwd_dkdv", code)
+    return dk, dv
+
+
+def flash_attn_bwd_dq(q, k, v, do, lse, dvec, causal=True, window=0, scale=None, dq=None,
+                      tiles=(0, 0), stream=None):
+    B, T, H, HKV, D = _dims(q, k)
+    dq = torch.empty(q.shape, device=q.device, dtype=torch.float32) if dq is None else dq
+    _want(dq, q.shape, torch.float32, "dq")
+    code = _lib.lib().flash_attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse),
+                                        _ptr(dvec), _ptr(dq), B, T, H, HKV, D, _scale(scale, D),
+                                        int(bool(causal)), int(window), _DT[q.dtype],
+                                        _stream(stream), int(tiles[0]), int(tiles[1]))
+    _check("flash_attn_bwd_dq", code)
+    return dq
+
+
+def flash_attn_bwd(q, k, v, o, lse, do, causal=True, window=0, scale=None, dq=None, dk=None,
+                   dv=None, tiles=(0, 0), stream=None):
+    """dQ, dK, dV (float32) of sum(O * dO); O, L from flash_attn_fwd on the same inputs."""
+    B, T, H, HKV, D = _dims(q, k)
+    _want(o, q.shape, q.dtype, "o")
+    _want(do, q.shape, q.dtype, "do")
+    _want(lse, (B, H, T), torch.float32, "lse")
+    dq, dk, dv = _grads(q, k, dq, dk, dv)
+    code = _lib.lib().flash_attn_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                                        _ptr(dq), _ptr(dk), _ptr(dv), B, T, H, HKV, D,
+                                        _scale(scale, D), int(bool(causal)), int(window),
+                                        _DT[q.dtype], _stream(stream), int(tiles[0]),
+                                        int(tiles[1]))
+    _check("flash_attn_bwd", code)
+    return dq, dk, dv
+
+
+def flash_attn_block_class(T, bq, bk, causal, window, i, j):
+    """(class, off) of block (i, j): class 0 skip, 1 full, 2 masked; off = i*bq - j*bk."""
+    off = ctypes.c_int(0)
+    cls = _lib.lib().flash_attn_block_class(T, bq, bk, int(bool(causal)), window, i, j,
+                                            ctypes.byref(off))
+    if cls < 0:
+        raise FlashAttnError("flash_attn_block_class", _lib.FA_ERR_INVALID_ARG)
+    return cls, off.value
+
+
+def flash_attn_kv_block_range(T, bq, bk, causal, window, i):
+    lo, hi = ctypes.c_int(0), ctypes.c_int(0)
+    _check("flash_attn_kv_block_range",
+           _lib.lib().flash_attn_kv_block_range(T, bq, bk, int(bool(causal)), window, i,
+                                                ctypes.byref(lo), ctypes.byref(hi)))
+    return lo.value, hi.value
+
+
+def flash_attn_default_tiles(dtype, D, pass_):
+    bq, bk = ctypes.c_int(0), ctypes.c_int(0)
+    dt = _DT[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    _check("flash_attn_default_tiles",
+           _lib.lib().flash_attn_default_tiles(dt, D, pass_, ctypes.byref(bq), ctypes.byref(bk)))
+    return bq.value, bk.value
+
+
+def flash_attn_version():
+    return _lib.lib().flash_attn_version()

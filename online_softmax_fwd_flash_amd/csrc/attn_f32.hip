@@ -1,0 +1,440 @@
+// fp32 attention kernels for gfx950: forward, dK/dV and dQ, on the 16x16x4 fp32 MFMA
+// (true fp32 products, fp32 accumulation).  Head dim D is a runtime multiple of 8 up to 128,
+// padded to DP in {16, 32, 64, 128} for the register tiles; a workgroup's tiling (BQ query
+// rows x BK keys per block) is a template parameter so the tilings the pages use (32 x 32,
+// 64 x 16) run as such.
+//
+// Orientation.  Scores are formed transposed, S^T = K Q^T, so MFMA column n (lane l % 16) is a
+// query row: a query's running max / sum live in its own lanes and only the four 16-lane
+// groups of a wave exchange values.  P^T then feeds O^T += V^T P^T directly from the
+// accumulator layout, and O^T keeps each query in its own lanes for the rescale.
+//
+// Method: the forge page "flash_attention.metal" (forward kernel: K/V staged through on-chip
+// memory per block, online softmax with m from -FLT_MAX, causal key bound, window block skip,
+// diagonal-only mask, l == 0 guard; backward kernels dQ / dV / dK) and the Graphcore page
+// "flash_attention_qkv_packed.cpp" (block skip / mask conditions, log-sum-exp stash,
+// key-chunk-outer backward).
+#include "common.h"
+#include "kernels.h"
+
+namespace fa {
+
+namespace {
+
+template <int DP>
+struct F32Tile {
+    static constexpr int KS = DP / 4;   // MFMA k-steps over the (padded) head dim
+    static constexpr int LD = DP + 4;   // padded LDS row (floats): conflict-free column reads
+    static constexpr int NDB = DP / 16; // 16-wide blocks of the head dim in O / dQ / dK / dV
+};
+
+// Stage rows [row0, row0 + ROWS) of a [*, ld] matrix (head slice at `base`) into LDS
+// (ROWS x DP, zero outside [0, T) x [0, D)).
+template <int DP, int ROWS, int NT>
+__device__ __forceinline__ void stage_rows(float* __restrict__ dst, const float* __restrict__ base,
+                                           int64_t ld, int row0, int T, int D) {
+    constexpr int C4 = DP / 4;
+    for (int e = threadIdx.x; e < ROWS * C4; e += NT) {
+        const int r = e / C4, d = (e % C4) * 4;
+        const int row = row0 + r;
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        if (row < T && d < D) {
+            // D is a multiple of 8, so a float4 never straddles D
+            x = *reinterpret_cast<const f32x4*>(base + (int64_t)row * ld + d);
+        }
+        *reinterpret_cast<f32x4*>(dst + r * F32Tile<DP>::LD + d) = x;
+    }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------------ forward
+template <int DP, int BQ, int BK>
+__global__ __launch_bounds__(BQ / 16 * 64) void fwd_f32_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    float* __restrict__ O, float* __restrict__ L, int B, int T, int H, int HKV, int D,
+    float scale, int causal, int window, int nqt) {
+    using Tl = F32Tile<DP>;
+    constexpr int NW = BQ / 16, NT = NW * 64, KS = Tl::KS, LD = Tl::LD, NDB = Tl::NDB;
+    __shared__ __attribute__((aligned(16))) float Ks[BK * LD];
+    __shared__ __attribute__((aligned(16))) float Vs[BK * LD];
+
+    const int BH = B * H;
+    const int qt = nqt - 1 - (int)(blockIdx.x / BH);   // longest key ranges first
+    const int bh = blockIdx.x % BH;
+    const int b = bh / H, h = bh % H, hk = h / (H / HKV);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    const int wr0 = qt * BQ + w * 16;
+    const int q = wr0 + n;
+    const int64_t ldq = (int64_t)H * D, ldk = (int64_t)HKV * D;
+    const float* Qh = Q + (int64_t)b * T * ldq + (int64_t)h * D;
+    const float* Kh = K + (int64_t)b * T * ldk + (int64_t)hk * D;
+    const float* Vh = V + (int64_t)b * T * ldk + (int64_t)hk * D;
+
+    float qreg[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const int d = g * KS + s;
+        qreg[s] = (q < T && d < D) ? Qh[(int64_t)q * ldq + d] : 0.f;
+    }
+    f32x4 oacc[NDB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = kNegMax, lsum = 0.f;
+    const float c = scale * kLog2e;
+    const bool cz = causal != 0;
+
+    int jlo, jhi;
+    kv_block_range(T, qt * BQ, qt * BQ + BQ, BK, cz, window, jlo, jhi);
+    for (int j = jlo; j < jhi; ++j) {
+        __syncthreads();
+        stage_rows<DP, BK, NT>(Ks, Kh, ldk, j * BK, T, D);
+        stage_rows<DP, BK, NT>(Vs, Vh, ldk, j * BK, T, D);
+        __syncthreads();
+        const int cls = block_class(T, wr0, wr0 + 16, j * BK, j * BK + BK, cz, window);
+        if (cls == kSkip) continue;
+
+        f32x4 s[BK / 16];
+#pragma unroll
+        for (int kb = 0; kb < BK / 16; ++kb) {
+            s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const float* krow = Ks + (kb * 16 + n) * LD + g * KS;
+#pragma unroll
+            for (int st = 0; st < KS; ++st) s[kb] = mfma16x16x4f32(krow[st], qreg[st], s[kb]);
+        }
+        if (cls == kPartial) {
+#pragma unroll
+            for (int kb = 0; kb < BK / 16; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int key = j * BK + kb * 16 + 4 * g + r;
+                    if (!visible(q, key, T, cz, window)) s[kb][r] = -INFINITY;
+                }
+        }
+        float mx = kNegMax;
+#pragma unroll
+        for (int kb = 0; kb < BK / 16; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][r]);
+        mx = fmaxf(mx, xor_shfl(mx, 16));
+        mx = fmaxf(mx, xor_shfl(mx, 32));
+        const float mnew = fmaxf(m, mx);
+        const float corr = fast_exp2((m - mnew) * c);
+        m = mnew;
+        const float mc = fmaxf(m * c, kNegMax);   // finite even while m = -FLT_MAX
+        float ps = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < BK / 16; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float p = fast_exp2(fmaf(s[kb][r], c, -mc));
+                s[kb][r] = p;
+                ps += p;
+            }
+        lsum = lsum * corr + ps;
+#pragma unroll
+        for (int i = 0; i < NDB; ++i) oacc[i] *= corr;
+#pragma unroll
+        for (int kb = 0; kb < BK / 16; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float* vrow = Vs + (kb * 16 + 4 * g + r) * LD + n;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    oacc[db] = mfma16x16x4f32(vrow[db * 16], s[kb][r], oacc[db]);
+            }
+    }
+
+    lsum += xor_shfl(lsum, 16);
+    lsum += xor_shfl(lsum, 32);
+    if (q >= T) return;
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    float* Oq = O + (int64_t)b * T * ldq + (int64_t)q * ldq + (int64_t)h * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        const int d = db * 16 + 4 * g;
+        if (d < D) *reinterpret_cast<f32x4*>(Oq + d) = oacc[db] * inv;
+    }
+    if (g == 0)
+        L[((int64_t)b * H + h) * T + q] = lsum > 0.f ? m * scale + fast_log2(lsum) * kLn2 : 0.f;
+}
+
+// ------------------------------------------------------------------------------ dK / dV
+// One workgroup per (b, kv head, key block of BK keys); wave w owns keys [w*16, w*16+16) of
+// the block and loops over the query heads of the group and the query blocks that see them.
+template <int DP, int BQ, int BK>
+__global__ __launch_bounds__(BK / 16 * 64) void dkdv_f32_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    const float* __restrict__ dO, const float* __restrict__ L, const float* __restrict__ Dv,
+    float* __restrict__ dK, float* __restrict__ dV, int B, int T, int H, int HKV, int D,
+    float scale, int causal, int window, int nkt) {
+    using Tl = F32Tile<DP>;
+    constexpr int NW = BK / 16, NT = NW * 64, KS = Tl::KS, LD = Tl::LD, NDB = Tl::NDB;
+    __shared__ __attribute__((aligned(16))) float Qs[BQ * LD];
+    __shared__ __attribute__((aligned(16))) float dOs[BQ * LD];
+    __shared__ float Ls[BQ], Ds[BQ];
+
+    const int BG = B * HKV;
+    const int kt = (int)(blockIdx.x / BG);
+    const int bg = blockIdx.x % BG;
+    const int b = bg / HKV, hk = bg % HKV, rep = H / HKV;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    const int kw0 = kt * BK + w * 16;
+    const int key = kw0 + n;
+    const int64_t ldq = (int64_t)H * D, ldk = (int64_t)HKV * D;
+    const float* Kh = K + (int64_t)b * T * ldk + (int64_t)hk * D;
+    const float* Vh = V + (int64_t)b * T * ldk + (int64_t)hk * D;
+    const bool cz = causal != 0;
+    const float c = scale * kLog2e;
+
+    float kreg[KS], vreg[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const int d = g * KS + s;
+        const bool ok = key < T && d < D;
+        kreg[s] = ok ? Kh[(int64_t)key * ldk + d] : 0.f;
+        vreg[s] = ok ? Vh[(int64_t)key * ldk + d] : 0.f;
+    }
+    f32x4 dka[NDB], dva[NDB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) dka[i] = dva[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    int ilo, ihi;
+    q_block_range(T, kt * BK, kt * BK + BK, BQ, cz, window, ilo, ihi);
+    for (int hh = 0; hh < rep; ++hh) {
+        const int h = hk * rep + hh;
+        const float* Qh = Q + (int64_t)b * T * ldq + (int64_t)h * D;
+        const float* dOh = dO + (int64_t)b * T * ldq + (int64_t)h * D;
+        const float* Lh = L + ((int64_t)b * H + h) * T;
+        const float* Dh = Dv + ((int64_t)b * H + h) * T;
+        for (int i = ilo; i < ihi; ++i) {
+            __syncthreads();
+            stage_rows<DP, BQ, NT>(Qs, Qh, ldq, i * BQ, T, D);
+            stage_rows<DP, BQ, NT>(dOs, dOh, ldq, i * BQ, T, D);
+            for (int e = threadIdx.x; e < BQ; e += NT) {
+                const int row = i * BQ + e;
+                Ls[e] = row < T ? Lh[row] * kLog2e : 0.f;
+                Ds[e] = row < T ? Dh[row] : 0.f;
+            }
+            __syncthreads();
+#pragma unroll 1
+            for (int qs = 0; qs < BQ; qs += 16) {
+                const int qr0 = i * BQ + qs;
+                const int cls = block_class(T, qr0, qr0 + 16, kw0, kw0 + 16, cz, window);
+                if (cls == kSkip) continue;
+                f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+                const float* qrow = Qs + (qs + n) * LD + g * KS;
+                const float* orow = dOs + (qs + n) * LD + g * KS;
+#pragma unroll
+                for (int st = 0; st < KS; ++st) {
+                    sc = mfma16x16x4f32(qrow[st], kreg[st], sc);
+                    dp = mfma16x16x4f32(orow[st], vreg[st], dp);
+                }
+                // lane (n, g), element r: query qr0 + 4g + r, key kw0 + n
+                f32x4 p, ds;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int qq = qs + 4 * g + r;
+                    float pr = fast_exp2(fmaf(sc[r], c, -Ls[qq]));
+                    if (cls == kPartial && !visible(qr0 + 4 * g + r, key, T, cz, window)) pr = 0.f;
+                    p[r] = pr;
+                    ds[r] = pr * (dp[r] - Ds[qq]);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float* dorow = dOs + (qs + 4 * g + r) * LD + n;
+                    const float* qcol = Qs + (qs + 4 * g + r) * LD + n;
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        dva[db] = mfma16x16x4f32(p[r], dorow[db * 16], dva[db]);
+                        dka[db] = mfma16x16x4f32(ds[r], qcol[db * 16], dka[db]);
+                    }
+                }
+            }
+        }
+    }
+    // lane (n, g), element r: key kw0 + 4g + r, column d = db*16 + n
+    float* dKh = dK + (int64_t)b * T * ldk + (int64_t)hk * D;
+    float* dVh = dV + (int64_t)b * T * ldk + (int64_t)hk * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        const int d = db * 16 + n;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int kk = kw0 + 4 * g + r;
+            if (kk < T && d < D) {
+                dKh[(int64_t)kk * ldk + d] = dka[db][r] * scale;
+                dVh[(int64_t)kk * ldk + d] = dva[db][r];
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------ dQ
+template <int DP, int BQ, int BK>
+__global__ __launch_bounds__(BQ / 16 * 64) void dq_f32_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    const float* __restrict__ dO, const float* __restrict__ L, const float* __restrict__ Dv,
+    float* __restrict__ dQ, int B, int T, int H, int HKV, int D, float scale, int causal,
+    int window, int nqt) {
+    using Tl = F32Tile<DP>;
+    constexpr int NW = BQ / 16, NT = NW * 64, KS = Tl::KS, LD = Tl::LD, NDB = Tl::NDB;
+    __shared__ __attribute__((aligned(16))) float Ks[BK * LD];
+    __shared__ __attribute__((aligned(16))) float Vs[BK * LD];
+
+    const int BH = B * H;
+    const int qt = nqt - 1 - (int)(blockIdx.x / BH);
+    const int bh = blockIdx.x % BH;
+    const int b = bh / H, h = bh % H, hk = h / (H / HKV);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    const int wr0 = qt * BQ + w * 16;
+    const int q = wr0 + n;
+    const int64_t ldq = (int64_t)H * D, ldk = (int64_t)HKV * D;
+    const float* Qh = Q + (int64_t)b * T * ldq + (int64_t)h * D;
+    const float* dOh = dO + (int64_t)b * T * ldq + (int64_t)h * D;
+    const float* Kh = K + (int64_t)b * T * ldk + (int64_t)hk * D;
+    const float* Vh = V + (int64_t)b * T * ldk + (int64_t)hk * D;
+    const bool cz = causal != 0;
+    const float c = scale * kLog2e;
+
+    float qreg[KS], doreg[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const int d = g * KS + s;
+        const bool ok = q < T && d < D;
+        qreg[s] = ok ? Qh[(int64_t)q * ldq + d] : 0.f;
+        doreg[s] = ok ? dOh[(int64_t)q * ldq + d] : 0.f;
+    }
+    const float l2 = q < T ? L[((int64_t)b * H + h) * T + q] * kLog2e : 0.f;
+    const float dq_i = q < T ? Dv[((int64_t)b * H + h) * T + q] : 0.f;
+    f32x4 dqa[NDB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) dqa[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    int jlo, jhi;
+    kv_block_range(T, qt * BQ, qt * BQ + BQ, BK, cz, window, jlo, jhi);
+    for (int j = jlo; j < jhi; ++j) {
+        __syncthreads();
+        stage_rows<DP, BK, NT>(Ks, Kh, ldk, j * BK, T, D);
+        stage_rows<DP, BK, NT>(Vs, Vh, ldk, j * BK, T, D);
+        __syncthreads();
+#pragma unroll 1
+        for (int kb = 0; kb < BK / 16; ++kb) {
+            const int kc0 = j * BK + kb * 16;
+            const int cls = block_class(T, wr0, wr0 + 16, kc0, kc0 + 16, cz, window);
+            if (cls == kSkip) continue;
+            f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+            const float* krow = Ks + (kb * 16 + n) * LD + g * KS;
+            const float* vrow = Vs + (kb * 16 + n) * LD + g * KS;
+#pragma unroll
+            for (int st = 0; st < KS; ++st) {
+                sc = mfma16x16x4f32(krow[st], qreg[st], sc);
+                dp = mfma16x16x4f32(vrow[st], doreg[st], dp);
+            }
+            // lane (n, g), element r: key kc0 + 4g + r, query q
+            f32x4 ds;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float pr = fast_exp2(fmaf(sc[r], c, -l2));
+                if (cls == kPartial && !visible(q, kc0 + 4 * g + r, T, cz, window)) pr = 0.f;
+                ds[r] = pr * (dp[r] - dq_i);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float* kcol = Ks + (kb * 16 + 4 * g + r) * LD + n;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    dqa[db] = mfma16x16x4f32(kcol[db * 16], ds[r], dqa[db]);
+            }
+        }
+    }
+    if (q >= T) return;
+    float* dQq = dQ + (int64_t)b * T * ldq + (int64_t)q * ldq + (int64_t)h * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        const int d = db * 16 + 4 * g;
+        if (d < D) *reinterpret_cast<f32x4*>(dQq + d) = dqa[db] * scale;
+    }
+}
+
+// ------------------------------------------------------------------------------ launchers
+namespace {
+
+template <int DP, int BQ, int BK>
+hipError_t launch_fwd_f32_t(const AttnArgs& a) {
+    const int nqt = (a.T + BQ - 1) / BQ;
+    const unsigned grid = (unsigned)nqt * a.B * a.H;
+    hipLaunchKernelGGL((fwd_f32_kernel<DP, BQ, BK>), dim3(grid), dim3(BQ / 16 * 64), 0,
+                       a.stream, (const float*)a.Q, (const float*)a.K, (const float*)a.V,
+                       (float*)a.Oout, a.L, a.B, a.T, a.H, a.HKV, a.D, a.scale, a.causal,
+                       a.window, nqt);
+    return hipGetLastError();
+}
+
+template <int DP, int BQ, int BK>
+hipError_t launch_dkdv_f32_t(const AttnArgs& a) {
+    const int nkt = (a.T + BK - 1) / BK;
+    const unsigned grid = (unsigned)nkt * a.B * a.HKV;
+    hipLaunchKernelGGL((dkdv_f32_kernel<DP, BQ, BK>), dim3(grid), dim3(BK / 16 * 64), 0,
+                       a.stream, (const float*)a.Q, (const float*)a.K, (const float*)a.V,
+                       (const float*)a.dO, a.Lin, a.Dvec, a.dK, a.dV, a.B, a.T, a.H, a.HKV, a.D,
+                       a.scale, a.causal, a.window, nkt);
+    return hipGetLastError();
+}
+
+template <int DP, int BQ, int BK>
+hipError_t launch_dq_f32_t(const AttnArgs& a) {
+    const int nqt = (a.T + BQ - 1) / BQ;
+    const unsigned grid = (unsigned)nqt * a.B * a.H;
+    hipLaunchKernelGGL((dq_f32_kernel<DP, BQ, BK>), dim3(grid), dim3(BQ / 16 * 64), 0,
+                       a.stream, (const float*)a.Q, (const float*)a.K, (const float*)a.V,
+                       (const float*)a.dO, a.Lin, a.Dvec, a.dQ, a.B, a.T, a.H, a.HKV, a.D,
+                       a.scale, a.causal, a.window, nqt);
+    return hipGetLastError();
+}
+
+template <template <int, int, int> class Fn, int DP>
+hipError_t by_tiles(const AttnArgs& a, int bq, int bk) {
+    if (bq == 32 && bk == 32) return Fn<DP, 32, 32>::run(a);
+    if (bq == 64 && bk == 16) return Fn<DP, 64, 16>::run(a);
+    if (bq == 64 && bk == 64) return Fn<DP, 64, 64>::run(a);
+    if (bq == 64 && bk == 32) return Fn<DP, 64, 32>::run(a);
+    if (bq == 32 && bk == 16) return Fn<DP, 32, 16>::run(a);
+    if (bq == 32 && bk == 64) return Fn<DP, 32, 64>::run(a);
+    return hipErrorInvalidValue;
+}
+
+template <template <int, int, int> class Fn>
+hipError_t by_dim(const AttnArgs& a, int bq, int bk) {
+    if (a.D <= 16) return by_tiles<Fn, 16>(a, bq, bk);
+    if (a.D <= 32) return by_tiles<Fn, 32>(a, bq, bk);
+    if (a.D <= 64) return by_tiles<Fn, 64>(a, bq, bk);
+    return by_tiles<Fn, 128>(a, bq, bk);
+}
+
+template <int DP, int BQ, int BK> struct FwdF32 {
+    static hipError_t run(const AttnArgs& a) { return launch_fwd_f32_t<DP, BQ, BK>(a); }
+};
+template <int DP, int BQ, int BK> struct DkdvF32 {
+    static hipError_t run(const AttnArgs& a) { return launch_dkdv_f32_t<DP, BQ, BK>(a); }
+};
+template <int DP, int BQ, int BK> struct DqF32 {
+    static hipError_t run(const AttnArgs& a) { return launch_dq_f32_t<DP, BQ, BK>(a); }
+};
+
+}  // namespace
+
+bool f32_tiles_supported(int bq, int bk) {
+    return (bq == 32 || bq == 64) && (bk == 16 || bk == 32 || bk == 64);
+}
+
+hipError_t launch_fwd_f32(const AttnArgs& a, int bq, int bk) { return by_dim<FwdF32>(a, bq, bk); }
+hipError_t launch_dkdv_f32(const AttnArgs& a, int bq, int bk) {
+    return by_dim<DkdvF32>(a, bq, bk);
+}
+hipError_t launch_dq_f32(const AttnArgs& a, int bq, int bk) { return by_dim<DqF32>(a, bq, bk); }
+
+}  // namespace fa

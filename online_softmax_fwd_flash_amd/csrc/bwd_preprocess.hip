@@ -1,0 +1,89 @@
+// Backward stage 1: Dvec[b,h,i] = sum_d dO[b,i,h,d] * O[b,i,h,d] in fp32 — the row dot the
+// Graphcore page (flashAttentionQKVPackedGrad) computes as rowsum(O * grad) and the forge page
+// ("flash_attention.metal", backward section) passes to its dQ / dK kernels; it equals
+// rowsum(dP * P).  Memory-bound: each (b, i, h) row of O and dO is read once with 16-byte
+// loads by a team of 8 lanes, reduced across the team with lane exchanges.
+#include "common.h"
+#include "kernels.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kTeam = 8, kThreads = 256;
+
+template <typename Elem>
+__device__ __forceinline__ float dot16B(const u32x4& a, const u32x4& b);
+
+template <>
+__device__ __forceinline__ float dot16B<float>(const u32x4& a, const u32x4& b) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // bit-cast a copied element: casting the vector-element lvalue itself reads element 0
+        const uint32_t x = a[i], y = b[i];
+        s = fmaf(__builtin_bit_cast(float, x), __builtin_bit_cast(float, y), s);
+    }
+    return s;
+}
+
+template <>
+__device__ __forceinline__ float dot16B<uint16_t>(const u32x4& a, const u32x4& b) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        s = fmaf(__builtin_bit_cast(float, a[i] << 16), __builtin_bit_cast(float, b[i] << 16), s);
+        s = fmaf(__builtin_bit_cast(float, a[i] & 0xffff0000u),
+                 __builtin_bit_cast(float, b[i] & 0xffff0000u), s);
+    }
+    return s;
+}
+
+template <typename Elem>
+__global__ __launch_bounds__(kThreads) void bwd_preprocess_kernel(
+    const Elem* __restrict__ O, const Elem* __restrict__ dO, float* __restrict__ Dv, int B, int T,
+    int H, int D) {
+    const int64_t rows = (int64_t)B * T * H;
+    const int64_t row = (int64_t)blockIdx.x * (kThreads / kTeam) + threadIdx.x / kTeam;
+    const int sub = threadIdx.x % kTeam;
+    const int nch = D * (int)sizeof(Elem) / 16;   // 16-byte chunks per row
+    float s = 0.f;
+    if (row < rows) {
+        const Elem* o = O + row * D;
+        const Elem* go = dO + row * D;
+        for (int ch = sub; ch < nch; ch += kTeam) {
+            const u32x4 a = *reinterpret_cast<const u32x4*>(o + ch * (16 / sizeof(Elem)));
+            const u32x4 b = *reinterpret_cast<const u32x4*>(go + ch * (16 / sizeof(Elem)));
+            s += dot16B<Elem>(a, b);
+        }
+    }
+    s += __shfl_xor(s, 1, 64);
+    s += __shfl_xor(s, 2, 64);
+    s += __shfl_xor(s, 4, 64);
+    if (row < rows && sub == 0) {
+        // row = (b*T + i)*H + h  ->  Dv[(b*H + h)*T + i]
+        const int h = (int)(row % H);
+        const int64_t bi = row / H;
+        const int i = (int)(bi % T);
+        const int64_t b = bi / T;
+        Dv[(b * H + h) * T + i] = s;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_preprocess(const void* O, const void* dO, float* Dvec, int B, int T, int H,
+                                 int D, int dtype, hipStream_t stream) {
+    const int64_t rows = (int64_t)B * T * H;
+    const int64_t per = kThreads / kTeam;
+    const unsigned grid = (unsigned)((rows + per - 1) / per);
+    if (dtype == 0)
+        hipLaunchKernelGGL(bwd_preprocess_kernel<float>, dim3(grid), dim3(kThreads), 0, stream,
+                           (const float*)O, (const float*)dO, Dvec, B, T, H, D);
+    else
+        hipLaunchKernelGGL(bwd_preprocess_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, stream,
+                           (const uint16_t*)O, (const uint16_t*)dO, Dvec, B, T, H, D);
+    return hipGetLastError();
+}
+
+}  // namespace fa

@@ -1,0 +1,60 @@
+// Shared device helpers for the gfx950 attention kernels: vector types, MFMA wrappers and the
+// cross-lane reductions the online softmax needs.  CDNA4 only (wave64, MFMA, LDS).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "block_class.h"
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kMaxDevices = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegMax = -3.402823466e+38f;  // running max starts here, never at -inf
+
+// D(32x32) += A(32x16) * B(16x32), bf16 inputs, fp32 accumulate.
+// Lane l supplies A row (l % 32) and B column (l % 32), each with 8 consecutive k of the
+// half (l / 32); D element r of lane l is row 8*(r/4) + 4*(l/32) + (r%4), column l % 32.
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// D(16x16) += A(16x4) * B(4x16), fp32.  Lane l supplies A[l%16][l/16] and B[l/16][l%16];
+// D element r of lane l is row 4*(l/16) + r, column l % 16.
+__device__ __forceinline__ f32x4 mfma16x16x4f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value held by lane l ^ 32 (the other half of the wave).
+__device__ __forceinline__ float swap_halves(float v) { return __shfl_xor(v, 32, 64); }
+
+__device__ __forceinline__ float xor_shfl(float v, int mask) {
+    return __shfl_xor(v, mask, 64);
+}
+
+// Round-to-nearest-even float -> bf16 pair (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2 r;
+    r[0] = (__bf16)lo;
+    r[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+
+}  // namespace fa

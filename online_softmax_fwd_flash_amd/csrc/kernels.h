@@ -1,0 +1,41 @@
+// Host-side launch interface between the C-ABI layer (api.hip) and the kernel translation
+// units.  Arguments have been validated before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace fa {
+
+struct AttnArgs {
+    const void* Q;
+    const void* K;
+    const void* V;
+    const void* O;     // forward output / backward input
+    void* Oout;        // forward output pointer (same buffer as O in the forward)
+    float* L;          // forward output
+    const float* Lin;  // backward input
+    const void* dO;
+    float* Dvec;
+    float* dQ;
+    float* dK;
+    float* dV;
+    int B, T, H, HKV, D;
+    float scale;
+    int causal, window;
+    hipStream_t stream;
+};
+
+bool f32_tiles_supported(int bq, int bk);
+hipError_t launch_fwd_f32(const AttnArgs& a, int bq, int bk);
+hipError_t launch_dkdv_f32(const AttnArgs& a, int bq, int bk);
+hipError_t launch_dq_f32(const AttnArgs& a, int bq, int bk);
+
+hipError_t launch_fwd_bf16(const AttnArgs& a);
+hipError_t launch_dkdv_bf16(const AttnArgs& a);
+hipError_t launch_dq_bf16(const AttnArgs& a);
+
+// dtype: 0 = f32, 1 = bf16
+hipError_t launch_bwd_preprocess(const void* O, const void* dO, float* Dvec, int B, int T,
+                                 int H, int D, int dtype, hipStream_t stream);
+
+}  // namespace fa

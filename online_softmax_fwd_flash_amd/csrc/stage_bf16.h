@@ -1,0 +1,151 @@
+// Staging of bf16 [rows x D] tiles from HBM into LDS for the 32x32x16 MFMA kernels, in the
+// natural layout (row-major, a row's 16-byte chunks contiguous) and/or transposed (column
+// major: element (row, d) at [d][pos(row)]).
+//
+// pos() swaps bits 2 and 3 of the row index inside each group of 16 rows.  An MFMA whose
+// contraction runs over rows (keys or queries) takes one operand straight from the 32x32
+// accumulator of an earlier MFMA; lane half g of that accumulator holds rows
+// 8*(r/4) + 4g + r%4 of each 32-row group, and after the swap the 8 rows it pairs with one
+// 16-row k-step sit at 8 consecutive positions, so the other operand is one 16-byte read.
+//
+// Row padding keeps 16 lanes reading 16 different rows conflict-free: a natural row is
+// D + 8 elements (D*2 + 16 bytes) and a transposed row ROWS + 8 elements.
+#pragma once
+
+#include "common.h"
+
+namespace fa {
+
+__device__ __forceinline__ int swap23(int k) {
+    return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
+
+// Element i (0..7) of two 16-byte rows paired into one 32-bit word: (a[i], b[i]).
+__device__ __forceinline__ uint32_t pair_elems(const u32x4& a, const u32x4& b, int i) {
+    const uint32_t x = a[i >> 1], y = b[i >> 1];
+    return (i & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
+}
+
+// A ROWS x D tile loaded as 4-row x 8-column blocks, block index t + p*NT for thread t.
+template <int ROWS, int D, int NT>
+struct Blocks4x8 {
+    static constexpr int RG = ROWS / 4;          // row groups
+    static constexpr int NB = RG * (D / 8);      // blocks in the tile
+    static constexpr int PER = (NB + NT - 1) / NT;
+    static constexpr int LDN = D + 8;            // natural row, elements
+    static constexpr int LDT = ROWS + 8;         // transposed row, elements
+    u32x4 v[PER][4];
+
+    __device__ __forceinline__ void load(const uint16_t* __restrict__ base, int64_t ld, int row0,
+                                         int T) {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int blk = threadIdx.x + p * NT;
+            if (NB % NT == 0 || blk < NB) {
+                const int rg = blk % RG, dc = blk / RG;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int row = row0 + rg * 4 + u;
+                    v[p][u] = row < T ? *reinterpret_cast<const u32x4*>(base + row * ld + dc * 8)
+                                      : u32x4{0u, 0u, 0u, 0u};
+                }
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store_natural(uint16_t* __restrict__ dst) const {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int blk = threadIdx.x + p * NT;
+            if (NB % NT == 0 || blk < NB) {
+                const int rg = blk % RG, dc = blk / RG;
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    *reinterpret_cast<u32x4*>(dst + (rg * 4 + u) * LDN + dc * 8) = v[p][u];
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store_transposed(uint16_t* __restrict__ dst) const {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int blk = threadIdx.x + p * NT;
+            if (NB % NT == 0 || blk < NB) {
+                const int rg = blk % RG, dc = blk / RG;
+                const int pos = (rg * 4 & ~15) | swap23(rg * 4 & 15);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    u32x2 w;
+                    w[0] = pair_elems(v[p][0], v[p][1], i);
+                    w[1] = pair_elems(v[p][2], v[p][3], i);
+                    *reinterpret_cast<u32x2*>(dst + (dc * 8 + i) * LDT + pos) = w;
+                }
+            }
+        }
+    }
+};
+
+// A ROWS x D tile loaded row-major: 16-byte chunk t + p*NT of the tile for thread t
+// (consecutive threads read consecutive bytes of a row), stored in the natural layout.
+template <int ROWS, int D, int NT>
+struct RowChunks {
+    static constexpr int NCH = ROWS * D / 8;
+    static constexpr int PER = (NCH + NT - 1) / NT;
+    static constexpr int LDN = D + 8;
+    u32x4 v[PER];
+
+    __device__ __forceinline__ void load(const uint16_t* __restrict__ base, int64_t ld, int row0,
+                                         int T) {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int e = threadIdx.x + p * NT;
+            if (NCH % NT == 0 || e < NCH) {
+                const int r = e / (D / 8), cc = e % (D / 8);
+                const int row = row0 + r;
+                v[p] = row < T ? *reinterpret_cast<const u32x4*>(base + row * ld + cc * 8)
+                               : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store(uint16_t* __restrict__ dst) const {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int e = threadIdx.x + p * NT;
+            if (NCH % NT == 0 || e < NCH) {
+                const int r = e / (D / 8), cc = e % (D / 8);
+                *reinterpret_cast<u32x4*>(dst + r * LDN + cc * 8) = v[p];
+            }
+        }
+    }
+};
+
+// Work item (query tile, b, h) of a workgroup id for query-tile-major kernels: longest key
+// ranges (last query tiles) first; with GQA (xcd_group), the rep query heads of a KV head
+// get ids congruent mod 8, so the round-robin dispatcher puts them on one XCD together.
+__device__ __forceinline__ void decode_q_work(int id, int nqt, int B, int H, int HKV,
+                                              int xcd_group, int& qt, int& b, int& h) {
+    int rank;
+    if (xcd_group) {
+        const int rep = H / HKV;
+        const int hig = (id >> 3) % rep;
+        const int rest = (id / (8 * rep)) * 8 + (id & 7);
+        rank = rest / (B * HKV);
+        const int grp = rest % (B * HKV);
+        b = grp / HKV;
+        h = (grp % HKV) * rep + hig;
+    } else {
+        rank = id / (B * H);
+        const int bh = id % (B * H);
+        b = bh / H;
+        h = bh % H;
+    }
+    qt = nqt - 1 - rank;
+}
+
+inline int xcd_group_for(int nqt, int B, int H, int HKV) {
+    const int rep = H / HKV;
+    return (rep > 1 && ((long)nqt * B * HKV) % 8 == 0) ? 1 : 0;
+}
+
+}  // namespace fa

@@ -1,0 +1,132 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, rejects invalid
+arguments before touching the GPU, and its host-side block classifier (the same header the
+kernels use) agrees bit for bit with the oracle's brute-force classification."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import online_softmax_fwd_flash_amd as fa
+from online_softmax_fwd_flash_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flash_attn.h")
+
+
+def declared_symbols():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(flash_attn_\w+)\s*\(", src)))
+
+
+def test_header_and_exports_agree():
+    decl = declared_symbols()
+    assert len(decl) >= 12
+    assert sorted(_lib.EXPORTS) == decl
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in decl:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_strings():
+    assert fa.flash_attn_version() == 100
+    assert _lib.status_string(0) == "FA_OK"
+    assert _lib.status_string(2) == "FA_ERR_UNSUPPORTED"
+
+
+A = ctypes.c_void_p(0x1000)       # aligned, never dereferenced: every call below fails validation
+MIS = ctypes.c_void_p(0x1004)
+NUL = ctypes.c_void_p(0)
+S0 = ctypes.c_void_p(0)
+
+GOOD = dict(B=1, T=16, H=4, HKV=2, D=64, scale=0.125, causal=1, window=0, dtype=1)
+
+
+def fwd(ptrs=(A, A, A, A, A), **kw):
+    p = dict(GOOD, **kw)
+    return _lib.lib().flash_attn_fwd(*ptrs, p["B"], p["T"], p["H"], p["HKV"], p["D"], p["scale"],
+                                     p["causal"], p["window"], p["dtype"], S0)
+
+
+def bwd(ptrs=(A,) * 9, **kw):
+    p = dict(GOOD, **kw)
+    return _lib.lib().flash_attn_bwd(*ptrs, p["B"], p["T"], p["H"], p["HKV"], p["D"], p["scale"],
+                                     p["causal"], p["window"], p["dtype"], S0)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), 1), (dict(T=0), 1), (dict(H=0), 1), (dict(HKV=0), 1), (dict(D=0), 1),
+    (dict(H=6, HKV=4), 1), (dict(window=-1), 1), (dict(scale=float("nan")), 1),
+    (dict(scale=float("inf")), 1), (dict(scale=0.0), 1), (dict(scale=-0.5), 1),
+    (dict(causal=2), 1), (dict(dtype=7), 1),
+    (dict(D=96), 2), (dict(D=32), 2), (dict(dtype=0, D=12), 2), (dict(dtype=0, D=136), 2),
+    (dict(T=1 << 30, H=64, D=128), 1),
+])
+def test_fwd_and_bwd_reject_before_launch(kw, code):
+    assert fwd(**kw) == code
+    assert bwd(**kw) == code
+
+
+@pytest.mark.parametrize("which", range(5))
+def test_null_and_misaligned_pointers(which):
+    for bad in (NUL, MIS):
+        ptrs = [A] * 5
+        ptrs[which] = bad
+        assert fwd(tuple(ptrs)) == 1
+        ptrs9 = [A] * 9
+        ptrs9[which + 4] = bad
+        assert bwd(tuple(ptrs9)) == 1
+
+
+def test_bad_tiles_rejected():
+    L = _lib.lib()
+    args = (A, A, A, A, A, 1, 64, 2, 2, 64, 0.125, 1, 0, 0, S0)
+    assert L.flash_attn_fwd_ex(*args, 48, 16) == 1
+    assert L.flash_attn_fwd_ex(*args, 64, 8) == 1
+    args16 = (A, A, A, A, A, 1, 64, 2, 2, 64, 0.125, 1, 0, 1, S0)
+    assert L.flash_attn_fwd_ex(*args16, 64, 64) == 1
+
+
+def test_default_tiles():
+    assert fa.flash_attn_default_tiles(1, 128, 0) == (128, 64)
+    assert fa.flash_attn_default_tiles(0, 8, 0) == (64, 64)
+    with pytest.raises(fa.FlashAttnError):
+        fa.flash_attn_default_tiles(1, 80, 0)
+
+
+CLASS_SWEEP = [(T, bq, bk, c, w) for T in (1, 7, 64, 100, 129, 257, 300)
+               for bq, bk in ((32, 32), (64, 16), (16, 64), (128, 64), (64, 128), (32, 64),
+                              (16, 16), (5, 3))
+               for c, w in ((True, 0), (True, 1), (True, 9), (True, 64), (False, 0),
+                            (False, 5), (True, 1000))]
+
+
+@pytest.mark.parametrize("T,bq,bk,causal,window", CLASS_SWEEP)
+def test_device_classifier_matches_oracle(T, bq, bk, causal, window):
+    cls = oracle.classify_blocks(T, bq, bk, causal, window)
+    for i in range(cls.shape[0]):
+        for j in range(cls.shape[1]):
+            got, off = fa.flash_attn_block_class(T, bq, bk, causal, window, i, j)
+            assert got == cls[i, j], (i, j)
+            assert off == i * bq - j * bk
+        lo, hi = fa.flash_attn_kv_block_range(T, bq, bk, causal, window, i)
+        want = oracle.kv_block_range(i, bq, bk, T, causal, window)
+        assert (lo, hi) == want, i
+
+
+def test_device_partial_offsets_cycle_like_the_graphcore_walk():
+    """Causal masked blocks met by the kernels' loops carry the offsets of the diagonal walk."""
+    for bq, bk in ((64, 16), (32, 32), (16, 64), (128, 64)):
+        T = 4 * np.lcm(bq, bk)
+        seq = []
+        for i in range(T // bq):
+            lo, hi = fa.flash_attn_kv_block_range(T, bq, bk, True, 0, i)
+            for j in range(lo, hi):
+                c, off = fa.flash_attn_block_class(T, bq, bk, True, 0, i, j)
+                if c == 2:
+                    seq.append(off + 1)
+        cyc = oracle.triu_offset_sequence(bq, bk)
+        assert seq == [cyc[n % len(cyc)] for n in range(len(seq))]
