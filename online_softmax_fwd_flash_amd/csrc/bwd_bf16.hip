@@ -61,8 +61,9 @@ struct DkdvStage {
     __device__ __forceinline__ void load(const uint16_t* Qh, const uint16_t* dOh,
                                          const float* Lh, const float* Dh, int64_t ldq, int i,
                                          int T) {
-        q.load(Qh, ldq, i * C::BQ, T);
-        go.load(dOh, ldq, i * C::BQ, T);
+        const uint32_t ldb = (uint32_t)(ldq * 2);
+        q.load(rows_buf(Qh, ldq, T), ldb, i * C::BQ);
+        go.load(rows_buf(dOh, ldq, T), ldb, i * C::BQ);
         const int t = threadIdx.x;
         if (t < C::BQ) {
             const int row = i * C::BQ + t;
@@ -109,6 +110,9 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_bf16_kernel(
     const int64_t ldq = (int64_t)H * D, ldk = (int64_t)HKV * D;
     const bool cz = causal != 0;
     const float c = scale * kLog2e;
+    // queries that see this lane's key: [qlo, qhi] (lanes of keys past T are never stored)
+    const int qlo = cz ? key : 0;
+    const int qhi = min(window > 0 ? key + window - 1 : T - 1, T - 1);
 
     // B operands of S = Q K^T and dP = dO V^T: lane (n, g) holds K/V[key][16*dc + 8g .. +7]
     bf16x8 kreg[C::DC], vreg[C::DC];
@@ -169,12 +173,21 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_bf16_kernel(
             f32x16 sc, dp;
 #pragma unroll
             for (int r = 0; r < 16; ++r) sc[r] = dp[r] = 0.f;
+            // A operands of S and dP, four k-steps issued ahead of their MFMAs
 #pragma unroll
-            for (int dc = 0; dc < C::DC; ++dc) {
-                const bf16x8 aq = *reinterpret_cast<const bf16x8*>(Qn + (qs * 32 + n) * C::LDN + dc * 16 + 8 * g);
-                const bf16x8 ao = *reinterpret_cast<const bf16x8*>(dOn + (qs * 32 + n) * C::LDN + dc * 16 + 8 * g);
-                sc = mfma32x32x16(aq, kreg[dc], sc);
-                dp = mfma32x32x16(ao, vreg[dc], dp);
+            for (int d0 = 0; d0 < C::DC; d0 += 4) {
+                bf16x8 aq[4], ao[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int off = (qs * 32 + n) * C::LDN + (d0 + u) * 16 + 8 * g;
+                    aq[u] = *reinterpret_cast<const bf16x8*>(Qn + off);
+                    ao[u] = *reinterpret_cast<const bf16x8*>(dOn + off);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    sc = mfma32x32x16(aq[u], kreg[d0 + u], sc);
+                    dp = mfma32x32x16(ao[u], vreg[d0 + u], dp);
+                }
             }
             // entry r of lane (n, g): query qr0 + 8*(r/4) + 4g + r%4, key kw0 + n
             bf16x8 pp[2], pd[2];
@@ -185,25 +198,38 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_bf16_kernel(
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int r = 4 * t4 + u;
-                    float p = fast_exp2(fmaf(sc[r], c, -l4[u]));
-                    if (cls == kPartial && !visible(qr0 + 8 * t4 + 4 * g + u, key, T, cz, window))
-                        p = 0.f;
-                    const float ds = p * (dp[r] - d4[u]);
-                    pp[r >> 3][r & 7] = (__bf16)p;
-                    pd[r >> 3][r & 7] = (__bf16)ds;
+                    sc[r] = fast_exp2(fmaf(sc[r], c, -l4[u]));
+                    dp[r] = dp[r] - d4[u];
                 }
+            }
+            if (cls == kPartial) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int qi = qr0 + 8 * (r >> 2) + 4 * g + (r & 3);
+                    if ((unsigned)(qi - qlo) > (unsigned)(qhi - qlo)) sc[r] = 0.f;
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                pp[r >> 3][r & 7] = (__bf16)sc[r];
+                pd[r >> 3][r & 7] = (__bf16)(sc[r] * dp[r]);
             }
             // dV += P^T dO and dK += dS^T Q over the 32 rows, 16 per k-step
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
+            for (int hf = 0; hf < 2; ++hf) {
+                bf16x8 bo[C::NDB], bq[C::NDB];
 #pragma unroll
                 for (int db = 0; db < C::NDB; ++db) {
                     const int off = (db * 32 + n) * C::LDT + qs * 32 + 16 * hf + 8 * g;
-                    const bf16x8 bo = *reinterpret_cast<const bf16x8*>(dOt + off);
-                    const bf16x8 bq = *reinterpret_cast<const bf16x8*>(Qt + off);
-                    dva[db] = mfma32x32x16(pp[hf], bo, dva[db]);
-                    dka[db] = mfma32x32x16(pd[hf], bq, dka[db]);
+                    bo[db] = *reinterpret_cast<const bf16x8*>(dOt + off);
+                    bq[db] = *reinterpret_cast<const bf16x8*>(Qt + off);
                 }
+#pragma unroll
+                for (int db = 0; db < C::NDB; ++db) {
+                    dva[db] = mfma32x32x16(pp[hf], bo[db], dva[db]);
+                    dka[db] = mfma32x32x16(pd[hf], bq[db], dka[db]);
+                }
+            }
         }
         if (more) st.store(smem + ((it + 1) & 1) * C::STAGE);
         __syncthreads();
@@ -248,10 +274,9 @@ struct DqStage {
     using C = DqCfg<D>;
     typename C::KTile k;
     typename C::VTile v;
-    __device__ __forceinline__ void load(const uint16_t* Kh, const uint16_t* Vh, int64_t ldk,
-                                         int j, int T) {
-        k.load(Kh, ldk, j * C::BK, T);
-        v.load(Vh, ldk, j * C::BK, T);
+    __device__ __forceinline__ void load(const Buf& kb, const Buf& vb, uint32_t ldb, int j) {
+        k.load(kb, ldb, j * C::BK);
+        v.load(vb, ldb, j * C::BK);
     }
     __device__ __forceinline__ void store(uint16_t* buf) const {
         k.store_natural(buf);
@@ -279,8 +304,9 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(
     const int wr0 = qt * C::BQ + w * 32;
     const int q = wr0 + n;
     const int64_t ldq = (int64_t)H * D, ldk = (int64_t)HKV * D;
-    const uint16_t* Kh = K + (int64_t)b * T * ldk + (int64_t)hk * D;
-    const uint16_t* Vh = V + (int64_t)b * T * ldk + (int64_t)hk * D;
+    const uint32_t ldk_b = (uint32_t)(ldk * 2);
+    const Buf kbuf = rows_buf(K + (int64_t)b * T * ldk + (int64_t)hk * D, ldk, T);
+    const Buf vbuf = rows_buf(V + (int64_t)b * T * ldk + (int64_t)hk * D, ldk, T);
     const bool cz = causal != 0;
     const float c = scale * kLog2e;
 
@@ -297,6 +323,9 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(
     }
     const float l2 = q < T ? L[((int64_t)b * H + h) * T + q] * kLog2e : kBigLse;
     const float dq_i = q < T ? Dv[((int64_t)b * H + h) * T + q] : 0.f;
+    // keys this query row may see: [klo, khi]
+    const int klo = window > 0 ? q - window + 1 : 0;
+    const int khi = cz ? q : T - 1;
     f32x16 dqa[C::NDB];
 #pragma unroll
     for (int i = 0; i < C::NDB; ++i)
@@ -307,7 +336,7 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(
     kv_block_range(T, qt * C::BQ, qt * C::BQ + C::BQ, C::BK, cz, window, jlo, jhi);
     DqStage<D> st;
     if (jlo < jhi) {
-        st.load(Kh, Vh, ldk, jlo, T);
+        st.load(kbuf, vbuf, ldk_b, jlo);
         st.store(smem);
     }
     __syncthreads();
@@ -315,46 +344,53 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(
     for (int j = jlo; j < jhi; ++j) {
         const uint16_t* buf = smem + ((j - jlo) & 1) * C::STAGE;
         const bool more = j + 1 < jhi;
-        if (more) st.load(Kh, Vh, ldk, j + 1, T);
+        if (more) st.load(kbuf, vbuf, ldk_b, j + 1);
         const int cls = block_class(T, wr0, wr0 + 32, j * C::BK, j * C::BK + C::BK, cz, window);
         if (cls != kSkip) {
             const uint16_t* Kn = buf;
             const uint16_t* Vn = buf + C::OFF_VN;
             const uint16_t* Kt = buf + C::OFF_KT;
             f32x16 s[2], dp[2];
+            bf16x8 pd[4];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb) {
+                // A operands of S^T and dP^T for this 32-key half, issued before the MFMAs
+                bf16x8 ak[C::DC], av[C::DC];
+#pragma unroll
+                for (int dc = 0; dc < C::DC; ++dc) {
+                    const int off = (kb * 32 + n) * C::LDN + dc * 16 + 8 * g;
+                    ak[dc] = *reinterpret_cast<const bf16x8*>(Kn + off);
+                    av[dc] = *reinterpret_cast<const bf16x8*>(Vn + off);
+                }
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[kb][r] = dp[kb][r] = 0.f;
 #pragma unroll
-            for (int dc = 0; dc < C::DC; ++dc)
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const int off = (kb * 32 + n) * C::LDN + dc * 16 + 8 * g;
-                    const bf16x8 ak = *reinterpret_cast<const bf16x8*>(Kn + off);
-                    const bf16x8 av = *reinterpret_cast<const bf16x8*>(Vn + off);
-                    s[kb] = mfma32x32x16(ak, qreg[dc], s[kb]);
-                    dp[kb] = mfma32x32x16(av, oreg[dc], dp[kb]);
+                for (int dc = 0; dc < C::DC; ++dc) {
+                    s[kb] = mfma32x32x16(ak[dc], qreg[dc], s[kb]);
+                    dp[kb] = mfma32x32x16(av[dc], oreg[dc], dp[kb]);
                 }
+            }
+            // A operands of dQ^T += K^T dS^T, read while the softmax runs
+            bf16x8 at[4][C::NDB];
+#pragma unroll
+            for (int kh = 0; kh < 4; ++kh)
+#pragma unroll
+                for (int db = 0; db < C::NDB; ++db)
+                    at[kh][db] = *reinterpret_cast<const bf16x8*>(Kt + (db * 32 + n) * C::LDT + kh * 16 + 8 * g);
             // entry r of lane (n, g) in s[kb]: key j*64 + 32kb + 8*(r/4) + 4g + r%4, query q
-            bf16x8 pd[4];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     float p = fast_exp2(fmaf(s[kb][r], c, -l2));
-                    if (cls == kPartial &&
-                        !visible(q, j * C::BK + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3), T, cz, window))
-                        p = 0.f;
+                    const int kk = j * C::BK + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+                    if (cls == kPartial && (unsigned)(kk - klo) > (unsigned)(khi - klo)) p = 0.f;
                     pd[2 * kb + (r >> 3)][r & 7] = (__bf16)(p * (dp[kb][r] - dq_i));
                 }
 #pragma unroll
             for (int kh = 0; kh < 4; ++kh)
 #pragma unroll
-                for (int db = 0; db < C::NDB; ++db) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kt + (db * 32 + n) * C::LDT + kh * 16 + 8 * g);
-                    dqa[db] = mfma32x32x16(a, pd[kh], dqa[db]);
-                }
+                for (int db = 0; db < C::NDB; ++db) dqa[db] = mfma32x32x16(at[kh][db], pd[kh], dqa[db]);
         }
         if (more) st.store(smem + ((j + 1 - jlo) & 1) * C::STAGE);
         __syncthreads();

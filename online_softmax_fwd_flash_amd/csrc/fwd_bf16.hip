@@ -50,10 +50,9 @@ template <int D>
 struct Stage {
     typename Bf16Fwd<D>::KTile k;
     typename Bf16Fwd<D>::VTile v;
-    __device__ __forceinline__ void load(const uint16_t* Kh, const uint16_t* Vh, int64_t ldk,
-                                         int j, int T) {
-        k.load(Kh, ldk, j * kBK, T);
-        v.load(Vh, ldk, j * kBK, T);
+    __device__ __forceinline__ void load(const Buf& kb, const Buf& vb, uint32_t ld_bytes, int j) {
+        k.load(kb, ld_bytes, j * kBK);
+        v.load(vb, ld_bytes, j * kBK);
     }
     __device__ __forceinline__ void store(uint16_t* buf) const {
         k.store(buf);
@@ -79,21 +78,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const int wr0 = qt * kBQ + w * 32;
     const int q = wr0 + n;
     const int64_t ldq = (int64_t)H * D, ldk = (int64_t)HKV * D;
-    const uint16_t* Kh = K + (int64_t)b * T * ldk + (int64_t)hk * D;
-    const uint16_t* Vh = V + (int64_t)b * T * ldk + (int64_t)hk * D;
+    const uint32_t ldk_b = (uint32_t)(ldk * 2);
+    const Buf kbuf = rows_buf(K + (int64_t)b * T * ldk + (int64_t)hk * D, ldk, T);
+    const Buf vbuf = rows_buf(V + (int64_t)b * T * ldk + (int64_t)hk * D, ldk, T);
     const bool cz = causal != 0;
     const float c = scale * kLog2e;
+    // keys this query row may see: [klo, khi]
+    const int klo = window > 0 ? q - window + 1 : 0;
+    const int khi = cz ? q : T - 1;
 
-    // Q^T operand: lane (n, g) holds Q[q][16*dc + 8*g .. +7]
+    // Q^T operand: lane (n, g) holds Q[q][16*dc + 8*g .. +7] (zero past T)
     bf16x8 qreg[C::DC];
     {
-        const uint16_t* Qq = Q + ((int64_t)b * T + q) * ldq + (int64_t)h * D + 8 * g;
+        const Buf qbuf = rows_buf(Q + (int64_t)b * T * ldq + (int64_t)h * D, ldq, T);
+        const uint32_t off = (uint32_t)q * (uint32_t)(ldq * 2) + 16 * g;
 #pragma unroll
-        for (int dc = 0; dc < C::DC; ++dc) {
-            u32x4 x = q < T ? *reinterpret_cast<const u32x4*>(Qq + dc * 16)
-                            : u32x4{0u, 0u, 0u, 0u};
-            qreg[dc] = __builtin_bit_cast(bf16x8, x);
-        }
+        for (int dc = 0; dc < C::DC; ++dc) qreg[dc] = __builtin_bit_cast(bf16x8, qbuf.load16(off + dc * 32));
     }
     f32x16 oacc[C::NDB];
 #pragma unroll
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
     Stage<D> st;
     if (jlo < jhi) {
-        st.load(Kh, Vh, ldk, jlo, T);
+        st.load(kbuf, vbuf, ldk_b, jlo);
         st.store(smem);
     }
     __syncthreads();
@@ -115,8 +115,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     for (int j = jlo; j < jhi; ++j) {
         const uint16_t* buf = smem + ((j - jlo) & 1) * C::BUF;
         const bool more = j + 1 < jhi;
-        if (more) st.load(Kh, Vh, ldk, j + 1, T);
-
         const int cls = block_class(T, wr0, wr0 + 32, j * kBK, j * kBK + kBK, cz, window);
         if (cls != kSkip) {
             const uint16_t* Ks = buf;
@@ -132,19 +130,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
                 s0 = mfma32x32x16(a0, qreg[dc], s0);
                 s1 = mfma32x32x16(a1, qreg[dc], s1);
             }
+            // next block's K/V global loads fly while this block's softmax and P V run
+            if (more) st.load(kbuf, vbuf, ldk_b, j + 1);
             if (cls == kPartial) {
+                // entry r of lane (n, g): key j*64 + 32*half + 8*(r/4) + 4g + r%4
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int kl = 8 * (r >> 2) + 4 * g + (r & 3);
-                    if (!visible(q, j * kBK + kl, T, cz, window)) s0[r] = -INFINITY;
-                    if (!visible(q, j * kBK + 32 + kl, T, cz, window)) s1[r] = -INFINITY;
+                    const int k0 = j * kBK + 8 * (r >> 2) + 4 * g + (r & 3);
+                    if ((unsigned)(k0 - klo) > (unsigned)(khi - klo)) s0[r] = -INFINITY;
+                    if ((unsigned)(k0 + 32 - klo) > (unsigned)(khi - klo)) s1[r] = -INFINITY;
                 }
             }
-            float mx = kNegMax;
+            float mx = vmax(s0[0], s1[0]);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-            mx = fmaxf(mx, swap_halves(mx));
-            const float mnew = fmaxf(m, mx);
+            for (int r = 1; r < 16; ++r) mx = vmax(mx, vmax(s0[r], s1[r]));
+            mx = vmax(mx, swap_halves(mx));
+            const float mnew = vmax(m, mx);
             // a row whose max is still the -FLT_MAX start rescales on its first visible key
             if (__any(mnew > m && (m == kNegMax || (mnew - m) * c > 8.0f))) {
                 const float corr = fast_exp2((m - mnew) * c);
@@ -153,15 +154,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 #pragma unroll
                 for (int i = 0; i < C::NDB; ++i) oacc[i] *= corr;
             }
-            const float mc = fmaxf(m * c, kNegMax);   // finite even while m = -FLT_MAX
-            float ps = 0.f;
+            const float mc = vmax(m * c, kNegMax);   // finite even while m = -FLT_MAX
+            float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 s0[r] = fast_exp2(fmaf(s0[r], c, -mc));
                 s1[r] = fast_exp2(fmaf(s1[r], c, -mc));
-                ps += s0[r] + s1[r];
+                ps0 += s0[r];
+                ps1 += s1[r];
             }
-            lsum += ps;
+            lsum += ps0 + ps1;
             // P^T operand: 8 keys per 16-key half, element e <-> accumulator entry 8*half + e
             bf16x8 pb[4];
 #pragma unroll
@@ -179,6 +181,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
                         *reinterpret_cast<const bf16x8*>(Vt + (db * 32 + n) * C::VLD + kh * 16 + 8 * g);
                     oacc[db] = mfma32x32x16(a, pb[kh], oacc[db]);
                 }
+        } else if (more) {
+            st.load(kbuf, vbuf, ldk_b, j + 1);
         }
         if (more) st.store(smem + ((j + 1 - jlo) & 1) * C::BUF);
         __syncthreads();

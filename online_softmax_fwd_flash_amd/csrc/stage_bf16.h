@@ -16,6 +16,24 @@
 
 namespace fa {
 
+// Raw buffer resource over [base, base + bytes): loads at offsets >= bytes return zero
+// without touching memory, which zero-fills rows past T with no branch.  Descriptor word 3
+// is the gfx9-family raw-buffer format.
+struct Buf {
+    __amdgpu_buffer_rsrc_t r;
+    __device__ __forceinline__ Buf(const void* base, uint32_t bytes)
+        : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                              0x00020000)) {}
+    __device__ __forceinline__ u32x4 load16(uint32_t off) const {
+        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+    }
+};
+
+// Buffer over rows [0, T) of a head slice whose rows are `ld` elements apart (bf16).
+__device__ __forceinline__ Buf rows_buf(const uint16_t* base, int64_t ld, int T) {
+    return Buf(base, (uint32_t)(T * ld * 2));
+}
+
 __device__ __forceinline__ int swap23(int k) {
     return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
@@ -36,19 +54,16 @@ struct Blocks4x8 {
     static constexpr int LDT = ROWS + 8;         // transposed row, elements
     u32x4 v[PER][4];
 
-    __device__ __forceinline__ void load(const uint16_t* __restrict__ base, int64_t ld, int row0,
-                                         int T) {
+    // rows past the buffer's end read as zero
+    __device__ __forceinline__ void load(const Buf& src, uint32_t ld_bytes, int row0) {
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
             const int blk = threadIdx.x + p * NT;
             if (NB % NT == 0 || blk < NB) {
                 const int rg = blk % RG, dc = blk / RG;
+                const uint32_t off = (uint32_t)(row0 + rg * 4) * ld_bytes + dc * 16;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int row = row0 + rg * 4 + u;
-                    v[p][u] = row < T ? *reinterpret_cast<const u32x4*>(base + row * ld + dc * 8)
-                                      : u32x4{0u, 0u, 0u, 0u};
-                }
+                for (int u = 0; u < 4; ++u) v[p][u] = src.load16(off + u * ld_bytes);
             }
         }
     }
@@ -94,16 +109,13 @@ struct RowChunks {
     static constexpr int LDN = D + 8;
     u32x4 v[PER];
 
-    __device__ __forceinline__ void load(const uint16_t* __restrict__ base, int64_t ld, int row0,
-                                         int T) {
+    __device__ __forceinline__ void load(const Buf& src, uint32_t ld_bytes, int row0) {
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
             const int e = threadIdx.x + p * NT;
             if (NCH % NT == 0 || e < NCH) {
                 const int r = e / (D / 8), cc = e % (D / 8);
-                const int row = row0 + r;
-                v[p] = row < T ? *reinterpret_cast<const u32x4*>(base + row * ld + cc * 8)
-                               : u32x4{0u, 0u, 0u, 0u};
+                v[p] = src.load16((uint32_t)(row0 + r) * ld_bytes + cc * 16);
             }
         }
     }
@@ -142,6 +154,9 @@ __device__ __forceinline__ void decode_q_work(int id, int nqt, int B, int H, int
     }
     qt = nqt - 1 - rank;
 }
+
+// max over an accumulator tile without NaN canonicalisation (v_maximum3_f32)
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 inline int xcd_group_for(int nqt, int B, int H, int HKV) {
     const int rep = H / HKV;
