@@ -19,7 +19,7 @@
 // accumulator columns, so P and dS leave the accumulator already in the layout the next two
 // MFMAs take as their A operand.
 //
-// dQ pass.  Workgroup = 4 waves x 32 query rows of one (b, h) walking its key blocks of 64;
+// dQ pass.  Workgroup = 8 waves x 32 query rows of one (b, h) walking its key blocks of 64;
 // K row-major and transposed plus V row-major in LDS.  S^T = K Q^T and dP^T = V dO^T keep a
 // query per accumulator column, so L and D are per-lane scalars and dS^T feeds
 // dQ^T += K^T dS^T directly, as P^T feeds O^T in the forward.
@@ -254,10 +254,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_bf16_kernel(
 // ------------------------------------------------------------------------------ dQ
 namespace {
 
-template <int D>
+template <int D, int NW>
 struct DqCfg {
-    static constexpr int NT = 256;
-    static constexpr int BQ = 128;    // 4 waves x 32 query rows
+    static constexpr int NT = NW * 64;
+    static constexpr int BQ = NW * 32;   // NW waves x 32 query rows
     static constexpr int BK = 64;     // keys per staged block
     static constexpr int DC = D / 16;
     static constexpr int NDB = D / 32;
@@ -269,9 +269,9 @@ struct DqCfg {
     static constexpr int STAGE = 2 * KN + KT;
 };
 
-template <int D>
+template <int D, int NW>
 struct DqStage {
-    using C = DqCfg<D>;
+    using C = DqCfg<D, NW>;
     typename C::KTile k;
     typename C::VTile v;
     __device__ __forceinline__ void load(const Buf& kb, const Buf& vb, uint32_t ldb, int j) {
@@ -287,13 +287,13 @@ struct DqStage {
 
 }  // namespace
 
-template <int D>
-__global__ __launch_bounds__(256, 1) void dq_bf16_kernel(
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void dq_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ L, const float* __restrict__ Dv, float* __restrict__ dQ, int B,
     int T, int H, int HKV, float scale, int causal, int window, int nqt, int xcd_group) {
-    using C = DqCfg<D>;
+    using C = DqCfg<D, NW>;
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
     int qt, b, h;
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(
 
     int jlo, jhi;
     kv_block_range(T, qt * C::BQ, qt * C::BQ + C::BQ, C::BK, cz, window, jlo, jhi);
-    DqStage<D> st;
+    DqStage<D, NW> st;
     if (jlo < jhi) {
         st.load(kbuf, vbuf, ldk_b, jlo);
         st.store(smem);
@@ -350,47 +350,55 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(
             const uint16_t* Kn = buf;
             const uint16_t* Vn = buf + C::OFF_VN;
             const uint16_t* Kt = buf + C::OFF_KT;
-            f32x16 s[2], dp[2];
-            bf16x8 pd[4];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                // A operands of S^T and dP^T for this 32-key half, issued before the MFMAs
-                bf16x8 ak[C::DC], av[C::DC];
+                f32x16 sk, dk;
 #pragma unroll
-                for (int dc = 0; dc < C::DC; ++dc) {
-                    const int off = (kb * 32 + n) * C::LDN + dc * 16 + 8 * g;
-                    ak[dc] = *reinterpret_cast<const bf16x8*>(Kn + off);
-                    av[dc] = *reinterpret_cast<const bf16x8*>(Vn + off);
+                for (int r = 0; r < 16; ++r) sk[r] = dk[r] = 0.f;
+                // A operands of S^T and dP^T for this 32-key half, four k-steps ahead
+#pragma unroll
+                for (int d0 = 0; d0 < C::DC; d0 += 4) {
+                    bf16x8 ak[4], av[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int off = (kb * 32 + n) * C::LDN + (d0 + u) * 16 + 8 * g;
+                        ak[u] = *reinterpret_cast<const bf16x8*>(Kn + off);
+                        av[u] = *reinterpret_cast<const bf16x8*>(Vn + off);
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        sk = mfma32x32x16(ak[u], qreg[d0 + u], sk);
+                        dk = mfma32x32x16(av[u], oreg[d0 + u], dk);
+                    }
                 }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[kb][r] = dp[kb][r] = 0.f;
-#pragma unroll
-                for (int dc = 0; dc < C::DC; ++dc) {
-                    s[kb] = mfma32x32x16(ak[dc], qreg[dc], s[kb]);
-                    dp[kb] = mfma32x32x16(av[dc], oreg[dc], dp[kb]);
-                }
-            }
-            // A operands of dQ^T += K^T dS^T, read while the softmax runs
-            bf16x8 at[4][C::NDB];
-#pragma unroll
-            for (int kh = 0; kh < 4; ++kh)
-#pragma unroll
-                for (int db = 0; db < C::NDB; ++db)
-                    at[kh][db] = *reinterpret_cast<const bf16x8*>(Kt + (db * 32 + n) * C::LDT + kh * 16 + 8 * g);
-            // entry r of lane (n, g) in s[kb]: key j*64 + 32kb + 8*(r/4) + 4g + r%4, query q
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+                // entry r of lane (n, g): key j*64 + 32kb + 8*(r/4) + 4g + r%4, query q
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float p = fast_exp2(fmaf(s[kb][r], c, -l2));
-                    const int kk = j * C::BK + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-                    if (cls == kPartial && (unsigned)(kk - klo) > (unsigned)(khi - klo)) p = 0.f;
-                    pd[2 * kb + (r >> 3)][r & 7] = (__bf16)(p * (dp[kb][r] - dq_i));
+                    sk[r] = fast_exp2(fmaf(sk[r], c, -l2));
+                    dk[r] = dk[r] - dq_i;
                 }
+                if (cls == kPartial) {
 #pragma unroll
-            for (int kh = 0; kh < 4; ++kh)
+                    for (int r = 0; r < 16; ++r) {
+                        const int kk = j * C::BK + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+                        if ((unsigned)(kk - klo) > (unsigned)(khi - klo)) sk[r] = 0.f;
+                    }
+                }
+                bf16x8 pd[2];
 #pragma unroll
-                for (int db = 0; db < C::NDB; ++db) dqa[db] = mfma32x32x16(at[kh][db], pd[kh], dqa[db]);
+                for (int r = 0; r < 16; ++r) pd[r >> 3][r & 7] = (__bf16)(sk[r] * dk[r]);
+                // dQ^T += K^T dS^T over this half's 32 keys, 16 per k-step
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    bf16x8 at[C::NDB];
+#pragma unroll
+                    for (int db = 0; db < C::NDB; ++db)
+                        at[db] = *reinterpret_cast<const bf16x8*>(
+                            Kt + (db * 32 + n) * C::LDT + kb * 32 + hf * 16 + 8 * g);
+#pragma unroll
+                    for (int db = 0; db < C::NDB; ++db) dqa[db] = mfma32x32x16(at[db], pd[hf], dqa[db]);
+                }
+            }
         }
         if (more) st.store(smem + ((j + 1 - jlo) & 1) * C::STAGE);
         __syncthreads();
@@ -446,16 +454,18 @@ hipError_t launch_dkdv_bf16_t(const AttnArgs& a) {
     return hipGetLastError();
 }
 
+constexpr int kDqWaves = 8;
+
 template <int D>
 hipError_t launch_dq_bf16_t(const AttnArgs& a) {
-    using C = DqCfg<D>;
+    using C = DqCfg<D, kDqWaves>;
     static bool set[kMaxDevices] = {};
     const size_t lds = 2 * C::STAGE * sizeof(uint16_t);
-    hipError_t e = allow_lds(dq_bf16_kernel<D>, lds, set);
+    hipError_t e = allow_lds(dq_bf16_kernel<D, kDqWaves>, lds, set);
     if (e != hipSuccess) return e;
     const int nqt = (a.T + C::BQ - 1) / C::BQ;
     const unsigned grid = (unsigned)nqt * a.B * a.H;
-    hipLaunchKernelGGL((dq_bf16_kernel<D>), dim3(grid), dim3(C::NT), lds, a.stream,
+    hipLaunchKernelGGL((dq_bf16_kernel<D, kDqWaves>), dim3(grid), dim3(C::NT), lds, a.stream,
                        (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
                        (const uint16_t*)a.dO, a.Lin, a.Dvec, a.dQ, a.B, a.T, a.H, a.HKV, a.scale,
                        a.causal, a.window, nqt, xcd_group_for(nqt, a.B, a.H, a.HKV));

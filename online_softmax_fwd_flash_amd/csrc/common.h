@@ -29,6 +29,13 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// D(16x16) += A(16x32) * B(32x16), bf16 inputs, fp32 accumulate.  Lane l supplies A row
+// (l % 16) and B column (l % 16), each with 8 consecutive k of group l / 16; D element r of
+// lane l is row 4*(l/16) + r, column l % 16.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // D(16x16) += A(16x4) * B(4x16), fp32.  Lane l supplies A[l%16][l/16] and B[l/16][l%16];
 // D element r of lane l is row 4*(l/16) + r, column l % 16.
 __device__ __forceinline__ f32x4 mfma16x16x4f32(float a, float b, f32x4 c) {
