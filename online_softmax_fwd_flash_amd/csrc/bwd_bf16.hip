@@ -11,13 +11,11 @@
 // formulas); Graphcore "flash_attention_qkv_packed.cpp", flashAttentionQKVPackedGrad
 // (key-chunk-outer loop with dV += P^T dO, dP = dO V^T, dS, dK += dS^T Q).
 //
-// dK/dV pass.  Workgroup = NW waves x 32 keys of one (b, kv head); it walks every
+// dK/dV pass.  Workgroup = 8 waves x 16 keys of one (b, kv head); it walks every
 // (query head of the group, 64-row query block) pair that sees its keys, Q / dO staged in
 // LDS both row-major (operand of S = Q K^T and dP = dO V^T) and transposed (operand of
 // dV += P^T dO and dK += dS^T Q, rows permuted to match the accumulator layout of P / dS).
-// K and V of the wave's 32 keys stay in registers.  S = Q K^T puts the wave's keys on the
-// accumulator columns, so P and dS leave the accumulator already in the layout the next two
-// MFMAs take as their A operand.
+// K and V of the wave's 16 keys stay in registers.
 //
 // dQ pass.  Workgroup = 8 waves x 32 query rows of one (b, h) walking its key blocks of 64;
 // K row-major and transposed plus V row-major in LDS.  S^T = K Q^T and dP^T = V dO^T keep a
@@ -33,78 +31,112 @@ namespace {
 
 constexpr float kBigLse = 3.0e38f;   // L of a padding row: exp2(s*c - big) = 0
 
+}  // namespace
+
 // ------------------------------------------------------------------------------ dK / dV
-template <int D, int NW>
-struct DkdvCfg {
-    static constexpr int NT = NW * 64;
-    static constexpr int BQ = 64;                      // query rows per staged block
-    static constexpr int KPW = 32;                     // keys per wave
-    static constexpr int BKW = NW * KPW;               // keys per workgroup
-    static constexpr int DC = D / 16;
-    static constexpr int NDB = D / 32;
-    using QTile = Blocks4x8<BQ, D, NT>;
-    static constexpr int LDN = QTile::LDN, LDT = QTile::LDT;
-    static constexpr int QN = BQ * LDN;                // elements of one natural tile
-    static constexpr int QT = D * LDT;                 // elements of one transposed tile
-    // stage layout (bf16 elements): Qn | dOn | Qt | dOt | L (BQ floats) | D (BQ floats)
+// Workgroup = 8 waves x 16 keys of one (b, kv head), two waves per SIMD.  16x16x32 MFMAs: S = Q K^T puts the wave's 16 keys on the accumulator columns and 4
+// query rows per lane, so P and dS of two 16-row blocks concatenate into the A operand of
+// dV += P^T dO and dK += dS^T Q (32 query rows per k-step); the transposed Q / dO tiles
+// store their rows in pos32 order to match.  Per wave: K / V operands 32 registers,
+// dK / dV accumulators 64.
+namespace {
+
+template <int D>
+struct Dkdv16Cfg {
+    static constexpr int NW = 8, NT = 512;
+    static constexpr int KPW = 16, BKW = NW * KPW;   // keys per wave / workgroup
+    static constexpr int BQ = 64;                     // query rows per staged block
+    static constexpr int DS = D / 32;                 // 32-wide k-steps of S and dP
+    static constexpr int NDB = D / 16;                // 16-wide column blocks of dK / dV
+    static constexpr int RG = BQ / 4, DCN = D / 8;    // 4-row groups, 8-column chunks
+    static constexpr int LDN = D + 8, LDT = BQ + 8;   // padded rows (elements)
+    static constexpr int QN = BQ * LDN, QT = D * LDT;
     static constexpr int OFF_DON = QN, OFF_QT = 2 * QN, OFF_DOT = 2 * QN + QT;
-    static constexpr int OFF_L = 2 * QN + 2 * QT;       // element offset of the float arrays
-    static constexpr int STAGE = OFF_L + 4 * BQ;        // 2*BQ floats = 4*BQ bf16 slots
+    static constexpr int OFF_L = 2 * QN + 2 * QT;
+    static constexpr int STAGE = OFF_L + 4 * BQ;      // + 2*BQ floats (L, D)
 };
 
-template <int D, int NW>
-struct DkdvStage {
-    using C = DkdvCfg<D, NW>;
-    typename C::QTile q, go;
+// Threads 0..255 stage Q, threads 256..511 stage dO: one 4-row x 8-column block each.  Lane
+// bits 0-1 pick the column chunk and bits 2-3 the row group, so 16 lanes' row-major 16-byte
+// stores land in 16 different bank groups.
+template <int D>
+struct Dkdv16Stage {
+    using C = Dkdv16Cfg<D>;
+    static constexpr int NBH = C::RG * C::DCN;   // blocks per tile: 256 (D=128), 128 (D=64)
+    static_assert(C::RG == 16 && NBH <= 256, "16 row groups, at most one block per thread");
+    u32x4 v[4];
     float lv, dv;
 
-    __device__ __forceinline__ void load(const uint16_t* Qh, const uint16_t* dOh,
-                                         const float* Lh, const float* Dh, int64_t ldq, int i,
-                                         int T) {
+    __device__ __forceinline__ static void block_of(int t, int& rg, int& dc) {
+        dc = (t & 3) | ((t >> 6) << 2);
+        rg = ((t >> 2) & 3) | (((t >> 4) & 3) << 2);
+    }
+
+    __device__ __forceinline__ void load(const uint16_t* Qh, const uint16_t* dOh, const float* Lh,
+                                         const float* Dh, int64_t ldq, int i, int T) {
+        const int t = threadIdx.x & 255;
+        const uint16_t* base = threadIdx.x < 256 ? Qh : dOh;
+        const Buf src = rows_buf(base, ldq, T);
         const uint32_t ldb = (uint32_t)(ldq * 2);
-        q.load(rows_buf(Qh, ldq, T), ldb, i * C::BQ);
-        go.load(rows_buf(dOh, ldq, T), ldb, i * C::BQ);
-        const int t = threadIdx.x;
-        if (t < C::BQ) {
-            const int row = i * C::BQ + t;
+        int rg, dc;
+        block_of(t, rg, dc);
+        if (t < NBH) {
+            const uint32_t off = (uint32_t)(i * C::BQ + rg * 4) * ldb + dc * 16;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = src.load16(off + u * ldb);
+        }
+        if (threadIdx.x < C::BQ) {
+            const int row = i * C::BQ + threadIdx.x;
             lv = row < T ? Lh[row] * kLog2e : kBigLse;
             dv = row < T ? Dh[row] : 0.f;
         }
     }
 
     __device__ __forceinline__ void store(uint16_t* buf) const {
-        q.store_natural(buf);
-        go.store_natural(buf + C::OFF_DON);
-        q.store_transposed(buf + C::OFF_QT);
-        go.store_transposed(buf + C::OFF_DOT);
-        const int t = threadIdx.x;
-        if (t < C::BQ) {
+        const int t = threadIdx.x & 255;
+        int rg, dc;
+        block_of(t, rg, dc);
+        uint16_t* nat = buf + (threadIdx.x < 256 ? 0 : C::OFF_DON);
+        uint16_t* tra = buf + (threadIdx.x < 256 ? C::OFF_QT : C::OFF_DOT);
+        if (t < NBH) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                *reinterpret_cast<u32x4*>(nat + (rg * 4 + u) * C::LDN + dc * 8) = v[u];
+            const int pos = pos32(rg * 4);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                u32x2 w;
+                w[0] = pair_elems(v[0], v[1], e);
+                w[1] = pair_elems(v[2], v[3], e);
+                *reinterpret_cast<u32x2*>(tra + (dc * 8 + e) * C::LDT + pos) = w;
+            }
+        }
+        if (threadIdx.x < C::BQ) {
             float* f = reinterpret_cast<float*>(buf + C::OFF_L);
-            f[t] = lv;
-            f[C::BQ + t] = dv;
+            f[threadIdx.x] = lv;
+            f[C::BQ + threadIdx.x] = dv;
         }
     }
 };
 
 }  // namespace
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64, 1) void dkdv_bf16_kernel(
+template <int D>
+__global__ __launch_bounds__(512, 1) void dkdv16_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ L, const float* __restrict__ Dv, float* __restrict__ dK,
     float* __restrict__ dV, int B, int T, int H, int HKV, float scale, int causal, int window) {
-    using C = DkdvCfg<D, NW>;
+    using C = Dkdv16Cfg<D>;
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
-    // longest query ranges (first key blocks under causal) first; consecutive ids walk the
-    // (b, kv head) groups, so a group's blocks keep landing on the same XCD
+    // longest query ranges (first key blocks under causal) first
     const int BG = B * HKV;
     const int kt = (int)(blockIdx.x / BG);
     const int bg = blockIdx.x % BG;
     const int b = bg / HKV, hk = bg % HKV, rep = H / HKV;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int n = lane & 31, g = lane >> 5;
+    const int n = lane & 15, g = lane >> 4;
     const int kw0 = kt * C::BKW + w * C::KPW;
     const int key = kw0 + n;
     const int64_t ldq = (int64_t)H * D, ldk = (int64_t)HKV * D;
@@ -114,35 +146,32 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_bf16_kernel(
     const int qlo = cz ? key : 0;
     const int qhi = min(window > 0 ? key + window - 1 : T - 1, T - 1);
 
-    // B operands of S = Q K^T and dP = dO V^T: lane (n, g) holds K/V[key][16*dc + 8g .. +7]
-    bf16x8 kreg[C::DC], vreg[C::DC];
+    // B operands of S = Q K^T and dP = dO V^T: lane (n, g) holds K/V[key][32*ds + 8g .. +7]
+    bf16x8 kreg[C::DS], vreg[C::DS];
     {
-        const uint16_t* Kk = K + ((int64_t)b * T + key) * ldk + (int64_t)hk * D + 8 * g;
-        const uint16_t* Vk = V + ((int64_t)b * T + key) * ldk + (int64_t)hk * D + 8 * g;
+        const Buf kb = rows_buf(K + (int64_t)b * T * ldk + (int64_t)hk * D, ldk, T);
+        const Buf vb = rows_buf(V + (int64_t)b * T * ldk + (int64_t)hk * D, ldk, T);
+        const uint32_t off = (uint32_t)key * (uint32_t)(ldk * 2) + 16 * g;
 #pragma unroll
-        for (int dc = 0; dc < C::DC; ++dc) {
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            kreg[dc] = __builtin_bit_cast(bf16x8, key < T ? *reinterpret_cast<const u32x4*>(Kk + dc * 16) : z);
-            vreg[dc] = __builtin_bit_cast(bf16x8, key < T ? *reinterpret_cast<const u32x4*>(Vk + dc * 16) : z);
+        for (int ds = 0; ds < C::DS; ++ds) {
+            kreg[ds] = __builtin_bit_cast(bf16x8, kb.load16(off + ds * 64));
+            vreg[ds] = __builtin_bit_cast(bf16x8, vb.load16(off + ds * 64));
         }
     }
-    f32x16 dka[C::NDB], dva[C::NDB];
+    f32x4 dka[C::NDB], dva[C::NDB];
 #pragma unroll
-    for (int i = 0; i < C::NDB; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dka[i][r] = dva[i][r] = 0.f;
+    for (int i = 0; i < C::NDB; ++i) dka[i] = dva[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     int ilo, ihi;
     q_block_range(T, kt * C::BKW, kt * C::BKW + C::BKW, C::BQ, cz, window, ilo, ihi);
     const int nqb = ihi - ilo;
     const int niter = rep * nqb;
-
     const uint16_t* Qg = Q + (int64_t)b * T * ldq + (int64_t)hk * rep * D;
     const uint16_t* dOg = dO + (int64_t)b * T * ldq + (int64_t)hk * rep * D;
     const float* Lg = L + ((int64_t)b * H + (int64_t)hk * rep) * T;
     const float* Dg = Dv + ((int64_t)b * H + (int64_t)hk * rep) * T;
 
-    DkdvStage<D, NW> st;
+    Dkdv16Stage<D> st;
     if (niter > 0) {
         st.load(Qg, dOg, Lg, Dg, ldq, ilo, T);
         st.store(smem);
@@ -158,94 +187,84 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_bf16_kernel(
             st.load(Qg + h2 * D, dOg + h2 * D, Lg + (int64_t)h2 * T, Dg + (int64_t)h2 * T, ldq,
                     i2, T);
         }
-        const uint16_t* Qn = buf;
-        const uint16_t* dOn = buf + C::OFF_DON;
-        const uint16_t* Qt = buf + C::OFF_QT;
-        const uint16_t* dOt = buf + C::OFF_DOT;
-        const float* Ls = reinterpret_cast<const float*>(buf + C::OFF_L);
-        const float* Ds = Ls + C::BQ;
-
-#pragma unroll 1
-        for (int qs = 0; qs < C::BQ / 32; ++qs) {
-            const int qr0 = i * C::BQ + qs * 32;
-            const int cls = block_class(T, qr0, qr0 + 32, kw0, kw0 + 32, cz, window);
-            if (cls == kSkip) continue;
-            f32x16 sc, dp;
+        const int qr0 = i * C::BQ;
+        const int cls = block_class(T, qr0, qr0 + C::BQ, kw0, kw0 + C::KPW, cz, window);
+        if (cls != kSkip) {
+            const uint16_t* Qn = buf;
+            const uint16_t* dOn = buf + C::OFF_DON;
+            const uint16_t* Qt = buf + C::OFF_QT;
+            const uint16_t* dOt = buf + C::OFF_DOT;
+            const float* Ls = reinterpret_cast<const float*>(buf + C::OFF_L);
+            const float* Ds = Ls + C::BQ;
+            // S, dP for four 16-row blocks; entry r of lane (n, g): row 16qb + 4g + r, key n
+            f32x4 sc[4], dp[4];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sc[r] = dp[r] = 0.f;
-            // A operands of S and dP, four k-steps issued ahead of their MFMAs
+            for (int qb = 0; qb < 4; ++qb) {
+                sc[qb] = dp[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                bf16x8 aq[C::DS], ao[C::DS];
 #pragma unroll
-            for (int d0 = 0; d0 < C::DC; d0 += 4) {
-                bf16x8 aq[4], ao[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int off = (qs * 32 + n) * C::LDN + (d0 + u) * 16 + 8 * g;
-                    aq[u] = *reinterpret_cast<const bf16x8*>(Qn + off);
-                    ao[u] = *reinterpret_cast<const bf16x8*>(dOn + off);
+                for (int ds = 0; ds < C::DS; ++ds) {
+                    const int off = (qb * 16 + n) * C::LDN + ds * 32 + 8 * g;
+                    aq[ds] = *reinterpret_cast<const bf16x8*>(Qn + off);
+                    ao[ds] = *reinterpret_cast<const bf16x8*>(dOn + off);
                 }
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    sc = mfma32x32x16(aq[u], kreg[d0 + u], sc);
-                    dp = mfma32x32x16(ao[u], vreg[d0 + u], dp);
+                for (int ds = 0; ds < C::DS; ++ds) {
+                    sc[qb] = mfma16x16x32(aq[ds], kreg[ds], sc[qb]);
+                    dp[qb] = mfma16x16x32(ao[ds], vreg[ds], dp[qb]);
                 }
             }
-            // entry r of lane (n, g): query qr0 + 8*(r/4) + 4g + r%4, key kw0 + n
             bf16x8 pp[2], pd[2];
 #pragma unroll
-            for (int t4 = 0; t4 < 4; ++t4) {
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + qs * 32 + 8 * t4 + 4 * g);
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + qs * 32 + 8 * t4 + 4 * g);
+            for (int qb = 0; qb < 4; ++qb) {
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + qb * 16 + 4 * g);
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + qb * 16 + 4 * g);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int r = 4 * t4 + u;
-                    sc[r] = fast_exp2(fmaf(sc[r], c, -l4[u]));
-                    dp[r] = dp[r] - d4[u];
+                for (int r = 0; r < 4; ++r) {
+                    float p = fast_exp2(fmaf(sc[qb][r], c, -l4[r]));
+                    if (cls == kPartial) {
+                        const int qi = qr0 + qb * 16 + 4 * g + r;
+                        p = ((unsigned)(qi - qlo) > (unsigned)(qhi - qlo)) ? 0.f : p;
+                    }
+                    // k-step kk = qb/2 takes rows of blocks 2kk (elements 0-3), 2kk+1 (4-7)
+                    pp[qb >> 1][4 * (qb & 1) + r] = (__bf16)p;
+                    pd[qb >> 1][4 * (qb & 1) + r] = (__bf16)(p * (dp[qb][r] - d4[r]));
                 }
             }
-            if (cls == kPartial) {
+            // dV += P^T dO and dK += dS^T Q, 32 query rows per k-step
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int qi = qr0 + 8 * (r >> 2) + 4 * g + (r & 3);
-                    if ((unsigned)(qi - qlo) > (unsigned)(qhi - qlo)) sc[r] = 0.f;
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int d0 = 0; d0 < C::NDB; d0 += 4) {
+                    bf16x8 bo[4], bq[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int off = ((d0 + u) * 16 + n) * C::LDT + kk * 32 + 8 * g;
+                        bo[u] = *reinterpret_cast<const bf16x8*>(dOt + off);
+                        bq[u] = *reinterpret_cast<const bf16x8*>(Qt + off);
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        dva[d0 + u] = mfma16x16x32(pp[kk], bo[u], dva[d0 + u]);
+                        dka[d0 + u] = mfma16x16x32(pd[kk], bq[u], dka[d0 + u]);
+                    }
                 }
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                pp[r >> 3][r & 7] = (__bf16)sc[r];
-                pd[r >> 3][r & 7] = (__bf16)(sc[r] * dp[r]);
-            }
-            // dV += P^T dO and dK += dS^T Q over the 32 rows, 16 per k-step
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                bf16x8 bo[C::NDB], bq[C::NDB];
-#pragma unroll
-                for (int db = 0; db < C::NDB; ++db) {
-                    const int off = (db * 32 + n) * C::LDT + qs * 32 + 16 * hf + 8 * g;
-                    bo[db] = *reinterpret_cast<const bf16x8*>(dOt + off);
-                    bq[db] = *reinterpret_cast<const bf16x8*>(Qt + off);
-                }
-#pragma unroll
-                for (int db = 0; db < C::NDB; ++db) {
-                    dva[db] = mfma32x32x16(pp[hf], bo[db], dva[db]);
-                    dka[db] = mfma32x32x16(pd[hf], bq[db], dka[db]);
-                }
-            }
         }
         if (more) st.store(smem + ((it + 1) & 1) * C::STAGE);
         __syncthreads();
     }
 
-    // entry r of lane (n, g) in block db: key kw0 + 8*(r/4) + 4g + r%4, column db*32 + n
+    // entry r of lane (n, g) in block db: key kw0 + 4g + r, column db*16 + n
     float* dKg = dK + (int64_t)b * T * ldk + (int64_t)hk * D;
     float* dVg = dV + (int64_t)b * T * ldk + (int64_t)hk * D;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int kk = kw0 + 8 * (r >> 2) + 4 * g + (r & 3);
+    for (int r = 0; r < 4; ++r) {
+        const int kk = kw0 + 4 * g + r;
         if (kk < T) {
 #pragma unroll
             for (int db = 0; db < C::NDB; ++db) {
-                dKg[(int64_t)kk * ldk + db * 32 + n] = dka[db][r] * scale;
-                dVg[(int64_t)kk * ldk + db * 32 + n] = dva[db][r];
+                dKg[(int64_t)kk * ldk + db * 16 + n] = dka[db][r] * scale;
+                dVg[(int64_t)kk * ldk + db * 16 + n] = dva[db][r];
             }
         }
     }
@@ -436,18 +455,16 @@ hipError_t allow_lds(Kern kern, size_t lds, bool* set_flags) {
     return hipSuccess;
 }
 
-constexpr int kDkdvWaves = 4;
-
 template <int D>
-hipError_t launch_dkdv_bf16_t(const AttnArgs& a) {
-    using C = DkdvCfg<D, kDkdvWaves>;
+hipError_t launch_dkdv16_bf16_t(const AttnArgs& a) {
+    using C = Dkdv16Cfg<D>;
     static bool set[kMaxDevices] = {};
     const size_t lds = 2 * C::STAGE * sizeof(uint16_t);
-    hipError_t e = allow_lds(dkdv_bf16_kernel<D, kDkdvWaves>, lds, set);
+    hipError_t e = allow_lds(dkdv16_bf16_kernel<D>, lds, set);
     if (e != hipSuccess) return e;
     const int nkt = (a.T + C::BKW - 1) / C::BKW;
     const unsigned grid = (unsigned)nkt * a.B * a.HKV;
-    hipLaunchKernelGGL((dkdv_bf16_kernel<D, kDkdvWaves>), dim3(grid), dim3(C::NT), lds, a.stream,
+    hipLaunchKernelGGL((dkdv16_bf16_kernel<D>), dim3(grid), dim3(C::NT), lds, a.stream,
                        (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
                        (const uint16_t*)a.dO, a.Lin, a.Dvec, a.dK, a.dV, a.B, a.T, a.H, a.HKV,
                        a.scale, a.causal, a.window);
@@ -475,8 +492,8 @@ hipError_t launch_dq_bf16_t(const AttnArgs& a) {
 }  // namespace
 
 hipError_t launch_dkdv_bf16(const AttnArgs& a) {
-    if (a.D == 64) return launch_dkdv_bf16_t<64>(a);
-    if (a.D == 128) return launch_dkdv_bf16_t<128>(a);
+    if (a.D == 64) return launch_dkdv16_bf16_t<64>(a);
+    if (a.D == 128) return launch_dkdv16_bf16_t<128>(a);
     return hipErrorInvalidValue;
 }
 

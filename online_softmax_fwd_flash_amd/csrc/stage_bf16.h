@@ -158,6 +158,14 @@ __device__ __forceinline__ void decode_q_work(int id, int nqt, int B, int H, int
 // max over an accumulator tile without NaN canonicalisation (v_maximum3_f32)
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
+// Position of row q (0..31) inside a 32-row group of a transposed tile read by 16x16x32
+// MFMAs whose other operand comes from two 16x16 accumulators: lane group g of those holds
+// rows 4g..4g+3 of each 16-row block, so rows {4g + u, 16 + 4g + u} (u = 0..3) must sit at
+// the 8 consecutive positions 8g .. 8g+7.  Four consecutive rows stay consecutive.
+__device__ __forceinline__ int pos32(int q) {
+    return (q & ~31) | ((q & 12) << 1) | ((q & 16) >> 2) | (q & 3);
+}
+
 inline int xcd_group_for(int nqt, int B, int H, int HKV) {
     const int rep = H / HKV;
     return (rep > 1 && ((long)nqt * B * HKV) % 8 == 0) ? 1 : 0;
