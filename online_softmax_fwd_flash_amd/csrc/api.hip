@@ -3,7 +3,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "../../include/flash_attn.h"
+#include "flash_attn.h"
 #include "block_class.h"
 #include "kernels.h"
 

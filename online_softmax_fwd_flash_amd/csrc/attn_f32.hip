@@ -63,7 +63,8 @@ __global__ __launch_bounds__(BQ / 16 * 64) void fwd_f32_kernel(
     const int qt = nqt - 1 - (int)(blockIdx.x / BH);   // longest key ranges first
     const int bh = blockIdx.x % BH;
     const int b = bh / H, h = bh % H, hk = h / (H / HKV);
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index (uniform)
     const int n = lane & 15, g = lane >> 4;
     const int wr0 = qt * BQ + w * 16;
     const int q = wr0 + n;
@@ -179,7 +180,8 @@ __global__ __launch_bounds__(BK / 16 * 64) void dkdv_f32_kernel(
     const int kt = (int)(blockIdx.x / BG);
     const int bg = blockIdx.x % BG;
     const int b = bg / HKV, hk = bg % HKV, rep = H / HKV;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index (uniform)
     const int n = lane & 15, g = lane >> 4;
     const int kw0 = kt * BK + w * 16;
     const int key = kw0 + n;
@@ -288,7 +290,8 @@ __global__ __launch_bounds__(BQ / 16 * 64) void dq_f32_kernel(
     const int qt = nqt - 1 - (int)(blockIdx.x / BH);
     const int bh = blockIdx.x % BH;
     const int b = bh / H, h = bh % H, hk = h / (H / HKV);
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index (uniform)
     const int n = lane & 15, g = lane >> 4;
     const int wr0 = qt * BQ + w * 16;
     const int q = wr0 + n;

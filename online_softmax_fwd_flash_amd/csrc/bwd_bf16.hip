@@ -36,8 +36,8 @@ constexpr float kBigLse = 3.0e38f;   // L of a padding row: exp2(s*c - big) = 0
 // ------------------------------------------------------------------------------ dK / dV
 // Workgroup = 8 waves x 16 keys of one (b, kv head), two waves per SIMD.  16x16x32 MFMAs: S = Q K^T puts the wave's 16 keys on the accumulator columns and 4
 // query rows per lane, so P and dS of two 16-row blocks concatenate into the A operand of
-// dV += P^T dO and dK += dS^T Q (32 query rows per k-step); the transposed Q / dO tiles
-// store their rows in pos32 order to match.  Per wave: K / V operands 32 registers,
+// dV += P^T dO and dK += dS^T Q (32 query rows per k-step), whose B operands come from the
+// same row-major Q / dO tiles through LDS transpose reads.  Per wave: K / V operands 32 registers,
 // dK / dV accumulators 64.
 namespace {
 
@@ -49,16 +49,20 @@ struct Dkdv16Cfg {
     static constexpr int DS = D / 32;                 // 32-wide k-steps of S and dP
     static constexpr int NDB = D / 16;                // 16-wide column blocks of dK / dV
     static constexpr int RG = BQ / 4, DCN = D / 8;    // 4-row groups, 8-column chunks
-    static constexpr int LDN = D + 8, LDT = BQ + 8;   // padded rows (elements)
-    static constexpr int QN = BQ * LDN, QT = D * LDT;
-    static constexpr int OFF_DON = QN, OFF_QT = 2 * QN, OFF_DOT = 2 * QN + QT;
-    static constexpr int OFF_L = 2 * QN + 2 * QT;
+    // Padded row (elements).  Row-major Q / dO tiles serve both operand reads: 16-byte reads
+    // of 16 rows x 2 column groups per half-wave (A of S, dP) and 8-byte transpose reads of
+    // 16 rows x 8 dwords per wave (B of dV, dK).  With 128 LDS banks both are conflict-free
+    // when the row stride is 8 x odd dwords: D + 16 elements (72 or 40 dwords).
+    static constexpr int LDN = D + 16;
+    static constexpr int QN = BQ * LDN;
+    static constexpr int OFF_DON = QN;
+    static constexpr int OFF_L = 2 * QN;
     static constexpr int STAGE = OFF_L + 4 * BQ;      // + 2*BQ floats (L, D)
 };
 
-// Threads 0..255 stage Q, threads 256..511 stage dO: one 4-row x 8-column block each.  Lane
-// bits 0-1 pick the column chunk and bits 2-3 the row group, so 16 lanes' row-major 16-byte
-// stores land in 16 different bank groups.
+// Threads 0..255 stage Q, threads 256..511 stage dO, one 4-row x 8-column block each.  Lane
+// bits 0-2 pick the column chunk and bits 3-6 the row group, so a half-wave's 16-byte stores
+// cover 32 different bank groups (gfx950 LDS has 128 banks).
 template <int D>
 struct Dkdv16Stage {
     using C = Dkdv16Cfg<D>;
@@ -68,19 +72,21 @@ struct Dkdv16Stage {
     float lv, dv;
 
     __device__ __forceinline__ static void block_of(int t, int& rg, int& dc) {
-        dc = (t & 3) | ((t >> 6) << 2);
-        rg = ((t >> 2) & 3) | (((t >> 4) & 3) << 2);
+        dc = (t & 7) | ((t >> 7) << 3);
+        rg = (t >> 3) & 15;
     }
 
     __device__ __forceinline__ void load(const uint16_t* Qh, const uint16_t* dOh, const float* Lh,
                                          const float* Dh, int64_t ldq, int i, int T) {
         const int t = threadIdx.x & 255;
-        const uint16_t* base = threadIdx.x < 256 ? Qh : dOh;
-        const Buf src = rows_buf(base, ldq, T);
+        // waves 0-3 stage Q, waves 4-7 dO: a wave-uniform choice, so the buffer descriptor
+        // stays in scalar registers (no per-lane waterfall over descriptors)
+        const bool is_q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8) == 0;
+        const Buf src = rows_buf(is_q ? Qh : dOh, ldq, T);
         const uint32_t ldb = (uint32_t)(ldq * 2);
-        int rg, dc;
-        block_of(t, rg, dc);
         if (t < NBH) {
+            int rg, dc;
+            block_of(t, rg, dc);
             const uint32_t off = (uint32_t)(i * C::BQ + rg * 4) * ldb + dc * 16;
 #pragma unroll
             for (int u = 0; u < 4; ++u) v[u] = src.load16(off + u * ldb);
@@ -94,22 +100,13 @@ struct Dkdv16Stage {
 
     __device__ __forceinline__ void store(uint16_t* buf) const {
         const int t = threadIdx.x & 255;
-        int rg, dc;
-        block_of(t, rg, dc);
         uint16_t* nat = buf + (threadIdx.x < 256 ? 0 : C::OFF_DON);
-        uint16_t* tra = buf + (threadIdx.x < 256 ? C::OFF_QT : C::OFF_DOT);
         if (t < NBH) {
+            int rg, dc;
+            block_of(t, rg, dc);
 #pragma unroll
             for (int u = 0; u < 4; ++u)
                 *reinterpret_cast<u32x4*>(nat + (rg * 4 + u) * C::LDN + dc * 8) = v[u];
-            const int pos = pos32(rg * 4);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                u32x2 w;
-                w[0] = pair_elems(v[0], v[1], e);
-                w[1] = pair_elems(v[2], v[3], e);
-                *reinterpret_cast<u32x2*>(tra + (dc * 8 + e) * C::LDT + pos) = w;
-            }
         }
         if (threadIdx.x < C::BQ) {
             float* f = reinterpret_cast<float*>(buf + C::OFF_L);
@@ -118,6 +115,24 @@ struct Dkdv16Stage {
         }
     }
 };
+
+// B operand of dV += P^T dO / dK += dS^T Q (K = 32 query rows, N = 16 columns) straight from
+// a row-major tile: lane (i, g) element e holds row 32kk + 16*(e/4) + 4g + e%4 of column
+// 16db + i, matching the order P / dS take as A operand.  Two transpose reads of 4 rows.
+template <int LDN>
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int kk, int db, int lane) {
+    const int j = lane & 15, g = lane >> 4;
+    const uint16_t* p = tile + (32 * kk + 4 * g + (j >> 2)) * LDN + 16 * db + 4 * (j & 3);
+    const bf16x4 lo = lds_read_tr4(p);
+    const bf16x4 hi = lds_read_tr4(p + 16 * LDN);
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        r[e] = lo[e];
+        r[4 + e] = hi[e];
+    }
+    return r;
+}
 
 }  // namespace
 
@@ -135,8 +150,13 @@ __global__ __launch_bounds__(512, 1) void dkdv16_bf16_kernel(
     const int kt = (int)(blockIdx.x / BG);
     const int bg = blockIdx.x % BG;
     const int b = bg / HKV, hk = bg % HKV, rep = H / HKV;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index (uniform)
     const int n = lane & 15, g = lane >> 4;
+    // Waves w and w+4 share a SIMD and leave every barrier in the same phase.  A higher issue
+    // priority for the first four lets one wave run its MFMA phase while the other works
+    // through its VALU / LDS phase, instead of both contending for the same unit.
+    if (w < 4) __builtin_amdgcn_s_setprio(1);
     const int kw0 = kt * C::BKW + w * C::KPW;
     const int key = kw0 + n;
     const int64_t ldq = (int64_t)H * D, ldk = (int64_t)HKV * D;
@@ -164,26 +184,28 @@ __global__ __launch_bounds__(512, 1) void dkdv16_bf16_kernel(
 
     int ilo, ihi;
     q_block_range(T, kt * C::BKW, kt * C::BKW + C::BKW, C::BQ, cz, window, ilo, ihi);
-    const int nqb = ihi - ilo;
-    const int niter = rep * nqb;
+    const int niter = rep * (ihi - ilo);
     const uint16_t* Qg = Q + (int64_t)b * T * ldq + (int64_t)hk * rep * D;
     const uint16_t* dOg = dO + (int64_t)b * T * ldq + (int64_t)hk * rep * D;
     const float* Lg = L + ((int64_t)b * H + (int64_t)hk * rep) * T;
     const float* Dg = Dv + ((int64_t)b * H + (int64_t)hk * rep) * T;
 
+    // Query blocks are walked last-first (heads inner): every key block of a KV group needs
+    // the last query blocks, so the group's co-resident workgroups (same XCD) stream the same
+    // Q / dO blocks at about the same time and share them in L2.
     Dkdv16Stage<D> st;
     if (niter > 0) {
-        st.load(Qg, dOg, Lg, Dg, ldq, ilo, T);
+        st.load(Qg, dOg, Lg, Dg, ldq, ihi - 1, T);
         st.store(smem);
     }
     __syncthreads();
 
     for (int it = 0; it < niter; ++it) {
-        const int i = ilo + it % nqb;
+        const int i = ihi - 1 - it / rep;
         const uint16_t* buf = smem + (it & 1) * C::STAGE;
         const bool more = it + 1 < niter;
         if (more) {
-            const int h2 = (it + 1) / nqb, i2 = ilo + (it + 1) % nqb;
+            const int h2 = (it + 1) % rep, i2 = ihi - 1 - (it + 1) / rep;
             st.load(Qg + h2 * D, dOg + h2 * D, Lg + (int64_t)h2 * T, Dg + (int64_t)h2 * T, ldq,
                     i2, T);
         }
@@ -192,8 +214,6 @@ __global__ __launch_bounds__(512, 1) void dkdv16_bf16_kernel(
         if (cls != kSkip) {
             const uint16_t* Qn = buf;
             const uint16_t* dOn = buf + C::OFF_DON;
-            const uint16_t* Qt = buf + C::OFF_QT;
-            const uint16_t* dOt = buf + C::OFF_DOT;
             const float* Ls = reinterpret_cast<const float*>(buf + C::OFF_L);
             const float* Ds = Ls + C::BQ;
             // S, dP for four 16-row blocks; entry r of lane (n, g): row 16qb + 4g + r, key n
@@ -239,9 +259,8 @@ __global__ __launch_bounds__(512, 1) void dkdv16_bf16_kernel(
                     bf16x8 bo[4], bq[4];
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
-                        const int off = ((d0 + u) * 16 + n) * C::LDT + kk * 32 + 8 * g;
-                        bo[u] = *reinterpret_cast<const bf16x8*>(dOt + off);
-                        bq[u] = *reinterpret_cast<const bf16x8*>(Qt + off);
+                        bo[u] = tr_operand<C::LDN>(dOn, kk, d0 + u, lane);
+                        bq[u] = tr_operand<C::LDN>(Qn, kk, d0 + u, lane);
                     }
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
@@ -318,8 +337,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_bf16_kernel(
     int qt, b, h;
     decode_q_work(blockIdx.x, nqt, B, H, HKV, xcd_group, qt, b, h);
     const int hk = h / (H / HKV);
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index (uniform)
     const int n = lane & 31, g = lane >> 5;
+    if (NW == 8 && w < 4) __builtin_amdgcn_s_setprio(1);   // see the dK/dV kernel
     const int wr0 = qt * C::BQ + w * 32;
     const int q = wr0 + n;
     const int64_t ldq = (int64_t)H * D, ldk = (int64_t)HKV * D;

@@ -42,6 +42,15 @@ __device__ __forceinline__ f32x4 mfma16x16x4f32(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// LDS transpose read (ds_read_b64_tr_b16), per 16-lane group: when lane j of the group reads
+// 4 consecutive bf16 of row r0 + j/4 starting at column c0 + 4*(j%4), lane i receives column
+// c0 + i of rows r0 .. r0+3.  `p` must point into LDS.
+__device__ __forceinline__ bf16x4 lds_read_tr4(const uint16_t* p) {
+    typedef __bf16 v4bf16 __attribute__((ext_vector_type(4)));
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (__attribute__((address_space(3))) v4bf16*)(p));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
