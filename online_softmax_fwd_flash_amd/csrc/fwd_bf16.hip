@@ -14,9 +14,9 @@
 //  * Scores are formed transposed, S^T = K Q^T: the accumulator column (lane % 32) is a query
 //    row, so each query's max / sum are in-lane plus one exchange between wave halves.
 //  * P^T (bf16, RNE) feeds O^T += V^T P^T straight from the accumulator registers.  The
-//    accumulator gives lane half g the keys 8*(r/4) + 4g + r%4 of each 32-key group; V is
-//    staged transposed (Vt[d][key]) with bits 2 and 3 of the key index swapped, which makes
-//    those 8 keys contiguous, so every operand read is one 16-byte LDS load.
+//    accumulator gives lane half g the keys 8*(r/4) + 4g + r%4 of each 32-key group; the
+//    V^T operand in that key order comes from the row-major V tile through two LDS
+//    transpose reads (ds_read_b64_tr_b16) per MFMA, so V needs no transposed copy.
 //  * The running max is rescaled lazily: O and l are only rescaled when some row's max grew
 //    by more than 2^8 (the stale max keeps every exp2 argument below 8, so nothing overflows
 //    and the final O / l and L = m*scale + ln l are exact up to rounding).
@@ -37,12 +37,16 @@ template <int D>
 struct Bf16Fwd {
     static constexpr int DC = D / 16;          // 16-wide k-steps of S^T = K Q^T
     static constexpr int NDB = D / 32;         // 32-row blocks of O^T
-    using KTile = RowChunks<kBK, D, kThreads>;   // K natural [key][d]
-    using VTile = Blocks4x8<kBK, D, kThreads>;   // V transposed [d][pos(key)]
+    // Both tiles row-major [key][d].  K rows are read 16 bytes per lane, 32 rows per
+    // half-wave: an odd stride in 16-byte units (D + 8 elements) is conflict-free on the
+    // 128-bank LDS.  V is read through transpose reads of 8 rows x 16 dwords per wave: a
+    // stride of 16 x odd dwords (D + 32 elements) is conflict-free.
+    using KTile = RowChunks<kBK, D, kThreads, D + 8>;
+    using VTile = RowChunks<kBK, D, kThreads, D + 32>;
     static constexpr int KLD = KTile::LDN;
-    static constexpr int VLD = VTile::LDT;
+    static constexpr int VLD = VTile::LDN;
     static constexpr int KBUF = kBK * KLD;
-    static constexpr int VBUF = D * VLD;
+    static constexpr int VBUF = kBK * VLD;
     static constexpr int BUF = KBUF + VBUF;    // one stage, bf16 elements
 };
 
@@ -56,7 +60,7 @@ struct Stage {
     }
     __device__ __forceinline__ void store(uint16_t* buf) const {
         k.store(buf);
-        v.store_transposed(buf + Bf16Fwd<D>::KBUF);
+        v.store(buf + Bf16Fwd<D>::KBUF);
     }
 };
 
@@ -118,7 +122,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         const int cls = block_class(T, wr0, wr0 + 32, j * kBK, j * kBK + kBK, cz, window);
         if (cls != kSkip) {
             const uint16_t* Ks = buf;
-            const uint16_t* Vt = buf + C::KBUF;
+            const uint16_t* Vs = buf + C::KBUF;
             f32x16 s0, s1;
 #pragma unroll
             for (int r = 0; r < 16; ++r) s0[r] = s1[r] = 0.f;
@@ -177,8 +181,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
             for (int kh = 0; kh < 4; ++kh)
 #pragma unroll
                 for (int db = 0; db < C::NDB; ++db) {
-                    const bf16x8 a =
-                        *reinterpret_cast<const bf16x8*>(Vt + (db * 32 + n) * C::VLD + kh * 16 + 8 * g);
+                    const bf16x8 a = tr_operand32<C::VLD>(Vs, 16 * kh, 32 * db, lane);
                     oacc[db] = mfma32x32x16(a, pb[kh], oacc[db]);
                 }
         } else if (more) {

@@ -102,11 +102,11 @@ struct Blocks4x8 {
 
 // A ROWS x D tile loaded row-major: 16-byte chunk t + p*NT of the tile for thread t
 // (consecutive threads read consecutive bytes of a row), stored in the natural layout.
-template <int ROWS, int D, int NT>
+template <int ROWS, int D, int NT, int LD = D + 8>
 struct RowChunks {
     static constexpr int NCH = ROWS * D / 8;
     static constexpr int PER = (NCH + NT - 1) / NT;
-    static constexpr int LDN = D + 8;
+    static constexpr int LDN = LD;
     u32x4 v[PER];
 
     __device__ __forceinline__ void load(const Buf& src, uint32_t ld_bytes, int row0) {
@@ -157,6 +157,25 @@ __device__ __forceinline__ void decode_q_work(int id, int nqt, int B, int H, int
 
 // max over an accumulator tile without NaN canonicalisation (v_maximum3_f32)
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// A operand (M = 32 columns of a row-major tile, K = 16 rows) of a 32x32x16 MFMA whose B
+// operand comes from a 32x32 accumulator: lane l = 16c + j covers column c0 + 16*(c%2) + j,
+// half g = c/2, and element e holds row r0 + 8*(e/4) + 4g + e%4 -- the row order in which
+// accumulator lane half g holds its rows.  Two LDS transpose reads of 4 rows each.
+template <int LD>
+__device__ __forceinline__ bf16x8 tr_operand32(const uint16_t* tile, int r0, int c0, int lane) {
+    const int j = lane & 15, c = lane >> 4, g = c >> 1;
+    const uint16_t* p = tile + (r0 + 4 * g + (j >> 2)) * LD + c0 + 16 * (c & 1) + 4 * (j & 3);
+    const bf16x4 lo = lds_read_tr4(p);
+    const bf16x4 hi = lds_read_tr4(p + 8 * LD);
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        r[e] = lo[e];
+        r[4 + e] = hi[e];
+    }
+    return r;
+}
 
 // Position of row q (0..31) inside a 32-row group of a transposed tile read by 16x16x32
 // MFMAs whose other operand comes from two 16x16 accumulators: lane group g of those holds
