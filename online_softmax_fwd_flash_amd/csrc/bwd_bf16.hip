@@ -18,7 +18,7 @@
 // K and V of the wave's 16 keys stay in registers.
 //
 // dQ pass.  Workgroup = 8 waves x 32 query rows of one (b, h) walking its key blocks of 64;
-// K row-major and transposed plus V row-major in LDS.  S^T = K Q^T and dP^T = V dO^T keep a
+// K and V row-major in LDS (K twice, at the two strides its two kinds of reads want).  S^T = K Q^T and dP^T = V dO^T keep a
 // query per accumulator column, so L and D are per-lane scalars and dS^T feeds
 // dQ^T += K^T dS^T directly, as P^T feeds O^T in the forward.
 #include "common.h"
@@ -296,30 +296,39 @@ template <int D, int NW>
 struct DqCfg {
     static constexpr int NT = NW * 64;
     static constexpr int BQ = NW * 32;   // NW waves x 32 query rows
-    static constexpr int BK = 64;     // keys per staged block
+    static constexpr int BK = 64;        // keys per staged block
     static constexpr int DC = D / 16;
     static constexpr int NDB = D / 32;
-    using KTile = Blocks4x8<BK, D, NT>;   // K: natural + transposed
-    using VTile = RowChunks<BK, D, NT>;   // V: natural
-    static constexpr int LDN = KTile::LDN, LDT = KTile::LDT;
-    static constexpr int KN = BK * LDN, KT = D * LDT;
-    static constexpr int OFF_VN = KN, OFF_KT = 2 * KN;
-    static constexpr int STAGE = 2 * KN + KT;
+    // Row-major tiles.  K and V are read 16 bytes per lane, 32 rows per half-wave (A of S^T,
+    // dP^T): odd 16-byte stride D + 8.  A second copy of K is read through transpose reads
+    // (A of dQ^T += K^T dS^T), 8 rows x 16 dwords per wave: 16 x odd dword stride D + 32.
+    using KTile = RowChunks<BK, D, NT, D + 8>;
+    static constexpr int LDN = D + 8, LDK2 = D + 32;
+    static constexpr int KN = BK * LDN, K2 = BK * LDK2;
+    static constexpr int OFF_VN = KN, OFF_K2 = 2 * KN;
+    static constexpr int STAGE = 2 * KN + K2;
 };
 
 template <int D, int NW>
 struct DqStage {
     using C = DqCfg<D, NW>;
-    typename C::KTile k;
-    typename C::VTile v;
+    typename C::KTile k, v;
     __device__ __forceinline__ void load(const Buf& kb, const Buf& vb, uint32_t ldb, int j) {
         k.load(kb, ldb, j * C::BK);
         v.load(vb, ldb, j * C::BK);
     }
     __device__ __forceinline__ void store(uint16_t* buf) const {
-        k.store_natural(buf);
+        k.store(buf);
         v.store(buf + C::OFF_VN);
-        k.store_transposed(buf + C::OFF_KT);
+        // second copy of K at the transpose-read stride (same chunk-to-thread mapping)
+#pragma unroll
+        for (int p = 0; p < C::KTile::PER; ++p) {
+            const int e = threadIdx.x + p * C::NT;
+            if (C::KTile::NCH % C::NT == 0 || e < C::KTile::NCH) {
+                const int r = e / (D / 8), cc = e % (D / 8);
+                *reinterpret_cast<u32x4*>(buf + C::OFF_K2 + r * C::LDK2 + cc * 8) = k.v[p];
+            }
+        }
     }
 };
 
@@ -389,7 +398,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_bf16_kernel(
         if (cls != kSkip) {
             const uint16_t* Kn = buf;
             const uint16_t* Vn = buf + C::OFF_VN;
-            const uint16_t* Kt = buf + C::OFF_KT;
+            const uint16_t* K2 = buf + C::OFF_K2;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 f32x16 sk, dk;
@@ -433,8 +442,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_bf16_kernel(
                     bf16x8 at[C::NDB];
 #pragma unroll
                     for (int db = 0; db < C::NDB; ++db)
-                        at[db] = *reinterpret_cast<const bf16x8*>(
-                            Kt + (db * 32 + n) * C::LDT + kb * 32 + hf * 16 + 8 * g);
+                        at[db] = tr_operand32<C::LDK2>(K2, kb * 32 + hf * 16, db * 32, lane);
 #pragma unroll
                     for (int db = 0; db < C::NDB; ++db) dqa[db] = mfma32x32x16(at[db], pd[hf], dqa[db]);
                 }

@@ -1,15 +1,13 @@
-// Staging of bf16 [rows x D] tiles from HBM into LDS for the 32x32x16 MFMA kernels, in the
-// natural layout (row-major, a row's 16-byte chunks contiguous) and/or transposed (column
-// major: element (row, d) at [d][pos(row)]).
+// Staging of bf16 [rows x D] tiles from HBM into row-major LDS tiles for the MFMA kernels,
+// plus the operand-read helpers that work on those tiles.
 //
-// pos() swaps bits 2 and 3 of the row index inside each group of 16 rows.  An MFMA whose
-// contraction runs over rows (keys or queries) takes one operand straight from the 32x32
-// accumulator of an earlier MFMA; lane half g of that accumulator holds rows
-// 8*(r/4) + 4g + r%4 of each 32-row group, and after the swap the 8 rows it pairs with one
-// 16-row k-step sit at 8 consecutive positions, so the other operand is one 16-byte read.
-//
-// Row padding keeps 16 lanes reading 16 different rows conflict-free: a natural row is
-// D + 8 elements (D*2 + 16 bytes) and a transposed row ROWS + 8 elements.
+// gfx950 LDS has 128 four-byte banks.  Measured on MI355X: a 16-byte-per-lane read serves 32
+// lanes per cycle, and an 8-byte transpose read (ds_read_b64_tr_b16) 64 lanes; row strides
+// are padded so that the rows a read touches in one cycle fall on distinct banks.  An MFMA
+// whose contraction runs over rows (keys or queries) takes one operand straight from an
+// earlier accumulator; the other operand, whose rows must be in the accumulator's row order,
+// comes from the same row-major tile through transpose reads, so no transposed copy of any
+// tile is ever stored.
 #pragma once
 
 #include "common.h"
@@ -33,72 +31,6 @@ struct Buf {
 __device__ __forceinline__ Buf rows_buf(const uint16_t* base, int64_t ld, int T) {
     return Buf(base, (uint32_t)(T * ld * 2));
 }
-
-__device__ __forceinline__ int swap23(int k) {
-    return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
-}
-
-// Element i (0..7) of two 16-byte rows paired into one 32-bit word: (a[i], b[i]).
-__device__ __forceinline__ uint32_t pair_elems(const u32x4& a, const u32x4& b, int i) {
-    const uint32_t x = a[i >> 1], y = b[i >> 1];
-    return (i & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
-}
-
-// A ROWS x D tile loaded as 4-row x 8-column blocks, block index t + p*NT for thread t.
-template <int ROWS, int D, int NT>
-struct Blocks4x8 {
-    static constexpr int RG = ROWS / 4;          // row groups
-    static constexpr int NB = RG * (D / 8);      // blocks in the tile
-    static constexpr int PER = (NB + NT - 1) / NT;
-    static constexpr int LDN = D + 8;            // natural row, elements
-    static constexpr int LDT = ROWS + 8;         // transposed row, elements
-    u32x4 v[PER][4];
-
-    // rows past the buffer's end read as zero
-    __device__ __forceinline__ void load(const Buf& src, uint32_t ld_bytes, int row0) {
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int blk = threadIdx.x + p * NT;
-            if (NB % NT == 0 || blk < NB) {
-                const int rg = blk % RG, dc = blk / RG;
-                const uint32_t off = (uint32_t)(row0 + rg * 4) * ld_bytes + dc * 16;
-#pragma unroll
-                for (int u = 0; u < 4; ++u) v[p][u] = src.load16(off + u * ld_bytes);
-            }
-        }
-    }
-
-    __device__ __forceinline__ void store_natural(uint16_t* __restrict__ dst) const {
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int blk = threadIdx.x + p * NT;
-            if (NB % NT == 0 || blk < NB) {
-                const int rg = blk % RG, dc = blk / RG;
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    *reinterpret_cast<u32x4*>(dst + (rg * 4 + u) * LDN + dc * 8) = v[p][u];
-            }
-        }
-    }
-
-    __device__ __forceinline__ void store_transposed(uint16_t* __restrict__ dst) const {
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int blk = threadIdx.x + p * NT;
-            if (NB % NT == 0 || blk < NB) {
-                const int rg = blk % RG, dc = blk / RG;
-                const int pos = (rg * 4 & ~15) | swap23(rg * 4 & 15);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    u32x2 w;
-                    w[0] = pair_elems(v[p][0], v[p][1], i);
-                    w[1] = pair_elems(v[p][2], v[p][3], i);
-                    *reinterpret_cast<u32x2*>(dst + (dc * 8 + i) * LDT + pos) = w;
-                }
-            }
-        }
-    }
-};
 
 // A ROWS x D tile loaded row-major: 16-byte chunk t + p*NT of the tile for thread t
 // (consecutive threads read consecutive bytes of a row), stored in the natural layout.
@@ -175,14 +107,6 @@ __device__ __forceinline__ bf16x8 tr_operand32(const uint16_t* tile, int r0, int
         r[4 + e] = hi[e];
     }
     return r;
-}
-
-// Position of row q (0..31) inside a 32-row group of a transposed tile read by 16x16x32
-// MFMAs whose other operand comes from two 16x16 accumulators: lane group g of those holds
-// rows 4g..4g+3 of each 16-row block, so rows {4g + u, 16 + 4g + u} (u = 0..3) must sit at
-// the 8 consecutive positions 8g .. 8g+7.  Four consecutive rows stay consecutive.
-__device__ __forceinline__ int pos32(int q) {
-    return (q & ~31) | ((q & 12) << 1) | ((q & 16) >> 2) | (q & 3);
 }
 
 inline int xcd_group_for(int nqt, int B, int H, int HKV) {
