@@ -38,8 +38,9 @@
  *
  *  Errors: arguments are validated on the host before anything is enqueued.
  *    FA_ERR_INVALID_ARG  null pointer, B/T/H/HKV/D < 1, H % HKV != 0, window < 0,
- *                        scale not finite or <= 0, misaligned pointer, size overflow,
- *                        tile sizes that are not supported values;
+ *                        scale not finite or <= 0, misaligned pointer, size overflow
+ *                        (B*T*H*D > 2^40 elements, or for bf16 one batch slice of Q/K
+ *                        reaching 2 GiB), tile sizes that are not supported values;
  *    FA_ERR_UNSUPPORTED  a valid request this build has no kernel for (head dim);
  *    FA_ERR_HIP          a HIP runtime error while enqueueing (hipGetLastError).
  *  No C++ exception crosses this interface.

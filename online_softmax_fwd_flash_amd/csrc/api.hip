@@ -31,6 +31,8 @@ fa_status_t check_dims(int B, int T, int H, int HKV, int D, float scale, int cau
         if (D % 8 != 0 || D > 128) return FA_ERR_UNSUPPORTED;
     } else {
         if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+        // the bf16 kernels address one batch slice of a tensor with 32-bit buffer offsets
+        if ((double)T * (H > HKV ? H : HKV) * D * 2.0 >= 2147483648.0) return FA_ERR_INVALID_ARG;
     }
     return FA_OK;
 }

@@ -64,6 +64,7 @@ def bwd(ptrs=(A,) * 9, **kw):
     (dict(causal=2), 1), (dict(dtype=7), 1),
     (dict(D=96), 2), (dict(D=32), 2), (dict(dtype=0, D=12), 2), (dict(dtype=0, D=136), 2),
     (dict(T=1 << 30, H=64, D=128), 1),
+    (dict(T=1 << 24, H=64, HKV=8, D=128), 1),     # bf16 batch slice of Q reaches 2 GiB
 ])
 def test_fwd_and_bwd_reject_before_launch(kw, code):
     assert fwd(**kw) == code
