@@ -11,6 +11,11 @@ FLOP convention: forward 4*B*H*T^2*D (halved when causal), backward 2.5x that; t
 fwd+bwd TFLOP/s, with the forward alone and the fraction of the MI355X dense bf16 MFMA peak
 (2516.6 TFLOP/s = 256 CU x 2.4 GHz x 4096 FLOP/clk) reported beside it.
 
+roofline.traffic is the HBM byte count (read + write) per launch of the dominant kernel, taken
+from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary scaled by a plain device copy of
+known size (`--calibrate-copy` adds that copy to a profiled run); it is null for other
+workloads and whenever the kernel sources no longer match the ones the counters were taken on.
+
 The CPU baseline times the fp64 oracle (a plain materialised-softmax reference) on the host
 cores on a bounded sample of the same workload: whole (batch, KV-head) groups, forward and
 backward, until about 10 s have elapsed.
@@ -27,6 +32,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16 = 2516.6    # TFLOP/s, dense bf16 MFMA (AMD MI355X specification)
 PEAK_FP32 = 157.3     # TFLOP/s, fp32 matrix / vector
+COPY_BYTES = 512 * 1024 * 1024
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_c4_hbm_traffic.md")
+CSRC = os.path.join(ROOT, "online_softmax_fwd_flash_amd", "csrc")
 METRIC = "causal attn TFLOP/s fwd & fwd+bwd (bf16, GQA, T=4096, D=128); % MFMA peak"
 
 
@@ -37,6 +45,35 @@ def visible_pairs(T, causal, window):
     hi = i if causal else np.full(T, T - 1)
     lo = np.maximum(0, i - window + 1) if window > 0 else np.zeros(T, dtype=np.int64)
     return int(np.maximum(0, hi - lo + 1).sum())
+
+
+def kernel_source_hash():
+    """sha256 over the kernel sources (csrc/*.hip and *.h, sorted by name)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch (read + write) of `kernel` on the B=4 H=32 HKV=8 T=4096 D=128 causal
+    workload, from the committed counter summary; None when there is none or when the kernel
+    sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            lines = [ln.split() for ln in fh if ln.strip().startswith("traffic kernel=")]
+    except OSError:
+        return None
+    sha = kernel_source_hash()
+    for parts in lines:
+        kv = dict(p.split("=", 1) for p in parts[1:])
+        if kv.get("kernel") == kernel and kv.get("source_sha256") == sha:
+            return int(kv["read_bytes"]) + int(kv["write_bytes"])
+    return None
 
 
 def cpu_baseline(cfg, budget_s=10.0):
@@ -75,6 +112,9 @@ def main():
     ap.add_argument("--config", default="C4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after timing, copy a 512 MiB device buffer once (a plain copy of known "
+                         "size, for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the path has no multi-GPU component); "
@@ -132,6 +172,14 @@ def main():
             per_kernel[n] += ev[i].elapsed_time(ev[i + 1])
     per_kernel = {n: t / args.steps for n, t in per_kernel.items()}   # ms per launch
 
+    if args.calibrate_copy:
+        src = torch.empty(COPY_BYTES // 4, device=dev, dtype=torch.float32).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     ms_step = wall * 1e3 / args.steps
     ff, bf = fwd_flops(cfg), bwd_flops(cfg)
     fwd_ms = per_kernel["fwd"]
@@ -164,7 +212,8 @@ def main():
     dk_ = kernels[dom]
     roofline = {"bound": dk_["bound"], "achieved": dk_["achieved"],
                 "peak": peak if dk_["bound"] == "mfma" else 8000.0, "unit": dk_["unit"],
-                "frac": dk_["frac"], "traffic": None, "kernel": dom}
+                "frac": dk_["frac"], "kernel": dom,
+                "traffic": measured_traffic(dom) if cfg.name == "C4" else None}
 
     out = {
         "metric": METRIC,
