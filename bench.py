@@ -99,7 +99,8 @@ def cpu_baseline(cfg, budget_s=10.0):
     cores = len(os.sched_getaffinity(0))
     return {"value": per_group * done / dt / 1e12, "unit": "TFLOP/s", "cores": threads or cores,
             "kind": "oracle",
-            "sample": f"{done} of {len(groups)} (batch, kv-head) groups of {cfg.name} "
+            "sample": f"{done} of {len(groups)} (batch, kv-head) groups of the "
+                      f"{cfg.describe()} workload "
                       f"({cfg.H // cfg.HKV} query heads each), fwd+bwd in fp64 numpy, "
                       f"{dt:.1f} s wall; host has {cores} usable cores"}
 
