@@ -10,9 +10,6 @@
 namespace {
 
 constexpr int kF32DefaultBq = 64, kF32DefaultBk = 64;
-constexpr int kBf16FwdBq = 128, kBf16FwdBk = 64;
-constexpr int kBf16DkdvBq = 64, kBf16DkdvBk = 128;
-constexpr int kBf16DqBq = 128, kBf16DqBk = 64;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -105,8 +102,8 @@ fa_status_t flash_attn_default_tiles(fa_dtype_t dtype, int D, int pass, int* bq,
     }
     if (dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARG;
     if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
-    const int tq[3] = {kBf16FwdBq, kBf16DkdvBq, kBf16DqBq};
-    const int tk[3] = {kBf16FwdBk, kBf16DkdvBk, kBf16DqBk};
+    const int tq[3] = {fa::kBf16FwdBq, fa::kBf16DkdvBq, fa::kBf16DqBq};
+    const int tk[3] = {fa::kBf16FwdBk, fa::kBf16DkdvBk, fa::kBf16DqBk};
     *bq = tq[pass];
     *bk = tk[pass];
     return FA_OK;
@@ -124,7 +121,7 @@ fa_status_t flash_attn_fwd_ex(const void* Q, const void* K, const void* V, void*
         if ((s = resolve_f32_tiles(bq, bk)) != FA_OK) return s;
         return hip_status(fa::launch_fwd_f32(a, bq, bk));
     }
-    if (!((bq == 0 && bk == 0) || (bq == kBf16FwdBq && bk == kBf16FwdBk)))
+    if (!((bq == 0 && bk == 0) || (bq == fa::kBf16FwdBq && bk == fa::kBf16FwdBk)))
         return FA_ERR_INVALID_ARG;
     return hip_status(fa::launch_fwd_bf16(a));
 }
@@ -159,7 +156,7 @@ fa_status_t flash_attn_bwd_dkdv(const void* Q, const void* K, const void* V, con
         if ((s = resolve_f32_tiles(bq, bk)) != FA_OK) return s;
         return hip_status(fa::launch_dkdv_f32(a, bq, bk));
     }
-    if (!((bq == 0 && bk == 0) || (bq == kBf16DkdvBq && bk == kBf16DkdvBk)))
+    if (!((bq == 0 && bk == 0) || (bq == fa::kBf16DkdvBq && bk == fa::kBf16DkdvBk)))
         return FA_ERR_INVALID_ARG;
     return hip_status(fa::launch_dkdv_bf16(a));
 }
@@ -178,7 +175,7 @@ fa_status_t flash_attn_bwd_dq(const void* Q, const void* K, const void* V, const
         if ((s = resolve_f32_tiles(bq, bk)) != FA_OK) return s;
         return hip_status(fa::launch_dq_f32(a, bq, bk));
     }
-    if (!((bq == 0 && bk == 0) || (bq == kBf16DqBq && bk == kBf16DqBk)))
+    if (!((bq == 0 && bk == 0) || (bq == fa::kBf16DqBq && bk == fa::kBf16DqBk)))
         return FA_ERR_INVALID_ARG;
     return hip_status(fa::launch_dq_bf16(a));
 }

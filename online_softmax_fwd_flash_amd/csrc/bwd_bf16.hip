@@ -501,6 +501,10 @@ hipError_t launch_dkdv16_bf16_t(const AttnArgs& a) {
 }
 
 constexpr int kDqWaves = 8;
+static_assert(DqCfg<128, kDqWaves>::BQ == kBf16DqBq && DqCfg<128, kDqWaves>::BK == kBf16DqBk,
+              "dQ tiling differs from kernels.h");
+static_assert(Dkdv16Cfg<128>::BQ == kBf16DkdvBq && Dkdv16Cfg<128>::BKW == kBf16DkdvBk,
+              "dK/dV tiling differs from kernels.h");
 
 template <int D>
 hipError_t launch_dq_bf16_t(const AttnArgs& a) {

@@ -32,6 +32,7 @@ namespace fa {
 namespace {
 
 constexpr int kBQ = 128, kBK = 64, kThreads = 256;
+static_assert(kBQ == kBf16FwdBq && kBK == kBf16FwdBk, "forward tiling differs from kernels.h");
 
 template <int D>
 struct Bf16Fwd {

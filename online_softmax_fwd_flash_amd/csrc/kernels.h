@@ -25,6 +25,12 @@ struct AttnArgs {
     hipStream_t stream;
 };
 
+// Tilings of the bf16 kernels: query rows x keys handled per workgroup block.  Each kernel
+// translation unit static_asserts its own constants against these.
+constexpr int kBf16FwdBq = 128, kBf16FwdBk = 64;    // forward: q-tile x staged key block
+constexpr int kBf16DkdvBq = 64, kBf16DkdvBk = 128;  // dK/dV: staged query block x key tile
+constexpr int kBf16DqBq = 256, kBf16DqBk = 64;      // dQ: q-tile x staged key block
+
 bool f32_tiles_supported(int bq, int bk);
 hipError_t launch_fwd_f32(const AttnArgs& a, int bq, int bk);
 hipError_t launch_dkdv_f32(const AttnArgs& a, int bq, int bk);
