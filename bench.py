@@ -48,14 +48,19 @@ def visible_pairs(T, causal, window):
 
 
 def kernel_source_hash():
-    """sha256 over the kernel sources (csrc/*.hip and *.h, sorted by name)."""
+    """sha256 over the kernel sources (csrc/*.hip and *.h, sorted by name), with comments and
+    whitespace removed so that edits to comments alone keep the hash."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in sorted(os.listdir(CSRC)):
         if f.endswith((".hip", ".h")):
+            with open(os.path.join(CSRC, f)) as fh:
+                code = fh.read()
+            code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)
+            code = re.sub(r"//[^\n]*", " ", code)
             h.update(f.encode())
-            with open(os.path.join(CSRC, f), "rb") as fh:
-                h.update(fh.read())
+            h.update(" ".join(code.split()).encode())
     return h.hexdigest()
 
 

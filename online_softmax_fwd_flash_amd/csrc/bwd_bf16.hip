@@ -1,7 +1,6 @@
-// bf16 backward attention for gfx950 (D in {64, 128}): a dK/dV pass and a separate dQ pass,
-// both on bf16 MFMA 32x32x16 with fp32 accumulation; P is recomputed from the stored
-// log-sum-exp, never stored.  Gradients are written once, in fp32, without atomics, so
-// results are deterministic.
+// bf16 backward attention for gfx950 (D in {64, 128}): a dK/dV pass and a separate dQ pass on
+// bf16 MFMA with fp32 accumulation; P is recomputed from the stored log-sum-exp, never stored.
+// Gradients are written once, in fp32, without atomics, so results are deterministic.
 //
 // Method (prior art, other hardware): forge "flash_attention.metal", backward section and the
 // kernels flash_attn_bwd_dq / flash_attn_bwd_dv / flash_attn_bwd_dk (P = exp(s*scale - L),
@@ -11,16 +10,18 @@
 // formulas); Graphcore "flash_attention_qkv_packed.cpp", flashAttentionQKVPackedGrad
 // (key-chunk-outer loop with dV += P^T dO, dP = dO V^T, dS, dK += dS^T Q).
 //
-// dK/dV pass.  Workgroup = 8 waves x 16 keys of one (b, kv head); it walks every
-// (query head of the group, 64-row query block) pair that sees its keys, Q / dO staged in
-// LDS both row-major (operand of S = Q K^T and dP = dO V^T) and transposed (operand of
-// dV += P^T dO and dK += dS^T Q, rows permuted to match the accumulator layout of P / dS).
-// K and V of the wave's 16 keys stay in registers.
+// dK/dV pass (16x16x32 MFMA).  Workgroup = 8 waves x 16 keys of one (b, kv head); it walks
+// every (query head of the group, 64-row query block) pair that sees its keys, last query
+// block first.  Q, dO (row-major) and L, D of a block are staged in LDS, double-buffered.
+// S = Q K^T and dP = dO V^T keep a key per accumulator column, so P and dS leave the
+// accumulators already in the A-operand layout of dV += P^T dO and dK += dS^T Q; the B
+// operands of those (dO and Q with rows in the accumulator's order) come from the row-major
+// tiles through LDS transpose reads.  K and V of the wave's 16 keys stay in registers.
 //
-// dQ pass.  Workgroup = 8 waves x 32 query rows of one (b, h) walking its key blocks of 64;
-// K and V row-major in LDS (K twice, at the two strides its two kinds of reads want).  S^T = K Q^T and dP^T = V dO^T keep a
-// query per accumulator column, so L and D are per-lane scalars and dS^T feeds
-// dQ^T += K^T dS^T directly, as P^T feeds O^T in the forward.
+// dQ pass (32x32x16 MFMA).  Workgroup = 8 waves x 32 query rows of one (b, h) walking its key
+// blocks of 64; K and V row-major in LDS (K twice, at the two strides its two kinds of reads
+// want).  S^T = K Q^T and dP^T = V dO^T keep a query per accumulator column, so L and D are
+// per-lane scalars and dS^T feeds dQ^T += K^T dS^T directly, as P^T feeds O^T in the forward.
 #include "common.h"
 #include "kernels.h"
 #include "stage_bf16.h"
