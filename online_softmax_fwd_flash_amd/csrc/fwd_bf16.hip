@@ -9,8 +9,12 @@
 //
 // gfx950 design
 //  * Workgroup = 4 waves = 128 query rows of one (b, h); wave w owns 32 rows.  Key blocks of
-//    64 are double-buffered in LDS (one barrier per block); the next block's global loads are
-//    issued before the current block's MFMAs so their latency hides behind them.
+//    64 go HBM -> LDS by LDS-DMA (buffer_load ... lds, 16 bytes per lane): no staging
+//    registers and no LDS write instructions.  Two stages: block j + 1 is fetched while
+//    block j is computed; one barrier per block, which does not wait for that fetch.
+//  * K and V tiles are unpadded with XOR-swizzled 16-byte chunks, so that K operand reads
+//    (16 bytes x 32 rows at one chunk) and V transpose reads (8 rows x 4 chunks) are free of
+//    bank conflicts.
 //  * Scores are formed transposed, S^T = K Q^T: the accumulator column (lane % 32) is a query
 //    row, so each query's max / sum are in-lane plus one exchange between wave halves.
 //  * P^T (bf16, RNE) feeds O^T += V^T P^T straight from the accumulator registers.  The
@@ -38,32 +42,27 @@ template <int D>
 struct Bf16Fwd {
     static constexpr int DC = D / 16;          // 16-wide k-steps of S^T = K Q^T
     static constexpr int NDB = D / 32;         // 32-row blocks of O^T
-    // Both tiles row-major [key][d].  K rows are read 16 bytes per lane, 32 rows per
-    // half-wave: an odd stride in 16-byte units (D + 8 elements) is conflict-free on the
-    // 128-bank LDS.  V is read through transpose reads of 8 rows x 16 dwords per wave: a
-    // stride of 16 x odd dwords (D + 32 elements) is conflict-free.
-    using KTile = RowChunks<kBK, D, kThreads, D + 8>;
-    using VTile = RowChunks<kBK, D, kThreads, D + 32>;
-    static constexpr int KLD = KTile::LDN;
-    static constexpr int VLD = VTile::LDN;
-    static constexpr int KBUF = kBK * KLD;
-    static constexpr int VBUF = kBK * VLD;
-    static constexpr int BUF = KBUF + VBUF;    // one stage, bf16 elements
+    static constexpr int ROWB = 2 * D;         // bytes per tile row (unpadded, swizzled)
+    static constexpr int TILEB = kBK * ROWB;   // bytes per K or V tile
+    static constexpr int STAGEB = 2 * TILEB;   // K tile then V tile
+    static constexpr int PPW = TILEB / 1024 / (kThreads / 64);   // DMA pieces per wave per tile
+    static_assert(PPW * 1024 * (kThreads / 64) == TILEB, "tile must split evenly over the waves");
 };
 
+// LDS-DMA of key block jb into stage buffer `stage`: wave wu fills pieces [wu*PPW, +PPW) of
+// the K tile (swizzled for operand-row reads) and of the V tile (swizzled for transpose reads).
 template <int D>
-struct Stage {
-    typename Bf16Fwd<D>::KTile k;
-    typename Bf16Fwd<D>::VTile v;
-    __device__ __forceinline__ void load(const Buf& kb, const Buf& vb, uint32_t ld_bytes, int j) {
-        k.load(kb, ld_bytes, j * kBK);
-        v.load(vb, ld_bytes, j * kBK);
-    }
-    __device__ __forceinline__ void store(uint16_t* buf) const {
-        k.store(buf);
-        v.store(buf + Bf16Fwd<D>::KBUF);
-    }
-};
+__device__ __forceinline__ void fwd_issue(const Buf& kb, const Buf& vb, const uint32_t* koff,
+                                          const uint32_t* voff, char* stage, int wu,
+                                          uint32_t ld_bytes, int jb) {
+    using C = Bf16Fwd<D>;
+    char* base = stage + wu * C::PPW * 1024;
+    const int soff = __builtin_amdgcn_readfirstlane((int)((uint32_t)jb * kBK * ld_bytes));
+#pragma unroll
+    for (int i = 0; i < C::PPW; ++i) dma_piece(kb, base + i * 1024, koff[i], soff);
+#pragma unroll
+    for (int i = 0; i < C::PPW; ++i) dma_piece(vb, base + C::TILEB + i * 1024, voff[i], soff);
+}
 
 }  // namespace
 
@@ -73,7 +72,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ L, int B,
     int T, int H, int HKV, float scale, int causal, int window, int nqt, int xcd_group) {
     using C = Bf16Fwd<D>;
-    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+    extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
 
     int qt, b, h;
     decode_q_work(blockIdx.x, nqt, B, H, HKV, xcd_group, qt, b, h);
@@ -110,86 +109,116 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     int jlo, jhi;
     kv_block_range(T, qt * kBQ, qt * kBQ + kBQ, kBK, cz, window, jlo, jhi);
 
-    Stage<D> st;
-    if (jlo < jhi) {
-        st.load(kbuf, vbuf, ldk_b, jlo);
-        st.store(smem);
+    // LDS-DMA source offsets of this lane in its wave's pieces of a K / V tile
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    uint32_t koff[C::PPW], voff[C::PPW];
+#pragma unroll
+    for (int i = 0; i < C::PPW; ++i) {
+        koff[i] = dma_src_offset<D, false>(w * C::PPW + i, lane, ldk_b);
+        voff[i] = dma_src_offset<D, true>(w * C::PPW + i, lane, ldk_b);
     }
-    __syncthreads();
+    // LDS read offsets inside a stage.  K operand: rows n and 32 + n (same swizzle), chunk
+    // 2*dc + g.  V^T operand via transpose reads: lane 16*cq + jj reads 8 bytes of row
+    // 16*kh + 4*(cq/2) + jj/4 (and 8 rows further) at column 32*db + 16*(cq%2) + 4*(jj%4).
+    uint32_t kaddr[C::DC], vaddr[C::NDB];
+    {
+        const int kx = Swz<D>::k(n);
+#pragma unroll
+        for (int dc = 0; dc < C::DC; ++dc)
+            kaddr[dc] = (uint32_t)(n * C::ROWB + 16 * ((2 * dc + g) ^ kx));
+        const int jj = lane & 15, cq = lane >> 4;
+        const int vr = 4 * (cq >> 1) + (jj >> 2);
+        const int vx = Swz<D>::v(vr) >> 2;
+        const int lo2 = 2 * (cq & 1) + ((jj & 3) >> 1);
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+            vaddr[db] = (uint32_t)(C::TILEB + vr * C::ROWB + 16 * (4 * (db ^ vx) + lo2) +
+                                   8 * (jj & 1));
+    }
+
+    char* sm = reinterpret_cast<char*>(smem);
+    if (jlo < jhi) fwd_issue<D>(kbuf, vbuf, koff, voff, sm, wu, ldk_b, jlo);
 
     for (int j = jlo; j < jhi; ++j) {
-        const uint16_t* buf = smem + ((j - jlo) & 1) * C::BUF;
-        const bool more = j + 1 < jhi;
+        const int stg = (j - jlo) & 1;
+        wait_vmcnt<0>();   // block j's pieces, the only ones in flight
+        // all pieces visible; every wave is done with the other stage (block j - 1)
+        lds_barrier();
+        if (j + 1 < jhi) fwd_issue<D>(kbuf, vbuf, koff, voff, sm + (stg ^ 1) * C::STAGEB, wu, ldk_b, j + 1);
         const int cls = block_class(T, wr0, wr0 + 32, j * kBK, j * kBK + kBK, cz, window);
-        if (cls != kSkip) {
-            const uint16_t* Ks = buf;
-            const uint16_t* Vs = buf + C::KBUF;
-            f32x16 s0, s1;
+        if (cls == kSkip) continue;
+        const char* sb = sm + stg * C::STAGEB;
+        f32x16 s0, s1;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s0[r] = s1[r] = 0.f;
+        for (int r = 0; r < 16; ++r) s0[r] = s1[r] = 0.f;
+        // all K operands of the block first (64 VGPRs), so the LDS latency is paid once
+        bf16x8 ka[C::DC][2];
 #pragma unroll
-            for (int dc = 0; dc < C::DC; ++dc) {
-                const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(Ks + n * C::KLD + dc * 16 + 8 * g);
-                const bf16x8 a1 =
-                    *reinterpret_cast<const bf16x8*>(Ks + (32 + n) * C::KLD + dc * 16 + 8 * g);
-                s0 = mfma32x32x16(a0, qreg[dc], s0);
-                s1 = mfma32x32x16(a1, qreg[dc], s1);
-            }
-            // next block's K/V global loads fly while this block's softmax and P V run
-            if (more) st.load(kbuf, vbuf, ldk_b, j + 1);
-            if (cls == kPartial) {
-                // entry r of lane (n, g): key j*64 + 32*half + 8*(r/4) + 4g + r%4
+        for (int dc = 0; dc < C::DC; ++dc) {
+            ka[dc][0] = *reinterpret_cast<const bf16x8*>(sb + kaddr[dc]);
+            ka[dc][1] = *reinterpret_cast<const bf16x8*>(sb + kaddr[dc] + 32 * C::ROWB);
+        }
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int k0 = j * kBK + 8 * (r >> 2) + 4 * g + (r & 3);
-                    if ((unsigned)(k0 - klo) > (unsigned)(khi - klo)) s0[r] = -INFINITY;
-                    if ((unsigned)(k0 + 32 - klo) > (unsigned)(khi - klo)) s1[r] = -INFINITY;
-                }
-            }
-            float mx = vmax(s0[0], s1[0]);
-#pragma unroll
-            for (int r = 1; r < 16; ++r) mx = vmax(mx, vmax(s0[r], s1[r]));
-            mx = vmax(mx, swap_halves(mx));
-            const float mnew = vmax(m, mx);
-            // a row whose max is still the -FLT_MAX start rescales on its first visible key
-            if (__any(mnew > m && (m == kNegMax || (mnew - m) * c > 8.0f))) {
-                const float corr = fast_exp2((m - mnew) * c);
-                m = mnew;
-                lsum *= corr;
-#pragma unroll
-                for (int i = 0; i < C::NDB; ++i) oacc[i] *= corr;
-            }
-            const float mc = vmax(m * c, kNegMax);   // finite even while m = -FLT_MAX
-            float ps0 = 0.f, ps1 = 0.f;
+        for (int dc = 0; dc < C::DC; ++dc) {
+            s0 = mfma32x32x16(ka[dc][0], qreg[dc], s0);
+            s1 = mfma32x32x16(ka[dc][1], qreg[dc], s1);
+        }
+        if (cls == kPartial) {
+            // entry r of lane (n, g): key j*64 + 32*half + 8*(r/4) + 4g + r%4
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                s0[r] = fast_exp2(fmaf(s0[r], c, -mc));
-                s1[r] = fast_exp2(fmaf(s1[r], c, -mc));
-                ps0 += s0[r];
-                ps1 += s1[r];
+                const int k0 = j * kBK + 8 * (r >> 2) + 4 * g + (r & 3);
+                if ((unsigned)(k0 - klo) > (unsigned)(khi - klo)) s0[r] = -INFINITY;
+                if ((unsigned)(k0 + 32 - klo) > (unsigned)(khi - klo)) s1[r] = -INFINITY;
             }
-            lsum += ps0 + ps1;
-            // P^T operand: 8 keys per 16-key half, element e <-> accumulator entry 8*half + e
-            bf16x8 pb[4];
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    pb[hf][e] = (__bf16)s0[8 * hf + e];
-                    pb[2 + hf][e] = (__bf16)s1[8 * hf + e];
-                }
-#pragma unroll
-            for (int kh = 0; kh < 4; ++kh)
-#pragma unroll
-                for (int db = 0; db < C::NDB; ++db) {
-                    const bf16x8 a = tr_operand32<C::VLD>(Vs, 16 * kh, 32 * db, lane);
-                    oacc[db] = mfma32x32x16(a, pb[kh], oacc[db]);
-                }
-        } else if (more) {
-            st.load(kbuf, vbuf, ldk_b, j + 1);
         }
-        if (more) st.store(smem + ((j + 1 - jlo) & 1) * C::BUF);
-        __syncthreads();
+        float mx = vmax(s0[0], s1[0]);
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = vmax(mx, vmax(s0[r], s1[r]));
+        mx = vmax(mx, swap_halves(mx));
+        const float mnew = vmax(m, mx);
+        // a row whose max is still the -FLT_MAX start rescales on its first visible key
+        if (__any(mnew > m && (m == kNegMax || (mnew - m) * c > 8.0f))) {
+            const float corr = fast_exp2((m - mnew) * c);
+            m = mnew;
+            lsum *= corr;
+#pragma unroll
+            for (int i = 0; i < C::NDB; ++i) oacc[i] *= corr;
+        }
+        const float mc = vmax(m * c, kNegMax);   // finite even while m = -FLT_MAX
+        float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            s0[r] = fast_exp2(fmaf(s0[r], c, -mc));
+            s1[r] = fast_exp2(fmaf(s1[r], c, -mc));
+            ps0 += s0[r];
+            ps1 += s1[r];
+        }
+        lsum += ps0 + ps1;
+        // P^T operand: 8 keys per 16-key half, element e <-> accumulator entry 8*half + e
+        bf16x8 pb[4];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pb[hf][e] = (__bf16)s0[8 * hf + e];
+                pb[2 + hf][e] = (__bf16)s1[8 * hf + e];
+            }
+#pragma unroll
+        for (int kh = 0; kh < 4; ++kh)
+#pragma unroll
+            for (int db = 0; db < C::NDB; ++db) {
+                const char* pv = sb + vaddr[db] + 16 * kh * C::ROWB;
+                const bf16x4 lo = lds_read_tr4(reinterpret_cast<const uint16_t*>(pv));
+                const bf16x4 hi = lds_read_tr4(reinterpret_cast<const uint16_t*>(pv + 8 * C::ROWB));
+                bf16x8 av;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    av[e] = lo[e];
+                    av[4 + e] = hi[e];
+                }
+                oacc[db] = mfma32x32x16(av, pb[kh], oacc[db]);
+            }
     }
 
     lsum += swap_halves(lsum);
@@ -218,7 +247,7 @@ hipError_t launch_fwd_bf16_t(const AttnArgs& a) {
     const int nqt = (a.T + kBQ - 1) / kBQ;
     const unsigned grid = (unsigned)nqt * a.B * a.H;
     const int xcd_group = xcd_group_for(nqt, a.B, a.H, a.HKV);
-    const size_t lds = 2 * C::BUF * sizeof(uint16_t);
+    const size_t lds = 2 * C::STAGEB;
     static bool attr_set[kMaxDevices] = {};
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);

@@ -64,6 +64,56 @@ struct RowChunks {
     }
 };
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// s_waitcnt vmcnt(N) only (gfx9 encoding: vmcnt in [3:0] and [15:14]; expcnt [6:4] and
+// lgkmcnt [11:8] left at their "no wait" maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that does not also wait for outstanding vector-memory loads (which
+// __syncthreads() does); the memory clobber keeps the compiler from moving LDS accesses
+// across it.  Data written to LDS by a wave's LDS-DMA loads is visible to the other waves
+// after the barrier once that wave has waited for those loads (wait_vmcnt).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Unpadded row-major [rows x D] bf16 tile in LDS whose 16-byte chunks are XOR-swizzled per
+// row, filled by LDS-DMA (buffer_load ... lds, 16 bytes per lane: a wave instruction writes
+// 1 KB of consecutive LDS bytes, so padding is impossible and the swizzle does its job).
+// 128 four-byte banks = 512 bytes per bank line = RP rows.
+//  * kswz: for tiles read 16 bytes per lane by 32 lanes at one logical chunk of 32
+//    consecutive rows (MFMA operand rows): rows sharing a bank line position get distinct
+//    chunks.
+//  * vswz: for tiles read with ds_read_b64_tr_b16 (8 consecutive rows x 4 adjacent chunks
+//    per wave): XOR with a multiple of 4 keeps the 4 chunks adjacent and spreads the rows.
+template <int D>
+struct Swz {
+    static constexpr int ROWB = 2 * D;         // bytes per row
+    static constexpr int CPR = D / 8;          // 16-byte chunks per row
+    static constexpr int RP = 512 / ROWB;      // rows per bank line
+    static __device__ __forceinline__ int k(int r) { return (r / RP) % CPR; }
+    static __device__ __forceinline__ int v(int r) { return 4 * ((r / RP) % (CPR / 4)); }
+};
+
+// Byte offset, relative to the tile's first global row, of the 16 bytes lane `lane` moves
+// into slot `lane` of LDS-DMA piece p (tile bytes [p KB, p KB + 1 KB)), for swizzle S.
+template <int D, bool VSWZ>
+__device__ __forceinline__ uint32_t dma_src_offset(int p, int lane, uint32_t ld_bytes) {
+    using S = Swz<D>;
+    const int byte = p * 1024 + 16 * lane;
+    const int r = byte / S::ROWB, pc = (byte % S::ROWB) / 16;
+    return (uint32_t)r * ld_bytes + 16u * (uint32_t)(pc ^ (VSWZ ? S::v(r) : S::k(r)));
+}
+
+// One LDS-DMA piece: 64 lanes x 16 bytes from `src` (voffset per lane, soffset uniform)
+// into the 1 KB of LDS at `dst` (wave-uniform).
+__device__ __forceinline__ void dma_piece(const Buf& src, void* dst, uint32_t voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.r, (lds_ptr_t)dst, 16, voff, soff, 0, 0);
+}
+
 // Work item (query tile, b, h) of a workgroup id for query-tile-major kernels: longest key
 // ranges (last query tiles) first; with GQA (xcd_group), the rep query heads of a KV head
 // get ids congruent mod 8, so the round-robin dispatcher puts them on one XCD together.
