@@ -12,9 +12,10 @@
 //    64 go HBM -> LDS by LDS-DMA (buffer_load ... lds, 16 bytes per lane): no staging
 //    registers and no LDS write instructions.  Two stages: block j + 1 is fetched while
 //    block j is computed; one barrier per block, which does not wait for that fetch.
-//  * K and V tiles are unpadded with XOR-swizzled 16-byte chunks, so that K operand reads
-//    (16 bytes x 32 rows at one chunk) and V transpose reads (8 rows x 4 chunks) are free of
-//    bank conflicts.
+//  * The K tile keeps padded rows (D + 8 elements: 16-byte operand-row reads of consecutive
+//    rows at one chunk are free of bank conflicts; each row's pad slot gets a copy of a valid
+//    chunk); the V tile is unpadded with XOR-swizzled 16-byte chunks for its transpose reads
+//    (8 rows x 4 chunks per wave).
 //  * Scores are formed transposed, S^T = K Q^T: the accumulator column (lane % 32) is a query
 //    row, so each query's max / sum are in-lane plus one exchange between wave halves.
 //  * P^T (bf16, RNE) feeds O^T += V^T P^T straight from the accumulator registers.  The
@@ -42,26 +43,34 @@ template <int D>
 struct Bf16Fwd {
     static constexpr int DC = D / 16;          // 16-wide k-steps of S^T = K Q^T
     static constexpr int NDB = D / 32;         // 32-row blocks of O^T
-    static constexpr int ROWB = 2 * D;         // bytes per tile row (unpadded, swizzled)
-    static constexpr int TILEB = kBK * ROWB;   // bytes per K or V tile
-    static constexpr int STAGEB = 2 * TILEB;   // K tile then V tile
-    static constexpr int PPW = TILEB / 1024 / (kThreads / 64);   // DMA pieces per wave per tile
-    static_assert(PPW * 1024 * (kThreads / 64) == TILEB, "tile must split evenly over the waves");
+    static constexpr int NW = kThreads / 64;
+    // K tile padded (operand-row reads), V tile unpadded and swizzled (transpose reads)
+    static constexpr int KROWB = Pad<D>::ROWB;
+    static constexpr int VROWB = 2 * D;
+    static constexpr int KPIECES = kBK * KROWB / 1024;       // LDS-DMA pieces of 1 KB
+    static constexpr int VPIECES = kBK * VROWB / 1024;
+    static constexpr int KMAX = (KPIECES + NW - 1) / NW;      // K pieces per wave (at most)
+    static constexpr int VPW = VPIECES / NW;                  // V pieces per wave
+    static constexpr int KTILEB = KPIECES * 1024;
+    static constexpr int STAGEB = KTILEB + VPIECES * 1024;    // K tile then V tile
+    static_assert(KPIECES * 1024 == kBK * KROWB, "K tile must be whole pieces");
+    static_assert(VPW * NW == VPIECES, "V tile must split evenly over the waves");
 };
 
-// LDS-DMA of key block jb into stage buffer `stage`: wave wu fills pieces [wu*PPW, +PPW) of
-// the K tile (swizzled for operand-row reads) and of the V tile (swizzled for transpose reads).
+// LDS-DMA of key block jb into stage buffer `stage`: wave wu fills K pieces wu, wu + NW, ...
+// and V pieces [wu*VPW, +VPW).
 template <int D>
 __device__ __forceinline__ void fwd_issue(const Buf& kb, const Buf& vb, const uint32_t* koff,
                                           const uint32_t* voff, char* stage, int wu,
                                           uint32_t ld_bytes, int jb) {
     using C = Bf16Fwd<D>;
-    char* base = stage + wu * C::PPW * 1024;
     const int soff = __builtin_amdgcn_readfirstlane((int)((uint32_t)jb * kBK * ld_bytes));
 #pragma unroll
-    for (int i = 0; i < C::PPW; ++i) dma_piece(kb, base + i * 1024, koff[i], soff);
+    for (int i = 0; i < C::KMAX; ++i)
+        if (wu + i * C::NW < C::KPIECES) dma_piece(kb, stage + (wu + i * C::NW) * 1024, koff[i], soff);
+    char* vbase = stage + C::KTILEB + wu * C::VPW * 1024;
 #pragma unroll
-    for (int i = 0; i < C::PPW; ++i) dma_piece(vb, base + C::TILEB + i * 1024, voff[i], soff);
+    for (int i = 0; i < C::VPW; ++i) dma_piece(vb, vbase + i * 1024, voff[i], soff);
 }
 
 }  // namespace
@@ -111,28 +120,25 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
     // LDS-DMA source offsets of this lane in its wave's pieces of a K / V tile
     const int wu = __builtin_amdgcn_readfirstlane(w);
-    uint32_t koff[C::PPW], voff[C::PPW];
+    uint32_t koff[C::KMAX], voff[C::VPW];
 #pragma unroll
-    for (int i = 0; i < C::PPW; ++i) {
-        koff[i] = dma_src_offset<D, false>(w * C::PPW + i, lane, ldk_b);
-        voff[i] = dma_src_offset<D, true>(w * C::PPW + i, lane, ldk_b);
-    }
-    // LDS read offsets inside a stage.  K operand: rows n and 32 + n (same swizzle), chunk
-    // 2*dc + g.  V^T operand via transpose reads: lane 16*cq + jj reads 8 bytes of row
-    // 16*kh + 4*(cq/2) + jj/4 (and 8 rows further) at column 32*db + 16*(cq%2) + 4*(jj%4).
-    uint32_t kaddr[C::DC], vaddr[C::NDB];
+    for (int i = 0; i < C::KMAX; ++i) koff[i] = dma_src_offset_padded<D>(w + i * C::NW, lane, ldk_b);
+#pragma unroll
+    for (int i = 0; i < C::VPW; ++i) voff[i] = dma_src_offset<D, true>(w * C::VPW + i, lane, ldk_b);
+    // LDS read offsets inside a stage.  K operand: rows n and 32 + n, chunk 2*dc + g (padded
+    // rows: consecutive k-steps are 32 bytes apart).  V^T operand via transpose reads: lane
+    // 16*cq + jj reads 8 bytes of row 16*kh + 4*(cq/2) + jj/4 (and 8 rows further) at
+    // column 32*db + 16*(cq%2) + 4*(jj%4).
+    const uint32_t kaddr = (uint32_t)(n * C::KROWB + 16 * g);
+    uint32_t vaddr[C::NDB];
     {
-        const int kx = Swz<D>::k(n);
-#pragma unroll
-        for (int dc = 0; dc < C::DC; ++dc)
-            kaddr[dc] = (uint32_t)(n * C::ROWB + 16 * ((2 * dc + g) ^ kx));
         const int jj = lane & 15, cq = lane >> 4;
         const int vr = 4 * (cq >> 1) + (jj >> 2);
         const int vx = Swz<D>::v(vr) >> 2;
         const int lo2 = 2 * (cq & 1) + ((jj & 3) >> 1);
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db)
-            vaddr[db] = (uint32_t)(C::TILEB + vr * C::ROWB + 16 * (4 * (db ^ vx) + lo2) +
+            vaddr[db] = (uint32_t)(C::KTILEB + vr * C::VROWB + 16 * (4 * (db ^ vx) + lo2) +
                                    8 * (jj & 1));
     }
 
@@ -151,18 +157,26 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         f32x16 s0, s1;
 #pragma unroll
         for (int r = 0; r < 16; ++r) s0[r] = s1[r] = 0.f;
-        // all K operands of the block first (64 VGPRs), so the LDS latency is paid once
         bf16x8 ka[C::DC][2];
 #pragma unroll
         for (int dc = 0; dc < C::DC; ++dc) {
-            ka[dc][0] = *reinterpret_cast<const bf16x8*>(sb + kaddr[dc]);
-            ka[dc][1] = *reinterpret_cast<const bf16x8*>(sb + kaddr[dc] + 32 * C::ROWB);
+            ka[dc][0] = *reinterpret_cast<const bf16x8*>(sb + kaddr + 32 * dc);
+            ka[dc][1] = *reinterpret_cast<const bf16x8*>(sb + kaddr + 32 * dc + 32 * C::KROWB);
         }
 #pragma unroll
         for (int dc = 0; dc < C::DC; ++dc) {
             s0 = mfma32x32x16(ka[dc][0], qreg[dc], s0);
             s1 = mfma32x32x16(ka[dc][1], qreg[dc], s1);
         }
+        // schedule: the first DC K reads up front, then one read per MFMA, so the LDS
+        // latency hides behind the MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, C::DC, 0);
+#pragma unroll
+        for (int i = 0; i < C::DC; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, C::DC, 0);
         if (cls == kPartial) {
             // entry r of lane (n, g): key j*64 + 32*half + 8*(r/4) + 4g + r%4
 #pragma unroll
@@ -208,9 +222,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         for (int kh = 0; kh < 4; ++kh)
 #pragma unroll
             for (int db = 0; db < C::NDB; ++db) {
-                const char* pv = sb + vaddr[db] + 16 * kh * C::ROWB;
+                const char* pv = sb + vaddr[db] + 16 * kh * C::VROWB;
                 const bf16x4 lo = lds_read_tr4(reinterpret_cast<const uint16_t*>(pv));
-                const bf16x4 hi = lds_read_tr4(reinterpret_cast<const uint16_t*>(pv + 8 * C::ROWB));
+                const bf16x4 hi = lds_read_tr4(reinterpret_cast<const uint16_t*>(pv + 8 * C::VROWB));
                 bf16x8 av;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {

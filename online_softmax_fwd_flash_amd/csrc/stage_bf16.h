@@ -108,10 +108,36 @@ __device__ __forceinline__ uint32_t dma_src_offset(int p, int lane, uint32_t ld_
     return (uint32_t)r * ld_bytes + 16u * (uint32_t)(pc ^ (VSWZ ? S::v(r) : S::k(r)));
 }
 
+// Padded row-major [rows x D] bf16 tile filled by LDS-DMA: rows are D + 8 elements (an odd
+// number of 16-byte chunks) apart, which keeps 16-byte operand-row reads of 16 consecutive
+// rows at one chunk free of bank conflicts (the XOR swizzle above is not, for those reads).
+// Slot s (16 bytes) of the tile is row s / (CPR + 1), chunk s % (CPR + 1); the pad chunk
+// receives a copy of the row's last chunk, so every lane of a piece loads valid bytes.
+template <int D>
+struct Pad {
+    static constexpr int CPR = D / 8;               // data chunks per row
+    static constexpr int ROWB = 16 * (CPR + 1);     // bytes per row
+};
+template <int D>
+__device__ __forceinline__ uint32_t dma_src_offset_padded(int p, int lane, uint32_t ld_bytes) {
+    const int slot = p * 64 + lane;
+    const int r = slot / (Pad<D>::CPR + 1);
+    int cch = slot % (Pad<D>::CPR + 1);
+    if (cch == Pad<D>::CPR) cch = Pad<D>::CPR - 1;
+    return (uint32_t)r * ld_bytes + 16u * (uint32_t)cch;
+}
+
 // One LDS-DMA piece: 64 lanes x 16 bytes from `src` (voffset per lane, soffset uniform)
-// into the 1 KB of LDS at `dst` (wave-uniform).
+// into the 1 KB of LDS at `dst` (wave-uniform).  Issued from asm: the compiler then adds no
+// implicit waits for it (it cannot tell which LDS reads it may alias and would wait for
+// every outstanding load before them); the kernels order it explicitly with wait_vmcnt
+// and lds_barrier.  M0 carries the LDS address; one wait state after writing it.
 __device__ __forceinline__ void dma_piece(const Buf& src, void* dst, uint32_t voff, int soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.r, (lds_ptr_t)dst, 16, voff, soff, 0, 0);
+    const uint32_t lds = (uint32_t)(uintptr_t)(lds_ptr_t)dst;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(src.r), "s"(soff)
+                 : "memory", "m0");
 }
 
 // Work item (query tile, b, h) of a workgroup id for query-tile-major kernels: longest key
