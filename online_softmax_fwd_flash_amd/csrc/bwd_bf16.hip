@@ -10,13 +10,15 @@
 // formulas); Graphcore "flash_attention_qkv_packed.cpp", flashAttentionQKVPackedGrad
 // (key-chunk-outer loop with dV += P^T dO, dP = dO V^T, dS, dK += dS^T Q).
 //
-// dK/dV pass (16x16x32 MFMA).  Workgroup = 8 waves x 16 keys of one (b, kv head); it walks
-// every (query head of the group, 64-row query block) pair that sees its keys, last query
-// block first.  Q, dO (row-major) and L, D of a block are staged in LDS, double-buffered.
-// S = Q K^T and dP = dO V^T keep a key per accumulator column, so P and dS leave the
-// accumulators already in the A-operand layout of dV += P^T dO and dK += dS^T Q; the B
-// operands of those (dO and Q with rows in the accumulator's order) come from the row-major
-// tiles through LDS transpose reads.  K and V of the wave's 16 keys stay in registers.
+// dK/dV pass (16x16x32 MFMA).  Workgroup = 4 waves x 16 keys of one (b, kv head), two
+// workgroups per CU (one's barrier waits are covered by the other's work); it walks every
+// (query head of the group, 64-row query block) pair that sees its keys, last query block
+// first.  Q, dO (row-major, padded rows) and L, D of a block reach LDS by LDS-DMA,
+// double-buffered.  S = Q K^T and dP = dO V^T keep a key per accumulator column, so P and dS
+// leave the accumulators already in the A-operand layout of dV += P^T dO and dK += dS^T Q;
+// the B operands of those (dO and Q with rows in the accumulator's order) come from the
+// row-major tiles through LDS transpose reads.  K and V of the wave's 16 keys stay in
+// registers.
 //
 // dQ pass (32x32x16 MFMA).  Workgroup = 8 waves x 32 query rows of one (b, h) walking its key
 // blocks of 64; K and V row-major in LDS (K twice, at the two strides its two kinds of reads
@@ -44,78 +46,52 @@ namespace {
 
 template <int D>
 struct Dkdv16Cfg {
-    static constexpr int NW = 8, NT = 512;
+    static constexpr int NW = 4, NT = 256;
     static constexpr int KPW = 16, BKW = NW * KPW;   // keys per wave / workgroup
     static constexpr int BQ = 64;                     // query rows per staged block
     static constexpr int DS = D / 32;                 // 32-wide k-steps of S and dP
     static constexpr int NDB = D / 16;                // 16-wide column blocks of dK / dV
-    static constexpr int RG = BQ / 4, DCN = D / 8;    // 4-row groups, 8-column chunks
     // Padded row (elements).  Row-major Q / dO tiles serve both operand reads: 16-byte reads
     // of 16 rows x 2 column groups per half-wave (A of S, dP) and 8-byte transpose reads of
-    // 16 rows x 8 dwords per wave (B of dV, dK).  With 128 LDS banks both are conflict-free
-    // when the row stride is 8 x odd dwords: D + 16 elements (72 or 40 dwords).
-    static constexpr int LDN = D + 16;
-    static constexpr int QN = BQ * LDN;
-    static constexpr int OFF_DON = QN;
-    static constexpr int OFF_L = 2 * QN;
-    static constexpr int STAGE = OFF_L + 4 * BQ;      // + 2*BQ floats (L, D)
+    // 16 rows x 8 dwords per wave (B of dV, dK); both are conflict-free at a row stride of
+    // D + 16 elements.  The tiles reach LDS by LDS-DMA (the pad slots get copies).
+    using PadT = Pad<D, 2>;
+    static constexpr int LDN = PadT::ROWB / 2;
+    static constexpr int TPIECES = BQ * PadT::ROWB / 1024;   // 1 KB pieces per tile
+    static constexpr int OFF_DO = TPIECES * 1024;             // bytes
+    static constexpr int OFF_L = 2 * OFF_DO;                  // 64 floats of L, then 64 of D
+    static constexpr int STAGE = OFF_L + 2 * 256;             // bytes per stage
+    static constexpr int QW = NW / 2;                         // waves per tile
+    static constexpr int PMAX = (TPIECES + QW - 1) / QW;      // pieces per wave (at most)
+    static_assert(TPIECES * 1024 == BQ * PadT::ROWB, "tile must be whole pieces");
 };
 
-// Threads 0..255 stage Q, threads 256..511 stage dO, one 4-row x 8-column block each.  Lane
-// bits 0-2 pick the column chunk and bits 3-6 the row group, so a half-wave's 16-byte stores
-// cover 32 different bank groups (gfx950 LDS has 128 banks).
+// LDS-DMA of the stage of iteration it (query block ihi - 1 - it / rep of head it % rep)
+// into buffer it % 2.  The first half of the waves fill the Q tile (pieces w, w + NW/2, ...),
+// the second half the dO tile; wave 0 also moves the block's L values, wave 1 its D values.
 template <int D>
-struct Dkdv16Stage {
+__device__ __forceinline__ void dkdv16_issue(char* sm, const Buf& qbuf, const Buf& obuf,
+                                             const float* Lg, const float* Dg,
+                                             const uint32_t* voff, int w, int rep, int ihi,
+                                             int T, uint32_t ldq_b, int it) {
     using C = Dkdv16Cfg<D>;
-    static constexpr int NBH = C::RG * C::DCN;   // blocks per tile: 256 (D=128), 128 (D=64)
-    static_assert(C::RG == 16 && NBH <= 256, "16 row groups, at most one block per thread");
-    u32x4 v[4];
-    float lv, dv;
-
-    __device__ __forceinline__ static void block_of(int t, int& rg, int& dc) {
-        dc = (t & 7) | ((t >> 7) << 3);
-        rg = (t >> 3) & 15;
-    }
-
-    __device__ __forceinline__ void load(const uint16_t* Qh, const uint16_t* dOh, const float* Lh,
-                                         const float* Dh, int64_t ldq, int i, int T) {
-        const int t = threadIdx.x & 255;
-        // waves 0-3 stage Q, waves 4-7 dO: a wave-uniform choice, so the buffer descriptor
-        // stays in scalar registers (no per-lane waterfall over descriptors)
-        const bool is_q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8) == 0;
-        const Buf src = rows_buf(is_q ? Qh : dOh, ldq, T);
-        const uint32_t ldb = (uint32_t)(ldq * 2);
-        if (t < NBH) {
-            int rg, dc;
-            block_of(t, rg, dc);
-            const uint32_t off = (uint32_t)(i * C::BQ + rg * 4) * ldb + dc * 16;
+    const int h2 = it % rep, i2 = ihi - 1 - it / rep;
+    char* st = sm + (it & 1) * C::STAGE;
+    const int tso = __builtin_amdgcn_readfirstlane(
+        (int)((uint32_t)i2 * C::BQ * ldq_b + (uint32_t)h2 * D * 2));
+    const int wq = w % C::QW;
+    char* dst = st + (w / C::QW) * C::OFF_DO;
+    const Buf& src = w < C::QW ? qbuf : obuf;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) v[u] = src.load16(off + u * ldb);
-        }
-        if (threadIdx.x < C::BQ) {
-            const int row = i * C::BQ + threadIdx.x;
-            lv = row < T ? Lh[row] * kLog2e : kBigLse;
-            dv = row < T ? Dh[row] : 0.f;
-        }
+    for (int i = 0; i < C::PMAX; ++i)
+        if (wq + C::QW * i < C::TPIECES) dma_piece(src, dst + (wq + C::QW * i) * 1024, voff[i], tso);
+    if (w < 2) {
+        const int rso = __builtin_amdgcn_readfirstlane(i2 * C::BQ * 4);
+        // rows past T read as 0
+        const Buf rb(w == 0 ? Lg + (int64_t)h2 * T : Dg + (int64_t)h2 * T, (uint32_t)T * 4u);
+        dma_dwords(rb, st + C::OFF_L + w * 256, voff[C::PMAX], rso);
     }
-
-    __device__ __forceinline__ void store(uint16_t* buf) const {
-        const int t = threadIdx.x & 255;
-        uint16_t* nat = buf + (threadIdx.x < 256 ? 0 : C::OFF_DON);
-        if (t < NBH) {
-            int rg, dc;
-            block_of(t, rg, dc);
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                *reinterpret_cast<u32x4*>(nat + (rg * 4 + u) * C::LDN + dc * 8) = v[u];
-        }
-        if (threadIdx.x < C::BQ) {
-            float* f = reinterpret_cast<float*>(buf + C::OFF_L);
-            f[threadIdx.x] = lv;
-            f[C::BQ + threadIdx.x] = dv;
-        }
-    }
-};
+}
 
 // B operand of dV += P^T dO / dK += dS^T Q (K = 32 query rows, N = 16 columns) straight from
 // a row-major tile: lane (i, g) element e holds row 32kk + 16*(e/4) + 4g + e%4 of column
@@ -138,13 +114,14 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int kk, int d
 }  // namespace
 
 template <int D>
-__global__ __launch_bounds__(512, 1) void dkdv16_bf16_kernel(
+__global__ __launch_bounds__(256, 2) void dkdv16_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ L, const float* __restrict__ Dv, float* __restrict__ dK,
     float* __restrict__ dV, int B, int T, int H, int HKV, float scale, int causal, int window) {
     using C = Dkdv16Cfg<D>;
-    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+    extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
+    char* sm = reinterpret_cast<char*>(smem);
 
     // longest query ranges (first key blocks under causal) first
     const int BG = B * HKV;
@@ -154,10 +131,6 @@ __global__ __launch_bounds__(512, 1) void dkdv16_bf16_kernel(
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index (uniform)
     const int n = lane & 15, g = lane >> 4;
-    // Waves w and w+4 share a SIMD and leave every barrier in the same phase.  A higher issue
-    // priority for the first four lets one wave run its MFMA phase while the other works
-    // through its VALU / LDS phase, instead of both contending for the same unit.
-    if (w < 4) __builtin_amdgcn_s_setprio(1);
     const int kw0 = kt * C::BKW + w * C::KPW;
     const int key = kw0 + n;
     const int64_t ldq = (int64_t)H * D, ldk = (int64_t)HKV * D;
@@ -186,92 +159,90 @@ __global__ __launch_bounds__(512, 1) void dkdv16_bf16_kernel(
     int ilo, ihi;
     q_block_range(T, kt * C::BKW, kt * C::BKW + C::BKW, C::BQ, cz, window, ilo, ihi);
     const int niter = rep * (ihi - ilo);
-    const uint16_t* Qg = Q + (int64_t)b * T * ldq + (int64_t)hk * rep * D;
-    const uint16_t* dOg = dO + (int64_t)b * T * ldq + (int64_t)hk * rep * D;
+    // one descriptor per tensor over the group's heads: head h2 is h2*D elements further
+    // along each row, rows past T read as zeros
+    const uint32_t ldq_b = (uint32_t)(ldq * 2);
+    const Buf qbuf = rows_buf(Q + (int64_t)b * T * ldq + (int64_t)hk * rep * D, ldq, T);
+    const Buf obuf = rows_buf(dO + (int64_t)b * T * ldq + (int64_t)hk * rep * D, ldq, T);
     const float* Lg = L + ((int64_t)b * H + (int64_t)hk * rep) * T;
     const float* Dg = Dv + ((int64_t)b * H + (int64_t)hk * rep) * T;
+    uint32_t voff[C::PMAX + 1];
+#pragma unroll
+    for (int i = 0; i < C::PMAX; ++i)
+        voff[i] = dma_src_offset_padded<D, 2>(w % C::QW + C::QW * i, lane, ldq_b);
+    voff[C::PMAX] = 4u * (uint32_t)lane;
 
     // Query blocks are walked last-first (heads inner): every key block of a KV group needs
     // the last query blocks, so the group's co-resident workgroups (same XCD) stream the same
     // Q / dO blocks at about the same time and share them in L2.
-    Dkdv16Stage<D> st;
-    if (niter > 0) {
-        st.load(Qg, dOg, Lg, Dg, ldq, ihi - 1, T);
-        st.store(smem);
-    }
-    __syncthreads();
-
+    if (niter > 0) dkdv16_issue<D>(sm, qbuf, obuf, Lg, Dg, voff, w, rep, ihi, T, ldq_b, 0);
     for (int it = 0; it < niter; ++it) {
         const int i = ihi - 1 - it / rep;
-        const uint16_t* buf = smem + (it & 1) * C::STAGE;
-        const bool more = it + 1 < niter;
-        if (more) {
-            const int h2 = (it + 1) % rep, i2 = ihi - 1 - (it + 1) / rep;
-            st.load(Qg + h2 * D, dOg + h2 * D, Lg + (int64_t)h2 * T, Dg + (int64_t)h2 * T, ldq,
-                    i2, T);
-        }
+        wait_vmcnt<0>();   // this stage's pieces, the only loads in flight
+        // every wave's pieces are visible; every wave is done with the other stage
+        lds_barrier();
+        if (it + 1 < niter) dkdv16_issue<D>(sm, qbuf, obuf, Lg, Dg, voff, w, rep, ihi, T, ldq_b, it + 1);
         const int qr0 = i * C::BQ;
         const int cls = block_class(T, qr0, qr0 + C::BQ, kw0, kw0 + C::KPW, cz, window);
-        if (cls != kSkip) {
-            const uint16_t* Qn = buf;
-            const uint16_t* dOn = buf + C::OFF_DON;
-            const float* Ls = reinterpret_cast<const float*>(buf + C::OFF_L);
-            const float* Ds = Ls + C::BQ;
-            // S, dP for four 16-row blocks; entry r of lane (n, g): row 16qb + 4g + r, key n
-            f32x4 sc[4], dp[4];
+        if (cls == kSkip) continue;
+        const char* stg = sm + (it & 1) * C::STAGE;
+        const uint16_t* Qn = reinterpret_cast<const uint16_t*>(stg);
+        const uint16_t* dOn = reinterpret_cast<const uint16_t*>(stg + C::OFF_DO);
+        const float* Ls = reinterpret_cast<const float*>(stg + C::OFF_L);
+        const float* Ds = Ls + C::BQ;
+        // S, dP for four 16-row blocks; entry r of lane (n, g): row 16qb + 4g + r, key n
+        f32x4 sc[4], dp[4];
 #pragma unroll
-            for (int qb = 0; qb < 4; ++qb) {
-                sc[qb] = dp[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                bf16x8 aq[C::DS], ao[C::DS];
+        for (int qb = 0; qb < 4; ++qb) {
+            sc[qb] = dp[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            bf16x8 aq[C::DS], ao[C::DS];
 #pragma unroll
-                for (int ds = 0; ds < C::DS; ++ds) {
-                    const int off = (qb * 16 + n) * C::LDN + ds * 32 + 8 * g;
-                    aq[ds] = *reinterpret_cast<const bf16x8*>(Qn + off);
-                    ao[ds] = *reinterpret_cast<const bf16x8*>(dOn + off);
-                }
-#pragma unroll
-                for (int ds = 0; ds < C::DS; ++ds) {
-                    sc[qb] = mfma16x16x32(aq[ds], kreg[ds], sc[qb]);
-                    dp[qb] = mfma16x16x32(ao[ds], vreg[ds], dp[qb]);
-                }
+            for (int ds = 0; ds < C::DS; ++ds) {
+                const int off = (qb * 16 + n) * C::LDN + ds * 32 + 8 * g;
+                aq[ds] = *reinterpret_cast<const bf16x8*>(Qn + off);
+                ao[ds] = *reinterpret_cast<const bf16x8*>(dOn + off);
             }
-            bf16x8 pp[2], pd[2];
 #pragma unroll
-            for (int qb = 0; qb < 4; ++qb) {
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + qb * 16 + 4 * g);
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + qb * 16 + 4 * g);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float p = fast_exp2(fmaf(sc[qb][r], c, -l4[r]));
-                    if (cls == kPartial) {
-                        const int qi = qr0 + qb * 16 + 4 * g + r;
-                        p = ((unsigned)(qi - qlo) > (unsigned)(qhi - qlo)) ? 0.f : p;
-                    }
-                    // k-step kk = qb/2 takes rows of blocks 2kk (elements 0-3), 2kk+1 (4-7)
-                    pp[qb >> 1][4 * (qb & 1) + r] = (__bf16)p;
-                    pd[qb >> 1][4 * (qb & 1) + r] = (__bf16)(p * (dp[qb][r] - d4[r]));
-                }
+            for (int ds = 0; ds < C::DS; ++ds) {
+                sc[qb] = mfma16x16x32(aq[ds], kreg[ds], sc[qb]);
+                dp[qb] = mfma16x16x32(ao[ds], vreg[ds], dp[qb]);
             }
-            // dV += P^T dO and dK += dS^T Q, 32 query rows per k-step
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                for (int d0 = 0; d0 < C::NDB; d0 += 4) {
-                    bf16x8 bo[4], bq[4];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        bo[u] = tr_operand<C::LDN>(dOn, kk, d0 + u, lane);
-                        bq[u] = tr_operand<C::LDN>(Qn, kk, d0 + u, lane);
-                    }
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        dva[d0 + u] = mfma16x16x32(pp[kk], bo[u], dva[d0 + u]);
-                        dka[d0 + u] = mfma16x16x32(pd[kk], bq[u], dka[d0 + u]);
-                    }
-                }
         }
-        if (more) st.store(smem + ((it + 1) & 1) * C::STAGE);
-        __syncthreads();
+        bf16x8 pp[2], pd[2];
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) {
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + qb * 16 + 4 * g);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + qb * 16 + 4 * g);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                // rows past T have L = D = 0 and zero Q / dO: they add nothing
+                float p = fast_exp2(fmaf(sc[qb][r], c, -l4[r] * kLog2e));
+                if (cls == kPartial) {
+                    const int qi = qr0 + qb * 16 + 4 * g + r;
+                    p = ((unsigned)(qi - qlo) > (unsigned)(qhi - qlo)) ? 0.f : p;
+                }
+                // k-step kk = qb/2 takes rows of blocks 2kk (elements 0-3), 2kk+1 (4-7)
+                pp[qb >> 1][4 * (qb & 1) + r] = (__bf16)p;
+                pd[qb >> 1][4 * (qb & 1) + r] = (__bf16)(p * (dp[qb][r] - d4[r]));
+            }
+        }
+        // dV += P^T dO and dK += dS^T Q, 32 query rows per k-step
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int d0 = 0; d0 < C::NDB; d0 += 4) {
+                bf16x8 bo[4], bq[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    bo[u] = tr_operand<C::LDN>(dOn, kk, d0 + u, lane);
+                    bq[u] = tr_operand<C::LDN>(Qn, kk, d0 + u, lane);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    dva[d0 + u] = mfma16x16x32(pp[kk], bo[u], dva[d0 + u]);
+                    dka[d0 + u] = mfma16x16x32(pd[kk], bq[u], dka[d0 + u]);
+                }
+            }
     }
 
     // entry r of lane (n, g) in block db: key kw0 + 4g + r, column db*16 + n
@@ -489,7 +460,7 @@ template <int D>
 hipError_t launch_dkdv16_bf16_t(const AttnArgs& a) {
     using C = Dkdv16Cfg<D>;
     static bool set[kMaxDevices] = {};
-    const size_t lds = 2 * C::STAGE * sizeof(uint16_t);
+    const size_t lds = 2 * (size_t)C::STAGE;
     hipError_t e = allow_lds(dkdv16_bf16_kernel<D>, lds, set);
     if (e != hipSuccess) return e;
     const int nkt = (a.T + C::BKW - 1) / C::BKW;

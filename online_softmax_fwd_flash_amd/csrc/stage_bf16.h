@@ -108,23 +108,35 @@ __device__ __forceinline__ uint32_t dma_src_offset(int p, int lane, uint32_t ld_
     return (uint32_t)r * ld_bytes + 16u * (uint32_t)(pc ^ (VSWZ ? S::v(r) : S::k(r)));
 }
 
-// Padded row-major [rows x D] bf16 tile filled by LDS-DMA: rows are D + 8 elements (an odd
-// number of 16-byte chunks) apart, which keeps 16-byte operand-row reads of 16 consecutive
-// rows at one chunk free of bank conflicts (the XOR swizzle above is not, for those reads).
-// Slot s (16 bytes) of the tile is row s / (CPR + 1), chunk s % (CPR + 1); the pad chunk
-// receives a copy of the row's last chunk, so every lane of a piece loads valid bytes.
-template <int D>
+// Padded row-major [rows x D] bf16 tile filled by LDS-DMA: rows are D + 8*PADC elements
+// apart.  PADC = 1 (an odd number of 16-byte chunks per row) keeps 16-byte operand-row reads
+// of 16 consecutive rows at one chunk free of bank conflicts (the XOR swizzle above is not,
+// for those reads); PADC = 2 (D + 16) serves those reads and transpose reads of 8 rows x
+// 32 bytes.  Slot s (16 bytes) of the tile is row s / (CPR + PADC), chunk s % (CPR + PADC);
+// a pad slot receives a copy of the row's last chunk, so every lane loads valid bytes.
+template <int D, int PADC = 1>
 struct Pad {
     static constexpr int CPR = D / 8;               // data chunks per row
-    static constexpr int ROWB = 16 * (CPR + 1);     // bytes per row
+    static constexpr int SPR = CPR + PADC;          // slots per row
+    static constexpr int ROWB = 16 * SPR;           // bytes per row
 };
-template <int D>
+template <int D, int PADC = 1>
 __device__ __forceinline__ uint32_t dma_src_offset_padded(int p, int lane, uint32_t ld_bytes) {
+    using P = Pad<D, PADC>;
     const int slot = p * 64 + lane;
-    const int r = slot / (Pad<D>::CPR + 1);
-    int cch = slot % (Pad<D>::CPR + 1);
-    if (cch == Pad<D>::CPR) cch = Pad<D>::CPR - 1;
+    const int r = slot / P::SPR;
+    int cch = slot % P::SPR;
+    if (cch >= P::CPR) cch = P::CPR - 1;
     return (uint32_t)r * ld_bytes + 16u * (uint32_t)cch;
+}
+
+// LDS-DMA of 64 lanes x 4 bytes (256 consecutive LDS bytes at `dst`).
+__device__ __forceinline__ void dma_dwords(const Buf& src, void* dst, uint32_t voff, int soff) {
+    const uint32_t lds = (uint32_t)(uintptr_t)(lds_ptr_t)dst;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(src.r), "s"(soff)
+                 : "memory", "m0");
 }
 
 // One LDS-DMA piece: 64 lanes x 16 bytes from `src` (voffset per lane, soffset uniform)
