@@ -20,10 +20,12 @@
 // row-major tiles through LDS transpose reads.  K and V of the wave's 16 keys stay in
 // registers.
 //
-// dQ pass (32x32x16 MFMA).  Workgroup = 8 waves x 32 query rows of one (b, h) walking its key
-// blocks of 64; K and V row-major in LDS (K twice, at the two strides its two kinds of reads
-// want).  S^T = K Q^T and dP^T = V dO^T keep a query per accumulator column, so L and D are
-// per-lane scalars and dS^T feeds dQ^T += K^T dS^T directly, as P^T feeds O^T in the forward.
+// dQ pass (32x32x16 MFMA).  Workgroup = 4 waves x 32 query rows of one (b, h), two
+// workgroups per CU, walking its key blocks of 64; K and V reach LDS by LDS-DMA (padded
+// rows, double-buffered).  S^T = K Q^T and dP^T = V dO^T keep a query per accumulator
+// column, so L and D are per-lane scalars and dS^T feeds dQ^T += K^T dS^T directly, as P^T
+// feeds O^T in the forward; the K^T operand comes from the same K tile through transpose
+// reads.
 #include "common.h"
 #include "kernels.h"
 #include "stage_bf16.h"
@@ -271,49 +273,47 @@ struct DqCfg {
     static constexpr int BK = 64;        // keys per staged block
     static constexpr int DC = D / 16;
     static constexpr int NDB = D / 32;
-    // Row-major tiles.  K and V are read 16 bytes per lane, 32 rows per half-wave (A of S^T,
-    // dP^T): odd 16-byte stride D + 8.  A second copy of K is read through transpose reads
-    // (A of dQ^T += K^T dS^T), 8 rows x 16 dwords per wave: 16 x odd dword stride D + 32.
-    using KTile = RowChunks<BK, D, NT, D + 8>;
-    static constexpr int LDN = D + 8, LDK2 = D + 32;
-    static constexpr int KN = BK * LDN, K2 = BK * LDK2;
-    static constexpr int OFF_VN = KN, OFF_K2 = 2 * KN;
-    static constexpr int STAGE = 2 * KN + K2;
+    // Row-major K and V tiles with padded rows of D + 16 elements (LDS-DMA fills the pad
+    // slots with copies).  K and V are read 16 bytes per lane as A operands of S^T and dP^T
+    // (32 rows at one chunk per half-wave); K is also read through transpose reads as the A
+    // operand of dQ^T += K^T dS^T (8 rows x 32 bytes per 16 lanes); both are conflict-free
+    // at this stride.
+    using PadT = Pad<D, 2>;
+    static constexpr int LDN = PadT::ROWB / 2;                // elements per row
+    static constexpr int TPIECES = BK * PadT::ROWB / 1024;    // 1 KB pieces per tile
+    static constexpr int OFF_V = TPIECES * 1024;              // bytes
+    static constexpr int STAGE = 2 * OFF_V;                   // bytes per stage
+    static constexpr int TW = NW / 2;                         // waves per tile
+    static constexpr int PMAX = (TPIECES + TW - 1) / TW;      // pieces per wave (at most)
+    static_assert(TPIECES * 1024 == BK * PadT::ROWB, "tile must be whole pieces");
 };
 
+// LDS-DMA of key block jb into stage buffer `st`: the first half of the waves fill the K
+// tile (pieces w, w + NW/2, ...), the second half the V tile.
 template <int D, int NW>
-struct DqStage {
+__device__ __forceinline__ void dq_issue(char* st, const Buf& kbuf, const Buf& vbuf,
+                                         const uint32_t* voff, int w, uint32_t ldk_b, int jb) {
     using C = DqCfg<D, NW>;
-    typename C::KTile k, v;
-    __device__ __forceinline__ void load(const Buf& kb, const Buf& vb, uint32_t ldb, int j) {
-        k.load(kb, ldb, j * C::BK);
-        v.load(vb, ldb, j * C::BK);
-    }
-    __device__ __forceinline__ void store(uint16_t* buf) const {
-        k.store(buf);
-        v.store(buf + C::OFF_VN);
-        // second copy of K at the transpose-read stride (same chunk-to-thread mapping)
+    const int soff = __builtin_amdgcn_readfirstlane((int)((uint32_t)jb * C::BK * ldk_b));
+    const int wt = w % C::TW;
+    char* dst = st + (w / C::TW) * C::OFF_V;
+    const Buf& src = w < C::TW ? kbuf : vbuf;
 #pragma unroll
-        for (int p = 0; p < C::KTile::PER; ++p) {
-            const int e = threadIdx.x + p * C::NT;
-            if (C::KTile::NCH % C::NT == 0 || e < C::KTile::NCH) {
-                const int r = e / (D / 8), cc = e % (D / 8);
-                *reinterpret_cast<u32x4*>(buf + C::OFF_K2 + r * C::LDK2 + cc * 8) = k.v[p];
-            }
-        }
-    }
-};
+    for (int i = 0; i < C::PMAX; ++i)
+        if (wt + C::TW * i < C::TPIECES) dma_piece(src, dst + (wt + C::TW * i) * 1024, voff[i], soff);
+}
 
 }  // namespace
 
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64, 1) void dq_bf16_kernel(
+__global__ __launch_bounds__(NW * 64, 8 / NW) void dq_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ L, const float* __restrict__ Dv, float* __restrict__ dQ, int B,
     int T, int H, int HKV, float scale, int causal, int window, int nqt, int xcd_group) {
     using C = DqCfg<D, NW>;
-    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+    extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
+    char* sm = reinterpret_cast<char*>(smem);
 
     int qt, b, h;
     decode_q_work(blockIdx.x, nqt, B, H, HKV, xcd_group, qt, b, h);
@@ -321,7 +321,6 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_bf16_kernel(
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index (uniform)
     const int n = lane & 31, g = lane >> 5;
-    if (NW == 8 && w < 4) __builtin_amdgcn_s_setprio(1);   // see the dK/dV kernel
     const int wr0 = qt * C::BQ + w * 32;
     const int q = wr0 + n;
     const int64_t ldq = (int64_t)H * D, ldk = (int64_t)HKV * D;
@@ -355,73 +354,70 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_bf16_kernel(
 
     int jlo, jhi;
     kv_block_range(T, qt * C::BQ, qt * C::BQ + C::BQ, C::BK, cz, window, jlo, jhi);
-    DqStage<D, NW> st;
-    if (jlo < jhi) {
-        st.load(kbuf, vbuf, ldk_b, jlo);
-        st.store(smem);
-    }
-    __syncthreads();
+    uint32_t voff[C::PMAX];
+#pragma unroll
+    for (int i = 0; i < C::PMAX; ++i)
+        voff[i] = dma_src_offset_padded<D, 2>(w % C::TW + C::TW * i, lane, ldk_b);
 
+    if (jlo < jhi) dq_issue<D, NW>(sm, kbuf, vbuf, voff, w, ldk_b, jlo);
     for (int j = jlo; j < jhi; ++j) {
-        const uint16_t* buf = smem + ((j - jlo) & 1) * C::STAGE;
-        const bool more = j + 1 < jhi;
-        if (more) st.load(kbuf, vbuf, ldk_b, j + 1);
+        const int stg = (j - jlo) & 1;
+        wait_vmcnt<0>();   // block j's pieces, the only loads in flight
+        // every wave's pieces are visible; every wave is done with the other stage
+        lds_barrier();
+        if (j + 1 < jhi) dq_issue<D, NW>(sm + (stg ^ 1) * C::STAGE, kbuf, vbuf, voff, w, ldk_b, j + 1);
         const int cls = block_class(T, wr0, wr0 + 32, j * C::BK, j * C::BK + C::BK, cz, window);
-        if (cls != kSkip) {
-            const uint16_t* Kn = buf;
-            const uint16_t* Vn = buf + C::OFF_VN;
-            const uint16_t* K2 = buf + C::OFF_K2;
+        if (cls == kSkip) continue;
+        const uint16_t* Kn = reinterpret_cast<const uint16_t*>(sm + stg * C::STAGE);
+        const uint16_t* Vn = reinterpret_cast<const uint16_t*>(sm + stg * C::STAGE + C::OFF_V);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                f32x16 sk, dk;
+        for (int kb = 0; kb < 2; ++kb) {
+            f32x16 sk, dk;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sk[r] = dk[r] = 0.f;
-                // A operands of S^T and dP^T for this 32-key half, four k-steps ahead
+            for (int r = 0; r < 16; ++r) sk[r] = dk[r] = 0.f;
+            // A operands of S^T and dP^T for this 32-key half, four k-steps ahead
 #pragma unroll
-                for (int d0 = 0; d0 < C::DC; d0 += 4) {
-                    bf16x8 ak[4], av[4];
+            for (int d0 = 0; d0 < C::DC; d0 += 4) {
+                bf16x8 ak[4], av[4];
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int off = (kb * 32 + n) * C::LDN + (d0 + u) * 16 + 8 * g;
-                        ak[u] = *reinterpret_cast<const bf16x8*>(Kn + off);
-                        av[u] = *reinterpret_cast<const bf16x8*>(Vn + off);
-                    }
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        sk = mfma32x32x16(ak[u], qreg[d0 + u], sk);
-                        dk = mfma32x32x16(av[u], oreg[d0 + u], dk);
-                    }
+                for (int u = 0; u < 4; ++u) {
+                    const int off = (kb * 32 + n) * C::LDN + (d0 + u) * 16 + 8 * g;
+                    ak[u] = *reinterpret_cast<const bf16x8*>(Kn + off);
+                    av[u] = *reinterpret_cast<const bf16x8*>(Vn + off);
                 }
-                // entry r of lane (n, g): key j*64 + 32kb + 8*(r/4) + 4g + r%4, query q
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    sk[r] = fast_exp2(fmaf(sk[r], c, -l2));
-                    dk[r] = dk[r] - dq_i;
-                }
-                if (cls == kPartial) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int kk = j * C::BK + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-                        if ((unsigned)(kk - klo) > (unsigned)(khi - klo)) sk[r] = 0.f;
-                    }
-                }
-                bf16x8 pd[2];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) pd[r >> 3][r & 7] = (__bf16)(sk[r] * dk[r]);
-                // dQ^T += K^T dS^T over this half's 32 keys, 16 per k-step
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    bf16x8 at[C::NDB];
-#pragma unroll
-                    for (int db = 0; db < C::NDB; ++db)
-                        at[db] = tr_operand32<C::LDK2>(K2, kb * 32 + hf * 16, db * 32, lane);
-#pragma unroll
-                    for (int db = 0; db < C::NDB; ++db) dqa[db] = mfma32x32x16(at[db], pd[hf], dqa[db]);
+                for (int u = 0; u < 4; ++u) {
+                    sk = mfma32x32x16(ak[u], qreg[d0 + u], sk);
+                    dk = mfma32x32x16(av[u], oreg[d0 + u], dk);
                 }
             }
+            // entry r of lane (n, g): key j*64 + 32kb + 8*(r/4) + 4g + r%4, query q
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                sk[r] = fast_exp2(fmaf(sk[r], c, -l2));
+                dk[r] = dk[r] - dq_i;
+            }
+            if (cls == kPartial) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int kk = j * C::BK + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+                    if ((unsigned)(kk - klo) > (unsigned)(khi - klo)) sk[r] = 0.f;
+                }
+            }
+            bf16x8 pd[2];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) pd[r >> 3][r & 7] = (__bf16)(sk[r] * dk[r]);
+            // dQ^T += K^T dS^T over this half's 32 keys, 16 per k-step
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                bf16x8 at[C::NDB];
+#pragma unroll
+                for (int db = 0; db < C::NDB; ++db)
+                    at[db] = tr_operand32<C::LDN>(Kn, kb * 32 + hf * 16, db * 32, lane);
+#pragma unroll
+                for (int db = 0; db < C::NDB; ++db) dqa[db] = mfma32x32x16(at[db], pd[hf], dqa[db]);
+            }
         }
-        if (more) st.store(smem + ((j + 1 - jlo) & 1) * C::STAGE);
-        __syncthreads();
     }
 
     if (q >= T) return;
@@ -472,7 +468,7 @@ hipError_t launch_dkdv16_bf16_t(const AttnArgs& a) {
     return hipGetLastError();
 }
 
-constexpr int kDqWaves = 8;
+constexpr int kDqWaves = 4;
 static_assert(DqCfg<128, kDqWaves>::BQ == kBf16DqBq && DqCfg<128, kDqWaves>::BK == kBf16DqBk,
               "dQ tiling differs from kernels.h");
 static_assert(Dkdv16Cfg<128>::BQ == kBf16DkdvBq && Dkdv16Cfg<128>::BKW == kBf16DkdvBk,
@@ -482,7 +478,7 @@ template <int D>
 hipError_t launch_dq_bf16_t(const AttnArgs& a) {
     using C = DqCfg<D, kDqWaves>;
     static bool set[kMaxDevices] = {};
-    const size_t lds = 2 * C::STAGE * sizeof(uint16_t);
+    const size_t lds = 2 * (size_t)C::STAGE;
     hipError_t e = allow_lds(dq_bf16_kernel<D, kDqWaves>, lds, set);
     if (e != hipSuccess) return e;
     const int nqt = (a.T + C::BQ - 1) / C::BQ;

@@ -29,7 +29,7 @@ struct AttnArgs {
 // translation unit static_asserts its own constants against these.
 constexpr int kBf16FwdBq = 128, kBf16FwdBk = 64;    // forward: q-tile x staged key block
 constexpr int kBf16DkdvBq = 64, kBf16DkdvBk = 64;   // dK/dV: staged query block x key tile
-constexpr int kBf16DqBq = 256, kBf16DqBk = 64;      // dQ: q-tile x staged key block
+constexpr int kBf16DqBq = 128, kBf16DqBk = 64;      // dQ: q-tile x staged key block
 
 bool f32_tiles_supported(int bq, int bk);
 hipError_t launch_fwd_f32(const AttnArgs& a, int bq, int bk);
