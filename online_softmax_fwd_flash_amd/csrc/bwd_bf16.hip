@@ -10,9 +10,9 @@
 // formulas); Graphcore "flash_attention_qkv_packed.cpp", flashAttentionQKVPackedGrad
 // (key-chunk-outer loop with dV += P^T dO, dP = dO V^T, dS, dK += dS^T Q).
 //
-// dK/dV pass (16x16x32 MFMA).  Workgroup = 4 waves x 16 keys of one (b, kv head), two
-// workgroups per CU (one's barrier waits are covered by the other's work); it walks every
-// (query head of the group, 64-row query block) pair that sees its keys, last query block
+// dK/dV pass (16x16x32 MFMA).  Workgroup = 4 waves x 16 keys of one (b, kv head), three
+// workgroups per CU (one's barrier waits are covered by the others' work); it walks every
+// (query head of the group, 32-row query block) pair that sees its keys, last query block
 // first.  Q, dO (row-major, padded rows) and L, D of a block reach LDS by LDS-DMA,
 // double-buffered.  S = Q K^T and dP = dO V^T keep a key per accumulator column, so P and dS
 // leave the accumulators already in the A-operand layout of dV += P^T dO and dK += dS^T Q;
@@ -50,7 +50,9 @@ template <int D>
 struct Dkdv16Cfg {
     static constexpr int NW = 4, NT = 256;
     static constexpr int KPW = 16, BKW = NW * KPW;   // keys per wave / workgroup
-    static constexpr int BQ = 64;                     // query rows per staged block
+    static constexpr int BQ = 32;                     // query rows per staged block
+    static constexpr int WGS = 3;                     // workgroups per CU
+    static constexpr int QB16 = BQ / 16, KKS = BQ / 32;   // 16-row blocks, 32-row k-steps
     static constexpr int DS = D / 32;                 // 32-wide k-steps of S and dP
     static constexpr int NDB = D / 16;                // 16-wide column blocks of dK / dV
     // Padded row (elements).  Row-major Q / dO tiles serve both operand reads: 16-byte reads
@@ -116,7 +118,7 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int kk, int d
 }  // namespace
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void dkdv16_bf16_kernel(
+__global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv16_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ L, const float* __restrict__ Dv, float* __restrict__ dK,
@@ -191,11 +193,11 @@ __global__ __launch_bounds__(256, 2) void dkdv16_bf16_kernel(
         const uint16_t* Qn = reinterpret_cast<const uint16_t*>(stg);
         const uint16_t* dOn = reinterpret_cast<const uint16_t*>(stg + C::OFF_DO);
         const float* Ls = reinterpret_cast<const float*>(stg + C::OFF_L);
-        const float* Ds = Ls + C::BQ;
-        // S, dP for four 16-row blocks; entry r of lane (n, g): row 16qb + 4g + r, key n
-        f32x4 sc[4], dp[4];
+        const float* Ds = Ls + 64;
+        // S, dP for the 16-row blocks; entry r of lane (n, g): row 16qb + 4g + r, key n
+        f32x4 sc[C::QB16], dp[C::QB16];
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb) {
+        for (int qb = 0; qb < C::QB16; ++qb) {
             sc[qb] = dp[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
             bf16x8 aq[C::DS], ao[C::DS];
 #pragma unroll
@@ -210,9 +212,9 @@ __global__ __launch_bounds__(256, 2) void dkdv16_bf16_kernel(
                 dp[qb] = mfma16x16x32(ao[ds], vreg[ds], dp[qb]);
             }
         }
-        bf16x8 pp[2], pd[2];
+        bf16x8 pp[C::KKS], pd[C::KKS];
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb) {
+        for (int qb = 0; qb < C::QB16; ++qb) {
             const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + qb * 16 + 4 * g);
             const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + qb * 16 + 4 * g);
 #pragma unroll
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(256, 2) void dkdv16_bf16_kernel(
         }
         // dV += P^T dO and dK += dS^T Q, 32 query rows per k-step
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int kk = 0; kk < C::KKS; ++kk)
 #pragma unroll
             for (int d0 = 0; d0 < C::NDB; d0 += 4) {
                 bf16x8 bo[4], bq[4];
