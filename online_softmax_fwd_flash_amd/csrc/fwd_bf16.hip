@@ -8,10 +8,11 @@
 // mask conditions, L = m + log l stash).
 //
 // gfx950 design
-//  * Workgroup = 4 waves = 128 query rows of one (b, h); wave w owns 32 rows.  Key blocks of
-//    64 go HBM -> LDS by LDS-DMA (buffer_load ... lds, 16 bytes per lane): no staging
-//    registers and no LDS write instructions.  Two stages: block j + 1 is fetched while
-//    block j is computed; one barrier per block, which does not wait for that fetch.
+//  * Workgroup = 4 waves = 128 query rows of one (b, h); wave w owns 32 rows; three
+//    workgroups per CU, so one workgroup's barrier waits are covered by the others' work.
+//    Key blocks of 32 go HBM -> LDS by LDS-DMA (buffer_load ... lds, 16 bytes per lane): no
+//    staging registers and no LDS write instructions.  Two stages: block j + 1 is fetched
+//    while block j is computed; one barrier per block, which does not wait for that fetch.
 //  * The K tile keeps padded rows (D + 8 elements: 16-byte operand-row reads of consecutive
 //    rows at one chunk are free of bank conflicts; each row's pad slot gets a copy of a valid
 //    chunk); the V tile is unpadded with XOR-swizzled 16-byte chunks for its transpose reads
@@ -36,7 +37,9 @@ namespace fa {
 
 namespace {
 
-constexpr int kBQ = 128, kBK = 64, kThreads = 256;
+constexpr int kBQ = 128, kBK = 32, kThreads = 256;
+constexpr int kNH = kBK / 32;   // 32-key halves of a key block
+constexpr int kWgs = 3;         // workgroups per CU
 static_assert(kBQ == kBf16FwdBq && kBK == kBf16FwdBk, "forward tiling differs from kernels.h");
 
 template <int D>
@@ -47,13 +50,14 @@ struct Bf16Fwd {
     // K tile padded (operand-row reads), V tile unpadded and swizzled (transpose reads)
     static constexpr int KROWB = Pad<D>::ROWB;
     static constexpr int VROWB = 2 * D;
-    static constexpr int KPIECES = kBK * KROWB / 1024;       // LDS-DMA pieces of 1 KB
+    // LDS-DMA pieces of 1 KB (the K tile rounded up; slots past its last row take rows of
+    // the next block, which nothing reads)
+    static constexpr int KPIECES = (kBK * KROWB + 1023) / 1024;
     static constexpr int VPIECES = kBK * VROWB / 1024;
     static constexpr int KMAX = (KPIECES + NW - 1) / NW;      // K pieces per wave (at most)
     static constexpr int VPW = VPIECES / NW;                  // V pieces per wave
     static constexpr int KTILEB = KPIECES * 1024;
     static constexpr int STAGEB = KTILEB + VPIECES * 1024;    // K tile then V tile
-    static_assert(KPIECES * 1024 == kBK * KROWB, "K tile must be whole pieces");
     static_assert(VPW * NW == VPIECES, "V tile must split evenly over the waves");
 };
 
@@ -76,7 +80,7 @@ __device__ __forceinline__ void fwd_issue(const Buf& kb, const Buf& vb, const ui
 }  // namespace
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
+__global__ __launch_bounds__(kThreads, kWgs) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ L, int B,
     int T, int H, int HKV, float scale, int causal, int window, int nqt, int xcd_group) {
@@ -154,41 +158,46 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         const int cls = block_class(T, wr0, wr0 + 32, j * kBK, j * kBK + kBK, cz, window);
         if (cls == kSkip) continue;
         const char* sb = sm + stg * C::STAGEB;
-        f32x16 s0, s1;
+        // S^T for the block's 32-key halves: entry r of lane (n, g) in s[hk] is key
+        // j*BK + 32*hk + 8*(r/4) + 4g + r%4 of query n
+        f32x16 s[kNH];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s0[r] = s1[r] = 0.f;
-        bf16x8 ka[C::DC][2];
+        for (int hk = 0; hk < kNH; ++hk)
 #pragma unroll
-        for (int dc = 0; dc < C::DC; ++dc) {
-            ka[dc][0] = *reinterpret_cast<const bf16x8*>(sb + kaddr + 32 * dc);
-            ka[dc][1] = *reinterpret_cast<const bf16x8*>(sb + kaddr + 32 * dc + 32 * C::KROWB);
-        }
+            for (int r = 0; r < 16; ++r) s[hk][r] = 0.f;
+        bf16x8 ka[C::DC][kNH];
 #pragma unroll
-        for (int dc = 0; dc < C::DC; ++dc) {
-            s0 = mfma32x32x16(ka[dc][0], qreg[dc], s0);
-            s1 = mfma32x32x16(ka[dc][1], qreg[dc], s1);
-        }
+        for (int dc = 0; dc < C::DC; ++dc)
+#pragma unroll
+            for (int hk = 0; hk < kNH; ++hk)
+                ka[dc][hk] = *reinterpret_cast<const bf16x8*>(sb + kaddr + 32 * dc + 32 * hk * C::KROWB);
+#pragma unroll
+        for (int dc = 0; dc < C::DC; ++dc)
+#pragma unroll
+            for (int hk = 0; hk < kNH; ++hk) s[hk] = mfma32x32x16(ka[dc][hk], qreg[dc], s[hk]);
         // schedule: the first DC K reads up front, then one read per MFMA, so the LDS
         // latency hides behind the MFMAs
         __builtin_amdgcn_sched_group_barrier(0x100, C::DC, 0);
 #pragma unroll
-        for (int i = 0; i < C::DC; ++i) {
+        for (int i = 0; i < (kNH * C::DC) / 2; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, C::DC, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, (kNH * C::DC) / 2, 0);
         if (cls == kPartial) {
-            // entry r of lane (n, g): key j*64 + 32*half + 8*(r/4) + 4g + r%4
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int k0 = j * kBK + 8 * (r >> 2) + 4 * g + (r & 3);
-                if ((unsigned)(k0 - klo) > (unsigned)(khi - klo)) s0[r] = -INFINITY;
-                if ((unsigned)(k0 + 32 - klo) > (unsigned)(khi - klo)) s1[r] = -INFINITY;
-            }
+            for (int hk = 0; hk < kNH; ++hk)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int k0 = j * kBK + 32 * hk + 8 * (r >> 2) + 4 * g + (r & 3);
+                    if ((unsigned)(k0 - klo) > (unsigned)(khi - klo)) s[hk][r] = -INFINITY;
+                }
         }
-        float mx = vmax(s0[0], s1[0]);
+        float mx = s[0][0];
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = vmax(mx, vmax(s0[r], s1[r]));
+        for (int hk = 0; hk < kNH; ++hk)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) mx = vmax(mx, vmax(s[hk][r], s[hk][r + 1]));
         mx = vmax(mx, swap_halves(mx));
         const float mnew = vmax(m, mx);
         // a row whose max is still the -FLT_MAX start rescales on its first visible key
@@ -200,26 +209,27 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
             for (int i = 0; i < C::NDB; ++i) oacc[i] *= corr;
         }
         const float mc = vmax(m * c, kNegMax);   // finite even while m = -FLT_MAX
-        float ps0 = 0.f, ps1 = 0.f;
+        float ps[kNH];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            s0[r] = fast_exp2(fmaf(s0[r], c, -mc));
-            s1[r] = fast_exp2(fmaf(s1[r], c, -mc));
-            ps0 += s0[r];
-            ps1 += s1[r];
-        }
-        lsum += ps0 + ps1;
-        // P^T operand: 8 keys per 16-key half, element e <-> accumulator entry 8*half + e
-        bf16x8 pb[4];
+        for (int hk = 0; hk < kNH; ++hk) {
+            ps[hk] = 0.f;
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                pb[hf][e] = (__bf16)s0[8 * hf + e];
-                pb[2 + hf][e] = (__bf16)s1[8 * hf + e];
+            for (int r = 0; r < 16; ++r) {
+                s[hk][r] = fast_exp2(fmaf(s[hk][r], c, -mc));
+                ps[hk] += s[hk][r];
             }
+        }
 #pragma unroll
-        for (int kh = 0; kh < 4; ++kh)
+        for (int hk = 0; hk < kNH; ++hk) lsum += ps[hk];
+        // P^T operand of 16-key quarter kh: element e <-> accumulator entry 8*(kh % 2) + e of
+        // s[kh / 2]
+        bf16x8 pb[2 * kNH];
+#pragma unroll
+        for (int kh = 0; kh < 2 * kNH; ++kh)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pb[kh][e] = (__bf16)s[kh >> 1][8 * (kh & 1) + e];
+#pragma unroll
+        for (int kh = 0; kh < 2 * kNH; ++kh)
 #pragma unroll
             for (int db = 0; db < C::NDB; ++db) {
                 const char* pv = sb + vaddr[db] + 16 * kh * C::VROWB;

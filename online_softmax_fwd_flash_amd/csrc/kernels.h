@@ -27,7 +27,7 @@ struct AttnArgs {
 
 // Tilings of the bf16 kernels: query rows x keys handled per workgroup block.  Each kernel
 // translation unit static_asserts its own constants against these.
-constexpr int kBf16FwdBq = 128, kBf16FwdBk = 64;    // forward: q-tile x staged key block
+constexpr int kBf16FwdBq = 128, kBf16FwdBk = 32;    // forward: q-tile x staged key block
 constexpr int kBf16DkdvBq = 32, kBf16DkdvBk = 64;   // dK/dV: staged query block x key tile
 constexpr int kBf16DqBq = 128, kBf16DqBk = 64;      // dQ: q-tile x staged key block
 

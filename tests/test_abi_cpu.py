@@ -92,7 +92,7 @@ def test_bad_tiles_rejected():
 
 
 def test_default_tiles():
-    assert fa.flash_attn_default_tiles(1, 128, 0) == (128, 64)
+    assert fa.flash_attn_default_tiles(1, 128, 0) == (128, 32)
     assert fa.flash_attn_default_tiles(1, 128, 1) == (32, 64)
     assert fa.flash_attn_default_tiles(1, 128, 2) == (128, 64)
     assert fa.flash_attn_default_tiles(0, 8, 0) == (64, 64)
