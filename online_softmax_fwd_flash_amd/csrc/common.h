@@ -68,6 +68,16 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 // Value held by lane l ^ 32 (the other half of the wave).
 __device__ __forceinline__ float swap_halves(float v) { return __shfl_xor(v, 32, 64); }
 
+// max(v[l], v[l ^ 32]) for every lane l, in VALU (v_permlane32_swap_b32 exchanges lanes 32-63
+// of one copy of v with lanes 0-31 of another: the two results hold v[l % 32] and
+// v[32 + l % 32] in some order, and max does not care which)
+__device__ __forceinline__ float halves_max(float v) {
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const unsigned r0 = r[0], r1 = r[1];
+    return __builtin_elementwise_maximum(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
+}
+
 __device__ __forceinline__ float xor_shfl(float v, int mask) {
     return __shfl_xor(v, mask, 64);
 }

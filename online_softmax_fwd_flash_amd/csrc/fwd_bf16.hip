@@ -198,7 +198,7 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_bf16_kernel(
         for (int hk = 0; hk < kNH; ++hk)
 #pragma unroll
             for (int r = 0; r < 16; r += 2) mx = vmax(mx, vmax(s[hk][r], s[hk][r + 1]));
-        mx = vmax(mx, swap_halves(mx));
+        mx = halves_max(mx);
         const float mnew = vmax(m, mx);
         // a row whose max is still the -FLT_MAX start rescales on its first visible key
         if (__any(mnew > m && (m == kNegMax || (mnew - m) * c > 8.0f))) {
