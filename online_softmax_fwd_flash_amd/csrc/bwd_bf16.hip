@@ -275,12 +275,12 @@ struct DqCfg {
     static constexpr int BK = 64;        // keys per staged block
     static constexpr int DC = D / 16;
     static constexpr int NDB = D / 32;
-    // Row-major K and V tiles with padded rows of D + 16 elements (LDS-DMA fills the pad
+    // Row-major K and V tiles with padded rows of D + 24 elements (LDS-DMA fills the pad
     // slots with copies).  K and V are read 16 bytes per lane as A operands of S^T and dP^T
-    // (32 rows at one chunk per half-wave); K is also read through transpose reads as the A
-    // operand of dQ^T += K^T dS^T (8 rows x 32 bytes per 16 lanes); both are conflict-free
-    // at this stride.
-    using PadT = Pad<D, 2>;
+    // (32 consecutive rows at one chunk per half-wave: measured conflict-free at this stride,
+    // 2-way conflicted at D + 16); K is also read through transpose reads as the A operand
+    // of dQ^T += K^T dS^T (8 rows x 32 bytes per 16 lanes).
+    using PadT = Pad<D, 3>;
     static constexpr int LDN = PadT::ROWB / 2;                // elements per row
     static constexpr int TPIECES = BK * PadT::ROWB / 1024;    // 1 KB pieces per tile
     static constexpr int OFF_V = TPIECES * 1024;              // bytes
@@ -359,7 +359,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_bf16_kernel(
     uint32_t voff[C::PMAX];
 #pragma unroll
     for (int i = 0; i < C::PMAX; ++i)
-        voff[i] = dma_src_offset_padded<D, 2>(w % C::TW + C::TW * i, lane, ldk_b);
+        voff[i] = dma_src_offset_padded<D, 3>(w % C::TW + C::TW * i, lane, ldk_b);
 
     if (jlo < jhi) dq_issue<D, NW>(sm, kbuf, vbuf, voff, w, ldk_b, jlo);
     for (int j = jlo; j < jhi; ++j) {

@@ -109,10 +109,11 @@ __device__ __forceinline__ uint32_t dma_src_offset(int p, int lane, uint32_t ld_
 }
 
 // Padded row-major [rows x D] bf16 tile filled by LDS-DMA: rows are D + 8*PADC elements
-// apart.  PADC = 1 (an odd number of 16-byte chunks per row) keeps 16-byte operand-row reads
-// of 16 consecutive rows at one chunk free of bank conflicts (the XOR swizzle above is not,
-// for those reads); PADC = 2 (D + 16) serves those reads and transpose reads of 8 rows x
-// 32 bytes.  Slot s (16 bytes) of the tile is row s / (CPR + PADC), chunk s % (CPR + PADC);
+// apart.  Measured on gfx950 (128 banks, 32 lanes serviced together): 16-byte reads of 32
+// consecutive rows at one chunk are conflict-free at D + 8 and D + 24 (an odd number of
+// 16-byte slots per row whose product with 16 rows is not a multiple of the 512-byte bank
+// line) but 2-way conflicted at D + 16 and 16-way at D; transpose reads of 8 rows x 32 bytes
+// are conflict-free at D + 16 and D + 24 but 2-way at D and D + 8.  Slot s (16 bytes) of the tile is row s / (CPR + PADC), chunk s % (CPR + PADC);
 // a pad slot receives a copy of the row's last chunk, so every lane loads valid bytes.
 template <int D, int PADC = 1>
 struct Pad {
