@@ -3,9 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C4] [--no-cpu-baseline]
 
 A step is one pass of the whole path over one batch of synthetic input already resident in
-HBM: forward (flash_attn_fwd) and backward (flash_attn_bwd_preprocess, flash_attn_bwd_dkdv,
-flash_attn_bwd_dq — the three kernels flash_attn_bwd runs, called through their own entry
-points so each can be timed with HIP events on the launch stream).  Prints one JSON line.
+HBM: forward (flash_attn_fwd) and backward (flash_attn_bwd_dq_dvec, then flash_attn_bwd_dkdv —
+the two kernels flash_attn_bwd runs, called through their own entry points so each can be
+timed with HIP events on the launch stream).  Prints one JSON line.
 
 FLOP convention: forward 4*B*H*T^2*D (halved when causal), backward 2.5x that; the metric is
 fwd+bwd TFLOP/s, with the forward alone and the fraction of the MI355X dense bf16 MFMA peak
@@ -144,7 +144,7 @@ def main():
     dv = torch.empty(k.shape, device=dev, dtype=f32)
     kw = dict(causal=cfg.causal, window=cfg.window, scale=cfg.scale, tiles=cfg.tiles)
     stream = torch.cuda.current_stream()
-    names = ["fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq"]
+    names = ["fwd", "bwd_dq_dvec", "bwd_dkdv"]
 
     def step(ev=None):
         if ev is not None:
@@ -152,20 +152,18 @@ def main():
         fa.flash_attn_fwd(q, k, v, out=o, lse=lse, **kw)
         if ev is not None:
             ev[1].record(stream)
-        fa.flash_attn_bwd_preprocess(o, do, dvec)
+        fa.flash_attn_bwd_dq_dvec(q, k, v, o, do, lse, dvec=dvec, dq=dq, **kw)
         if ev is not None:
             ev[2].record(stream)
         fa.flash_attn_bwd_dkdv(q, k, v, do, lse, dvec, dk=dk, dv=dv, **kw)
         if ev is not None:
             ev[3].record(stream)
-        fa.flash_attn_bwd_dq(q, k, v, do, lse, dvec, dq=dq, **kw)
-        if ev is not None:
-            ev[4].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+              for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -189,35 +187,27 @@ def main():
     ms_step = wall * 1e3 / args.steps
     ff, bf = fwd_flops(cfg), bwd_flops(cfg)
     fwd_ms = per_kernel["fwd"]
-    bwd_ms = per_kernel["bwd_preprocess"] + per_kernel["bwd_dkdv"] + per_kernel["bwd_dq"]
+    bwd_ms = per_kernel["bwd_dq_dvec"] + per_kernel["bwd_dkdv"]
     value = (ff + bf) / (ms_step * 1e-3) / 1e12
     peak = PEAK_BF16 if cfg.dtype == "bf16" else PEAK_FP32
 
     # algorithmic work per launch: FLOP per visible score x visible scores
     vis = B * H * visible_pairs(T, cfg.causal, cfg.window)
-    io = 2 if cfg.dtype == "bf16" else 4
     algo = {
         "fwd": ("mfma", 4.0 * D * vis),                    # Q K^T and P V
         "bwd_dkdv": ("mfma", 8.0 * D * vis),               # Q K^T, dO V^T, P^T dO, dS^T Q
-        "bwd_dq": ("mfma", 6.0 * D * vis),                 # Q K^T, dO V^T, dS K
-        "bwd_preprocess": ("hbm", 2.0 * B * T * H * D * io + 4.0 * B * H * T),   # read O, dO
+        "bwd_dq_dvec": ("mfma", 6.0 * D * vis),            # Q K^T, dO V^T, dS K (+ rowsum(dO O))
     }
     kernels = {}
     for n in names:
         bound, work = algo[n]
-        t = per_kernel[n] * 1e-3
-        if bound == "mfma":
-            ach = work / t / 1e12
-            kernels[n] = {"ms": round(per_kernel[n], 4), "bound": "mfma", "achieved": round(ach, 1),
-                          "unit": "TFLOP/s", "frac": round(ach / peak, 4)}
-        else:
-            ach = work / t / 1e9
-            kernels[n] = {"ms": round(per_kernel[n], 4), "bound": "hbm", "achieved": round(ach, 1),
-                          "unit": "GB/s", "frac": round(ach / 8000.0, 4)}
+        ach = work / (per_kernel[n] * 1e-3) / 1e12
+        kernels[n] = {"ms": round(per_kernel[n], 4), "bound": bound, "achieved": round(ach, 1),
+                      "unit": "TFLOP/s", "frac": round(ach / peak, 4)}
     dom = max(names, key=lambda n: per_kernel[n])
     dk_ = kernels[dom]
     roofline = {"bound": dk_["bound"], "achieved": dk_["achieved"],
-                "peak": peak if dk_["bound"] == "mfma" else 8000.0, "unit": dk_["unit"],
+                "peak": peak, "unit": dk_["unit"],
                 "frac": dk_["frac"], "kernel": dom,
                 "traffic": measured_traffic(dom) if cfg.name == "C4" else None}
 

@@ -122,6 +122,19 @@ fa_status_t flash_attn_bwd_dq(const void* Q, const void* K, const void* V, const
                               int H, int HKV, int D, float scale, int causal, int window,
                               fa_dtype_t dtype, hipStream_t stream, int bq, int bk);
 
+/* Backward stages 1 and 3 in one pass ([ipu] flashAttentionQKVPackedGrad, its rowsum(O * grad)
+ * step; [forge] flash_attn_bwd_dq; [teeny] backward_dq): dQ exactly as flash_attn_bwd_dq, and
+ * Dvec[b,h,i] = sum_d dO[b,i,h,d] * O[b,i,h,d] (float32 accumulation) written to the
+ * caller-owned [B,H,T] float32 buffer Dvec, which flash_attn_bwd_dkdv then reads.  bf16: one
+ * kernel, each query block forming the Dvec values of its own rows from O and the dO rows it
+ * loads anyway.  f32: stage 1 then stage 3.  O and dO are [B,T,H,D] like Q; bq, bk as for
+ * flash_attn_bwd_dq. */
+fa_status_t flash_attn_bwd_dq_dvec(const void* Q, const void* K, const void* V, const void* O,
+                                   const void* dO, const float* L, float* Dvec, float* dQ, int B,
+                                   int T, int H, int HKV, int D, float scale, int causal,
+                                   int window, fa_dtype_t dtype, hipStream_t stream, int bq,
+                                   int bk);
+
 /* ---- host-only helpers (no GPU needed) ---- */
 
 /* Human-readable name of a status code (static string). */

@@ -14,6 +14,7 @@ FA_DTYPE_F32, FA_DTYPE_BF16 = 0, 1
 EXPORTS = [
     "flash_attn_fwd", "flash_attn_bwd", "flash_attn_fwd_ex", "flash_attn_bwd_ex",
     "flash_attn_bwd_preprocess", "flash_attn_bwd_dkdv", "flash_attn_bwd_dq",
+    "flash_attn_bwd_dq_dvec",
     "flash_attn_status_string", "flash_attn_block_class", "flash_attn_kv_block_range",
     "flash_attn_default_tiles", "flash_attn_version",
 ]
@@ -35,6 +36,7 @@ def _declare(lib):
         "flash_attn_bwd_preprocess": [P, P, P, I, I, I, I, I, P],
         "flash_attn_bwd_dkdv": [P] * 8 + _DIMS + [I, I],
         "flash_attn_bwd_dq": [P] * 7 + _DIMS + [I, I],
+        "flash_attn_bwd_dq_dvec": [P] * 8 + _DIMS + [I, I],
         "flash_attn_block_class": [I, I, I, I, I, I, I, ctypes.POINTER(I)],
         "flash_attn_kv_block_range": [I, I, I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)],
         "flash_attn_default_tiles": [I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)],

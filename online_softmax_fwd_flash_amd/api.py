@@ -123,6 +123,26 @@ def flash_attn_bwd_dq(q, k, v, do, lse, dvec, causal=True, window=0, scale=None,
     return dq
 
 
+def flash_attn_bwd_dq_dvec(q, k, v, o, do, lse, dvec=None, causal=True, window=0, scale=None,
+                           dq=None, tiles=(0, 0), stream=None):
+    """dQ (float32) and Dvec = rowsum(dO * O) ([B,H,T] float32) in one pass; returns (dq, dvec)."""
+    B, T, H, HKV, D = _dims(q, k)
+    _want(o, q.shape, q.dtype, "o")
+    _want(do, q.shape, q.dtype, "do")
+    _want(lse, (B, H, T), torch.float32, "lse")
+    dq = torch.empty(q.shape, device=q.device, dtype=torch.float32) if dq is None else dq
+    dvec = torch.empty(B, H, T, device=q.device, dtype=torch.float32) if dvec is None else dvec
+    _want(dq, q.shape, torch.float32, "dq")
+    _want(dvec, (B, H, T), torch.float32, "dvec")
+    code = _lib.lib().flash_attn_bwd_dq_dvec(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
+                                             _ptr(lse), _ptr(dvec), _ptr(dq), B, T, H, HKV, D,
+                                             _scale(scale, D), int(bool(causal)), int(window),
+                                             _DT[q.dtype], _stream(stream), int(tiles[0]),
+                                             int(tiles[1]))
+    _check("flash_attn_bwd_dq_dvec", code)
+    return dq, dvec
+
+
 def flash_attn_bwd(q, k, v, o, lse, do, causal=True, window=0, scale=None, dq=None, dk=None,
                    dv=None, tiles=(0, 0), stream=None):
     """dQ, dK, dV (float32) of sum(O * dO); O, L from flash_attn_fwd on the same inputs."""

@@ -180,6 +180,28 @@ fa_status_t flash_attn_bwd_dq(const void* Q, const void* K, const void* V, const
     return hip_status(fa::launch_dq_bf16(a));
 }
 
+fa_status_t flash_attn_bwd_dq_dvec(const void* Q, const void* K, const void* V, const void* O,
+                                   const void* dO, const float* L, float* Dvec, float* dQ, int B,
+                                   int T, int H, int HKV, int D, float scale, int causal,
+                                   int window, fa_dtype_t dtype, hipStream_t stream, int bq,
+                                   int bk) {
+    fa_status_t s = check_ptrs({Q, K, V, O, dO, L, Dvec, dQ});
+    if (s != FA_OK) return s;
+    if ((s = check_dims(B, T, H, HKV, D, scale, causal, window, dtype)) != FA_OK) return s;
+    if (dtype == FA_DTYPE_F32) {
+        if ((s = resolve_f32_tiles(bq, bk)) != FA_OK) return s;
+        s = flash_attn_bwd_preprocess(O, dO, Dvec, B, T, H, D, dtype, stream);
+        if (s != FA_OK) return s;
+        return flash_attn_bwd_dq(Q, K, V, dO, L, Dvec, dQ, B, T, H, HKV, D, scale, causal,
+                                 window, dtype, stream, bq, bk);
+    }
+    if (!((bq == 0 && bk == 0) || (bq == fa::kBf16DqBq && bk == fa::kBf16DqBk)))
+        return FA_ERR_INVALID_ARG;
+    fa::AttnArgs a = make_args(B, T, H, HKV, D, scale, causal, window, stream);
+    a.Q = Q; a.K = K; a.V = V; a.O = O; a.dO = dO; a.Lin = L; a.Dvec = Dvec; a.dQ = dQ;
+    return hip_status(fa::launch_dq_bf16_fused_d(a));
+}
+
 fa_status_t flash_attn_bwd_ex(const void* Q, const void* K, const void* V, const void* O,
                               const float* L, const void* dO, float* dQ, float* dK, float* dV,
                               int B, int T, int H, int HKV, int D, float scale, int causal,
@@ -195,13 +217,11 @@ fa_status_t flash_attn_bwd_ex(const void* Q, const void* K, const void* V, const
     float* Dvec = nullptr;
     const size_t bytes = (size_t)B * H * T * sizeof(float);
     if (hipMallocAsync((void**)&Dvec, bytes, stream) != hipSuccess) return FA_ERR_HIP;
-    s = flash_attn_bwd_preprocess(O, dO, Dvec, B, T, H, D, dtype, stream);
+    s = flash_attn_bwd_dq_dvec(Q, K, V, O, dO, L, Dvec, dQ, B, T, H, HKV, D, scale, causal,
+                               window, dtype, stream, bq, bk);
     if (s == FA_OK)
         s = flash_attn_bwd_dkdv(Q, K, V, dO, L, Dvec, dK, dV, B, T, H, HKV, D, scale, causal,
                                 window, dtype, stream, bq, bk);
-    if (s == FA_OK)
-        s = flash_attn_bwd_dq(Q, K, V, dO, L, Dvec, dQ, B, T, H, HKV, D, scale, causal, window,
-                              dtype, stream, bq, bk);
     const hipError_t fe = hipFreeAsync(Dvec, stream);
     if (s == FA_OK && fe != hipSuccess) s = FA_ERR_HIP;
     return s;

@@ -307,12 +307,13 @@ __device__ __forceinline__ void dq_issue(char* st, const Buf& kbuf, const Buf& v
 
 }  // namespace
 
-template <int D, int NW>
+template <int D, int NW, bool FUSE_D>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-    const float* __restrict__ L, const float* __restrict__ Dv, float* __restrict__ dQ, int B,
-    int T, int H, int HKV, float scale, int causal, int window, int nqt, int xcd_group) {
+    const uint16_t* __restrict__ O, const float* __restrict__ L, float* __restrict__ Dv,
+    float* __restrict__ dQ, int B, int T, int H, int HKV, float scale, int causal, int window,
+    int nqt, int xcd_group) {
     using C = DqCfg<D, NW>;
     extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
     char* sm = reinterpret_cast<char*>(smem);
@@ -344,7 +345,30 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_bf16_kernel(
         }
     }
     const float l2 = q < T ? L[((int64_t)b * H + h) * T + q] * kLog2e : kBigLse;
-    const float dq_i = q < T ? Dv[((int64_t)b * H + h) * T + q] : 0.f;
+    float dq_i;
+    if constexpr (FUSE_D) {
+        // D_i = sum_d dO[i][d] O[i][d] from this lane's 8*DC columns plus the other half's;
+        // rows past T load zeros and give 0
+        const int64_t base = ((int64_t)b * T + q) * ldq + (int64_t)h * D + 8 * g;
+        float s = 0.f;
+#pragma unroll
+        for (int dc = 0; dc < C::DC; ++dc) {
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            const u32x4 o = q < T ? *reinterpret_cast<const u32x4*>(O + base + dc * 16) : z;
+            const u32x4 d = __builtin_bit_cast(u32x4, oreg[dc]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t x = o[i], y = d[i];
+                s = fmaf(__builtin_bit_cast(float, x << 16), __builtin_bit_cast(float, y << 16), s);
+                s = fmaf(__builtin_bit_cast(float, x & 0xffff0000u),
+                         __builtin_bit_cast(float, y & 0xffff0000u), s);
+            }
+        }
+        dq_i = halves_sum(s);
+        if (g == 0 && q < T) Dv[((int64_t)b * H + h) * T + q] = dq_i;
+    } else {
+        dq_i = q < T ? Dv[((int64_t)b * H + h) * T + q] : 0.f;
+    }
     // keys this query row may see: [klo, khi]
     const int klo = window > 0 ? q - window + 1 : 0;
     const int khi = cz ? q : T - 1;
@@ -476,19 +500,20 @@ static_assert(DqCfg<128, kDqWaves>::BQ == kBf16DqBq && DqCfg<128, kDqWaves>::BK 
 static_assert(Dkdv16Cfg<128>::BQ == kBf16DkdvBq && Dkdv16Cfg<128>::BKW == kBf16DkdvBk,
               "dK/dV tiling differs from kernels.h");
 
-template <int D>
+template <int D, bool FUSE_D>
 hipError_t launch_dq_bf16_t(const AttnArgs& a) {
     using C = DqCfg<D, kDqWaves>;
     static bool set[kMaxDevices] = {};
     const size_t lds = 2 * (size_t)C::STAGE;
-    hipError_t e = allow_lds(dq_bf16_kernel<D, kDqWaves>, lds, set);
+    hipError_t e = allow_lds(dq_bf16_kernel<D, kDqWaves, FUSE_D>, lds, set);
     if (e != hipSuccess) return e;
     const int nqt = (a.T + C::BQ - 1) / C::BQ;
     const unsigned grid = (unsigned)nqt * a.B * a.H;
-    hipLaunchKernelGGL((dq_bf16_kernel<D, kDqWaves>), dim3(grid), dim3(C::NT), lds, a.stream,
-                       (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
-                       (const uint16_t*)a.dO, a.Lin, a.Dvec, a.dQ, a.B, a.T, a.H, a.HKV, a.scale,
-                       a.causal, a.window, nqt, xcd_group_for(nqt, a.B, a.H, a.HKV));
+    hipLaunchKernelGGL((dq_bf16_kernel<D, kDqWaves, FUSE_D>), dim3(grid), dim3(C::NT), lds,
+                       a.stream, (const uint16_t*)a.Q, (const uint16_t*)a.K,
+                       (const uint16_t*)a.V, (const uint16_t*)a.dO, (const uint16_t*)a.O, a.Lin,
+                       a.Dvec, a.dQ, a.B, a.T, a.H, a.HKV, a.scale, a.causal, a.window, nqt,
+                       xcd_group_for(nqt, a.B, a.H, a.HKV));
     return hipGetLastError();
 }
 
@@ -501,8 +526,15 @@ hipError_t launch_dkdv_bf16(const AttnArgs& a) {
 }
 
 hipError_t launch_dq_bf16(const AttnArgs& a) {
-    if (a.D == 64) return launch_dq_bf16_t<64>(a);
-    if (a.D == 128) return launch_dq_bf16_t<128>(a);
+    if (a.D == 64) return launch_dq_bf16_t<64, false>(a);
+    if (a.D == 128) return launch_dq_bf16_t<128, false>(a);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_dq_bf16_fused_d(const AttnArgs& a) {
+    if (a.O == nullptr) return hipErrorInvalidValue;
+    if (a.D == 64) return launch_dq_bf16_t<64, true>(a);
+    if (a.D == 128) return launch_dq_bf16_t<128, true>(a);
     return hipErrorInvalidValue;
 }
 

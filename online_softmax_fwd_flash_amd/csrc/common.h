@@ -78,6 +78,15 @@ __device__ __forceinline__ float halves_max(float v) {
     return __builtin_elementwise_maximum(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
 }
 
+// v[l] + v[l ^ 32] for every lane l (same exchange as halves_max; a two-term float sum is
+// commutative, so both halves get the same bits)
+__device__ __forceinline__ float halves_sum(float v) {
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const unsigned r0 = r[0], r1 = r[1];
+    return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+}
+
 __device__ __forceinline__ float xor_shfl(float v, int mask) {
     return __shfl_xor(v, mask, 64);
 }

@@ -39,6 +39,9 @@ hipError_t launch_dq_f32(const AttnArgs& a, int bq, int bk);
 hipError_t launch_fwd_bf16(const AttnArgs& a);
 hipError_t launch_dkdv_bf16(const AttnArgs& a);
 hipError_t launch_dq_bf16(const AttnArgs& a);
+// dQ that also computes Dvec[b,h,i] = rowsum(dO * O) for its own rows from a.O and writes it
+// to a.Dvec (the dK/dV pass launched after it reads those values)
+hipError_t launch_dq_bf16_fused_d(const AttnArgs& a);
 
 // dtype: 0 = f32, 1 = bf16
 hipError_t launch_bwd_preprocess(const void* O, const void* dO, float* Dvec, int B, int T,

@@ -57,6 +57,13 @@ def bwd(ptrs=(A,) * 9, **kw):
                                      p["causal"], p["window"], p["dtype"], S0)
 
 
+def dq_dvec(ptrs=(A,) * 8, bq=0, bk=0, **kw):
+    p = dict(GOOD, **kw)
+    return _lib.lib().flash_attn_bwd_dq_dvec(*ptrs, p["B"], p["T"], p["H"], p["HKV"], p["D"],
+                                             p["scale"], p["causal"], p["window"], p["dtype"], S0,
+                                             bq, bk)
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(B=0), 1), (dict(T=0), 1), (dict(H=0), 1), (dict(HKV=0), 1), (dict(D=0), 1),
     (dict(H=6, HKV=4), 1), (dict(window=-1), 1), (dict(scale=float("nan")), 1),
@@ -69,6 +76,7 @@ def bwd(ptrs=(A,) * 9, **kw):
 def test_fwd_and_bwd_reject_before_launch(kw, code):
     assert fwd(**kw) == code
     assert bwd(**kw) == code
+    assert dq_dvec(**kw) == code
 
 
 @pytest.mark.parametrize("which", range(5))
@@ -80,6 +88,9 @@ def test_null_and_misaligned_pointers(which):
         ptrs9 = [A] * 9
         ptrs9[which + 4] = bad
         assert bwd(tuple(ptrs9)) == 1
+        ptrs8 = [A] * 8
+        ptrs8[which + 3] = bad
+        assert dq_dvec(tuple(ptrs8)) == 1
 
 
 def test_bad_tiles_rejected():
@@ -89,6 +100,9 @@ def test_bad_tiles_rejected():
     assert L.flash_attn_fwd_ex(*args, 64, 8) == 1
     args16 = (A, A, A, A, A, 1, 64, 2, 2, 64, 0.125, 1, 0, 1, S0)
     assert L.flash_attn_fwd_ex(*args16, 64, 64) == 1
+    assert dq_dvec(bq=64, bk=64) == 1
+    assert dq_dvec(bq=128, bk=32) == 1
+    assert dq_dvec(dtype=0, bq=48, bk=16) == 1
 
 
 def test_default_tiles():

@@ -1,5 +1,6 @@
 """Each backward stage through its own C-ABI entry point vs the oracle (GPU): Dvec from the
-preprocess, then dK/dV and dQ given the oracle-checked forward outputs."""
+preprocess, then dK/dV and dQ given the oracle-checked forward outputs; and the fused pass that
+produces dQ and Dvec together."""
 import math
 
 import numpy as np
@@ -16,6 +17,19 @@ pytestmark = pytest.mark.gpu
 CASES = [("f32", 64, (32, 32)), ("f32", 16, (64, 16)), ("bf16", 64, (0, 0)), ("bf16", 128, (0, 0))]
 
 
+def check_dvec(dvec, o, dod, ref, dtype):
+    """Dvec is computed from the stored O (dtype precision), the oracle's from its fp64 O."""
+    if dtype == "f32":
+        compare("Dvec", to_np(dvec), ref["delta"], dtype)
+        return
+    # exact dot of the stored bf16 O with dO, up to fp32 summation
+    want = (to_np(o) * to_np(dod)).sum(-1).transpose(0, 2, 1)
+    assert np.abs(to_np(dvec) - want).max() < 1e-4
+    # and within bf16 rounding of O (unit roundoff 2^-8) of the exact fp64 D
+    bound = 2.0 ** -8 * np.abs(ref["o"] * to_np(dod)).sum(-1).transpose(0, 2, 1) + 1e-4
+    assert (np.abs(to_np(dvec) - ref["delta"]) <= bound).all()
+
+
 @pytest.mark.parametrize("dtype,D,tiles", CASES)
 @pytest.mark.parametrize("causal,window", [(True, 0), (True, 9), (False, 0)])
 def test_backward_stages(dtype, D, tiles, causal, window):
@@ -30,16 +44,7 @@ def test_backward_stages(dtype, D, tiles, causal, window):
     dvec = torch.full((B, H, T), float("nan"), device="cuda", dtype=torch.float32)
     fa.flash_attn_bwd_preprocess(o, dod, dvec)
     torch.cuda.synchronize()
-    # Dvec is computed from the stored O (dtype precision), the oracle's from its fp64 O
-    if dtype == "f32":
-        compare("Dvec", to_np(dvec), ref["delta"], dtype)
-    else:
-        # exact dot of the stored bf16 O with dO, up to fp32 summation
-        want = (to_np(o) * to_np(dod)).sum(-1).transpose(0, 2, 1)
-        assert np.abs(to_np(dvec) - want).max() < 1e-4
-        # and within bf16 rounding of O (unit roundoff 2^-8) of the exact fp64 D
-        bound = 2.0 ** -8 * np.abs(ref["o"] * to_np(dod)).sum(-1).transpose(0, 2, 1) + 1e-4
-        assert (np.abs(to_np(dvec) - ref["delta"]) <= bound).all()
+    check_dvec(dvec, o, dod, ref, dtype)
     nan = float("nan")
     dk = torch.full(kd.shape, nan, device="cuda", dtype=torch.float32)
     dv = torch.full(kd.shape, nan, device="cuda", dtype=torch.float32)
@@ -53,3 +58,11 @@ def test_backward_stages(dtype, D, tiles, causal, window):
                          dq=dq, tiles=tiles)
     torch.cuda.synchronize()
     compare("dQ", to_np(dq), ref["dq"], dtype)
+    # dQ and Dvec from the one fused pass
+    dq2 = torch.full(qd.shape, nan, device="cuda", dtype=torch.float32)
+    dvec2 = torch.full((B, H, T), nan, device="cuda", dtype=torch.float32)
+    fa.flash_attn_bwd_dq_dvec(qd, kd, vd, o, dod, lse, dvec=dvec2, causal=causal, window=window,
+                              scale=scale, dq=dq2, tiles=tiles)
+    torch.cuda.synchronize()
+    check_dvec(dvec2, o, dod, ref, dtype)
+    compare("dQ (fused Dvec)", to_np(dq2), ref["dq"], dtype)
