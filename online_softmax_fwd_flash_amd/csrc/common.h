@@ -42,17 +42,6 @@ __device__ __forceinline__ f32x4 mfma16x16x4f32(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// acc += a * b on the 32x32x16 bf16 MFMA with the accumulator held in AGPRs, for
-// accumulators that only MFMAs touch inside a loop (the VGPRs stay free for the operands and
-// the VALU work).  The compiler inserts no hazard wait states around inline asm: the two in
-// front cover a VALU write of `a`, `b` or an AGPR write of `acc` just before; any other read
-// of `acc` after the last call must follow mfma_drain().
-__device__ __forceinline__ void mfma32_agpr(f32x16& acc, bf16x8 a, bf16x8 b) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-// wait states between an MFMA writing an accumulator and another instruction reading it
-__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
-
 // LDS transpose read (ds_read_b64_tr_b16), per 16-lane group: when lane j of the group reads
 // 4 consecutive bf16 of row r0 + j/4 starting at column c0 + 4*(j%4), lane i receives column
 // c0 + i of rows r0 .. r0+3.  `p` must point into LDS.
