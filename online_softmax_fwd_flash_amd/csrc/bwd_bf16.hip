@@ -39,11 +39,12 @@ constexpr float kBigLse = 3.0e38f;   // L of a padding row: exp2(s*c - big) = 0
 }  // namespace
 
 // ------------------------------------------------------------------------------ dK / dV
-// Workgroup = 8 waves x 16 keys of one (b, kv head), two waves per SIMD.  16x16x32 MFMAs: S = Q K^T puts the wave's 16 keys on the accumulator columns and 4
-// query rows per lane, so P and dS of two 16-row blocks concatenate into the A operand of
-// dV += P^T dO and dK += dS^T Q (32 query rows per k-step), whose B operands come from the
-// same row-major Q / dO tiles through LDS transpose reads.  Per wave: K / V operands 32 registers,
-// dK / dV accumulators 64.
+// Workgroup = 4 waves x 16 keys of one (b, kv head), three workgroups per CU.  16x16x32
+// MFMAs: S = Q K^T puts the wave's 16 keys on the accumulator columns and 4 query rows per
+// lane, so P and dS of two 16-row blocks concatenate into the A operand of dV += P^T dO and
+// dK += dS^T Q (32 query rows per k-step), whose B operands come from the same row-major
+// Q / dO tiles through LDS transpose reads.  Per wave: K / V operands 32 registers, dK / dV
+// accumulators 64.
 namespace {
 
 template <int D>

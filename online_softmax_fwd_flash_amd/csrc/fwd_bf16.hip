@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < C::KMAX; ++i) koff[i] = dma_src_offset_padded<D>(w + i * C::NW, lane, ldk_b);
 #pragma unroll
-    for (int i = 0; i < C::VPW; ++i) voff[i] = dma_src_offset<D, true>(w * C::VPW + i, lane, ldk_b);
+    for (int i = 0; i < C::VPW; ++i) voff[i] = dma_src_offset_swz<D>(w * C::VPW + i, lane, ldk_b);
     // LDS read offsets inside a stage.  K operand: rows n and 32 + n, chunk 2*dc + g (padded
     // rows: consecutive k-steps are 32 bytes apart).  V^T operand via transpose reads: lane
     // 16*cq + jj reads 8 bytes of row 16*kh + 4*(cq/2) + jj/4 (and 8 rows further) at

@@ -32,38 +32,6 @@ __device__ __forceinline__ Buf rows_buf(const uint16_t* base, int64_t ld, int T)
     return Buf(base, (uint32_t)(T * ld * 2));
 }
 
-// A ROWS x D tile loaded row-major: 16-byte chunk t + p*NT of the tile for thread t
-// (consecutive threads read consecutive bytes of a row), stored in the natural layout.
-template <int ROWS, int D, int NT, int LD = D + 8>
-struct RowChunks {
-    static constexpr int NCH = ROWS * D / 8;
-    static constexpr int PER = (NCH + NT - 1) / NT;
-    static constexpr int LDN = LD;
-    u32x4 v[PER];
-
-    __device__ __forceinline__ void load(const Buf& src, uint32_t ld_bytes, int row0) {
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int e = threadIdx.x + p * NT;
-            if (NCH % NT == 0 || e < NCH) {
-                const int r = e / (D / 8), cc = e % (D / 8);
-                v[p] = src.load16((uint32_t)(row0 + r) * ld_bytes + cc * 16);
-            }
-        }
-    }
-
-    __device__ __forceinline__ void store(uint16_t* __restrict__ dst) const {
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int e = threadIdx.x + p * NT;
-            if (NCH % NT == 0 || e < NCH) {
-                const int r = e / (D / 8), cc = e % (D / 8);
-                *reinterpret_cast<u32x4*>(dst + r * LDN + cc * 8) = v[p];
-            }
-        }
-    }
-};
-
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // s_waitcnt vmcnt(N) only (gfx9 encoding: vmcnt in [3:0] and [15:14]; expcnt [6:4] and
@@ -82,30 +50,25 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "me
 
 // Unpadded row-major [rows x D] bf16 tile in LDS whose 16-byte chunks are XOR-swizzled per
 // row, filled by LDS-DMA (buffer_load ... lds, 16 bytes per lane: a wave instruction writes
-// 1 KB of consecutive LDS bytes, so padding is impossible and the swizzle does its job).
-// 128 four-byte banks = 512 bytes per bank line = RP rows.
-//  * kswz: for tiles read 16 bytes per lane by 32 lanes at one logical chunk of 32
-//    consecutive rows (MFMA operand rows): rows sharing a bank line position get distinct
-//    chunks.
-//  * vswz: for tiles read with ds_read_b64_tr_b16 (8 consecutive rows x 4 adjacent chunks
-//    per wave): XOR with a multiple of 4 keeps the 4 chunks adjacent and spreads the rows.
+// 1 KB of consecutive LDS bytes).  The swizzle serves tiles read with ds_read_b64_tr_b16
+// (8 consecutive rows x 4 adjacent chunks per wave): XOR with a multiple of 4 keeps the 4
+// chunks adjacent and spreads the rows over the 128 four-byte banks (512 bytes = RP rows).
 template <int D>
 struct Swz {
     static constexpr int ROWB = 2 * D;         // bytes per row
     static constexpr int CPR = D / 8;          // 16-byte chunks per row
     static constexpr int RP = 512 / ROWB;      // rows per bank line
-    static __device__ __forceinline__ int k(int r) { return (r / RP) % CPR; }
     static __device__ __forceinline__ int v(int r) { return 4 * ((r / RP) % (CPR / 4)); }
 };
 
 // Byte offset, relative to the tile's first global row, of the 16 bytes lane `lane` moves
-// into slot `lane` of LDS-DMA piece p (tile bytes [p KB, p KB + 1 KB)), for swizzle S.
-template <int D, bool VSWZ>
-__device__ __forceinline__ uint32_t dma_src_offset(int p, int lane, uint32_t ld_bytes) {
+// into slot `lane` of LDS-DMA piece p (tile bytes [p KB, p KB + 1 KB)) of a swizzled tile.
+template <int D>
+__device__ __forceinline__ uint32_t dma_src_offset_swz(int p, int lane, uint32_t ld_bytes) {
     using S = Swz<D>;
     const int byte = p * 1024 + 16 * lane;
     const int r = byte / S::ROWB, pc = (byte % S::ROWB) / 16;
-    return (uint32_t)r * ld_bytes + 16u * (uint32_t)(pc ^ (VSWZ ? S::v(r) : S::k(r)));
+    return (uint32_t)r * ld_bytes + 16u * (uint32_t)(pc ^ S::v(r));
 }
 
 // Padded row-major [rows x D] bf16 tile filled by LDS-DMA: rows are D + 8*PADC elements
