@@ -13,7 +13,9 @@
  *               flashAttentionQKVPackedGrad (backward), getTriuOffsetSequence (causal masks
  *               of non-square blocks).
  *   [teeny]     "flash_attn2.rs" (teeny-kernels 0.2.0): forward, backward_dq, backward_dkv
- *               doc comments.
+ *               doc comments; the module comment on the tensor layout.
+ *   [flashback] "flashback.metal" (FlashMetal): backprop_attention, its batch and head
+ *               offset arithmetic.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -39,8 +41,9 @@
  *  Errors: arguments are validated on the host before anything is enqueued.
  *    FA_ERR_INVALID_ARG  null pointer, B/T/H/HKV/D < 1, H % HKV != 0, window < 0,
  *                        scale not finite or <= 0, misaligned pointer, size overflow
- *                        (B*T*H*D > 2^40 elements, or for bf16 one batch slice of Q/K
- *                        reaching 2 GiB), tile sizes that are not supported values;
+ *                        (B*T*H*D > 2^40 elements, or for bf16 the T rows of one head
+ *                        spanning 2 GiB), an unusable layout (flash_attn_*_strided), tile
+ *                        sizes that are not supported values;
  *    FA_ERR_UNSUPPORTED  a valid request this build has no kernel for (head dim);
  *    FA_ERR_HIP          a HIP runtime error while enqueueing (hipGetLastError).
  *  No C++ exception crosses this interface.
@@ -50,6 +53,8 @@
  */
 #ifndef FLASH_ATTN_H
 #define FLASH_ATTN_H
+
+#include <stdint.h>
 
 #include <hip/hip_runtime_api.h>
 
@@ -78,9 +83,9 @@ fa_status_t flash_attn_fwd(const void* Q, const void* K, const void* V, void* O,
  *   Dvec_i = dO_i . O_i;  P = exp(scale * Q K^T - L) on visible entries;  dP = dO V^T;
  *   dS = P * (dP - Dvec);  dQ = scale dS K;  dK = scale dS^T Q;  dV = P^T dO,
  * dK and dV summed over the H/HKV query heads of each KV head.  O and L must be the forward's
- * outputs for the same inputs.  Outputs dQ, dK, dV are float32.  Runs the three stages below
- * in order on `stream`; the Dvec workspace (B*H*T floats) is allocated stream-ordered
- * (hipMallocAsync) and released the same way. */
+ * outputs for the same inputs.  Outputs dQ, dK, dV are float32.  Runs flash_attn_bwd_dq_dvec
+ * and then flash_attn_bwd_dkdv on `stream`; the Dvec workspace (B*H*T floats) is allocated
+ * stream-ordered (hipMallocAsync) and released the same way. */
 fa_status_t flash_attn_bwd(const void* Q, const void* K, const void* V, const void* O,
                            const float* L, const void* dO, float* dQ, float* dK, float* dV,
                            int B, int T, int H, int HKV, int D, float scale, int causal,
@@ -98,6 +103,34 @@ fa_status_t flash_attn_bwd_ex(const void* Q, const void* K, const void* V, const
                               const float* L, const void* dO, float* dQ, float* dK, float* dV,
                               int B, int T, int H, int HKV, int D, float scale, int causal,
                               int window, fa_dtype_t dtype, hipStream_t stream, int bq, int bk);
+
+/* Element strides of a [B, T, heads, D] tensor view: `batch`, `row` and `head` are the
+ * distances, in elements, from (b, t, h, 0) to (b + 1, t, h, 0), (b, t + 1, h, 0) and
+ * (b, t, h + 1, 0); the D elements of a row are contiguous.  For a tensor of `heads` heads:
+ *   contiguous [B, T, heads, D] (the layout of the entry points above): {T*heads*D, heads*D, D}
+ *   [B, heads, T, D] ([flashback] backprop_attention) and [B*heads, T, D] ([teeny] module
+ *   comment): {heads*T*D, D, T*D}
+ *   each third of a packed [3, B*H, T, D] QKV buffer ([ipu] flashAttentionQKVPackedWithStash,
+ *   whose qkv is 3 x G x L x D): the [B, H, T, D] strides, from that third's base pointer. */
+typedef struct fa_layout {
+    int64_t batch, row, head;
+} fa_layout_t;
+
+/* As flash_attn_fwd / flash_attn_bwd on strided views.  Q, O, dO and dQ follow q_layout
+ * (H heads), K, V, dK and dV follow kv_layout (HKV heads), in elements of each tensor's own
+ * type (so the float32 gradients take the same element strides as their bf16 inputs); L and
+ * Dvec stay [B, H, T] float32.  Default tiling.  A layout is rejected (FA_ERR_INVALID_ARG)
+ * unless its strides are non-negative multiples of 16 bytes, row >= D, distinct
+ * (b, t, head) never overlap, and, for bf16, one head's T rows span under 2 GiB. */
+fa_status_t flash_attn_fwd_strided(const void* Q, const void* K, const void* V, void* O,
+                                   float* L, int B, int T, int H, int HKV, int D, float scale,
+                                   int causal, int window, fa_dtype_t dtype, hipStream_t stream,
+                                   fa_layout_t q_layout, fa_layout_t kv_layout);
+fa_status_t flash_attn_bwd_strided(const void* Q, const void* K, const void* V, const void* O,
+                                   const float* L, const void* dO, float* dQ, float* dK,
+                                   float* dV, int B, int T, int H, int HKV, int D, float scale,
+                                   int causal, int window, fa_dtype_t dtype, hipStream_t stream,
+                                   fa_layout_t q_layout, fa_layout_t kv_layout);
 
 /* Backward stage 1 ([ipu] flashAttentionQKVPackedGrad, its D = rowsum(O * grad) step;
  * [forge] backward section comment; [teeny] backward_dq): Dvec[b,h,i] = sum_d dO[b,i,h,d] *
@@ -157,6 +190,13 @@ fa_status_t flash_attn_kv_block_range(int T, int bq, int bk, int causal, int win
 /* Tiling the library picks for a dtype / head dim: pass 0 = forward, 1 = dK/dV, 2 = dQ.
  * *bq, *bk are the query and key block sizes of that pass. */
 fa_status_t flash_attn_default_tiles(fa_dtype_t dtype, int D, int pass, int* bq, int* bk);
+
+/* The layout check flash_attn_*_strided apply to each view: FA_OK if `layout` describes a
+ * usable [B, T, heads, D] view of element type `dtype` (strides non-negative multiples of
+ * 16 bytes, row >= D, no two (b, t, head) rows overlapping, and for bf16 one head's T rows
+ * spanning under 2 GiB), FA_ERR_INVALID_ARG otherwise. */
+fa_status_t flash_attn_check_layout(fa_layout_t layout, int B, int T, int heads, int D,
+                                    fa_dtype_t dtype);
 
 /* Library ABI version (major * 100 + minor). */
 int flash_attn_version(void);

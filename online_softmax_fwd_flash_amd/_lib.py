@@ -14,7 +14,8 @@ FA_DTYPE_F32, FA_DTYPE_BF16 = 0, 1
 EXPORTS = [
     "flash_attn_fwd", "flash_attn_bwd", "flash_attn_fwd_ex", "flash_attn_bwd_ex",
     "flash_attn_bwd_preprocess", "flash_attn_bwd_dkdv", "flash_attn_bwd_dq",
-    "flash_attn_bwd_dq_dvec",
+    "flash_attn_bwd_dq_dvec", "flash_attn_fwd_strided", "flash_attn_bwd_strided",
+    "flash_attn_check_layout",
     "flash_attn_status_string", "flash_attn_block_class", "flash_attn_kv_block_range",
     "flash_attn_default_tiles", "flash_attn_version",
 ]
@@ -27,6 +28,11 @@ F = ctypes.c_float
 _DIMS = [I, I, I, I, I, F, I, I, I, P]          # B T H HKV D scale causal window dtype stream
 
 
+class Layout(ctypes.Structure):
+    """fa_layout_t: element strides (batch, row, head) of a [B, T, heads, D] view."""
+    _fields_ = [("batch", ctypes.c_int64), ("row", ctypes.c_int64), ("head", ctypes.c_int64)]
+
+
 def _declare(lib):
     sig = {
         "flash_attn_fwd": [P, P, P, P, P] + _DIMS,
@@ -37,6 +43,9 @@ def _declare(lib):
         "flash_attn_bwd_dkdv": [P] * 8 + _DIMS + [I, I],
         "flash_attn_bwd_dq": [P] * 7 + _DIMS + [I, I],
         "flash_attn_bwd_dq_dvec": [P] * 8 + _DIMS + [I, I],
+        "flash_attn_fwd_strided": [P] * 5 + _DIMS + [Layout, Layout],
+        "flash_attn_bwd_strided": [P] * 9 + _DIMS + [Layout, Layout],
+        "flash_attn_check_layout": [Layout, I, I, I, I, I],
         "flash_attn_block_class": [I, I, I, I, I, I, I, ctypes.POINTER(I)],
         "flash_attn_kv_block_range": [I, I, I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)],
         "flash_attn_default_tiles": [I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)],

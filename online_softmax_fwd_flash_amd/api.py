@@ -160,6 +160,71 @@ def flash_attn_bwd(q, k, v, o, lse, do, causal=True, window=0, scale=None, dq=No
     return dq, dk, dv
 
 
+def _layout(t, name):
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError(f"{name}: expected a [B, T, heads, D] view with a contiguous last axis")
+    sb, st, sh, _ = t.stride()
+    return _lib.Layout(sb, st, sh)
+
+
+def _want_view(t, like, dtype, name):
+    """t must be a cuda tensor of like's shape and strides (elements) in dtype."""
+    if (tuple(t.shape) != tuple(like.shape) or tuple(t.stride()) != tuple(like.stride())
+            or t.dtype != dtype or not t.is_cuda):
+        raise ValueError(f"{name}: expected a {dtype} cuda view with shape {tuple(like.shape)} "
+                         f"and strides {tuple(like.stride())}")
+
+
+def _empty_like_view(like, dtype):
+    return torch.empty_strided(like.shape, like.stride(), dtype=dtype, device=like.device)
+
+
+def flash_attn_fwd_strided(q, k, v, causal=True, window=0, scale=None, out=None, lse=None,
+                           stream=None):
+    """flash_attn_fwd on [B, T, heads, D] views with any strides (last axis contiguous), e.g.
+    x.transpose(1, 2) of a [B, H, T, D] tensor or of a third of a packed QKV buffer.  k and v
+    share strides; O takes q's strides."""
+    B, T, H, HKV, D = _dims(q, k)
+    _want_view(k, k, q.dtype, "k")
+    _want_view(v, k, q.dtype, "v")
+    out = _empty_like_view(q, q.dtype) if out is None else out
+    _want_view(out, q, q.dtype, "out")
+    lse = torch.empty(B, H, T, device=q.device, dtype=torch.float32) if lse is None else lse
+    _want(lse, (B, H, T), torch.float32, "lse")
+    code = _lib.lib().flash_attn_fwd_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                             B, T, H, HKV, D, _scale(scale, D),
+                                             int(bool(causal)), int(window), _DT[q.dtype],
+                                             _stream(stream), _layout(q, "q"), _layout(k, "k"))
+    _check("flash_attn_fwd_strided", code)
+    return out, lse
+
+
+def flash_attn_bwd_strided(q, k, v, o, lse, do, causal=True, window=0, scale=None, dq=None,
+                           dk=None, dv=None, stream=None):
+    """flash_attn_bwd on strided views: o, do and dq (float32) take q's strides, dk and dv
+    (float32) take k's."""
+    B, T, H, HKV, D = _dims(q, k)
+    _want_view(k, k, q.dtype, "k")
+    _want_view(v, k, q.dtype, "v")
+    _want_view(o, q, q.dtype, "o")
+    _want_view(do, q, q.dtype, "do")
+    _want(lse, (B, H, T), torch.float32, "lse")
+    f32 = torch.float32
+    dq = _empty_like_view(q, f32) if dq is None else dq
+    dk = _empty_like_view(k, f32) if dk is None else dk
+    dv = _empty_like_view(k, f32) if dv is None else dv
+    _want_view(dq, q, f32, "dq")
+    _want_view(dk, k, f32, "dk")
+    _want_view(dv, k, f32, "dv")
+    code = _lib.lib().flash_attn_bwd_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                             _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), B, T, H,
+                                             HKV, D, _scale(scale, D), int(bool(causal)),
+                                             int(window), _DT[q.dtype], _stream(stream),
+                                             _layout(q, "q"), _layout(k, "k"))
+    _check("flash_attn_bwd_strided", code)
+    return dq, dk, dv
+
+
 def flash_attn_block_class(T, bq, bk, causal, window, i, j):
     """(class, off) of block (i, j): class 0 skip, 1 full, 2 masked; off = i*bq - j*bk."""
     off = ctypes.c_int(0)
@@ -184,6 +249,12 @@ def flash_attn_default_tiles(dtype, D, pass_):
     _check("flash_attn_default_tiles",
            _lib.lib().flash_attn_default_tiles(dt, D, pass_, ctypes.byref(bq), ctypes.byref(bk)))
     return bq.value, bk.value
+
+
+def flash_attn_check_layout(strides, B, T, heads, D, dtype):
+    """Status code (0 = usable) of the library's check of element strides (batch, row, head)
+    for a [B, T, heads, D] view; dtype 0 = f32, 1 = bf16."""
+    return _lib.lib().flash_attn_check_layout(_lib.Layout(*strides), B, T, heads, D, dtype)
 
 
 def flash_attn_version():

@@ -28,11 +28,55 @@ fa_status_t check_dims(int B, int T, int H, int HKV, int D, float scale, int cau
         if (D % 8 != 0 || D > 128) return FA_ERR_UNSUPPORTED;
     } else {
         if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
-        // the bf16 kernels address one batch slice of a tensor with 32-bit buffer offsets
-        if ((double)T * (H > HKV ? H : HKV) * D * 2.0 >= 2147483648.0) return FA_ERR_INVALID_ARG;
     }
     return FA_OK;
 }
+
+// A [B, T, heads, D] view with element strides l (D contiguous) that the kernels can use:
+// strides non-negative and multiples of 16 bytes (every row starts 16-byte aligned), rows at
+// least D apart (so a head's rows end before row T begins: the bf16 kernels read rows past T
+// as zeros), distinct (b, t, h) never overlap, and, for bf16, one head's T rows (plus the
+// staging tiles' overhang) span less than 2 GiB (32-bit buffer offsets within a head).
+fa_status_t check_layout(const fa_layout_t& l, int B, int T, int heads, int D, fa_dtype_t dtype) {
+    const int64_t esz = dtype == FA_DTYPE_F32 ? 4 : 2, align = 16 / esz;
+    const int64_t st[3] = {l.row, l.head, l.batch};
+    const int64_t ext[3] = {T, heads, B};
+    for (int i = 0; i < 3; ++i) {
+        if (st[i] < 0) return FA_ERR_INVALID_ARG;
+        // the row stride is used even when T = 1 (for the rows past T the kernels read as zeros)
+        if ((i == 0 || ext[i] > 1) && st[i] % align != 0) return FA_ERR_INVALID_ARG;
+    }
+    if (l.row < D) return FA_ERR_INVALID_ARG;
+    // non-overlap: order the axes of extent > 1 by stride; each must step past the block the
+    // smaller ones span (the innermost block is the D contiguous elements)
+    int idx[3], n = 0;
+    for (int i = 0; i < 3; ++i)
+        if (ext[i] > 1) idx[n++] = i;
+    for (int i = 1; i < n; ++i)
+        for (int j = i; j > 0 && st[idx[j]] < st[idx[j - 1]]; --j) {
+            const int t = idx[j]; idx[j] = idx[j - 1]; idx[j - 1] = t;
+        }
+    double span = D;
+    for (int i = 0; i < n; ++i) {
+        if ((double)st[idx[i]] < span) return FA_ERR_INVALID_ARG;
+        span = (double)st[idx[i]] * (double)ext[idx[i]];
+    }
+    if (span * esz > 9.0e18) return FA_ERR_INVALID_ARG;
+    if (dtype != FA_DTYPE_F32 && ((double)(T - 1) * l.row + D + 128.0 * l.row) * esz >= 2147483648.0)
+        return FA_ERR_INVALID_ARG;
+    return FA_OK;
+}
+
+// The layouts of contiguous [B, T, H, D] (queries) and [B, T, HKV, D] (keys) tensors.
+fa_layout_t dense_layout(int T, int heads, int D) {
+    fa_layout_t l;
+    l.batch = (int64_t)T * heads * D;
+    l.row = (int64_t)heads * D;
+    l.head = D;
+    return l;
+}
+
+fa::Layout to_layout(const fa_layout_t& l) { return fa::Layout{l.batch, l.row, l.head}; }
 
 fa_status_t check_ptrs(std::initializer_list<const void*> ps) {
     for (const void* p : ps) {
@@ -53,11 +97,138 @@ fa_status_t resolve_f32_tiles(int& bq, int& bk) {
 fa_status_t hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
 fa::AttnArgs make_args(int B, int T, int H, int HKV, int D, float scale, int causal, int window,
-                       hipStream_t stream) {
+                       hipStream_t stream, const fa_layout_t& lq, const fa_layout_t& lk) {
     fa::AttnArgs a{};
     a.B = B; a.T = T; a.H = H; a.HKV = HKV; a.D = D;
     a.scale = scale; a.causal = causal; a.window = window; a.stream = stream;
+    a.lq = to_layout(lq); a.lk = to_layout(lk);
     return a;
+}
+
+// Shared validation of the attention entry points: pointers, sizes and both layouts.
+fa_status_t check_all(std::initializer_list<const void*> ps, int B, int T, int H, int HKV, int D,
+                      float scale, int causal, int window, fa_dtype_t dtype,
+                      const fa_layout_t& lq, const fa_layout_t& lk) {
+    fa_status_t s = check_ptrs(ps);
+    if (s != FA_OK) return s;
+    if ((s = check_dims(B, T, H, HKV, D, scale, causal, window, dtype)) != FA_OK) return s;
+    if ((s = check_layout(lq, B, T, H, D, dtype)) != FA_OK) return s;
+    return check_layout(lk, B, T, HKV, D, dtype);
+}
+
+fa_status_t fwd_impl(const void* Q, const void* K, const void* V, void* O, float* L, int B, int T,
+                     int H, int HKV, int D, float scale, int causal, int window,
+                     fa_dtype_t dtype, hipStream_t stream, int bq, int bk,
+                     const fa_layout_t& lq, const fa_layout_t& lk) {
+    fa_status_t s = check_all({Q, K, V, O, L}, B, T, H, HKV, D, scale, causal, window, dtype, lq, lk);
+    if (s != FA_OK) return s;
+    fa::AttnArgs a = make_args(B, T, H, HKV, D, scale, causal, window, stream, lq, lk);
+    a.Q = Q; a.K = K; a.V = V; a.Oout = O; a.O = O; a.L = L;
+    if (dtype == FA_DTYPE_F32) {
+        if ((s = resolve_f32_tiles(bq, bk)) != FA_OK) return s;
+        return hip_status(fa::launch_fwd_f32(a, bq, bk));
+    }
+    if (!((bq == 0 && bk == 0) || (bq == fa::kBf16FwdBq && bk == fa::kBf16FwdBk)))
+        return FA_ERR_INVALID_ARG;
+    return hip_status(fa::launch_fwd_bf16(a));
+}
+
+fa_status_t preprocess_impl(const void* O, const void* dO, float* Dvec, int B, int T, int H,
+                            int D, fa_dtype_t dtype, hipStream_t stream, const fa_layout_t& lq) {
+    fa_status_t s = check_ptrs({O, dO, Dvec});
+    if (s != FA_OK) return s;
+    if ((s = check_dims(B, T, H, H, D, 1.0f, 0, 0, dtype)) != FA_OK) return s;
+    if ((s = check_layout(lq, B, T, H, D, dtype)) != FA_OK) return s;
+    return hip_status(fa::launch_bwd_preprocess(O, dO, Dvec, B, T, H, D,
+                                                dtype == FA_DTYPE_F32 ? 0 : 1, stream,
+                                                to_layout(lq)));
+}
+
+fa_status_t dkdv_impl(const void* Q, const void* K, const void* V, const void* dO, const float* L,
+                      const float* Dvec, float* dK, float* dV, int B, int T, int H, int HKV,
+                      int D, float scale, int causal, int window, fa_dtype_t dtype,
+                      hipStream_t stream, int bq, int bk, const fa_layout_t& lq,
+                      const fa_layout_t& lk) {
+    fa_status_t s = check_all({Q, K, V, dO, L, Dvec, dK, dV}, B, T, H, HKV, D, scale, causal,
+                              window, dtype, lq, lk);
+    if (s != FA_OK) return s;
+    fa::AttnArgs a = make_args(B, T, H, HKV, D, scale, causal, window, stream, lq, lk);
+    a.Q = Q; a.K = K; a.V = V; a.dO = dO; a.Lin = L; a.Dvec = const_cast<float*>(Dvec);
+    a.dK = dK; a.dV = dV;
+    if (dtype == FA_DTYPE_F32) {
+        if ((s = resolve_f32_tiles(bq, bk)) != FA_OK) return s;
+        return hip_status(fa::launch_dkdv_f32(a, bq, bk));
+    }
+    if (!((bq == 0 && bk == 0) || (bq == fa::kBf16DkdvBq && bk == fa::kBf16DkdvBk)))
+        return FA_ERR_INVALID_ARG;
+    return hip_status(fa::launch_dkdv_bf16(a));
+}
+
+fa_status_t dq_impl(const void* Q, const void* K, const void* V, const void* dO, const float* L,
+                    const float* Dvec, float* dQ, int B, int T, int H, int HKV, int D,
+                    float scale, int causal, int window, fa_dtype_t dtype, hipStream_t stream,
+                    int bq, int bk, const fa_layout_t& lq, const fa_layout_t& lk) {
+    fa_status_t s = check_all({Q, K, V, dO, L, Dvec, dQ}, B, T, H, HKV, D, scale, causal, window,
+                              dtype, lq, lk);
+    if (s != FA_OK) return s;
+    fa::AttnArgs a = make_args(B, T, H, HKV, D, scale, causal, window, stream, lq, lk);
+    a.Q = Q; a.K = K; a.V = V; a.dO = dO; a.Lin = L; a.Dvec = const_cast<float*>(Dvec);
+    a.dQ = dQ;
+    if (dtype == FA_DTYPE_F32) {
+        if ((s = resolve_f32_tiles(bq, bk)) != FA_OK) return s;
+        return hip_status(fa::launch_dq_f32(a, bq, bk));
+    }
+    if (!((bq == 0 && bk == 0) || (bq == fa::kBf16DqBq && bk == fa::kBf16DqBk)))
+        return FA_ERR_INVALID_ARG;
+    return hip_status(fa::launch_dq_bf16(a));
+}
+
+fa_status_t dq_dvec_impl(const void* Q, const void* K, const void* V, const void* O,
+                         const void* dO, const float* L, float* Dvec, float* dQ, int B, int T,
+                         int H, int HKV, int D, float scale, int causal, int window,
+                         fa_dtype_t dtype, hipStream_t stream, int bq, int bk,
+                         const fa_layout_t& lq, const fa_layout_t& lk) {
+    fa_status_t s = check_all({Q, K, V, O, dO, L, Dvec, dQ}, B, T, H, HKV, D, scale, causal,
+                              window, dtype, lq, lk);
+    if (s != FA_OK) return s;
+    if (dtype == FA_DTYPE_F32) {
+        if ((s = resolve_f32_tiles(bq, bk)) != FA_OK) return s;
+        s = preprocess_impl(O, dO, Dvec, B, T, H, D, dtype, stream, lq);
+        if (s != FA_OK) return s;
+        return dq_impl(Q, K, V, dO, L, Dvec, dQ, B, T, H, HKV, D, scale, causal, window, dtype,
+                       stream, bq, bk, lq, lk);
+    }
+    if (!((bq == 0 && bk == 0) || (bq == fa::kBf16DqBq && bk == fa::kBf16DqBk)))
+        return FA_ERR_INVALID_ARG;
+    fa::AttnArgs a = make_args(B, T, H, HKV, D, scale, causal, window, stream, lq, lk);
+    a.Q = Q; a.K = K; a.V = V; a.O = O; a.dO = dO; a.Lin = L; a.Dvec = Dvec; a.dQ = dQ;
+    return hip_status(fa::launch_dq_bf16_fused_d(a));
+}
+
+fa_status_t bwd_impl(const void* Q, const void* K, const void* V, const void* O, const float* L,
+                     const void* dO, float* dQ, float* dK, float* dV, int B, int T, int H,
+                     int HKV, int D, float scale, int causal, int window, fa_dtype_t dtype,
+                     hipStream_t stream, int bq, int bk, const fa_layout_t& lq,
+                     const fa_layout_t& lk) {
+    fa_status_t s = check_all({Q, K, V, O, L, dO, dQ, dK, dV}, B, T, H, HKV, D, scale, causal,
+                              window, dtype, lq, lk);
+    if (s != FA_OK) return s;
+    if (dtype == FA_DTYPE_F32) {
+        if ((s = resolve_f32_tiles(bq, bk)) != FA_OK) return s;
+    } else if (!(bq == 0 && bk == 0)) {
+        return FA_ERR_INVALID_ARG;
+    }
+    float* Dvec = nullptr;
+    const size_t bytes = (size_t)B * H * T * sizeof(float);
+    if (hipMallocAsync((void**)&Dvec, bytes, stream) != hipSuccess) return FA_ERR_HIP;
+    s = dq_dvec_impl(Q, K, V, O, dO, L, Dvec, dQ, B, T, H, HKV, D, scale, causal, window, dtype,
+                     stream, bq, bk, lq, lk);
+    if (s == FA_OK)
+        s = dkdv_impl(Q, K, V, dO, L, Dvec, dK, dV, B, T, H, HKV, D, scale, causal, window,
+                      dtype, stream, bq, bk, lq, lk);
+    const hipError_t fe = hipFreeAsync(Dvec, stream);
+    if (s == FA_OK && fe != hipSuccess) s = FA_ERR_HIP;
+    return s;
 }
 
 }  // namespace
@@ -74,7 +245,14 @@ const char* flash_attn_status_string(fa_status_t s) {
     return "FA_UNKNOWN_STATUS";
 }
 
-int flash_attn_version(void) { return 100; }
+int flash_attn_version(void) { return 101; }
+
+fa_status_t flash_attn_check_layout(fa_layout_t layout, int B, int T, int heads, int D,
+                                    fa_dtype_t dtype) {
+    if (B < 1 || T < 1 || heads < 1 || D < 1) return FA_ERR_INVALID_ARG;
+    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARG;
+    return check_layout(layout, B, T, heads, D, dtype);
+}
 
 int flash_attn_block_class(int T, int bq, int bk, int causal, int window, int i, int j, int* off) {
     if (T < 1 || bq < 1 || bk < 1 || window < 0 || i < 0 || j < 0) return -1;
@@ -112,18 +290,8 @@ fa_status_t flash_attn_default_tiles(fa_dtype_t dtype, int D, int pass, int* bq,
 fa_status_t flash_attn_fwd_ex(const void* Q, const void* K, const void* V, void* O, float* L,
                               int B, int T, int H, int HKV, int D, float scale, int causal,
                               int window, fa_dtype_t dtype, hipStream_t stream, int bq, int bk) {
-    fa_status_t s = check_ptrs({Q, K, V, O, L});
-    if (s != FA_OK) return s;
-    if ((s = check_dims(B, T, H, HKV, D, scale, causal, window, dtype)) != FA_OK) return s;
-    fa::AttnArgs a = make_args(B, T, H, HKV, D, scale, causal, window, stream);
-    a.Q = Q; a.K = K; a.V = V; a.Oout = O; a.O = O; a.L = L;
-    if (dtype == FA_DTYPE_F32) {
-        if ((s = resolve_f32_tiles(bq, bk)) != FA_OK) return s;
-        return hip_status(fa::launch_fwd_f32(a, bq, bk));
-    }
-    if (!((bq == 0 && bk == 0) || (bq == fa::kBf16FwdBq && bk == fa::kBf16FwdBk)))
-        return FA_ERR_INVALID_ARG;
-    return hip_status(fa::launch_fwd_bf16(a));
+    return fwd_impl(Q, K, V, O, L, B, T, H, HKV, D, scale, causal, window, dtype, stream, bq, bk,
+                    dense_layout(T, H, D), dense_layout(T, HKV, D));
 }
 
 fa_status_t flash_attn_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int B,
@@ -133,51 +301,33 @@ fa_status_t flash_attn_fwd(const void* Q, const void* K, const void* V, void* O,
                              0, 0);
 }
 
+fa_status_t flash_attn_fwd_strided(const void* Q, const void* K, const void* V, void* O,
+                                   float* L, int B, int T, int H, int HKV, int D, float scale,
+                                   int causal, int window, fa_dtype_t dtype, hipStream_t stream,
+                                   fa_layout_t q_layout, fa_layout_t kv_layout) {
+    return fwd_impl(Q, K, V, O, L, B, T, H, HKV, D, scale, causal, window, dtype, stream, 0, 0,
+                    q_layout, kv_layout);
+}
+
 fa_status_t flash_attn_bwd_preprocess(const void* O, const void* dO, float* Dvec, int B, int T,
                                       int H, int D, fa_dtype_t dtype, hipStream_t stream) {
-    fa_status_t s = check_ptrs({O, dO, Dvec});
-    if (s != FA_OK) return s;
-    if ((s = check_dims(B, T, H, H, D, 1.0f, 0, 0, dtype)) != FA_OK) return s;
-    return hip_status(fa::launch_bwd_preprocess(O, dO, Dvec, B, T, H, D,
-                                                dtype == FA_DTYPE_F32 ? 0 : 1, stream));
+    return preprocess_impl(O, dO, Dvec, B, T, H, D, dtype, stream, dense_layout(T, H, D));
 }
 
 fa_status_t flash_attn_bwd_dkdv(const void* Q, const void* K, const void* V, const void* dO,
                                 const float* L, const float* Dvec, float* dK, float* dV, int B,
                                 int T, int H, int HKV, int D, float scale, int causal, int window,
                                 fa_dtype_t dtype, hipStream_t stream, int bq, int bk) {
-    fa_status_t s = check_ptrs({Q, K, V, dO, L, Dvec, dK, dV});
-    if (s != FA_OK) return s;
-    if ((s = check_dims(B, T, H, HKV, D, scale, causal, window, dtype)) != FA_OK) return s;
-    fa::AttnArgs a = make_args(B, T, H, HKV, D, scale, causal, window, stream);
-    a.Q = Q; a.K = K; a.V = V; a.dO = dO; a.Lin = L; a.Dvec = const_cast<float*>(Dvec);
-    a.dK = dK; a.dV = dV;
-    if (dtype == FA_DTYPE_F32) {
-        if ((s = resolve_f32_tiles(bq, bk)) != FA_OK) return s;
-        return hip_status(fa::launch_dkdv_f32(a, bq, bk));
-    }
-    if (!((bq == 0 && bk == 0) || (bq == fa::kBf16DkdvBq && bk == fa::kBf16DkdvBk)))
-        return FA_ERR_INVALID_ARG;
-    return hip_status(fa::launch_dkdv_bf16(a));
+    return dkdv_impl(Q, K, V, dO, L, Dvec, dK, dV, B, T, H, HKV, D, scale, causal, window, dtype,
+                     stream, bq, bk, dense_layout(T, H, D), dense_layout(T, HKV, D));
 }
 
 fa_status_t flash_attn_bwd_dq(const void* Q, const void* K, const void* V, const void* dO,
                               const float* L, const float* Dvec, float* dQ, int B, int T, int H,
                               int HKV, int D, float scale, int causal, int window,
                               fa_dtype_t dtype, hipStream_t stream, int bq, int bk) {
-    fa_status_t s = check_ptrs({Q, K, V, dO, L, Dvec, dQ});
-    if (s != FA_OK) return s;
-    if ((s = check_dims(B, T, H, HKV, D, scale, causal, window, dtype)) != FA_OK) return s;
-    fa::AttnArgs a = make_args(B, T, H, HKV, D, scale, causal, window, stream);
-    a.Q = Q; a.K = K; a.V = V; a.dO = dO; a.Lin = L; a.Dvec = const_cast<float*>(Dvec);
-    a.dQ = dQ;
-    if (dtype == FA_DTYPE_F32) {
-        if ((s = resolve_f32_tiles(bq, bk)) != FA_OK) return s;
-        return hip_status(fa::launch_dq_f32(a, bq, bk));
-    }
-    if (!((bq == 0 && bk == 0) || (bq == fa::kBf16DqBq && bk == fa::kBf16DqBk)))
-        return FA_ERR_INVALID_ARG;
-    return hip_status(fa::launch_dq_bf16(a));
+    return dq_impl(Q, K, V, dO, L, Dvec, dQ, B, T, H, HKV, D, scale, causal, window, dtype,
+                   stream, bq, bk, dense_layout(T, H, D), dense_layout(T, HKV, D));
 }
 
 fa_status_t flash_attn_bwd_dq_dvec(const void* Q, const void* K, const void* V, const void* O,
@@ -185,46 +335,16 @@ fa_status_t flash_attn_bwd_dq_dvec(const void* Q, const void* K, const void* V, 
                                    int T, int H, int HKV, int D, float scale, int causal,
                                    int window, fa_dtype_t dtype, hipStream_t stream, int bq,
                                    int bk) {
-    fa_status_t s = check_ptrs({Q, K, V, O, dO, L, Dvec, dQ});
-    if (s != FA_OK) return s;
-    if ((s = check_dims(B, T, H, HKV, D, scale, causal, window, dtype)) != FA_OK) return s;
-    if (dtype == FA_DTYPE_F32) {
-        if ((s = resolve_f32_tiles(bq, bk)) != FA_OK) return s;
-        s = flash_attn_bwd_preprocess(O, dO, Dvec, B, T, H, D, dtype, stream);
-        if (s != FA_OK) return s;
-        return flash_attn_bwd_dq(Q, K, V, dO, L, Dvec, dQ, B, T, H, HKV, D, scale, causal,
-                                 window, dtype, stream, bq, bk);
-    }
-    if (!((bq == 0 && bk == 0) || (bq == fa::kBf16DqBq && bk == fa::kBf16DqBk)))
-        return FA_ERR_INVALID_ARG;
-    fa::AttnArgs a = make_args(B, T, H, HKV, D, scale, causal, window, stream);
-    a.Q = Q; a.K = K; a.V = V; a.O = O; a.dO = dO; a.Lin = L; a.Dvec = Dvec; a.dQ = dQ;
-    return hip_status(fa::launch_dq_bf16_fused_d(a));
+    return dq_dvec_impl(Q, K, V, O, dO, L, Dvec, dQ, B, T, H, HKV, D, scale, causal, window,
+                        dtype, stream, bq, bk, dense_layout(T, H, D), dense_layout(T, HKV, D));
 }
 
 fa_status_t flash_attn_bwd_ex(const void* Q, const void* K, const void* V, const void* O,
                               const float* L, const void* dO, float* dQ, float* dK, float* dV,
                               int B, int T, int H, int HKV, int D, float scale, int causal,
                               int window, fa_dtype_t dtype, hipStream_t stream, int bq, int bk) {
-    fa_status_t s = check_ptrs({Q, K, V, O, L, dO, dQ, dK, dV});
-    if (s != FA_OK) return s;
-    if ((s = check_dims(B, T, H, HKV, D, scale, causal, window, dtype)) != FA_OK) return s;
-    if (dtype == FA_DTYPE_F32) {
-        if ((s = resolve_f32_tiles(bq, bk)) != FA_OK) return s;
-    } else if (!(bq == 0 && bk == 0)) {
-        return FA_ERR_INVALID_ARG;
-    }
-    float* Dvec = nullptr;
-    const size_t bytes = (size_t)B * H * T * sizeof(float);
-    if (hipMallocAsync((void**)&Dvec, bytes, stream) != hipSuccess) return FA_ERR_HIP;
-    s = flash_attn_bwd_dq_dvec(Q, K, V, O, dO, L, Dvec, dQ, B, T, H, HKV, D, scale, causal,
-                               window, dtype, stream, bq, bk);
-    if (s == FA_OK)
-        s = flash_attn_bwd_dkdv(Q, K, V, dO, L, Dvec, dK, dV, B, T, H, HKV, D, scale, causal,
-                                window, dtype, stream, bq, bk);
-    const hipError_t fe = hipFreeAsync(Dvec, stream);
-    if (s == FA_OK && fe != hipSuccess) s = FA_ERR_HIP;
-    return s;
+    return bwd_impl(Q, K, V, O, L, dO, dQ, dK, dV, B, T, H, HKV, D, scale, causal, window, dtype,
+                    stream, bq, bk, dense_layout(T, H, D), dense_layout(T, HKV, D));
 }
 
 fa_status_t flash_attn_bwd(const void* Q, const void* K, const void* V, const void* O,
@@ -233,6 +353,15 @@ fa_status_t flash_attn_bwd(const void* Q, const void* K, const void* V, const vo
                            fa_dtype_t dtype, hipStream_t stream) {
     return flash_attn_bwd_ex(Q, K, V, O, L, dO, dQ, dK, dV, B, T, H, HKV, D, scale, causal,
                              window, dtype, stream, 0, 0);
+}
+
+fa_status_t flash_attn_bwd_strided(const void* Q, const void* K, const void* V, const void* O,
+                                   const float* L, const void* dO, float* dQ, float* dK,
+                                   float* dV, int B, int T, int H, int HKV, int D, float scale,
+                                   int causal, int window, fa_dtype_t dtype, hipStream_t stream,
+                                   fa_layout_t q_layout, fa_layout_t kv_layout) {
+    return bwd_impl(Q, K, V, O, L, dO, dQ, dK, dV, B, T, H, HKV, D, scale, causal, window, dtype,
+                    stream, 0, 0, q_layout, kv_layout);
 }
 
 }  // extern "C"

@@ -53,7 +53,7 @@ template <int DP, int BQ, int BK>
 __global__ __launch_bounds__(BQ / 16 * 64) void fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ L, int B, int T, int H, int HKV, int D,
-    float scale, int causal, int window, int nqt) {
+    float scale, int causal, int window, int nqt, Layout lq, Layout lk) {
     using Tl = F32Tile<DP>;
     constexpr int NW = BQ / 16, NT = NW * 64, KS = Tl::KS, LD = Tl::LD, NDB = Tl::NDB;
     __shared__ __attribute__((aligned(16))) float Ks[BK * LD];
@@ -68,10 +68,10 @@ __global__ __launch_bounds__(BQ / 16 * 64) void fwd_f32_kernel(
     const int n = lane & 15, g = lane >> 4;
     const int wr0 = qt * BQ + w * 16;
     const int q = wr0 + n;
-    const int64_t ldq = (int64_t)H * D, ldk = (int64_t)HKV * D;
-    const float* Qh = Q + (int64_t)b * T * ldq + (int64_t)h * D;
-    const float* Kh = K + (int64_t)b * T * ldk + (int64_t)hk * D;
-    const float* Vh = V + (int64_t)b * T * ldk + (int64_t)hk * D;
+    const int64_t ldq = lq.t, ldk = lk.t;   // row strides (elements)
+    const float* Qh = Q + b * lq.b + h * lq.h;
+    const float* Kh = K + b * lk.b + hk * lk.h;
+    const float* Vh = V + b * lk.b + hk * lk.h;
 
     float qreg[KS];
 #pragma unroll
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(BQ / 16 * 64) void fwd_f32_kernel(
     lsum += xor_shfl(lsum, 32);
     if (q >= T) return;
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    float* Oq = O + (int64_t)b * T * ldq + (int64_t)q * ldq + (int64_t)h * D;
+    float* Oq = O + b * lq.b + (int64_t)q * ldq + h * lq.h;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
         const int d = db * 16 + 4 * g;
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(BK / 16 * 64) void dkdv_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ L, const float* __restrict__ Dv,
     float* __restrict__ dK, float* __restrict__ dV, int B, int T, int H, int HKV, int D,
-    float scale, int causal, int window, int nkt) {
+    float scale, int causal, int window, int nkt, Layout lq, Layout lk) {
     using Tl = F32Tile<DP>;
     constexpr int NW = BK / 16, NT = NW * 64, KS = Tl::KS, LD = Tl::LD, NDB = Tl::NDB;
     __shared__ __attribute__((aligned(16))) float Qs[BQ * LD];
@@ -185,9 +185,9 @@ __global__ __launch_bounds__(BK / 16 * 64) void dkdv_f32_kernel(
     const int n = lane & 15, g = lane >> 4;
     const int kw0 = kt * BK + w * 16;
     const int key = kw0 + n;
-    const int64_t ldq = (int64_t)H * D, ldk = (int64_t)HKV * D;
-    const float* Kh = K + (int64_t)b * T * ldk + (int64_t)hk * D;
-    const float* Vh = V + (int64_t)b * T * ldk + (int64_t)hk * D;
+    const int64_t ldq = lq.t, ldk = lk.t;   // row strides (elements)
+    const float* Kh = K + b * lk.b + hk * lk.h;
+    const float* Vh = V + b * lk.b + hk * lk.h;
     const bool cz = causal != 0;
     const float c = scale * kLog2e;
 
@@ -207,8 +207,8 @@ __global__ __launch_bounds__(BK / 16 * 64) void dkdv_f32_kernel(
     q_block_range(T, kt * BK, kt * BK + BK, BQ, cz, window, ilo, ihi);
     for (int hh = 0; hh < rep; ++hh) {
         const int h = hk * rep + hh;
-        const float* Qh = Q + (int64_t)b * T * ldq + (int64_t)h * D;
-        const float* dOh = dO + (int64_t)b * T * ldq + (int64_t)h * D;
+        const float* Qh = Q + b * lq.b + h * lq.h;
+        const float* dOh = dO + b * lq.b + h * lq.h;
         const float* Lh = L + ((int64_t)b * H + h) * T;
         const float* Dh = Dv + ((int64_t)b * H + h) * T;
         for (int i = ilo; i < ihi; ++i) {
@@ -258,8 +258,8 @@ __global__ __launch_bounds__(BK / 16 * 64) void dkdv_f32_kernel(
         }
     }
     // lane (n, g), element r: key kw0 + 4g + r, column d = db*16 + n
-    float* dKh = dK + (int64_t)b * T * ldk + (int64_t)hk * D;
-    float* dVh = dV + (int64_t)b * T * ldk + (int64_t)hk * D;
+    float* dKh = dK + b * lk.b + hk * lk.h;
+    float* dVh = dV + b * lk.b + hk * lk.h;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
         const int d = db * 16 + n;
@@ -280,7 +280,7 @@ __global__ __launch_bounds__(BQ / 16 * 64) void dq_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ L, const float* __restrict__ Dv,
     float* __restrict__ dQ, int B, int T, int H, int HKV, int D, float scale, int causal,
-    int window, int nqt) {
+    int window, int nqt, Layout lq, Layout lk) {
     using Tl = F32Tile<DP>;
     constexpr int NW = BQ / 16, NT = NW * 64, KS = Tl::KS, LD = Tl::LD, NDB = Tl::NDB;
     __shared__ __attribute__((aligned(16))) float Ks[BK * LD];
@@ -295,11 +295,11 @@ __global__ __launch_bounds__(BQ / 16 * 64) void dq_f32_kernel(
     const int n = lane & 15, g = lane >> 4;
     const int wr0 = qt * BQ + w * 16;
     const int q = wr0 + n;
-    const int64_t ldq = (int64_t)H * D, ldk = (int64_t)HKV * D;
-    const float* Qh = Q + (int64_t)b * T * ldq + (int64_t)h * D;
-    const float* dOh = dO + (int64_t)b * T * ldq + (int64_t)h * D;
-    const float* Kh = K + (int64_t)b * T * ldk + (int64_t)hk * D;
-    const float* Vh = V + (int64_t)b * T * ldk + (int64_t)hk * D;
+    const int64_t ldq = lq.t, ldk = lk.t;   // row strides (elements)
+    const float* Qh = Q + b * lq.b + h * lq.h;
+    const float* dOh = dO + b * lq.b + h * lq.h;
+    const float* Kh = K + b * lk.b + hk * lk.h;
+    const float* Vh = V + b * lk.b + hk * lk.h;
     const bool cz = causal != 0;
     const float c = scale * kLog2e;
 
@@ -355,7 +355,7 @@ __global__ __launch_bounds__(BQ / 16 * 64) void dq_f32_kernel(
         }
     }
     if (q >= T) return;
-    float* dQq = dQ + (int64_t)b * T * ldq + (int64_t)q * ldq + (int64_t)h * D;
+    float* dQq = dQ + b * lq.b + (int64_t)q * ldq + h * lq.h;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
         const int d = db * 16 + 4 * g;
@@ -373,7 +373,7 @@ hipError_t launch_fwd_f32_t(const AttnArgs& a) {
     hipLaunchKernelGGL((fwd_f32_kernel<DP, BQ, BK>), dim3(grid), dim3(BQ / 16 * 64), 0,
                        a.stream, (const float*)a.Q, (const float*)a.K, (const float*)a.V,
                        (float*)a.Oout, a.L, a.B, a.T, a.H, a.HKV, a.D, a.scale, a.causal,
-                       a.window, nqt);
+                       a.window, nqt, a.lq, a.lk);
     return hipGetLastError();
 }
 
@@ -384,7 +384,7 @@ hipError_t launch_dkdv_f32_t(const AttnArgs& a) {
     hipLaunchKernelGGL((dkdv_f32_kernel<DP, BQ, BK>), dim3(grid), dim3(BK / 16 * 64), 0,
                        a.stream, (const float*)a.Q, (const float*)a.K, (const float*)a.V,
                        (const float*)a.dO, a.Lin, a.Dvec, a.dK, a.dV, a.B, a.T, a.H, a.HKV, a.D,
-                       a.scale, a.causal, a.window, nkt);
+                       a.scale, a.causal, a.window, nkt, a.lq, a.lk);
     return hipGetLastError();
 }
 
@@ -395,7 +395,7 @@ hipError_t launch_dq_f32_t(const AttnArgs& a) {
     hipLaunchKernelGGL((dq_f32_kernel<DP, BQ, BK>), dim3(grid), dim3(BQ / 16 * 64), 0,
                        a.stream, (const float*)a.Q, (const float*)a.K, (const float*)a.V,
                        (const float*)a.dO, a.Lin, a.Dvec, a.dQ, a.B, a.T, a.H, a.HKV, a.D,
-                       a.scale, a.causal, a.window, nqt);
+                       a.scale, a.causal, a.window, nqt, a.lq, a.lk);
     return hipGetLastError();
 }
 

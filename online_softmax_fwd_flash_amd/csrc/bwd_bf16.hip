@@ -75,18 +75,18 @@ struct Dkdv16Cfg {
 // into buffer it % 2.  The first half of the waves fill the Q tile (pieces w, w + NW/2, ...),
 // the second half the dO tile; wave 0 also moves the block's L values, wave 1 its D values.
 template <int D>
-__device__ __forceinline__ void dkdv16_issue(char* sm, const Buf& qbuf, const Buf& obuf,
-                                             const float* Lg, const float* Dg,
-                                             const uint32_t* voff, int w, int rep, int ihi,
-                                             int T, uint32_t ldq_b, int it) {
+__device__ __forceinline__ void dkdv16_issue(char* sm, const uint16_t* Qg, const uint16_t* dOg,
+                                             int64_t ldq, int64_t qh, const float* Lg,
+                                             const float* Dg, const uint32_t* voff, int w,
+                                             int rep, int ihi, int T, int it) {
     using C = Dkdv16Cfg<D>;
     const int h2 = it % rep, i2 = ihi - 1 - it / rep;
     char* st = sm + (it & 1) * C::STAGE;
-    const int tso = __builtin_amdgcn_readfirstlane(
-        (int)((uint32_t)i2 * C::BQ * ldq_b + (uint32_t)h2 * D * 2));
+    const int tso = __builtin_amdgcn_readfirstlane((int)((uint32_t)i2 * C::BQ * (uint32_t)(ldq * 2)));
     const int wq = w % C::QW;
     char* dst = st + (w / C::QW) * C::OFF_DO;
-    const Buf& src = w < C::QW ? qbuf : obuf;
+    // one head's rows: rows past T read as zeros
+    const Buf src = head_buf<D>((w < C::QW ? Qg : dOg) + h2 * qh, ldq, T);
 #pragma unroll
     for (int i = 0; i < C::PMAX; ++i)
         if (wq + C::QW * i < C::TPIECES) dma_piece(src, dst + (wq + C::QW * i) * 1024, voff[i], tso);
@@ -123,7 +123,8 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv16_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ L, const float* __restrict__ Dv, float* __restrict__ dK,
-    float* __restrict__ dV, int B, int T, int H, int HKV, float scale, int causal, int window) {
+    float* __restrict__ dV, int B, int T, int H, int HKV, float scale, int causal, int window,
+    Layout lq, Layout lk) {
     using C = Dkdv16Cfg<D>;
     extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
     char* sm = reinterpret_cast<char*>(smem);
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv16_bf16_kernel(
     const int n = lane & 15, g = lane >> 4;
     const int kw0 = kt * C::BKW + w * C::KPW;
     const int key = kw0 + n;
-    const int64_t ldq = (int64_t)H * D, ldk = (int64_t)HKV * D;
+    const int64_t ldq = lq.t, ldk = lk.t;   // row strides (elements)
     const bool cz = causal != 0;
     const float c = scale * kLog2e;
     // queries that see this lane's key: [qlo, qhi] (lanes of keys past T are never stored)
@@ -148,8 +149,8 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv16_bf16_kernel(
     // B operands of S = Q K^T and dP = dO V^T: lane (n, g) holds K/V[key][32*ds + 8g .. +7]
     bf16x8 kreg[C::DS], vreg[C::DS];
     {
-        const Buf kb = rows_buf(K + (int64_t)b * T * ldk + (int64_t)hk * D, ldk, T);
-        const Buf vb = rows_buf(V + (int64_t)b * T * ldk + (int64_t)hk * D, ldk, T);
+        const Buf kb = head_buf<D>(K + b * lk.b + hk * lk.h, ldk, T);
+        const Buf vb = head_buf<D>(V + b * lk.b + hk * lk.h, ldk, T);
         const uint32_t off = (uint32_t)key * (uint32_t)(ldk * 2) + 16 * g;
 #pragma unroll
         for (int ds = 0; ds < C::DS; ++ds) {
@@ -164,11 +165,10 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv16_bf16_kernel(
     int ilo, ihi;
     q_block_range(T, kt * C::BKW, kt * C::BKW + C::BKW, C::BQ, cz, window, ilo, ihi);
     const int niter = rep * (ihi - ilo);
-    // one descriptor per tensor over the group's heads: head h2 is h2*D elements further
-    // along each row, rows past T read as zeros
+    // the group's first query head; head h2 of the group is h2 * lq.h elements further
     const uint32_t ldq_b = (uint32_t)(ldq * 2);
-    const Buf qbuf = rows_buf(Q + (int64_t)b * T * ldq + (int64_t)hk * rep * D, ldq, T);
-    const Buf obuf = rows_buf(dO + (int64_t)b * T * ldq + (int64_t)hk * rep * D, ldq, T);
+    const uint16_t* Qg = Q + b * lq.b + (int64_t)hk * rep * lq.h;
+    const uint16_t* dOg = dO + b * lq.b + (int64_t)hk * rep * lq.h;
     const float* Lg = L + ((int64_t)b * H + (int64_t)hk * rep) * T;
     const float* Dg = Dv + ((int64_t)b * H + (int64_t)hk * rep) * T;
     uint32_t voff[C::PMAX + 1];
@@ -180,13 +180,13 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv16_bf16_kernel(
     // Query blocks are walked last-first (heads inner): every key block of a KV group needs
     // the last query blocks, so the group's co-resident workgroups (same XCD) stream the same
     // Q / dO blocks at about the same time and share them in L2.
-    if (niter > 0) dkdv16_issue<D>(sm, qbuf, obuf, Lg, Dg, voff, w, rep, ihi, T, ldq_b, 0);
+    if (niter > 0) dkdv16_issue<D>(sm, Qg, dOg, ldq, lq.h, Lg, Dg, voff, w, rep, ihi, T, 0);
     for (int it = 0; it < niter; ++it) {
         const int i = ihi - 1 - it / rep;
         wait_vmcnt<0>();   // this stage's pieces, the only loads in flight
         // every wave's pieces are visible; every wave is done with the other stage
         lds_barrier();
-        if (it + 1 < niter) dkdv16_issue<D>(sm, qbuf, obuf, Lg, Dg, voff, w, rep, ihi, T, ldq_b, it + 1);
+        if (it + 1 < niter) dkdv16_issue<D>(sm, Qg, dOg, ldq, lq.h, Lg, Dg, voff, w, rep, ihi, T, it + 1);
         const int qr0 = i * C::BQ;
         const int cls = block_class(T, qr0, qr0 + C::BQ, kw0, kw0 + C::KPW, cz, window);
         if (cls == kSkip) continue;
@@ -251,8 +251,8 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv16_bf16_kernel(
     }
 
     // entry r of lane (n, g) in block db: key kw0 + 4g + r, column db*16 + n
-    float* dKg = dK + (int64_t)b * T * ldk + (int64_t)hk * D;
-    float* dVg = dV + (int64_t)b * T * ldk + (int64_t)hk * D;
+    float* dKg = dK + b * lk.b + hk * lk.h;
+    float* dVg = dV + b * lk.b + hk * lk.h;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int kk = kw0 + 4 * g + r;
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_bf16_kernel(
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const uint16_t* __restrict__ O, const float* __restrict__ L, float* __restrict__ Dv,
     float* __restrict__ dQ, int B, int T, int H, int HKV, float scale, int causal, int window,
-    int nqt, int xcd_group) {
+    int nqt, int xcd_group, Layout lq, Layout lk) {
     using C = DqCfg<D, NW>;
     extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
     char* sm = reinterpret_cast<char*>(smem);
@@ -327,17 +327,19 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_bf16_kernel(
     const int n = lane & 31, g = lane >> 5;
     const int wr0 = qt * C::BQ + w * 32;
     const int q = wr0 + n;
-    const int64_t ldq = (int64_t)H * D, ldk = (int64_t)HKV * D;
+    const int64_t ldq = lq.t, ldk = lk.t;   // row strides (elements)
     const uint32_t ldk_b = (uint32_t)(ldk * 2);
-    const Buf kbuf = rows_buf(K + (int64_t)b * T * ldk + (int64_t)hk * D, ldk, T);
-    const Buf vbuf = rows_buf(V + (int64_t)b * T * ldk + (int64_t)hk * D, ldk, T);
+    const Buf kbuf = head_buf<D>(K + b * lk.b + hk * lk.h, ldk, T);
+    const Buf vbuf = head_buf<D>(V + b * lk.b + hk * lk.h, ldk, T);
+    // element offset of this lane's query row in Q, O, dO and dQ
+    const int64_t qrow = b * lq.b + (int64_t)q * ldq + h * lq.h;
     const bool cz = causal != 0;
     const float c = scale * kLog2e;
 
     // B operands of S^T = K Q^T and dP^T = V dO^T: lane (n, g) holds Q/dO[q][16*dc + 8g ..]
     bf16x8 qreg[C::DC], oreg[C::DC];
     {
-        const int64_t base = ((int64_t)b * T + q) * ldq + (int64_t)h * D + 8 * g;
+        const int64_t base = qrow + 8 * g;
 #pragma unroll
         for (int dc = 0; dc < C::DC; ++dc) {
             const u32x4 z = {0u, 0u, 0u, 0u};
@@ -350,7 +352,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_bf16_kernel(
     if constexpr (FUSE_D) {
         // D_i = sum_d dO[i][d] O[i][d] from this lane's 8*DC columns plus the other half's;
         // rows past T load zeros and give 0
-        const int64_t base = ((int64_t)b * T + q) * ldq + (int64_t)h * D + 8 * g;
+        const int64_t base = qrow + 8 * g;
         float s = 0.f;
 #pragma unroll
         for (int dc = 0; dc < C::DC; ++dc) {
@@ -448,7 +450,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_bf16_kernel(
     }
 
     if (q >= T) return;
-    float* dQq = dQ + ((int64_t)b * T + q) * ldq + (int64_t)h * D;
+    float* dQq = dQ + qrow;
     // entry r of block db: dQ^T[db*32 + 8*(r/4) + 4g + r%4][query n]
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
@@ -491,7 +493,7 @@ hipError_t launch_dkdv16_bf16_t(const AttnArgs& a) {
     hipLaunchKernelGGL((dkdv16_bf16_kernel<D>), dim3(grid), dim3(C::NT), lds, a.stream,
                        (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
                        (const uint16_t*)a.dO, a.Lin, a.Dvec, a.dK, a.dV, a.B, a.T, a.H, a.HKV,
-                       a.scale, a.causal, a.window);
+                       a.scale, a.causal, a.window, a.lq, a.lk);
     return hipGetLastError();
 }
 
@@ -514,7 +516,7 @@ hipError_t launch_dq_bf16_t(const AttnArgs& a) {
                        a.stream, (const uint16_t*)a.Q, (const uint16_t*)a.K,
                        (const uint16_t*)a.V, (const uint16_t*)a.dO, (const uint16_t*)a.O, a.Lin,
                        a.Dvec, a.dQ, a.B, a.T, a.H, a.HKV, a.scale, a.causal, a.window, nqt,
-                       xcd_group_for(nqt, a.B, a.H, a.HKV));
+                       xcd_group_for(nqt, a.B, a.H, a.HKV), a.lq, a.lk);
     return hipGetLastError();
 }
 

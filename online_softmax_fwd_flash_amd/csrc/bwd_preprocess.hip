@@ -42,47 +42,46 @@ __device__ __forceinline__ float dot16B<uint16_t>(const u32x4& a, const u32x4& b
 template <typename Elem>
 __global__ __launch_bounds__(kThreads) void bwd_preprocess_kernel(
     const Elem* __restrict__ O, const Elem* __restrict__ dO, float* __restrict__ Dv, int B, int T,
-    int H, int D) {
+    int H, int D, Layout lq) {
+    // row = (b*T + i)*H + h; O and dO of that row start at b*lq.b + i*lq.t + h*lq.h
     const int64_t rows = (int64_t)B * T * H;
     const int64_t row = (int64_t)blockIdx.x * (kThreads / kTeam) + threadIdx.x / kTeam;
     const int sub = threadIdx.x % kTeam;
     const int nch = D * (int)sizeof(Elem) / 16;   // 16-byte chunks per row
+    const int h = (int)(row % H);
+    const int64_t bi = row / H;
+    const int i = (int)(bi % T);
+    const int64_t b = bi / T;
     float s = 0.f;
     if (row < rows) {
-        const Elem* o = O + row * D;
-        const Elem* go = dO + row * D;
+        const int64_t off = b * lq.b + (int64_t)i * lq.t + (int64_t)h * lq.h;
+        const Elem* o = O + off;
+        const Elem* go = dO + off;
         for (int ch = sub; ch < nch; ch += kTeam) {
             const u32x4 a = *reinterpret_cast<const u32x4*>(o + ch * (16 / sizeof(Elem)));
-            const u32x4 b = *reinterpret_cast<const u32x4*>(go + ch * (16 / sizeof(Elem)));
-            s += dot16B<Elem>(a, b);
+            const u32x4 c = *reinterpret_cast<const u32x4*>(go + ch * (16 / sizeof(Elem)));
+            s += dot16B<Elem>(a, c);
         }
     }
     s += __shfl_xor(s, 1, 64);
     s += __shfl_xor(s, 2, 64);
     s += __shfl_xor(s, 4, 64);
-    if (row < rows && sub == 0) {
-        // row = (b*T + i)*H + h  ->  Dv[(b*H + h)*T + i]
-        const int h = (int)(row % H);
-        const int64_t bi = row / H;
-        const int i = (int)(bi % T);
-        const int64_t b = bi / T;
-        Dv[(b * H + h) * T + i] = s;
-    }
+    if (row < rows && sub == 0) Dv[(b * H + h) * T + i] = s;
 }
 
 }  // namespace
 
 hipError_t launch_bwd_preprocess(const void* O, const void* dO, float* Dvec, int B, int T, int H,
-                                 int D, int dtype, hipStream_t stream) {
+                                 int D, int dtype, hipStream_t stream, Layout lq) {
     const int64_t rows = (int64_t)B * T * H;
     const int64_t per = kThreads / kTeam;
     const unsigned grid = (unsigned)((rows + per - 1) / per);
     if (dtype == 0)
         hipLaunchKernelGGL(bwd_preprocess_kernel<float>, dim3(grid), dim3(kThreads), 0, stream,
-                           (const float*)O, (const float*)dO, Dvec, B, T, H, D);
+                           (const float*)O, (const float*)dO, Dvec, B, T, H, D, lq);
     else
         hipLaunchKernelGGL(bwd_preprocess_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, stream,
-                           (const uint16_t*)O, (const uint16_t*)dO, Dvec, B, T, H, D);
+                           (const uint16_t*)O, (const uint16_t*)dO, Dvec, B, T, H, D, lq);
     return hipGetLastError();
 }
 

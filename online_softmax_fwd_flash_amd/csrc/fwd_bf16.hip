@@ -83,7 +83,8 @@ template <int D>
 __global__ __launch_bounds__(kThreads, kWgs) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ L, int B,
-    int T, int H, int HKV, float scale, int causal, int window, int nqt, int xcd_group) {
+    int T, int H, int HKV, float scale, int causal, int window, int nqt, int xcd_group,
+    Layout lq, Layout lk) {
     using C = Bf16Fwd<D>;
     extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
 
@@ -94,10 +95,10 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_bf16_kernel(
     const int n = lane & 31, g = lane >> 5;
     const int wr0 = qt * kBQ + w * 32;
     const int q = wr0 + n;
-    const int64_t ldq = (int64_t)H * D, ldk = (int64_t)HKV * D;
+    const int64_t ldq = lq.t, ldk = lk.t;   // row strides (elements)
     const uint32_t ldk_b = (uint32_t)(ldk * 2);
-    const Buf kbuf = rows_buf(K + (int64_t)b * T * ldk + (int64_t)hk * D, ldk, T);
-    const Buf vbuf = rows_buf(V + (int64_t)b * T * ldk + (int64_t)hk * D, ldk, T);
+    const Buf kbuf = head_buf<D>(K + b * lk.b + hk * lk.h, ldk, T);
+    const Buf vbuf = head_buf<D>(V + b * lk.b + hk * lk.h, ldk, T);
     const bool cz = causal != 0;
     const float c = scale * kLog2e;
     // keys this query row may see: [klo, khi]
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_bf16_kernel(
     // Q^T operand: lane (n, g) holds Q[q][16*dc + 8*g .. +7] (zero past T)
     bf16x8 qreg[C::DC];
     {
-        const Buf qbuf = rows_buf(Q + (int64_t)b * T * ldq + (int64_t)h * D, ldq, T);
+        const Buf qbuf = head_buf<D>(Q + b * lq.b + h * lq.h, ldq, T);
         const uint32_t off = (uint32_t)q * (uint32_t)(ldq * 2) + 16 * g;
 #pragma unroll
         for (int dc = 0; dc < C::DC; ++dc) qreg[dc] = __builtin_bit_cast(bf16x8, qbuf.load16(off + dc * 32));
@@ -248,7 +249,7 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_bf16_kernel(
     lsum += swap_halves(lsum);
     if (q >= T) return;
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    uint16_t* Oq = O + ((int64_t)b * T + q) * ldq + (int64_t)h * D;
+    uint16_t* Oq = O + b * lq.b + (int64_t)q * ldq + h * lq.h;
     // lane (n, g), entry r of block db: O^T[db*32 + 8*(r/4) + 4g + r%4][query n]
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
@@ -286,7 +287,7 @@ hipError_t launch_fwd_bf16_t(const AttnArgs& a) {
     hipLaunchKernelGGL((fwd_bf16_kernel<D>), dim3(grid), dim3(kThreads), lds, a.stream,
                        (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
                        (uint16_t*)a.Oout, a.L, a.B, a.T, a.H, a.HKV, a.scale, a.causal,
-                       a.window, nqt, xcd_group);
+                       a.window, nqt, xcd_group, a.lq, a.lk);
     return hipGetLastError();
 }
 

@@ -6,6 +6,12 @@
 
 namespace fa {
 
+// Element strides of a [B, T, heads, D] view (batch, row, head); the D axis is contiguous.
+// Q, O, dO and dQ share one layout, K, V, dK and dV another.
+struct Layout {
+    int64_t b, t, h;
+};
+
 struct AttnArgs {
     const void* Q;
     const void* K;
@@ -23,6 +29,7 @@ struct AttnArgs {
     float scale;
     int causal, window;
     hipStream_t stream;
+    Layout lq, lk;   // query-side and key-side layouts
 };
 
 // Tilings of the bf16 kernels: query rows x keys handled per workgroup block.  Each kernel
@@ -45,6 +52,6 @@ hipError_t launch_dq_bf16_fused_d(const AttnArgs& a);
 
 // dtype: 0 = f32, 1 = bf16
 hipError_t launch_bwd_preprocess(const void* O, const void* dO, float* Dvec, int B, int T,
-                                 int H, int D, int dtype, hipStream_t stream);
+                                 int H, int D, int dtype, hipStream_t stream, Layout lq);
 
 }  // namespace fa

@@ -27,9 +27,12 @@ struct Buf {
     }
 };
 
-// Buffer over rows [0, T) of a head slice whose rows are `ld` elements apart (bf16).
-__device__ __forceinline__ Buf rows_buf(const uint16_t* base, int64_t ld, int T) {
-    return Buf(base, (uint32_t)(T * ld * 2));
+// Buffer over rows [0, T) of one head: rows of D bf16 elements, `ld` elements apart
+// (ld >= D).  It ends with the last row's D elements, so reads at rows past T return zeros
+// whatever the layout puts there.
+template <int D>
+__device__ __forceinline__ Buf head_buf(const uint16_t* base, int64_t ld, int T) {
+    return Buf(base, (uint32_t)(((int64_t)(T - 1) * ld + D) * 2));
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;

@@ -32,7 +32,7 @@ def test_header_and_exports_agree():
 
 
 def test_version_and_strings():
-    assert fa.flash_attn_version() == 100
+    assert fa.flash_attn_version() == 101
     assert _lib.status_string(0) == "FA_OK"
     assert _lib.status_string(2) == "FA_ERR_UNSUPPORTED"
 
@@ -112,6 +112,51 @@ def test_default_tiles():
     assert fa.flash_attn_default_tiles(0, 8, 0) == (64, 64)
     with pytest.raises(fa.FlashAttnError):
         fa.flash_attn_default_tiles(1, 80, 0)
+
+
+# (strides (batch, row, head), B, T, heads, D, dtype, expected status)
+LAYOUTS = [
+    ((64 * 4 * 128, 4 * 128, 128), 2, 64, 4, 128, 1, 0),          # contiguous [B, T, h, D]
+    ((4 * 64 * 128, 128, 64 * 128), 2, 64, 4, 128, 1, 0),         # [B, h, T, D] / [B*h, T, D]
+    ((4 * 64 * 136, 136, 64 * 136), 2, 64, 4, 128, 1, 0),         # padded rows
+    ((0, 4 * 128, 128), 1, 64, 4, 128, 1, 0),                     # batch stride unused at B = 1
+    ((64 * 4 * 128, 4 * 128, 0), 2, 64, 1, 128, 1, 0),            # head stride unused at 1 head
+    ((64 * 4 * 64, 4 * 64, 64), 2, 64, 4, 64, 0, 0),              # f32
+    ((4 * 64 * 68, 68, 64 * 68), 2, 64, 4, 64, 0, 0),             # f32 rows of 68 (16 bytes)
+    ((64 * 4 * 128, 4 * 128, 128), 2, 64, 4, 128, 7, 1),          # bad dtype
+    ((64 * 4 * 128, -512, 128), 2, 64, 4, 128, 1, 1),             # negative stride
+    ((4 * 64 * 64, 64, 64 * 64), 2, 64, 4, 128, 1, 1),            # rows shorter than D
+    ((4 * 64 * 130, 130, 64 * 130), 2, 64, 4, 128, 1, 1),         # rows not 16-byte multiples
+    ((4 * 64 * 66, 66, 64 * 66), 2, 64, 4, 64, 0, 1),             # f32 rows not 16-byte multiples
+    ((64 * 128, 128, 128), 2, 64, 4, 128, 1, 1),                  # heads alias rows
+    ((0, 4 * 128, 128), 2, 64, 4, 128, 1, 1),                     # batches alias
+    ((64 * 4 * 128, 4 * 128, 64), 2, 64, 4, 128, 1, 1),           # heads overlap within a row
+    ((1 << 33, 2048, 0), 1, 1 << 20, 1, 128, 1, 1),               # bf16 head span >= 2 GiB
+    ((1 << 33, 2048, 0), 1, 1 << 20, 1, 128, 0, 0),               # same strides, f32: 64-bit
+    ((64 * 4 * 128, 4 * 128, 128), 0, 64, 4, 128, 1, 1),          # B < 1
+]
+
+
+@pytest.mark.parametrize("strides,B,T,heads,D,dtype,code", LAYOUTS)
+def test_layout_check(strides, B, T, heads, D, dtype, code):
+    assert fa.flash_attn_check_layout(strides, B, T, heads, D, dtype) == code
+
+
+def test_strided_entries_reject_before_launch():
+    L = _lib.lib()
+    dims = (1, 64, 4, 2, 128, 0.125, 1, 0, 1, S0)
+    good_q = _lib.Layout(64 * 4 * 128, 4 * 128, 128)
+    good_k = _lib.Layout(64 * 2 * 128, 2 * 128, 128)
+    bad = _lib.Layout(64 * 4 * 128, 64, 128)                       # rows shorter than D
+    assert L.flash_attn_fwd_strided(A, A, A, A, A, *dims, bad, good_k) == 1
+    assert L.flash_attn_fwd_strided(A, A, A, A, A, *dims, good_q, bad) == 1
+    assert L.flash_attn_fwd_strided(A, NUL, A, A, A, *dims, good_q, good_k) == 1
+    assert L.flash_attn_bwd_strided(*([A] * 9), *dims, bad, good_k) == 1
+    assert L.flash_attn_bwd_strided(*([A] * 9), *dims, good_q, bad) == 1
+    assert L.flash_attn_bwd_strided(*([A] * 8), MIS, *dims, good_q, good_k) == 1
+    # the KV layout is checked with HKV heads: a head stride that aliases only at 4 heads
+    kv2 = _lib.Layout(64 * 2 * 128, 2 * 128, 128)
+    assert fa.flash_attn_check_layout((kv2.batch, kv2.row, kv2.head), 1, 64, 2, 128, 1) == 0
 
 
 CLASS_SWEEP = [(T, bq, bk, c, w) for T in (1, 7, 64, 100, 129, 257, 300)
