@@ -14,7 +14,7 @@
  *               of non-square blocks).
  *   [teeny]     "flash_attn2.rs" (teeny-kernels 0.2.0): forward, backward_dq, backward_dkv
  *               doc comments; the module comment on the tensor layout.
- *   [flashback] "flashback.metal" (FlashMetal): backprop_attention, its batch and head
+ *   [metal5]    "flashback.metal" (FlashMetal): backprop_attention, its batch and head
  *               offset arithmetic.
  *
  * Conventions shared by every entry point
@@ -108,7 +108,7 @@ fa_status_t flash_attn_bwd_ex(const void* Q, const void* K, const void* V, const
  * distances, in elements, from (b, t, h, 0) to (b + 1, t, h, 0), (b, t + 1, h, 0) and
  * (b, t, h + 1, 0); the D elements of a row are contiguous.  For a tensor of `heads` heads:
  *   contiguous [B, T, heads, D] (the layout of the entry points above): {T*heads*D, heads*D, D}
- *   [B, heads, T, D] ([flashback] backprop_attention) and [B*heads, T, D] ([teeny] module
+ *   [B, heads, T, D] ([metal5] backprop_attention) and [B*heads, T, D] ([teeny] module
  *   comment): {heads*T*D, D, T*D}
  *   each third of a packed [3, B*H, T, D] QKV buffer ([ipu] flashAttentionQKVPackedWithStash,
  *   whose qkv is 3 x G x L x D): the [B, H, T, D] strides, from that third's base pointer. */
