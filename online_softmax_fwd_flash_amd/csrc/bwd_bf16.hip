@@ -74,19 +74,31 @@ struct Dkdv16Cfg {
 // LDS-DMA of the stage of iteration it (query block ihi - 1 - it / rep of head it % rep)
 // into buffer it % 2.  The first half of the waves fill the Q tile (pieces w, w + NW/2, ...),
 // the second half the dO tile; wave 0 also moves the block's L values, wave 1 its D values.
+// Q / dO rows reach LDS through one descriptor for the whole KV group when the group's heads
+// lie inside each row (row stride >= (rep - 1) * head stride + D, as in [B, T, H, D]): rows
+// past T are then beyond its end for every head.  Otherwise ([B, H, T, D]: the next head
+// follows row T - 1) each block gets a descriptor of its own head's rows.
+struct QdoSrc {
+    Buf q, o;                    // group descriptors (grp)
+    const uint16_t *Qg, *dOg;    // first head of the group
+    int64_t ldq, qh;             // row and head strides (elements)
+    bool grp;
+};
+
 template <int D>
-__device__ __forceinline__ void dkdv16_issue(char* sm, const uint16_t* Qg, const uint16_t* dOg,
-                                             int64_t ldq, int64_t qh, const float* Lg,
+__device__ __forceinline__ void dkdv16_issue(char* sm, const QdoSrc& qs, const float* Lg,
                                              const float* Dg, const uint32_t* voff, int w,
                                              int rep, int ihi, int T, int it) {
     using C = Dkdv16Cfg<D>;
     const int h2 = it % rep, i2 = ihi - 1 - it / rep;
     char* st = sm + (it & 1) * C::STAGE;
-    const int tso = __builtin_amdgcn_readfirstlane((int)((uint32_t)i2 * C::BQ * (uint32_t)(ldq * 2)));
+    const uint32_t rows = (uint32_t)i2 * C::BQ * (uint32_t)(qs.ldq * 2);
+    const int tso = __builtin_amdgcn_readfirstlane(
+        (int)(qs.grp ? rows + (uint32_t)(h2 * qs.qh * 2) : rows));
     const int wq = w % C::QW;
     char* dst = st + (w / C::QW) * C::OFF_DO;
-    // one head's rows: rows past T read as zeros
-    const Buf src = head_buf<D>((w < C::QW ? Qg : dOg) + h2 * qh, ldq, T);
+    const Buf src = qs.grp ? (w < C::QW ? qs.q : qs.o)
+                           : head_buf<D>((w < C::QW ? qs.Qg : qs.dOg) + h2 * qs.qh, qs.ldq, T);
 #pragma unroll
     for (int i = 0; i < C::PMAX; ++i)
         if (wq + C::QW * i < C::TPIECES) dma_piece(src, dst + (wq + C::QW * i) * 1024, voff[i], tso);
@@ -169,6 +181,9 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv16_bf16_kernel(
     const uint32_t ldq_b = (uint32_t)(ldq * 2);
     const uint16_t* Qg = Q + b * lq.b + (int64_t)hk * rep * lq.h;
     const uint16_t* dOg = dO + b * lq.b + (int64_t)hk * rep * lq.h;
+    const uint32_t gspan = (uint32_t)(((int64_t)(rep - 1) * lq.h + (int64_t)(T - 1) * ldq + D) * 2);
+    const QdoSrc qs{Buf(Qg, gspan), Buf(dOg, gspan), Qg, dOg, ldq, lq.h,
+                    ldq >= (int64_t)(rep - 1) * lq.h + D};
     const float* Lg = L + ((int64_t)b * H + (int64_t)hk * rep) * T;
     const float* Dg = Dv + ((int64_t)b * H + (int64_t)hk * rep) * T;
     uint32_t voff[C::PMAX + 1];
@@ -180,13 +195,13 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv16_bf16_kernel(
     // Query blocks are walked last-first (heads inner): every key block of a KV group needs
     // the last query blocks, so the group's co-resident workgroups (same XCD) stream the same
     // Q / dO blocks at about the same time and share them in L2.
-    if (niter > 0) dkdv16_issue<D>(sm, Qg, dOg, ldq, lq.h, Lg, Dg, voff, w, rep, ihi, T, 0);
+    if (niter > 0) dkdv16_issue<D>(sm, qs, Lg, Dg, voff, w, rep, ihi, T, 0);
     for (int it = 0; it < niter; ++it) {
         const int i = ihi - 1 - it / rep;
         wait_vmcnt<0>();   // this stage's pieces, the only loads in flight
         // every wave's pieces are visible; every wave is done with the other stage
         lds_barrier();
-        if (it + 1 < niter) dkdv16_issue<D>(sm, Qg, dOg, ldq, lq.h, Lg, Dg, voff, w, rep, ihi, T, it + 1);
+        if (it + 1 < niter) dkdv16_issue<D>(sm, qs, Lg, Dg, voff, w, rep, ihi, T, it + 1);
         const int qr0 = i * C::BQ;
         const int cls = block_class(T, qr0, qr0 + C::BQ, kw0, kw0 + C::KPW, cz, window);
         if (cls == kSkip) continue;
