@@ -69,7 +69,7 @@ typedef enum {
     FA_ERR_HIP = 3
 } fa_status_t;
 
-typedef enum { FA_DTYPE_F32 = 0, FA_DTYPE_BF16 = 1 } fa_dtype_t;
+typedef enum { FA_DTYPE_F32 = 0, FA_DTYPE_BF16 = 1, FA_DTYPE_F16 = 2 } fa_dtype_t;
 
 /* Forward ([forge] flash_attn_fwd; [ipu] flashAttentionQKVPackedWithStash; [teeny] forward):
  * O = softmax(scale * Q K^T, masked) V per (b, h), and L = row log-sum-exp of the masked,

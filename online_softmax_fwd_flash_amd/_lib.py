@@ -9,7 +9,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("FLASHATTN_LIB", os.path.join(_HERE, "libflashattn.so"))
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
-FA_DTYPE_F32, FA_DTYPE_BF16 = 0, 1
+FA_DTYPE_F32, FA_DTYPE_BF16, FA_DTYPE_F16 = 0, 1, 2
 
 EXPORTS = [
     "flash_attn_fwd", "flash_attn_bwd", "flash_attn_fwd_ex", "flash_attn_bwd_ex",

@@ -11,7 +11,8 @@ import torch
 
 from . import _lib
 
-_DT = {torch.float32: _lib.FA_DTYPE_F32, torch.bfloat16: _lib.FA_DTYPE_BF16}
+_DT = {torch.float32: _lib.FA_DTYPE_F32, torch.bfloat16: _lib.FA_DTYPE_BF16,
+       torch.float16: _lib.FA_DTYPE_F16}
 
 
 class FlashAttnError(RuntimeError):

@@ -19,7 +19,8 @@ fa_status_t check_dims(int B, int T, int H, int HKV, int D, float scale, int cau
     if (H % HKV != 0) return FA_ERR_INVALID_ARG;
     if (window < 0 || (causal != 0 && causal != 1)) return FA_ERR_INVALID_ARG;
     if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
-    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARG;
+    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16)
+        return FA_ERR_INVALID_ARG;
     // every element offset and every grid stays far inside its integer type
     const double elems = (double)B * T * H * D;
     if (elems > (double)(1ll << 40)) return FA_ERR_INVALID_ARG;
@@ -97,8 +98,10 @@ fa_status_t resolve_f32_tiles(int& bq, int& bk) {
 fa_status_t hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
 fa::AttnArgs make_args(int B, int T, int H, int HKV, int D, float scale, int causal, int window,
-                       hipStream_t stream, const fa_layout_t& lq, const fa_layout_t& lk) {
+                       hipStream_t stream, const fa_layout_t& lq, const fa_layout_t& lk,
+                       fa_dtype_t dtype) {
     fa::AttnArgs a{};
+    a.f16 = dtype == FA_DTYPE_F16 ? 1 : 0;
     a.B = B; a.T = T; a.H = H; a.HKV = HKV; a.D = D;
     a.scale = scale; a.causal = causal; a.window = window; a.stream = stream;
     a.lq = to_layout(lq); a.lk = to_layout(lk);
@@ -122,15 +125,15 @@ fa_status_t fwd_impl(const void* Q, const void* K, const void* V, void* O, float
                      const fa_layout_t& lq, const fa_layout_t& lk) {
     fa_status_t s = check_all({Q, K, V, O, L}, B, T, H, HKV, D, scale, causal, window, dtype, lq, lk);
     if (s != FA_OK) return s;
-    fa::AttnArgs a = make_args(B, T, H, HKV, D, scale, causal, window, stream, lq, lk);
+    fa::AttnArgs a = make_args(B, T, H, HKV, D, scale, causal, window, stream, lq, lk, dtype);
     a.Q = Q; a.K = K; a.V = V; a.Oout = O; a.O = O; a.L = L;
     if (dtype == FA_DTYPE_F32) {
         if ((s = resolve_f32_tiles(bq, bk)) != FA_OK) return s;
         return hip_status(fa::launch_fwd_f32(a, bq, bk));
     }
-    if (!((bq == 0 && bk == 0) || (bq == fa::kBf16FwdBq && bk == fa::kBf16FwdBk)))
+    if (!((bq == 0 && bk == 0) || (bq == fa::kB16FwdBq && bk == fa::kB16FwdBk)))
         return FA_ERR_INVALID_ARG;
-    return hip_status(fa::launch_fwd_bf16(a));
+    return hip_status(fa::launch_fwd_b16(a));
 }
 
 fa_status_t preprocess_impl(const void* O, const void* dO, float* Dvec, int B, int T, int H,
@@ -140,7 +143,7 @@ fa_status_t preprocess_impl(const void* O, const void* dO, float* Dvec, int B, i
     if ((s = check_dims(B, T, H, H, D, 1.0f, 0, 0, dtype)) != FA_OK) return s;
     if ((s = check_layout(lq, B, T, H, D, dtype)) != FA_OK) return s;
     return hip_status(fa::launch_bwd_preprocess(O, dO, Dvec, B, T, H, D,
-                                                dtype == FA_DTYPE_F32 ? 0 : 1, stream,
+                                                dtype == FA_DTYPE_F32 ? 0 : dtype == FA_DTYPE_BF16 ? 1 : 2, stream,
                                                 to_layout(lq)));
 }
 
@@ -152,16 +155,16 @@ fa_status_t dkdv_impl(const void* Q, const void* K, const void* V, const void* d
     fa_status_t s = check_all({Q, K, V, dO, L, Dvec, dK, dV}, B, T, H, HKV, D, scale, causal,
                               window, dtype, lq, lk);
     if (s != FA_OK) return s;
-    fa::AttnArgs a = make_args(B, T, H, HKV, D, scale, causal, window, stream, lq, lk);
+    fa::AttnArgs a = make_args(B, T, H, HKV, D, scale, causal, window, stream, lq, lk, dtype);
     a.Q = Q; a.K = K; a.V = V; a.dO = dO; a.Lin = L; a.Dvec = const_cast<float*>(Dvec);
     a.dK = dK; a.dV = dV;
     if (dtype == FA_DTYPE_F32) {
         if ((s = resolve_f32_tiles(bq, bk)) != FA_OK) return s;
         return hip_status(fa::launch_dkdv_f32(a, bq, bk));
     }
-    if (!((bq == 0 && bk == 0) || (bq == fa::kBf16DkdvBq && bk == fa::kBf16DkdvBk)))
+    if (!((bq == 0 && bk == 0) || (bq == fa::kB16DkdvBq && bk == fa::kB16DkdvBk)))
         return FA_ERR_INVALID_ARG;
-    return hip_status(fa::launch_dkdv_bf16(a));
+    return hip_status(fa::launch_dkdv_b16(a));
 }
 
 fa_status_t dq_impl(const void* Q, const void* K, const void* V, const void* dO, const float* L,
@@ -171,16 +174,16 @@ fa_status_t dq_impl(const void* Q, const void* K, const void* V, const void* dO,
     fa_status_t s = check_all({Q, K, V, dO, L, Dvec, dQ}, B, T, H, HKV, D, scale, causal, window,
                               dtype, lq, lk);
     if (s != FA_OK) return s;
-    fa::AttnArgs a = make_args(B, T, H, HKV, D, scale, causal, window, stream, lq, lk);
+    fa::AttnArgs a = make_args(B, T, H, HKV, D, scale, causal, window, stream, lq, lk, dtype);
     a.Q = Q; a.K = K; a.V = V; a.dO = dO; a.Lin = L; a.Dvec = const_cast<float*>(Dvec);
     a.dQ = dQ;
     if (dtype == FA_DTYPE_F32) {
         if ((s = resolve_f32_tiles(bq, bk)) != FA_OK) return s;
         return hip_status(fa::launch_dq_f32(a, bq, bk));
     }
-    if (!((bq == 0 && bk == 0) || (bq == fa::kBf16DqBq && bk == fa::kBf16DqBk)))
+    if (!((bq == 0 && bk == 0) || (bq == fa::kB16DqBq && bk == fa::kB16DqBk)))
         return FA_ERR_INVALID_ARG;
-    return hip_status(fa::launch_dq_bf16(a));
+    return hip_status(fa::launch_dq_b16(a));
 }
 
 fa_status_t dq_dvec_impl(const void* Q, const void* K, const void* V, const void* O,
@@ -198,11 +201,11 @@ fa_status_t dq_dvec_impl(const void* Q, const void* K, const void* V, const void
         return dq_impl(Q, K, V, dO, L, Dvec, dQ, B, T, H, HKV, D, scale, causal, window, dtype,
                        stream, bq, bk, lq, lk);
     }
-    if (!((bq == 0 && bk == 0) || (bq == fa::kBf16DqBq && bk == fa::kBf16DqBk)))
+    if (!((bq == 0 && bk == 0) || (bq == fa::kB16DqBq && bk == fa::kB16DqBk)))
         return FA_ERR_INVALID_ARG;
-    fa::AttnArgs a = make_args(B, T, H, HKV, D, scale, causal, window, stream, lq, lk);
+    fa::AttnArgs a = make_args(B, T, H, HKV, D, scale, causal, window, stream, lq, lk, dtype);
     a.Q = Q; a.K = K; a.V = V; a.O = O; a.dO = dO; a.Lin = L; a.Dvec = Dvec; a.dQ = dQ;
-    return hip_status(fa::launch_dq_bf16_fused_d(a));
+    return hip_status(fa::launch_dq_b16_fused_d(a));
 }
 
 fa_status_t bwd_impl(const void* Q, const void* K, const void* V, const void* O, const float* L,
@@ -250,7 +253,8 @@ int flash_attn_version(void) { return 101; }
 fa_status_t flash_attn_check_layout(fa_layout_t layout, int B, int T, int heads, int D,
                                     fa_dtype_t dtype) {
     if (B < 1 || T < 1 || heads < 1 || D < 1) return FA_ERR_INVALID_ARG;
-    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARG;
+    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16)
+        return FA_ERR_INVALID_ARG;
     return check_layout(layout, B, T, heads, D, dtype);
 }
 
@@ -278,10 +282,10 @@ fa_status_t flash_attn_default_tiles(fa_dtype_t dtype, int D, int pass, int* bq,
         *bk = kF32DefaultBk;
         return FA_OK;
     }
-    if (dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARG;
+    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return FA_ERR_INVALID_ARG;
     if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
-    const int tq[3] = {fa::kBf16FwdBq, fa::kBf16DkdvBq, fa::kBf16DqBq};
-    const int tk[3] = {fa::kBf16FwdBk, fa::kBf16DkdvBk, fa::kBf16DqBk};
+    const int tq[3] = {fa::kB16FwdBq, fa::kB16DkdvBq, fa::kB16DqBq};
+    const int tk[3] = {fa::kB16FwdBk, fa::kB16DkdvBk, fa::kB16DqBk};
     *bq = tq[pass];
     *bk = tk[pass];
     return FA_OK;

@@ -1,5 +1,6 @@
-// bf16 backward attention for gfx950 (D in {64, 128}): a dK/dV pass and a separate dQ pass on
-// bf16 MFMA with fp32 accumulation; P is recomputed from the stored log-sum-exp, never stored.
+// 16-bit backward attention for gfx950 (bf16 or fp16 I/O, D in {64, 128}): a dK/dV pass and a
+// separate dQ pass on MFMA with fp32 accumulation; P is recomputed from the stored
+// log-sum-exp, never stored.
 // Gradients are written once, in fp32, without atomics, so results are deterministic.
 //
 // Method (prior art, other hardware): forge "flash_attention.metal", backward section and the
@@ -28,7 +29,7 @@
 // reads.
 #include "common.h"
 #include "kernels.h"
-#include "stage_bf16.h"
+#include "stage_b16.h"
 
 namespace fa {
 
@@ -113,13 +114,13 @@ __device__ __forceinline__ void dkdv16_issue(char* sm, const QdoSrc& qs, const f
 // B operand of dV += P^T dO / dK += dS^T Q (K = 32 query rows, N = 16 columns) straight from
 // a row-major tile: lane (i, g) element e holds row 32kk + 16*(e/4) + 4g + e%4 of column
 // 16db + i, matching the order P / dS take as A operand.  Two transpose reads of 4 rows.
-template <int LDN>
-__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int kk, int db, int lane) {
+template <class E, int LDN>
+__device__ __forceinline__ typename E::v8 tr_operand(const uint16_t* tile, int kk, int db, int lane) {
     const int j = lane & 15, g = lane >> 4;
     const uint16_t* p = tile + (32 * kk + 4 * g + (j >> 2)) * LDN + 16 * db + 4 * (j & 3);
-    const bf16x4 lo = lds_read_tr4(p);
-    const bf16x4 hi = lds_read_tr4(p + 16 * LDN);
-    bf16x8 r;
+    const typename E::v4 lo = lds_read_tr4e<E>(p);
+    const typename E::v4 hi = lds_read_tr4e<E>(p + 16 * LDN);
+    typename E::v8 r;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         r[e] = lo[e];
@@ -130,14 +131,16 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int kk, int d
 
 }  // namespace
 
-template <int D>
-__global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv16_bf16_kernel(
+template <class E, int D>
+__global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv_b16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ L, const float* __restrict__ Dv, float* __restrict__ dK,
     float* __restrict__ dV, int B, int T, int H, int HKV, float scale, int causal, int window,
     Layout lq, Layout lk) {
     using C = Dkdv16Cfg<D>;
+    using V8 = typename E::v8;
+    using S16 = typename E::s;
     extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
     char* sm = reinterpret_cast<char*>(smem);
 
@@ -159,15 +162,15 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv16_bf16_kernel(
     const int qhi = min(window > 0 ? key + window - 1 : T - 1, T - 1);
 
     // B operands of S = Q K^T and dP = dO V^T: lane (n, g) holds K/V[key][32*ds + 8g .. +7]
-    bf16x8 kreg[C::DS], vreg[C::DS];
+    V8 kreg[C::DS], vreg[C::DS];
     {
         const Buf kb = head_buf<D>(K + b * lk.b + hk * lk.h, ldk, T);
         const Buf vb = head_buf<D>(V + b * lk.b + hk * lk.h, ldk, T);
         const uint32_t off = (uint32_t)key * (uint32_t)(ldk * 2) + 16 * g;
 #pragma unroll
         for (int ds = 0; ds < C::DS; ++ds) {
-            kreg[ds] = __builtin_bit_cast(bf16x8, kb.load16(off + ds * 64));
-            vreg[ds] = __builtin_bit_cast(bf16x8, vb.load16(off + ds * 64));
+            kreg[ds] = __builtin_bit_cast(V8, kb.load16(off + ds * 64));
+            vreg[ds] = __builtin_bit_cast(V8, vb.load16(off + ds * 64));
         }
     }
     f32x4 dka[C::NDB], dva[C::NDB];
@@ -215,12 +218,12 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv16_bf16_kernel(
 #pragma unroll
         for (int qb = 0; qb < C::QB16; ++qb) {
             sc[qb] = dp[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            bf16x8 aq[C::DS], ao[C::DS];
+            V8 aq[C::DS], ao[C::DS];
 #pragma unroll
             for (int ds = 0; ds < C::DS; ++ds) {
                 const int off = (qb * 16 + n) * C::LDN + ds * 32 + 8 * g;
-                aq[ds] = *reinterpret_cast<const bf16x8*>(Qn + off);
-                ao[ds] = *reinterpret_cast<const bf16x8*>(dOn + off);
+                aq[ds] = *reinterpret_cast<const V8*>(Qn + off);
+                ao[ds] = *reinterpret_cast<const V8*>(dOn + off);
             }
 #pragma unroll
             for (int ds = 0; ds < C::DS; ++ds) {
@@ -228,7 +231,7 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv16_bf16_kernel(
                 dp[qb] = mfma16x16x32(ao[ds], vreg[ds], dp[qb]);
             }
         }
-        bf16x8 pp[C::KKS], pd[C::KKS];
+        V8 pp[C::KKS], pd[C::KKS];
 #pragma unroll
         for (int qb = 0; qb < C::QB16; ++qb) {
             const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + qb * 16 + 4 * g);
@@ -242,8 +245,8 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv16_bf16_kernel(
                     p = ((unsigned)(qi - qlo) > (unsigned)(qhi - qlo)) ? 0.f : p;
                 }
                 // k-step kk = qb/2 takes rows of blocks 2kk (elements 0-3), 2kk+1 (4-7)
-                pp[qb >> 1][4 * (qb & 1) + r] = (__bf16)p;
-                pd[qb >> 1][4 * (qb & 1) + r] = (__bf16)(p * (dp[qb][r] - d4[r]));
+                pp[qb >> 1][4 * (qb & 1) + r] = (S16)p;
+                pd[qb >> 1][4 * (qb & 1) + r] = (S16)(p * (dp[qb][r] - d4[r]));
             }
         }
         // dV += P^T dO and dK += dS^T Q, 32 query rows per k-step
@@ -251,11 +254,11 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv16_bf16_kernel(
         for (int kk = 0; kk < C::KKS; ++kk)
 #pragma unroll
             for (int d0 = 0; d0 < C::NDB; d0 += 4) {
-                bf16x8 bo[4], bq[4];
+                V8 bo[4], bq[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    bo[u] = tr_operand<C::LDN>(dOn, kk, d0 + u, lane);
-                    bq[u] = tr_operand<C::LDN>(Qn, kk, d0 + u, lane);
+                    bo[u] = tr_operand<E, C::LDN>(dOn, kk, d0 + u, lane);
+                    bq[u] = tr_operand<E, C::LDN>(Qn, kk, d0 + u, lane);
                 }
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
@@ -323,14 +326,15 @@ __device__ __forceinline__ void dq_issue(char* st, const Buf& kbuf, const Buf& v
 
 }  // namespace
 
-template <int D, int NW, bool FUSE_D>
-__global__ __launch_bounds__(NW * 64, 8 / NW) void dq_bf16_kernel(
+template <class E, int D, int NW, bool FUSE_D>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void dq_b16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const uint16_t* __restrict__ O, const float* __restrict__ L, float* __restrict__ Dv,
     float* __restrict__ dQ, int B, int T, int H, int HKV, float scale, int causal, int window,
     int nqt, int xcd_group, Layout lq, Layout lk) {
     using C = DqCfg<D, NW>;
+    using V8 = typename E::v8;
     extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
     char* sm = reinterpret_cast<char*>(smem);
 
@@ -352,14 +356,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_bf16_kernel(
     const float c = scale * kLog2e;
 
     // B operands of S^T = K Q^T and dP^T = V dO^T: lane (n, g) holds Q/dO[q][16*dc + 8g ..]
-    bf16x8 qreg[C::DC], oreg[C::DC];
+    V8 qreg[C::DC], oreg[C::DC];
     {
         const int64_t base = qrow + 8 * g;
 #pragma unroll
         for (int dc = 0; dc < C::DC; ++dc) {
             const u32x4 z = {0u, 0u, 0u, 0u};
-            qreg[dc] = __builtin_bit_cast(bf16x8, q < T ? *reinterpret_cast<const u32x4*>(Q + base + dc * 16) : z);
-            oreg[dc] = __builtin_bit_cast(bf16x8, q < T ? *reinterpret_cast<const u32x4*>(dO + base + dc * 16) : z);
+            qreg[dc] = __builtin_bit_cast(V8, q < T ? *reinterpret_cast<const u32x4*>(Q + base + dc * 16) : z);
+            oreg[dc] = __builtin_bit_cast(V8, q < T ? *reinterpret_cast<const u32x4*>(dO + base + dc * 16) : z);
         }
     }
     const float l2 = q < T ? L[((int64_t)b * H + h) * T + q] * kLog2e : kBigLse;
@@ -373,14 +377,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_bf16_kernel(
         for (int dc = 0; dc < C::DC; ++dc) {
             const u32x4 z = {0u, 0u, 0u, 0u};
             const u32x4 o = q < T ? *reinterpret_cast<const u32x4*>(O + base + dc * 16) : z;
-            const u32x4 d = __builtin_bit_cast(u32x4, oreg[dc]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t x = o[i], y = d[i];
-                s = fmaf(__builtin_bit_cast(float, x << 16), __builtin_bit_cast(float, y << 16), s);
-                s = fmaf(__builtin_bit_cast(float, x & 0xffff0000u),
-                         __builtin_bit_cast(float, y & 0xffff0000u), s);
-            }
+            s = dot8<E>(o, __builtin_bit_cast(u32x4, oreg[dc]), s);
         }
         dq_i = halves_sum(s);
         if (g == 0 && q < T) Dv[((int64_t)b * H + h) * T + q] = dq_i;
@@ -422,12 +419,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_bf16_kernel(
             // A operands of S^T and dP^T for this 32-key half, four k-steps ahead
 #pragma unroll
             for (int d0 = 0; d0 < C::DC; d0 += 4) {
-                bf16x8 ak[4], av[4];
+                V8 ak[4], av[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int off = (kb * 32 + n) * C::LDN + (d0 + u) * 16 + 8 * g;
-                    ak[u] = *reinterpret_cast<const bf16x8*>(Kn + off);
-                    av[u] = *reinterpret_cast<const bf16x8*>(Vn + off);
+                    ak[u] = *reinterpret_cast<const V8*>(Kn + off);
+                    av[u] = *reinterpret_cast<const V8*>(Vn + off);
                 }
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
@@ -448,16 +445,16 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_bf16_kernel(
                     if ((unsigned)(kk - klo) > (unsigned)(khi - klo)) sk[r] = 0.f;
                 }
             }
-            bf16x8 pd[2];
+            V8 pd[2];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) pd[r >> 3][r & 7] = (__bf16)(sk[r] * dk[r]);
+            for (int r = 0; r < 16; ++r) pd[r >> 3][r & 7] = (typename E::s)(sk[r] * dk[r]);
             // dQ^T += K^T dS^T over this half's 32 keys, 16 per k-step
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
-                bf16x8 at[C::NDB];
+                V8 at[C::NDB];
 #pragma unroll
                 for (int db = 0; db < C::NDB; ++db)
-                    at[db] = tr_operand32<C::LDN>(Kn, kb * 32 + hf * 16, db * 32, lane);
+                    at[db] = tr_operand32<E, C::LDN>(Kn, kb * 32 + hf * 16, db * 32, lane);
 #pragma unroll
                 for (int db = 0; db < C::NDB; ++db) dqa[db] = mfma32x32x16(at[db], pd[hf], dqa[db]);
             }
@@ -496,16 +493,16 @@ hipError_t allow_lds(Kern kern, size_t lds, bool* set_flags) {
     return hipSuccess;
 }
 
-template <int D>
-hipError_t launch_dkdv16_bf16_t(const AttnArgs& a) {
+template <class E, int D>
+hipError_t launch_dkdv_b16_t(const AttnArgs& a) {
     using C = Dkdv16Cfg<D>;
     static bool set[kMaxDevices] = {};
     const size_t lds = 2 * (size_t)C::STAGE;
-    hipError_t e = allow_lds(dkdv16_bf16_kernel<D>, lds, set);
+    hipError_t e = allow_lds(dkdv_b16_kernel<E, D>, lds, set);
     if (e != hipSuccess) return e;
     const int nkt = (a.T + C::BKW - 1) / C::BKW;
     const unsigned grid = (unsigned)nkt * a.B * a.HKV;
-    hipLaunchKernelGGL((dkdv16_bf16_kernel<D>), dim3(grid), dim3(C::NT), lds, a.stream,
+    hipLaunchKernelGGL((dkdv_b16_kernel<E, D>), dim3(grid), dim3(C::NT), lds, a.stream,
                        (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
                        (const uint16_t*)a.dO, a.Lin, a.Dvec, a.dK, a.dV, a.B, a.T, a.H, a.HKV,
                        a.scale, a.causal, a.window, a.lq, a.lk);
@@ -513,21 +510,21 @@ hipError_t launch_dkdv16_bf16_t(const AttnArgs& a) {
 }
 
 constexpr int kDqWaves = 4;
-static_assert(DqCfg<128, kDqWaves>::BQ == kBf16DqBq && DqCfg<128, kDqWaves>::BK == kBf16DqBk,
+static_assert(DqCfg<128, kDqWaves>::BQ == kB16DqBq && DqCfg<128, kDqWaves>::BK == kB16DqBk,
               "dQ tiling differs from kernels.h");
-static_assert(Dkdv16Cfg<128>::BQ == kBf16DkdvBq && Dkdv16Cfg<128>::BKW == kBf16DkdvBk,
+static_assert(Dkdv16Cfg<128>::BQ == kB16DkdvBq && Dkdv16Cfg<128>::BKW == kB16DkdvBk,
               "dK/dV tiling differs from kernels.h");
 
-template <int D, bool FUSE_D>
-hipError_t launch_dq_bf16_t(const AttnArgs& a) {
+template <class E, int D, bool FUSE_D>
+hipError_t launch_dq_b16_t(const AttnArgs& a) {
     using C = DqCfg<D, kDqWaves>;
     static bool set[kMaxDevices] = {};
     const size_t lds = 2 * (size_t)C::STAGE;
-    hipError_t e = allow_lds(dq_bf16_kernel<D, kDqWaves, FUSE_D>, lds, set);
+    hipError_t e = allow_lds(dq_b16_kernel<E, D, kDqWaves, FUSE_D>, lds, set);
     if (e != hipSuccess) return e;
     const int nqt = (a.T + C::BQ - 1) / C::BQ;
     const unsigned grid = (unsigned)nqt * a.B * a.H;
-    hipLaunchKernelGGL((dq_bf16_kernel<D, kDqWaves, FUSE_D>), dim3(grid), dim3(C::NT), lds,
+    hipLaunchKernelGGL((dq_b16_kernel<E, D, kDqWaves, FUSE_D>), dim3(grid), dim3(C::NT), lds,
                        a.stream, (const uint16_t*)a.Q, (const uint16_t*)a.K,
                        (const uint16_t*)a.V, (const uint16_t*)a.dO, (const uint16_t*)a.O, a.Lin,
                        a.Dvec, a.dQ, a.B, a.T, a.H, a.HKV, a.scale, a.causal, a.window, nqt,
@@ -537,22 +534,22 @@ hipError_t launch_dq_bf16_t(const AttnArgs& a) {
 
 }  // namespace
 
-hipError_t launch_dkdv_bf16(const AttnArgs& a) {
-    if (a.D == 64) return launch_dkdv16_bf16_t<64>(a);
-    if (a.D == 128) return launch_dkdv16_bf16_t<128>(a);
+hipError_t launch_dkdv_b16(const AttnArgs& a) {
+    if (a.D == 64) return a.f16 ? launch_dkdv_b16_t<F16, 64>(a) : launch_dkdv_b16_t<Bf16, 64>(a);
+    if (a.D == 128) return a.f16 ? launch_dkdv_b16_t<F16, 128>(a) : launch_dkdv_b16_t<Bf16, 128>(a);
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_dq_bf16(const AttnArgs& a) {
-    if (a.D == 64) return launch_dq_bf16_t<64, false>(a);
-    if (a.D == 128) return launch_dq_bf16_t<128, false>(a);
+hipError_t launch_dq_b16(const AttnArgs& a) {
+    if (a.D == 64) return a.f16 ? launch_dq_b16_t<F16, 64, false>(a) : launch_dq_b16_t<Bf16, 64, false>(a);
+    if (a.D == 128) return a.f16 ? launch_dq_b16_t<F16, 128, false>(a) : launch_dq_b16_t<Bf16, 128, false>(a);
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_dq_bf16_fused_d(const AttnArgs& a) {
+hipError_t launch_dq_b16_fused_d(const AttnArgs& a) {
     if (a.O == nullptr) return hipErrorInvalidValue;
-    if (a.D == 64) return launch_dq_bf16_t<64, true>(a);
-    if (a.D == 128) return launch_dq_bf16_t<128, true>(a);
+    if (a.D == 64) return a.f16 ? launch_dq_b16_t<F16, 64, true>(a) : launch_dq_b16_t<Bf16, 64, true>(a);
+    if (a.D == 128) return a.f16 ? launch_dq_b16_t<F16, 128, true>(a) : launch_dq_b16_t<Bf16, 128, true>(a);
     return hipErrorInvalidValue;
 }
 

@@ -12,8 +12,11 @@ namespace {
 
 constexpr int kTeam = 8, kThreads = 256;
 
-template <typename Elem>
-__device__ __forceinline__ float dot16B(const u32x4& a, const u32x4& b);
+// fp32 dot of the elements in two 16-byte words: 4 floats, or 8 bf16 / fp16 (dot8)
+template <typename E>
+__device__ __forceinline__ float dot16B(const u32x4& a, const u32x4& b) {
+    return dot8<E>(a, b, 0.f);
+}
 
 template <>
 __device__ __forceinline__ float dot16B<float>(const u32x4& a, const u32x4& b) {
@@ -27,39 +30,34 @@ __device__ __forceinline__ float dot16B<float>(const u32x4& a, const u32x4& b) {
     return s;
 }
 
-template <>
-__device__ __forceinline__ float dot16B<uint16_t>(const u32x4& a, const u32x4& b) {
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        s = fmaf(__builtin_bit_cast(float, a[i] << 16), __builtin_bit_cast(float, b[i] << 16), s);
-        s = fmaf(__builtin_bit_cast(float, a[i] & 0xffff0000u),
-                 __builtin_bit_cast(float, b[i] & 0xffff0000u), s);
-    }
-    return s;
-}
+// element size in bytes of the I/O type
+template <typename E> constexpr int kElemBytes = 2;
+template <> constexpr int kElemBytes<float> = 4;
 
 template <typename Elem>
 __global__ __launch_bounds__(kThreads) void bwd_preprocess_kernel(
-    const Elem* __restrict__ O, const Elem* __restrict__ dO, float* __restrict__ Dv, int B, int T,
-    int H, int D, Layout lq) {
+    const void* __restrict__ Ov, const void* __restrict__ dOv, float* __restrict__ Dv, int B,
+    int T, int H, int D, Layout lq) {
+    constexpr int ES = kElemBytes<Elem>;
+    const char* O = static_cast<const char*>(Ov);
+    const char* dO = static_cast<const char*>(dOv);
     // row = (b*T + i)*H + h; O and dO of that row start at b*lq.b + i*lq.t + h*lq.h
     const int64_t rows = (int64_t)B * T * H;
     const int64_t row = (int64_t)blockIdx.x * (kThreads / kTeam) + threadIdx.x / kTeam;
     const int sub = threadIdx.x % kTeam;
-    const int nch = D * (int)sizeof(Elem) / 16;   // 16-byte chunks per row
+    const int nch = D * ES / 16;   // 16-byte chunks per row
     const int h = (int)(row % H);
     const int64_t bi = row / H;
     const int i = (int)(bi % T);
     const int64_t b = bi / T;
     float s = 0.f;
     if (row < rows) {
-        const int64_t off = b * lq.b + (int64_t)i * lq.t + (int64_t)h * lq.h;
-        const Elem* o = O + off;
-        const Elem* go = dO + off;
+        const int64_t off = (b * lq.b + (int64_t)i * lq.t + (int64_t)h * lq.h) * ES;
+        const char* o = O + off;
+        const char* go = dO + off;
         for (int ch = sub; ch < nch; ch += kTeam) {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(o + ch * (16 / sizeof(Elem)));
-            const u32x4 c = *reinterpret_cast<const u32x4*>(go + ch * (16 / sizeof(Elem)));
+            const u32x4 a = *reinterpret_cast<const u32x4*>(o + ch * 16);
+            const u32x4 c = *reinterpret_cast<const u32x4*>(go + ch * 16);
             s += dot16B<Elem>(a, c);
         }
     }
@@ -78,10 +76,13 @@ hipError_t launch_bwd_preprocess(const void* O, const void* dO, float* Dvec, int
     const unsigned grid = (unsigned)((rows + per - 1) / per);
     if (dtype == 0)
         hipLaunchKernelGGL(bwd_preprocess_kernel<float>, dim3(grid), dim3(kThreads), 0, stream,
-                           (const float*)O, (const float*)dO, Dvec, B, T, H, D, lq);
+                           O, dO, Dvec, B, T, H, D, lq);
+    else if (dtype == 1)
+        hipLaunchKernelGGL(bwd_preprocess_kernel<Bf16>, dim3(grid), dim3(kThreads), 0, stream,
+                           O, dO, Dvec, B, T, H, D, lq);
     else
-        hipLaunchKernelGGL(bwd_preprocess_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, stream,
-                           (const uint16_t*)O, (const uint16_t*)dO, Dvec, B, T, H, D, lq);
+        hipLaunchKernelGGL(bwd_preprocess_kernel<F16>, dim3(grid), dim3(kThreads), 0, stream,
+                           O, dO, Dvec, B, T, H, D, lq);
     return hipGetLastError();
 }
 

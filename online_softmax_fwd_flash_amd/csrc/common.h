@@ -12,6 +12,9 @@ namespace fa {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -34,6 +37,14 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
 // lane l is row 4*(l/16) + r, column l % 16.
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// The same two MFMA shapes with IEEE half inputs (same lane layouts).
+__device__ __forceinline__ f32x16 mfma32x32x16(f16x8 a, f16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 // D(16x16) += A(16x4) * B(4x16), fp32.  Lane l supplies A[l%16][l/16] and B[l/16][l%16];
@@ -90,6 +101,62 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+
+// The 16-bit element types of the MFMA kernels (the I/O type of Q, K, V, O and dO; products
+// accumulate in fp32): scalar, and the 8-, 4- and 2-element vectors the kernels move.
+struct Bf16 {
+    typedef __bf16 s;
+    typedef bf16x8 v8;
+    typedef bf16x4 v4;
+    typedef bf16x2 v2;
+};
+struct F16 {
+    typedef _Float16 s;
+    typedef f16x8 v8;
+    typedef f16x4 v4;
+    typedef f16x2 v2;
+};
+
+// Round-to-nearest-even float -> element pair, packed low element first.
+template <class E>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    typename E::v2 r;
+    r[0] = (typename E::s)lo;
+    r[1] = (typename E::s)hi;
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// LDS transpose read of 16-bit elements (the instruction moves 16-bit lanes whatever their
+// type; see lds_read_tr4).
+template <class E>
+__device__ __forceinline__ typename E::v4 lds_read_tr4e(const uint16_t* p) {
+    return __builtin_bit_cast(typename E::v4, lds_read_tr4(p));
+}
+
+// sum_i a_i * b_i over the 8 elements packed in two 16-byte words, in fp32 (exact products,
+// fp32 sums in element order).
+template <class E>
+__device__ __forceinline__ float dot8(const u32x4& a, const u32x4& b, float s);
+template <>
+__device__ __forceinline__ float dot8<Bf16>(const u32x4& a, const u32x4& b, float s) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t x = a[i], y = b[i];
+        s = fmaf(__builtin_bit_cast(float, x << 16), __builtin_bit_cast(float, y << 16), s);
+        s = fmaf(__builtin_bit_cast(float, x & 0xffff0000u), __builtin_bit_cast(float, y & 0xffff0000u), s);
+    }
+    return s;
+}
+template <>
+__device__ __forceinline__ float dot8<F16>(const u32x4& a, const u32x4& b, float s) {
+    const f16x8 x = __builtin_bit_cast(f16x8, a), y = __builtin_bit_cast(f16x8, b);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const _Float16 xi = x[i], yi = y[i];
+        s = fmaf((float)xi, (float)yi, s);
+    }
+    return s;
 }
 
 }  // namespace fa

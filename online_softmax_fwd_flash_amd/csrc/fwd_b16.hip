@@ -1,5 +1,5 @@
-// bf16 forward attention for gfx950 (D in {64, 128}): bf16 MFMA 32x32x16 with fp32
-// accumulation, online softmax in registers, O and one log-sum-exp per query row stored.
+// 16-bit forward attention for gfx950 (bf16 or fp16 I/O, D in {64, 128}): MFMA 32x32x16 with
+// fp32 accumulation, online softmax in registers, O and one log-sum-exp per query row stored.
 //
 // Method (prior art, other hardware): forge "flash_attention.metal", header comment and the
 // forward kernel (online-softmax update, m from -FLT_MAX, K/V staged per block through
@@ -19,7 +19,8 @@
 //    (8 rows x 4 chunks per wave).
 //  * Scores are formed transposed, S^T = K Q^T: the accumulator column (lane % 32) is a query
 //    row, so each query's max / sum are in-lane plus one exchange between wave halves.
-//  * P^T (bf16, RNE) feeds O^T += V^T P^T straight from the accumulator registers.  The
+//  * P^T (rounded to the element type, RNE) feeds O^T += V^T P^T straight from the
+//    accumulator registers.  The
 //    accumulator gives lane half g the keys 8*(r/4) + 4g + r%4 of each 32-key group; the
 //    V^T operand in that key order comes from the row-major V tile through two LDS
 //    transpose reads (ds_read_b64_tr_b16) per MFMA, so V needs no transposed copy.
@@ -31,7 +32,7 @@
 //    they share its K/V in that XCD's L2.
 #include "common.h"
 #include "kernels.h"
-#include "stage_bf16.h"
+#include "stage_b16.h"
 
 namespace fa {
 
@@ -40,7 +41,7 @@ namespace {
 constexpr int kBQ = 128, kBK = 32, kThreads = 256;
 constexpr int kNH = kBK / 32;   // 32-key halves of a key block
 constexpr int kWgs = 3;         // workgroups per CU
-static_assert(kBQ == kBf16FwdBq && kBK == kBf16FwdBk, "forward tiling differs from kernels.h");
+static_assert(kBQ == kB16FwdBq && kBK == kB16FwdBk, "forward tiling differs from kernels.h");
 
 template <int D>
 struct Bf16Fwd {
@@ -79,13 +80,15 @@ __device__ __forceinline__ void fwd_issue(const Buf& kb, const Buf& vb, const ui
 
 }  // namespace
 
-template <int D>
-__global__ __launch_bounds__(kThreads, kWgs) void fwd_bf16_kernel(
+template <class E, int D>
+__global__ __launch_bounds__(kThreads, kWgs) void fwd_b16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ L, int B,
     int T, int H, int HKV, float scale, int causal, int window, int nqt, int xcd_group,
     Layout lq, Layout lk) {
     using C = Bf16Fwd<D>;
+    using V8 = typename E::v8;
+    using V4 = typename E::v4;
     extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
 
     int qt, b, h;
@@ -106,12 +109,12 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_bf16_kernel(
     const int khi = cz ? q : T - 1;
 
     // Q^T operand: lane (n, g) holds Q[q][16*dc + 8*g .. +7] (zero past T)
-    bf16x8 qreg[C::DC];
+    V8 qreg[C::DC];
     {
         const Buf qbuf = head_buf<D>(Q + b * lq.b + h * lq.h, ldq, T);
         const uint32_t off = (uint32_t)q * (uint32_t)(ldq * 2) + 16 * g;
 #pragma unroll
-        for (int dc = 0; dc < C::DC; ++dc) qreg[dc] = __builtin_bit_cast(bf16x8, qbuf.load16(off + dc * 32));
+        for (int dc = 0; dc < C::DC; ++dc) qreg[dc] = __builtin_bit_cast(V8, qbuf.load16(off + dc * 32));
     }
     f32x16 oacc[C::NDB];
 #pragma unroll
@@ -166,12 +169,12 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_bf16_kernel(
         for (int hk = 0; hk < kNH; ++hk)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[hk][r] = 0.f;
-        bf16x8 ka[C::DC][kNH];
+        V8 ka[C::DC][kNH];
 #pragma unroll
         for (int dc = 0; dc < C::DC; ++dc)
 #pragma unroll
             for (int hk = 0; hk < kNH; ++hk)
-                ka[dc][hk] = *reinterpret_cast<const bf16x8*>(sb + kaddr + 32 * dc + 32 * hk * C::KROWB);
+                ka[dc][hk] = *reinterpret_cast<const V8*>(sb + kaddr + 32 * dc + 32 * hk * C::KROWB);
 #pragma unroll
         for (int dc = 0; dc < C::DC; ++dc)
 #pragma unroll
@@ -224,19 +227,19 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_bf16_kernel(
         for (int hk = 0; hk < kNH; ++hk) lsum += ps[hk];
         // P^T operand of 16-key quarter kh: element e <-> accumulator entry 8*(kh % 2) + e of
         // s[kh / 2]
-        bf16x8 pb[2 * kNH];
+        V8 pb[2 * kNH];
 #pragma unroll
         for (int kh = 0; kh < 2 * kNH; ++kh)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pb[kh][e] = (__bf16)s[kh >> 1][8 * (kh & 1) + e];
+            for (int e = 0; e < 8; ++e) pb[kh][e] = (typename E::s)s[kh >> 1][8 * (kh & 1) + e];
 #pragma unroll
         for (int kh = 0; kh < 2 * kNH; ++kh)
 #pragma unroll
             for (int db = 0; db < C::NDB; ++db) {
                 const char* pv = sb + vaddr[db] + 16 * kh * C::VROWB;
-                const bf16x4 lo = lds_read_tr4(reinterpret_cast<const uint16_t*>(pv));
-                const bf16x4 hi = lds_read_tr4(reinterpret_cast<const uint16_t*>(pv + 8 * C::VROWB));
-                bf16x8 av;
+                const V4 lo = lds_read_tr4e<E>(reinterpret_cast<const uint16_t*>(pv));
+                const V4 hi = lds_read_tr4e<E>(reinterpret_cast<const uint16_t*>(pv + 8 * C::VROWB));
+                V8 av;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     av[e] = lo[e];
@@ -256,8 +259,8 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_bf16_kernel(
 #pragma unroll
         for (int t4 = 0; t4 < 4; ++t4) {
             u32x2 wv;
-            wv[0] = pack_bf16x2(oacc[db][4 * t4 + 0] * inv, oacc[db][4 * t4 + 1] * inv);
-            wv[1] = pack_bf16x2(oacc[db][4 * t4 + 2] * inv, oacc[db][4 * t4 + 3] * inv);
+            wv[0] = pack2<E>(oacc[db][4 * t4 + 0] * inv, oacc[db][4 * t4 + 1] * inv);
+            wv[1] = pack2<E>(oacc[db][4 * t4 + 2] * inv, oacc[db][4 * t4 + 3] * inv);
             *reinterpret_cast<u32x2*>(Oq + db * 32 + 8 * t4 + 4 * g) = wv;
         }
     if (g == 0)
@@ -266,8 +269,8 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_bf16_kernel(
 
 namespace {
 
-template <int D>
-hipError_t launch_fwd_bf16_t(const AttnArgs& a) {
+template <class E, int D>
+hipError_t launch_fwd_b16_t(const AttnArgs& a) {
     using C = Bf16Fwd<D>;
     const int nqt = (a.T + kBQ - 1) / kBQ;
     const unsigned grid = (unsigned)nqt * a.B * a.H;
@@ -279,12 +282,12 @@ hipError_t launch_fwd_bf16_t(const AttnArgs& a) {
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
     if (!attr_set[dev]) {
-        e = hipFuncSetAttribute((const void*)fwd_bf16_kernel<D>,
+        e = hipFuncSetAttribute((const void*)fwd_b16_kernel<E, D>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         attr_set[dev] = true;
     }
-    hipLaunchKernelGGL((fwd_bf16_kernel<D>), dim3(grid), dim3(kThreads), lds, a.stream,
+    hipLaunchKernelGGL((fwd_b16_kernel<E, D>), dim3(grid), dim3(kThreads), lds, a.stream,
                        (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
                        (uint16_t*)a.Oout, a.L, a.B, a.T, a.H, a.HKV, a.scale, a.causal,
                        a.window, nqt, xcd_group, a.lq, a.lk);
@@ -293,9 +296,14 @@ hipError_t launch_fwd_bf16_t(const AttnArgs& a) {
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const AttnArgs& a) {
-    if (a.D == 64) return launch_fwd_bf16_t<64>(a);
-    if (a.D == 128) return launch_fwd_bf16_t<128>(a);
+hipError_t launch_fwd_b16(const AttnArgs& a) {
+    if (a.f16) {
+        if (a.D == 64) return launch_fwd_b16_t<F16, 64>(a);
+        if (a.D == 128) return launch_fwd_b16_t<F16, 128>(a);
+    } else {
+        if (a.D == 64) return launch_fwd_b16_t<Bf16, 64>(a);
+        if (a.D == 128) return launch_fwd_b16_t<Bf16, 128>(a);
+    }
     return hipErrorInvalidValue;
 }
 

@@ -30,27 +30,29 @@ struct AttnArgs {
     int causal, window;
     hipStream_t stream;
     Layout lq, lk;   // query-side and key-side layouts
+    int f16;         // 16-bit kernels: 1 = IEEE half elements, 0 = bfloat16
 };
 
 // Tilings of the bf16 kernels: query rows x keys handled per workgroup block.  Each kernel
 // translation unit static_asserts its own constants against these.
-constexpr int kBf16FwdBq = 128, kBf16FwdBk = 32;    // forward: q-tile x staged key block
-constexpr int kBf16DkdvBq = 32, kBf16DkdvBk = 64;   // dK/dV: staged query block x key tile
-constexpr int kBf16DqBq = 128, kBf16DqBk = 64;      // dQ: q-tile x staged key block
+constexpr int kB16FwdBq = 128, kB16FwdBk = 32;    // forward: q-tile x staged key block
+constexpr int kB16DkdvBq = 32, kB16DkdvBk = 64;   // dK/dV: staged query block x key tile
+constexpr int kB16DqBq = 128, kB16DqBk = 64;      // dQ: q-tile x staged key block
 
 bool f32_tiles_supported(int bq, int bk);
 hipError_t launch_fwd_f32(const AttnArgs& a, int bq, int bk);
 hipError_t launch_dkdv_f32(const AttnArgs& a, int bq, int bk);
 hipError_t launch_dq_f32(const AttnArgs& a, int bq, int bk);
 
-hipError_t launch_fwd_bf16(const AttnArgs& a);
-hipError_t launch_dkdv_bf16(const AttnArgs& a);
-hipError_t launch_dq_bf16(const AttnArgs& a);
+// 16-bit (bf16 / fp16 by a.f16) kernels
+hipError_t launch_fwd_b16(const AttnArgs& a);
+hipError_t launch_dkdv_b16(const AttnArgs& a);
+hipError_t launch_dq_b16(const AttnArgs& a);
 // dQ that also computes Dvec[b,h,i] = rowsum(dO * O) for its own rows from a.O and writes it
 // to a.Dvec (the dK/dV pass launched after it reads those values)
-hipError_t launch_dq_bf16_fused_d(const AttnArgs& a);
+hipError_t launch_dq_b16_fused_d(const AttnArgs& a);
 
-// dtype: 0 = f32, 1 = bf16
+// dtype: 0 = f32, 1 = bf16, 2 = fp16
 hipError_t launch_bwd_preprocess(const void* O, const void* dO, float* Dvec, int B, int T,
                                  int H, int D, int dtype, hipStream_t stream, Layout lq);
 

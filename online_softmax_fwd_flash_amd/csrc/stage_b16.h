@@ -149,13 +149,13 @@ __device__ __forceinline__ float vmax(float a, float b) { return __builtin_eleme
 // operand comes from a 32x32 accumulator: lane l = 16c + j covers column c0 + 16*(c%2) + j,
 // half g = c/2, and element e holds row r0 + 8*(e/4) + 4g + e%4 -- the row order in which
 // accumulator lane half g holds its rows.  Two LDS transpose reads of 4 rows each.
-template <int LD>
-__device__ __forceinline__ bf16x8 tr_operand32(const uint16_t* tile, int r0, int c0, int lane) {
+template <class E, int LD>
+__device__ __forceinline__ typename E::v8 tr_operand32(const uint16_t* tile, int r0, int c0, int lane) {
     const int j = lane & 15, c = lane >> 4, g = c >> 1;
     const uint16_t* p = tile + (r0 + 4 * g + (j >> 2)) * LD + c0 + 16 * (c & 1) + 4 * (j & 3);
-    const bf16x4 lo = lds_read_tr4(p);
-    const bf16x4 hi = lds_read_tr4(p + 8 * LD);
-    bf16x8 r;
+    const typename E::v4 lo = lds_read_tr4e<E>(p);
+    const typename E::v4 hi = lds_read_tr4e<E>(p + 8 * LD);
+    typename E::v8 r;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         r[e] = lo[e];

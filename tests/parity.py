@@ -12,8 +12,12 @@ from workloads import make_inputs_like
 
 # f32 path: max-abs <= 1e-4 on every output.  bf16 path (bf16 in, fp32 accumulate):
 # max-abs <= 2e-2 and relative L2 <= 5e-3 per tensor, against the oracle on the same
-# bf16-rounded inputs.
-TOL = {"f32": dict(max_abs=1e-4, rel_l2=None), "bf16": dict(max_abs=2e-2, rel_l2=5e-3)}
+# bf16-rounded inputs.  fp16 path: the same arithmetic with the 16-bit roundings (inputs
+# aside, P and dS as MFMA operands and the stored O) at a unit roundoff of 2^-11 instead of
+# 2^-8, so the bf16 bounds scaled by 2^-3, with a factor 2 of margin: max-abs <= 5e-3 and
+# relative L2 <= 1.25e-3.
+TOL = {"f32": dict(max_abs=1e-4, rel_l2=None), "bf16": dict(max_abs=2e-2, rel_l2=5e-3),
+       "f16": dict(max_abs=5e-3, rel_l2=1.25e-3)}
 
 
 def log(msg):

@@ -105,6 +105,18 @@ def test_bad_tiles_rejected():
     assert dq_dvec(dtype=0, bq=48, bk=16) == 1
 
 
+def test_f16_dtype():
+    # fp16 takes the 16-bit kernels: the same head dims and tilings as bf16
+    assert fwd(dtype=2, D=96) == 2
+    assert bwd(dtype=2, D=32) == 2
+    assert dq_dvec(dtype=2, bq=64, bk=64) == 1
+    for p in range(3):
+        assert fa.flash_attn_default_tiles(2, 128, p) == fa.flash_attn_default_tiles(1, 128, p)
+    assert fa.flash_attn_check_layout((64 * 4 * 128, 4 * 128, 128), 2, 64, 4, 128, 2) == 0
+    assert fa.flash_attn_check_layout((4 * 64 * 130, 130, 64 * 130), 2, 64, 4, 128, 2) == 1
+    assert fwd(dtype=3) == 1
+
+
 def test_default_tiles():
     assert fa.flash_attn_default_tiles(1, 128, 0) == (128, 32)
     assert fa.flash_attn_default_tiles(1, 128, 1) == (32, 64)

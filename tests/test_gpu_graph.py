@@ -14,7 +14,7 @@ from workloads import make_inputs_like
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f16", 128), ("f32", 64)])
 def test_graph_replay_matches_eager(dtype, D):
     B, T, H, HKV = 1, 300, 8, 2
     causal, window = True, 0

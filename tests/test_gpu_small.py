@@ -66,3 +66,21 @@ def test_bf16_backward_gqa(H, HKV):
 
 def test_bf16_backward_long_window():
     check_case(1, 1100, 4, 1, 128, "bf16", True, 300, seed=120)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("T", [1, 100, 257, 640])
+@pytest.mark.parametrize("causal,window", [(True, 0), (True, 7), (False, 0), (False, 13)])
+def test_f16_forward_backward(D, T, causal, window):
+    check_case(1, T, 8, 2, D, "f16", causal, window, seed=130 + T + D)
+
+
+@pytest.mark.parametrize("H,HKV", [(4, 4), (8, 1), (16, 2)])
+def test_f16_gqa(H, HKV):
+    check_case(2, 384, H, HKV, 128, "f16", True, 0, seed=140 + H * HKV)
+
+
+def test_f16_forward_large_scale_value():
+    """As the bf16 case: scale above 1, masked rows in the first key block (forward; the
+    absolute bounds are set for the 1/sqrt(D) scale the workloads use)."""
+    check_case(1, 200, 4, 2, 64, "f16", True, 3, seed=150, backward=False, scale=1.7)

@@ -14,7 +14,8 @@ from workloads import make_inputs_like
 
 pytestmark = pytest.mark.gpu
 
-CASES = [("f32", 64, (32, 32)), ("f32", 16, (64, 16)), ("bf16", 64, (0, 0)), ("bf16", 128, (0, 0))]
+CASES = [("f32", 64, (32, 32)), ("f32", 16, (64, 16)), ("bf16", 64, (0, 0)), ("bf16", 128, (0, 0)),
+         ("f16", 128, (0, 0))]
 
 
 def check_dvec(dvec, o, dod, ref, dtype):
@@ -22,11 +23,12 @@ def check_dvec(dvec, o, dod, ref, dtype):
     if dtype == "f32":
         compare("Dvec", to_np(dvec), ref["delta"], dtype)
         return
-    # exact dot of the stored bf16 O with dO, up to fp32 summation
+    # exact dot of the stored 16-bit O with dO, up to fp32 summation
     want = (to_np(o) * to_np(dod)).sum(-1).transpose(0, 2, 1)
     assert np.abs(to_np(dvec) - want).max() < 1e-4
-    # and within bf16 rounding of O (unit roundoff 2^-8) of the exact fp64 D
-    bound = 2.0 ** -8 * np.abs(ref["o"] * to_np(dod)).sum(-1).transpose(0, 2, 1) + 1e-4
+    # and within the rounding of O (unit roundoff 2^-8 bf16, 2^-11 fp16) of the exact fp64 D
+    u = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -11
+    bound = u * np.abs(ref["o"] * to_np(dod)).sum(-1).transpose(0, 2, 1) + 1e-4
     assert (np.abs(to_np(dvec) - ref["delta"]) <= bound).all()
 
 

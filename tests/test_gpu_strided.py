@@ -16,7 +16,7 @@ from workloads import make_inputs_like
 
 pytestmark = pytest.mark.gpu
 
-PAD = {"bf16": 8, "f32": 4}   # extra elements per padded row (16 bytes)
+PAD = {"bf16": 8, "f16": 8, "f32": 4}   # extra elements per padded row (16 bytes)
 
 
 def bhtd_view(x, pad=0):
@@ -52,7 +52,7 @@ def make_views(kind, q, k, v, do, dtype):
     raise ValueError(kind)
 
 
-CASES = [("bf16", 128), ("bf16", 64), ("f32", 64)]
+CASES = [("bf16", 128), ("bf16", 64), ("f16", 128), ("f32", 64)]
 KINDS = [("bhtd", 8, 2), ("padded", 8, 2), ("packed", 4, 4), ("mixed", 8, 2)]
 
 

@@ -1,11 +1,12 @@
 """Seeded input draws.  Q, K, V, dO are drawn in that order as float32 N(0,1) from a CPU
-torch.Generator, then rounded to the workload dtype (round-to-nearest-even for bf16).
+torch.Generator, then rounded to the workload dtype (round-to-nearest-even for bf16 and
+fp16).
 The same tensors go to the GPU path and, converted to float64, to the oracle."""
 import torch
 
 from .configs import Config
 
-_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
 def make_inputs_like(B, T, H, HKV, D, dtype="f32", seed=0):
