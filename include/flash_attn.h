@@ -29,8 +29,10 @@
  *  as in [forge] FlashParams and the per-row bounds of its kernels.
  *  L = m + ln(l) in natural-log units ([ipu] forward epilogue, [forge] forward epilogue);
  *  a row with no visible key gets O = 0 and L = 0 ([forge] forward epilogue guard).
- *  dtype selects the element type of Q, K, V, O and dO: FA_DTYPE_F32 (float) or
- *  FA_DTYPE_BF16 (bfloat16, fp32 accumulation).  L, Dvec, dQ, dK, dV are float32 in both.
+ *  dtype selects the element type of Q, K, V, O and dO: FA_DTYPE_F32 (float),
+ *  FA_DTYPE_BF16 (bfloat16) or FA_DTYPE_F16 (IEEE half, the 16-bit type of [ipu]'s op
+ *  definition), the 16-bit types with fp32 accumulation.  L, Dvec, dQ, dK, dV are float32
+ *  (flash_attn_bwd_grad16 aside).
  *
  *  Pointers are DEVICE pointers (HIP device memory of the current device), 16-byte aligned.
  *  The caller owns every buffer; the library keeps no pointer after a call returns.  Calls
@@ -49,7 +51,7 @@
  *  No C++ exception crosses this interface.
  *
  *  Supported head dims: FA_DTYPE_F32: D a multiple of 8 in [8, 128];
- *                       FA_DTYPE_BF16: D in {64, 128}.
+ *                       FA_DTYPE_BF16, FA_DTYPE_F16: D in {64, 128}.
  */
 #ifndef FLASH_ATTN_H
 #define FLASH_ATTN_H
@@ -93,7 +95,7 @@ fa_status_t flash_attn_bwd(const void* Q, const void* K, const void* V, const vo
 
 /* As flash_attn_fwd / flash_attn_bwd, with the block tiling forced: bq query rows by bk keys
  * per block (0, 0 = the library's choice).  FA_DTYPE_F32 accepts bq in {32, 64} and
- * bk in {16, 32, 64}; FA_DTYPE_BF16 accepts only (0, 0).  The tiling decides which blocks
+ * bk in {16, 32, 64}; the 16-bit types accept (0, 0) or their one tiling.  The tiling decides which blocks
  * are skipped, computed without a mask, or masked (causal diagonal, window edge, ragged T);
  * results agree with the automatic tiling up to rounding order. */
 fa_status_t flash_attn_fwd_ex(const void* Q, const void* K, const void* V, void* O, float* L,
@@ -131,6 +133,18 @@ fa_status_t flash_attn_bwd_strided(const void* Q, const void* K, const void* V, 
                                    float* dV, int B, int T, int H, int HKV, int D, float scale,
                                    int causal, int window, fa_dtype_t dtype, hipStream_t stream,
                                    fa_layout_t q_layout, fa_layout_t kv_layout);
+
+/* As flash_attn_bwd_strided, with dQ, dK and dV written in the input's 16-bit type (dtype
+ * FA_DTYPE_BF16 or FA_DTYPE_F16; FA_DTYPE_F32 is FA_ERR_INVALID_ARG) instead of float32:
+ * each value is the float32 result of flash_attn_bwd_strided rounded to nearest-even, at the
+ * same element strides.  Halves the gradient traffic; gradients of magnitude above ~4 lose
+ * more than the bf16 path's absolute bound on float32 outputs, so it suits consumers that
+ * keep 16-bit gradients anyway. */
+fa_status_t flash_attn_bwd_grad16(const void* Q, const void* K, const void* V, const void* O,
+                                  const float* L, const void* dO, void* dQ, void* dK, void* dV,
+                                  int B, int T, int H, int HKV, int D, float scale, int causal,
+                                  int window, fa_dtype_t dtype, hipStream_t stream,
+                                  fa_layout_t q_layout, fa_layout_t kv_layout);
 
 /* Backward stage 1 ([ipu] flashAttentionQKVPackedGrad, its D = rowsum(O * grad) step;
  * [forge] backward section comment; [teeny] backward_dq): Dvec[b,h,i] = sum_d dO[b,i,h,d] *

@@ -15,7 +15,7 @@ EXPORTS = [
     "flash_attn_fwd", "flash_attn_bwd", "flash_attn_fwd_ex", "flash_attn_bwd_ex",
     "flash_attn_bwd_preprocess", "flash_attn_bwd_dkdv", "flash_attn_bwd_dq",
     "flash_attn_bwd_dq_dvec", "flash_attn_fwd_strided", "flash_attn_bwd_strided",
-    "flash_attn_check_layout",
+    "flash_attn_check_layout", "flash_attn_bwd_grad16",
     "flash_attn_status_string", "flash_attn_block_class", "flash_attn_kv_block_range",
     "flash_attn_default_tiles", "flash_attn_version",
 ]
@@ -46,6 +46,7 @@ def _declare(lib):
         "flash_attn_fwd_strided": [P] * 5 + _DIMS + [Layout, Layout],
         "flash_attn_bwd_strided": [P] * 9 + _DIMS + [Layout, Layout],
         "flash_attn_check_layout": [Layout, I, I, I, I, I],
+        "flash_attn_bwd_grad16": [P] * 9 + _DIMS + [Layout, Layout],
         "flash_attn_block_class": [I, I, I, I, I, I, I, ctypes.POINTER(I)],
         "flash_attn_kv_block_range": [I, I, I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)],
         "flash_attn_default_tiles": [I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)],

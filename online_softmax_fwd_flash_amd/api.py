@@ -226,6 +226,33 @@ def flash_attn_bwd_strided(q, k, v, o, lse, do, causal=True, window=0, scale=Non
     return dq, dk, dv
 
 
+def flash_attn_bwd_grad16(q, k, v, o, lse, do, causal=True, window=0, scale=None, dq=None,
+                          dk=None, dv=None, stream=None):
+    """flash_attn_bwd_strided with dq, dk, dv in q's 16-bit dtype (each the float32 result
+    rounded to nearest-even); dq takes q's strides, dk and dv k's."""
+    B, T, H, HKV, D = _dims(q, k)
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("flash_attn_bwd_grad16 needs bfloat16 or float16 inputs")
+    _want_view(k, k, q.dtype, "k")
+    _want_view(v, k, q.dtype, "v")
+    _want_view(o, q, q.dtype, "o")
+    _want_view(do, q, q.dtype, "do")
+    _want(lse, (B, H, T), torch.float32, "lse")
+    dq = _empty_like_view(q, q.dtype) if dq is None else dq
+    dk = _empty_like_view(k, q.dtype) if dk is None else dk
+    dv = _empty_like_view(k, q.dtype) if dv is None else dv
+    _want_view(dq, q, q.dtype, "dq")
+    _want_view(dk, k, q.dtype, "dk")
+    _want_view(dv, k, q.dtype, "dv")
+    code = _lib.lib().flash_attn_bwd_grad16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                            _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), B, T, H,
+                                            HKV, D, _scale(scale, D), int(bool(causal)),
+                                            int(window), _DT[q.dtype], _stream(stream),
+                                            _layout(q, "q"), _layout(k, "k"))
+    _check("flash_attn_bwd_grad16", code)
+    return dq, dk, dv
+
+
 def flash_attn_block_class(T, bq, bk, causal, window, i, j):
     """(class, off) of block (i, j): class 0 skip, 1 full, 2 masked; off = i*bq - j*bk."""
     off = ctypes.c_int(0)

@@ -151,13 +151,13 @@ fa_status_t dkdv_impl(const void* Q, const void* K, const void* V, const void* d
                       const float* Dvec, float* dK, float* dV, int B, int T, int H, int HKV,
                       int D, float scale, int causal, int window, fa_dtype_t dtype,
                       hipStream_t stream, int bq, int bk, const fa_layout_t& lq,
-                      const fa_layout_t& lk) {
+                      const fa_layout_t& lk, int g16 = 0) {
     fa_status_t s = check_all({Q, K, V, dO, L, Dvec, dK, dV}, B, T, H, HKV, D, scale, causal,
                               window, dtype, lq, lk);
     if (s != FA_OK) return s;
     fa::AttnArgs a = make_args(B, T, H, HKV, D, scale, causal, window, stream, lq, lk, dtype);
     a.Q = Q; a.K = K; a.V = V; a.dO = dO; a.Lin = L; a.Dvec = const_cast<float*>(Dvec);
-    a.dK = dK; a.dV = dV;
+    a.dK = dK; a.dV = dV; a.g16 = g16;
     if (dtype == FA_DTYPE_F32) {
         if ((s = resolve_f32_tiles(bq, bk)) != FA_OK) return s;
         return hip_status(fa::launch_dkdv_f32(a, bq, bk));
@@ -190,7 +190,7 @@ fa_status_t dq_dvec_impl(const void* Q, const void* K, const void* V, const void
                          const void* dO, const float* L, float* Dvec, float* dQ, int B, int T,
                          int H, int HKV, int D, float scale, int causal, int window,
                          fa_dtype_t dtype, hipStream_t stream, int bq, int bk,
-                         const fa_layout_t& lq, const fa_layout_t& lk) {
+                         const fa_layout_t& lq, const fa_layout_t& lk, int g16 = 0) {
     fa_status_t s = check_all({Q, K, V, O, dO, L, Dvec, dQ}, B, T, H, HKV, D, scale, causal,
                               window, dtype, lq, lk);
     if (s != FA_OK) return s;
@@ -205,6 +205,7 @@ fa_status_t dq_dvec_impl(const void* Q, const void* K, const void* V, const void
         return FA_ERR_INVALID_ARG;
     fa::AttnArgs a = make_args(B, T, H, HKV, D, scale, causal, window, stream, lq, lk, dtype);
     a.Q = Q; a.K = K; a.V = V; a.O = O; a.dO = dO; a.Lin = L; a.Dvec = Dvec; a.dQ = dQ;
+    a.g16 = g16;
     return hip_status(fa::launch_dq_b16_fused_d(a));
 }
 
@@ -212,7 +213,7 @@ fa_status_t bwd_impl(const void* Q, const void* K, const void* V, const void* O,
                      const void* dO, float* dQ, float* dK, float* dV, int B, int T, int H,
                      int HKV, int D, float scale, int causal, int window, fa_dtype_t dtype,
                      hipStream_t stream, int bq, int bk, const fa_layout_t& lq,
-                     const fa_layout_t& lk) {
+                     const fa_layout_t& lk, int g16 = 0) {
     fa_status_t s = check_all({Q, K, V, O, L, dO, dQ, dK, dV}, B, T, H, HKV, D, scale, causal,
                               window, dtype, lq, lk);
     if (s != FA_OK) return s;
@@ -225,10 +226,10 @@ fa_status_t bwd_impl(const void* Q, const void* K, const void* V, const void* O,
     const size_t bytes = (size_t)B * H * T * sizeof(float);
     if (hipMallocAsync((void**)&Dvec, bytes, stream) != hipSuccess) return FA_ERR_HIP;
     s = dq_dvec_impl(Q, K, V, O, dO, L, Dvec, dQ, B, T, H, HKV, D, scale, causal, window, dtype,
-                     stream, bq, bk, lq, lk);
+                     stream, bq, bk, lq, lk, g16);
     if (s == FA_OK)
         s = dkdv_impl(Q, K, V, dO, L, Dvec, dK, dV, B, T, H, HKV, D, scale, causal, window,
-                      dtype, stream, bq, bk, lq, lk);
+                      dtype, stream, bq, bk, lq, lk, g16);
     const hipError_t fe = hipFreeAsync(Dvec, stream);
     if (s == FA_OK && fe != hipSuccess) s = FA_ERR_HIP;
     return s;
@@ -366,6 +367,17 @@ fa_status_t flash_attn_bwd_strided(const void* Q, const void* K, const void* V, 
                                    fa_layout_t q_layout, fa_layout_t kv_layout) {
     return bwd_impl(Q, K, V, O, L, dO, dQ, dK, dV, B, T, H, HKV, D, scale, causal, window, dtype,
                     stream, 0, 0, q_layout, kv_layout);
+}
+
+fa_status_t flash_attn_bwd_grad16(const void* Q, const void* K, const void* V, const void* O,
+                                  const float* L, const void* dO, void* dQ, void* dK, void* dV,
+                                  int B, int T, int H, int HKV, int D, float scale, int causal,
+                                  int window, fa_dtype_t dtype, hipStream_t stream,
+                                  fa_layout_t q_layout, fa_layout_t kv_layout) {
+    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return FA_ERR_INVALID_ARG;
+    return bwd_impl(Q, K, V, O, L, dO, static_cast<float*>(dQ), static_cast<float*>(dK),
+                    static_cast<float*>(dV), B, T, H, HKV, D, scale, causal, window, dtype,
+                    stream, 0, 0, q_layout, kv_layout, 1);
 }
 
 }  // extern "C"

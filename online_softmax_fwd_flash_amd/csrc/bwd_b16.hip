@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv_b16_kernel(
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ L, const float* __restrict__ Dv, float* __restrict__ dK,
     float* __restrict__ dV, int B, int T, int H, int HKV, float scale, int causal, int window,
-    Layout lq, Layout lk) {
+    Layout lq, Layout lk, int g16) {
     using C = Dkdv16Cfg<D>;
     using V8 = typename E::v8;
     using S16 = typename E::s;
@@ -268,17 +268,28 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv_b16_kernel(
             }
     }
 
-    // entry r of lane (n, g) in block db: key kw0 + 4g + r, column db*16 + n
-    float* dKg = dK + b * lk.b + hk * lk.h;
-    float* dVg = dV + b * lk.b + hk * lk.h;
+    // entry r of lane (n, g) in block db: key kw0 + 4g + r, column db*16 + n.  Stored as
+    // float32, or (g16) rounded to the element type.
+    const int64_t kbase = b * lk.b + hk * lk.h;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int kk = kw0 + 4 * g + r;
         if (kk < T) {
+            const int64_t row = kbase + (int64_t)kk * ldk + n;
+            if (g16) {
+                typename E::s* dKh = reinterpret_cast<typename E::s*>(dK) + row;
+                typename E::s* dVh = reinterpret_cast<typename E::s*>(dV) + row;
 #pragma unroll
-            for (int db = 0; db < C::NDB; ++db) {
-                dKg[(int64_t)kk * ldk + db * 16 + n] = dka[db][r] * scale;
-                dVg[(int64_t)kk * ldk + db * 16 + n] = dva[db][r];
+                for (int db = 0; db < C::NDB; ++db) {
+                    dKh[db * 16] = (typename E::s)opaque(dka[db][r] * scale);
+                    dVh[db * 16] = (typename E::s)opaque(dva[db][r]);
+                }
+            } else {
+#pragma unroll
+                for (int db = 0; db < C::NDB; ++db) {
+                    dK[row + db * 16] = dka[db][r] * scale;
+                    dV[row + db * 16] = dva[db][r];
+                }
             }
         }
     }
@@ -332,7 +343,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_b16_kernel(
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const uint16_t* __restrict__ O, const float* __restrict__ L, float* __restrict__ Dv,
     float* __restrict__ dQ, int B, int T, int H, int HKV, float scale, int causal, int window,
-    int nqt, int xcd_group, Layout lq, Layout lk) {
+    int nqt, int xcd_group, Layout lq, Layout lk, int g16) {
     using C = DqCfg<D, NW>;
     using V8 = typename E::v8;
     extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
@@ -462,8 +473,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_b16_kernel(
     }
 
     if (q >= T) return;
-    float* dQq = dQ + qrow;
-    // entry r of block db: dQ^T[db*32 + 8*(r/4) + 4g + r%4][query n]
+    // entry r of block db: dQ^T[db*32 + 8*(r/4) + 4g + r%4][query n]; float32, or (g16)
+    // rounded to the element type
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
@@ -471,7 +482,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_b16_kernel(
             f32x4 o;
 #pragma unroll
             for (int u = 0; u < 4; ++u) o[u] = dqa[db][4 * t4 + u] * scale;
-            *reinterpret_cast<f32x4*>(dQq + db * 32 + 8 * t4 + 4 * g) = o;
+            const int64_t at = qrow + db * 32 + 8 * t4 + 4 * g;
+            if (g16) {
+                u32x2 h;
+                h[0] = pack2<E>(opaque(o[0]), opaque(o[1]));
+                h[1] = pack2<E>(opaque(o[2]), opaque(o[3]));
+                *reinterpret_cast<u32x2*>(reinterpret_cast<typename E::s*>(dQ) + at) = h;
+            } else {
+                *reinterpret_cast<f32x4*>(dQ + at) = o;
+            }
         }
 }
 
@@ -505,7 +524,7 @@ hipError_t launch_dkdv_b16_t(const AttnArgs& a) {
     hipLaunchKernelGGL((dkdv_b16_kernel<E, D>), dim3(grid), dim3(C::NT), lds, a.stream,
                        (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
                        (const uint16_t*)a.dO, a.Lin, a.Dvec, a.dK, a.dV, a.B, a.T, a.H, a.HKV,
-                       a.scale, a.causal, a.window, a.lq, a.lk);
+                       a.scale, a.causal, a.window, a.lq, a.lk, a.g16);
     return hipGetLastError();
 }
 
@@ -528,7 +547,7 @@ hipError_t launch_dq_b16_t(const AttnArgs& a) {
                        a.stream, (const uint16_t*)a.Q, (const uint16_t*)a.K,
                        (const uint16_t*)a.V, (const uint16_t*)a.dO, (const uint16_t*)a.O, a.Lin,
                        a.Dvec, a.dQ, a.B, a.T, a.H, a.HKV, a.scale, a.causal, a.window, nqt,
-                       xcd_group_for(nqt, a.B, a.H, a.HKV), a.lq, a.lk);
+                       xcd_group_for(nqt, a.B, a.H, a.HKV), a.lq, a.lk, a.g16);
     return hipGetLastError();
 }
 

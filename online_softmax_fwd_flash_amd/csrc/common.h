@@ -118,6 +118,14 @@ struct F16 {
     typedef f16x2 v2;
 };
 
+// x unchanged, but opaque to the compiler: a float result rounded to 16 bits after this is
+// rounded from its float32 value (the compiler may otherwise fold the product feeding a
+// conversion into a mixed-precision multiply that rounds only once, to 16 bits).
+__device__ __forceinline__ float opaque(float x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 // Round-to-nearest-even float -> element pair, packed low element first.
 template <class E>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {

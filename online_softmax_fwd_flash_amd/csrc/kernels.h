@@ -31,6 +31,7 @@ struct AttnArgs {
     hipStream_t stream;
     Layout lq, lk;   // query-side and key-side layouts
     int f16;         // 16-bit kernels: 1 = IEEE half elements, 0 = bfloat16
+    int g16;         // 16-bit kernels: 1 = dQ, dK, dV stored in the element type, 0 = float32
 };
 
 // Tilings of the bf16 kernels: query rows x keys handled per workgroup block.  Each kernel

@@ -105,6 +105,17 @@ def test_bad_tiles_rejected():
     assert dq_dvec(dtype=0, bq=48, bk=16) == 1
 
 
+def test_grad16_rejects_before_launch():
+    L = _lib.lib()
+    q = _lib.Layout(64 * 4 * 128, 4 * 128, 128)
+    k = _lib.Layout(64 * 2 * 128, 2 * 128, 128)
+    dims = [1, 64, 4, 2, 128, 0.125, 1, 0, 1, S0]
+    dims32 = list(dims); dims32[8] = 0
+    assert L.flash_attn_bwd_grad16(*([A] * 9), *dims32, q, k) == 1          # f32 inputs
+    assert L.flash_attn_bwd_grad16(*([A] * 8), NUL, *dims, q, k) == 1
+    assert L.flash_attn_bwd_grad16(*([A] * 9), *dims, q, _lib.Layout(0, 64, 128)) == 1
+
+
 def test_f16_dtype():
     # fp16 takes the 16-bit kernels: the same head dims and tilings as bf16
     assert fwd(dtype=2, D=96) == 2
