@@ -118,21 +118,30 @@ typedef struct fa_layout {
     int64_t batch, row, head;
 } fa_layout_t;
 
-/* As flash_attn_fwd / flash_attn_bwd on strided views.  Q, O, dO and dQ follow q_layout
- * (H heads), K, V, dK and dV follow kv_layout (HKV heads), in elements of each tensor's own
- * type (so the float32 gradients take the same element strides as their bf16 inputs); L and
- * Dvec stay [B, H, T] float32.  Default tiling.  A layout is rejected (FA_ERR_INVALID_ARG)
- * unless its strides are non-negative multiples of 16 bytes, row >= D, distinct
- * (b, t, head) never overlap, and, for bf16, one head's T rows span under 2 GiB. */
+/* As flash_attn_fwd / flash_attn_bwd on strided views, and with T query rows and Tk keys
+ * (Tk = T for the other entry points).  Q, O, dO and dQ follow q_layout (H heads, T rows),
+ * K, V, dK and dV follow kv_layout (HKV heads, Tk rows), in elements of each tensor's own
+ * type (so the float32 gradients take the same element strides as their 16-bit inputs); L
+ * and Dvec stay [B, H, T] float32.  Default tiling.  A layout is rejected
+ * (FA_ERR_INVALID_ARG) unless its strides are non-negative multiples of 16 bytes, row >= D,
+ * distinct (b, t, head) never overlap, and, for the 16-bit types, one head's rows span under
+ * 2 GiB.
+ * Query and key lengths ([teeny] flash_attention2_forward, its n_ctx_q and n_ctx_k; no page
+ * states a causal rule for them): query row i sits at key position i + Tk - T, the last T
+ * positions, as when the keys start with a cached prefix.  causal keeps keys j <= i + Tk - T, window keeps
+ * j >= i + Tk - T - window + 1; a row with no visible key gets O = 0 and L = 0 (when T > Tk
+ * under causal, the first T - Tk rows). */
 fa_status_t flash_attn_fwd_strided(const void* Q, const void* K, const void* V, void* O,
-                                   float* L, int B, int T, int H, int HKV, int D, float scale,
-                                   int causal, int window, fa_dtype_t dtype, hipStream_t stream,
-                                   fa_layout_t q_layout, fa_layout_t kv_layout);
+                                   float* L, int B, int T, int Tk, int H, int HKV, int D,
+                                   float scale, int causal, int window, fa_dtype_t dtype,
+                                   hipStream_t stream, fa_layout_t q_layout,
+                                   fa_layout_t kv_layout);
 fa_status_t flash_attn_bwd_strided(const void* Q, const void* K, const void* V, const void* O,
                                    const float* L, const void* dO, float* dQ, float* dK,
-                                   float* dV, int B, int T, int H, int HKV, int D, float scale,
-                                   int causal, int window, fa_dtype_t dtype, hipStream_t stream,
-                                   fa_layout_t q_layout, fa_layout_t kv_layout);
+                                   float* dV, int B, int T, int Tk, int H, int HKV, int D,
+                                   float scale, int causal, int window, fa_dtype_t dtype,
+                                   hipStream_t stream, fa_layout_t q_layout,
+                                   fa_layout_t kv_layout);
 
 /* As flash_attn_bwd_strided, with dQ, dK and dV written in the input's 16-bit type (dtype
  * FA_DTYPE_BF16 or FA_DTYPE_F16; FA_DTYPE_F32 is FA_ERR_INVALID_ARG) instead of float32:
@@ -142,8 +151,8 @@ fa_status_t flash_attn_bwd_strided(const void* Q, const void* K, const void* V, 
  * keep 16-bit gradients anyway. */
 fa_status_t flash_attn_bwd_grad16(const void* Q, const void* K, const void* V, const void* O,
                                   const float* L, const void* dO, void* dQ, void* dK, void* dV,
-                                  int B, int T, int H, int HKV, int D, float scale, int causal,
-                                  int window, fa_dtype_t dtype, hipStream_t stream,
+                                  int B, int T, int Tk, int H, int HKV, int D, float scale,
+                                  int causal, int window, fa_dtype_t dtype, hipStream_t stream,
                                   fa_layout_t q_layout, fa_layout_t kv_layout);
 
 /* Backward stage 1 ([ipu] flashAttentionQKVPackedGrad, its D = rowsum(O * grad) step;
@@ -200,6 +209,12 @@ int flash_attn_block_class(int T, int bq, int bk, int causal, int window, int i,
 /* Key-block range [*j_lo, *j_hi) a query tile i loops over (same rule as the kernels). */
 fa_status_t flash_attn_kv_block_range(int T, int bq, int bk, int causal, int window, int i,
                                       int* j_lo, int* j_hi);
+
+/* The same two for T query rows against Tk keys (the rule of flash_attn_fwd_strided). */
+int flash_attn_block_class_qk(int Tq, int Tk, int bq, int bk, int causal, int window, int i,
+                              int j);
+fa_status_t flash_attn_kv_block_range_qk(int Tq, int Tk, int bq, int bk, int causal, int window,
+                                         int i, int* j_lo, int* j_hi);
 
 /* Tiling the library picks for a dtype / head dim: pass 0 = forward, 1 = dK/dV, 2 = dQ.
  * *bq, *bk are the query and key block sizes of that pass. */

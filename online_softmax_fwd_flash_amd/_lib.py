@@ -15,7 +15,8 @@ EXPORTS = [
     "flash_attn_fwd", "flash_attn_bwd", "flash_attn_fwd_ex", "flash_attn_bwd_ex",
     "flash_attn_bwd_preprocess", "flash_attn_bwd_dkdv", "flash_attn_bwd_dq",
     "flash_attn_bwd_dq_dvec", "flash_attn_fwd_strided", "flash_attn_bwd_strided",
-    "flash_attn_check_layout", "flash_attn_bwd_grad16",
+    "flash_attn_check_layout", "flash_attn_bwd_grad16", "flash_attn_block_class_qk",
+    "flash_attn_kv_block_range_qk",
     "flash_attn_status_string", "flash_attn_block_class", "flash_attn_kv_block_range",
     "flash_attn_default_tiles", "flash_attn_version",
 ]
@@ -26,6 +27,7 @@ P = ctypes.c_void_p
 I = ctypes.c_int
 F = ctypes.c_float
 _DIMS = [I, I, I, I, I, F, I, I, I, P]          # B T H HKV D scale causal window dtype stream
+_DIMS_QK = [I, I, I, I, I, I, F, I, I, I, P]    # B T Tk H HKV D scale causal window dtype stream
 
 
 class Layout(ctypes.Structure):
@@ -43,10 +45,12 @@ def _declare(lib):
         "flash_attn_bwd_dkdv": [P] * 8 + _DIMS + [I, I],
         "flash_attn_bwd_dq": [P] * 7 + _DIMS + [I, I],
         "flash_attn_bwd_dq_dvec": [P] * 8 + _DIMS + [I, I],
-        "flash_attn_fwd_strided": [P] * 5 + _DIMS + [Layout, Layout],
-        "flash_attn_bwd_strided": [P] * 9 + _DIMS + [Layout, Layout],
+        "flash_attn_fwd_strided": [P] * 5 + _DIMS_QK + [Layout, Layout],
+        "flash_attn_bwd_strided": [P] * 9 + _DIMS_QK + [Layout, Layout],
+        "flash_attn_block_class_qk": [I] * 8,
+        "flash_attn_kv_block_range_qk": [I] * 7 + [ctypes.POINTER(I), ctypes.POINTER(I)],
         "flash_attn_check_layout": [Layout, I, I, I, I, I],
-        "flash_attn_bwd_grad16": [P] * 9 + _DIMS + [Layout, Layout],
+        "flash_attn_bwd_grad16": [P] * 9 + _DIMS_QK + [Layout, Layout],
         "flash_attn_block_class": [I, I, I, I, I, I, I, ctypes.POINTER(I)],
         "flash_attn_kv_block_range": [I, I, I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)],
         "flash_attn_default_tiles": [I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)],

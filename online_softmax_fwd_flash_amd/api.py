@@ -37,11 +37,22 @@ def _ptr(t):
 
 
 def _dims(q, k):
-    if q.dim() != 4 or k.dim() != 4:
-        raise ValueError("expected q [B,T,H,D] and k/v [B,T,HKV,D]")
-    B, T, H, D = q.shape
-    HKV = k.shape[2]
+    """(B, T, H, HKV, D) of q [B,T,H,D] and k [B,T,HKV,D] (one length for queries and keys)."""
+    B, T, Tk, H, HKV, D = _dims_qk(q, k)
+    if Tk != T:
+        raise ValueError("q and k differ in length; use the *_strided entry points")
     return B, T, H, HKV, D
+
+
+def _dims_qk(q, k):
+    """(B, T, Tk, H, HKV, D) of q [B,T,H,D] and k [B,Tk,HKV,D]."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("expected q [B,T,H,D] and k/v [B,Tk,HKV,D]")
+    B, T, H, D = q.shape
+    Bk, Tk, HKV, Dk = k.shape
+    if (Bk, Dk) != (B, D):
+        raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} differ in batch or head dim")
+    return B, T, Tk, H, HKV, D
 
 
 def _want(t, shape, dtype, name):
@@ -185,7 +196,7 @@ def flash_attn_fwd_strided(q, k, v, causal=True, window=0, scale=None, out=None,
     """flash_attn_fwd on [B, T, heads, D] views with any strides (last axis contiguous), e.g.
     x.transpose(1, 2) of a [B, H, T, D] tensor or of a third of a packed QKV buffer.  k and v
     share strides; O takes q's strides."""
-    B, T, H, HKV, D = _dims(q, k)
+    B, T, Tk, H, HKV, D = _dims_qk(q, k)
     _want_view(k, k, q.dtype, "k")
     _want_view(v, k, q.dtype, "v")
     out = _empty_like_view(q, q.dtype) if out is None else out
@@ -193,7 +204,7 @@ def flash_attn_fwd_strided(q, k, v, causal=True, window=0, scale=None, out=None,
     lse = torch.empty(B, H, T, device=q.device, dtype=torch.float32) if lse is None else lse
     _want(lse, (B, H, T), torch.float32, "lse")
     code = _lib.lib().flash_attn_fwd_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
-                                             B, T, H, HKV, D, _scale(scale, D),
+                                             B, T, Tk, H, HKV, D, _scale(scale, D),
                                              int(bool(causal)), int(window), _DT[q.dtype],
                                              _stream(stream), _layout(q, "q"), _layout(k, "k"))
     _check("flash_attn_fwd_strided", code)
@@ -204,7 +215,7 @@ def flash_attn_bwd_strided(q, k, v, o, lse, do, causal=True, window=0, scale=Non
                            dk=None, dv=None, stream=None):
     """flash_attn_bwd on strided views: o, do and dq (float32) take q's strides, dk and dv
     (float32) take k's."""
-    B, T, H, HKV, D = _dims(q, k)
+    B, T, Tk, H, HKV, D = _dims_qk(q, k)
     _want_view(k, k, q.dtype, "k")
     _want_view(v, k, q.dtype, "v")
     _want_view(o, q, q.dtype, "o")
@@ -218,8 +229,8 @@ def flash_attn_bwd_strided(q, k, v, o, lse, do, causal=True, window=0, scale=Non
     _want_view(dk, k, f32, "dk")
     _want_view(dv, k, f32, "dv")
     code = _lib.lib().flash_attn_bwd_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                                             _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), B, T, H,
-                                             HKV, D, _scale(scale, D), int(bool(causal)),
+                                             _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), B, T, Tk,
+                                             H, HKV, D, _scale(scale, D), int(bool(causal)),
                                              int(window), _DT[q.dtype], _stream(stream),
                                              _layout(q, "q"), _layout(k, "k"))
     _check("flash_attn_bwd_strided", code)
@@ -230,7 +241,7 @@ def flash_attn_bwd_grad16(q, k, v, o, lse, do, causal=True, window=0, scale=None
                           dk=None, dv=None, stream=None):
     """flash_attn_bwd_strided with dq, dk, dv in q's 16-bit dtype (each the float32 result
     rounded to nearest-even); dq takes q's strides, dk and dv k's."""
-    B, T, H, HKV, D = _dims(q, k)
+    B, T, Tk, H, HKV, D = _dims_qk(q, k)
     if q.dtype not in (torch.bfloat16, torch.float16):
         raise ValueError("flash_attn_bwd_grad16 needs bfloat16 or float16 inputs")
     _want_view(k, k, q.dtype, "k")
@@ -245,8 +256,8 @@ def flash_attn_bwd_grad16(q, k, v, o, lse, do, causal=True, window=0, scale=None
     _want_view(dk, k, q.dtype, "dk")
     _want_view(dv, k, q.dtype, "dv")
     code = _lib.lib().flash_attn_bwd_grad16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                                            _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), B, T, H,
-                                            HKV, D, _scale(scale, D), int(bool(causal)),
+                                            _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), B, T, Tk,
+                                            H, HKV, D, _scale(scale, D), int(bool(causal)),
                                             int(window), _DT[q.dtype], _stream(stream),
                                             _layout(q, "q"), _layout(k, "k"))
     _check("flash_attn_bwd_grad16", code)
@@ -261,6 +272,19 @@ def flash_attn_block_class(T, bq, bk, causal, window, i, j):
     if cls < 0:
         raise FlashAttnError("flash_attn_block_class", _lib.FA_ERR_INVALID_ARG)
     return cls, off.value
+
+
+def flash_attn_block_class_qk(Tq, Tk, bq, bk, causal, window, i, j):
+    """Class of block (i, j) of a Tq x Tk problem (query rows at the last Tq key positions)."""
+    return _lib.lib().flash_attn_block_class_qk(Tq, Tk, bq, bk, int(bool(causal)), window, i, j)
+
+
+def flash_attn_kv_block_range_qk(Tq, Tk, bq, bk, causal, window, i):
+    lo, hi = ctypes.c_int(), ctypes.c_int()
+    code = _lib.lib().flash_attn_kv_block_range_qk(Tq, Tk, bq, bk, int(bool(causal)), window, i,
+                                                   ctypes.byref(lo), ctypes.byref(hi))
+    _check("flash_attn_kv_block_range_qk", code)
+    return lo.value, hi.value
 
 
 def flash_attn_kv_block_range(T, bq, bk, causal, window, i):

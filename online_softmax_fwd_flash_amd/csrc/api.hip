@@ -14,17 +14,18 @@ constexpr int kF32DefaultBq = 64, kF32DefaultBk = 64;
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 fa_status_t check_dims(int B, int T, int H, int HKV, int D, float scale, int causal, int window,
-                       fa_dtype_t dtype) {
-    if (B < 1 || T < 1 || H < 1 || HKV < 1 || D < 1) return FA_ERR_INVALID_ARG;
+                       fa_dtype_t dtype, int Tk = -1) {
+    if (Tk < 0) Tk = T;
+    if (B < 1 || T < 1 || Tk < 1 || H < 1 || HKV < 1 || D < 1) return FA_ERR_INVALID_ARG;
     if (H % HKV != 0) return FA_ERR_INVALID_ARG;
     if (window < 0 || (causal != 0 && causal != 1)) return FA_ERR_INVALID_ARG;
     if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
     if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16)
         return FA_ERR_INVALID_ARG;
     // every element offset and every grid stays far inside its integer type
-    const double elems = (double)B * T * H * D;
+    const double elems = (double)B * (T > Tk ? T : Tk) * H * D;
     if (elems > (double)(1ll << 40)) return FA_ERR_INVALID_ARG;
-    if ((double)B * H * ((T + 15) / 16) > 2147483647.0) return FA_ERR_INVALID_ARG;
+    if ((double)B * H * (((T > Tk ? T : Tk) + 15) / 16) > 2147483647.0) return FA_ERR_INVALID_ARG;
     if (dtype == FA_DTYPE_F32) {
         if (D % 8 != 0 || D > 128) return FA_ERR_UNSUPPORTED;
     } else {
@@ -97,35 +98,36 @@ fa_status_t resolve_f32_tiles(int& bq, int& bk) {
 
 fa_status_t hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
-fa::AttnArgs make_args(int B, int T, int H, int HKV, int D, float scale, int causal, int window,
+fa::AttnArgs make_args(int B, int T, int Tk, int H, int HKV, int D, float scale, int causal, int window,
                        hipStream_t stream, const fa_layout_t& lq, const fa_layout_t& lk,
                        fa_dtype_t dtype) {
     fa::AttnArgs a{};
     a.f16 = dtype == FA_DTYPE_F16 ? 1 : 0;
-    a.B = B; a.T = T; a.H = H; a.HKV = HKV; a.D = D;
+    a.B = B; a.T = T; a.Tk = Tk; a.H = H; a.HKV = HKV; a.D = D;
     a.scale = scale; a.causal = causal; a.window = window; a.stream = stream;
     a.lq = to_layout(lq); a.lk = to_layout(lk);
     return a;
 }
 
 // Shared validation of the attention entry points: pointers, sizes and both layouts.
-fa_status_t check_all(std::initializer_list<const void*> ps, int B, int T, int H, int HKV, int D,
+fa_status_t check_all(std::initializer_list<const void*> ps, int B, int T, int Tk, int H, int HKV,
+                      int D,
                       float scale, int causal, int window, fa_dtype_t dtype,
                       const fa_layout_t& lq, const fa_layout_t& lk) {
     fa_status_t s = check_ptrs(ps);
     if (s != FA_OK) return s;
-    if ((s = check_dims(B, T, H, HKV, D, scale, causal, window, dtype)) != FA_OK) return s;
+    if ((s = check_dims(B, T, H, HKV, D, scale, causal, window, dtype, Tk)) != FA_OK) return s;
     if ((s = check_layout(lq, B, T, H, D, dtype)) != FA_OK) return s;
-    return check_layout(lk, B, T, HKV, D, dtype);
+    return check_layout(lk, B, Tk, HKV, D, dtype);
 }
 
-fa_status_t fwd_impl(const void* Q, const void* K, const void* V, void* O, float* L, int B, int T,
+fa_status_t fwd_impl(const void* Q, const void* K, const void* V, void* O, float* L, int B, int T, int Tk,
                      int H, int HKV, int D, float scale, int causal, int window,
                      fa_dtype_t dtype, hipStream_t stream, int bq, int bk,
                      const fa_layout_t& lq, const fa_layout_t& lk) {
-    fa_status_t s = check_all({Q, K, V, O, L}, B, T, H, HKV, D, scale, causal, window, dtype, lq, lk);
+    fa_status_t s = check_all({Q, K, V, O, L}, B, T, Tk, H, HKV, D, scale, causal, window, dtype, lq, lk);
     if (s != FA_OK) return s;
-    fa::AttnArgs a = make_args(B, T, H, HKV, D, scale, causal, window, stream, lq, lk, dtype);
+    fa::AttnArgs a = make_args(B, T, Tk, H, HKV, D, scale, causal, window, stream, lq, lk, dtype);
     a.Q = Q; a.K = K; a.V = V; a.Oout = O; a.O = O; a.L = L;
     if (dtype == FA_DTYPE_F32) {
         if ((s = resolve_f32_tiles(bq, bk)) != FA_OK) return s;
@@ -148,14 +150,14 @@ fa_status_t preprocess_impl(const void* O, const void* dO, float* Dvec, int B, i
 }
 
 fa_status_t dkdv_impl(const void* Q, const void* K, const void* V, const void* dO, const float* L,
-                      const float* Dvec, float* dK, float* dV, int B, int T, int H, int HKV,
+                      const float* Dvec, float* dK, float* dV, int B, int T, int Tk, int H, int HKV,
                       int D, float scale, int causal, int window, fa_dtype_t dtype,
                       hipStream_t stream, int bq, int bk, const fa_layout_t& lq,
                       const fa_layout_t& lk, int g16 = 0) {
-    fa_status_t s = check_all({Q, K, V, dO, L, Dvec, dK, dV}, B, T, H, HKV, D, scale, causal,
+    fa_status_t s = check_all({Q, K, V, dO, L, Dvec, dK, dV}, B, T, Tk, H, HKV, D, scale, causal,
                               window, dtype, lq, lk);
     if (s != FA_OK) return s;
-    fa::AttnArgs a = make_args(B, T, H, HKV, D, scale, causal, window, stream, lq, lk, dtype);
+    fa::AttnArgs a = make_args(B, T, Tk, H, HKV, D, scale, causal, window, stream, lq, lk, dtype);
     a.Q = Q; a.K = K; a.V = V; a.dO = dO; a.Lin = L; a.Dvec = const_cast<float*>(Dvec);
     a.dK = dK; a.dV = dV; a.g16 = g16;
     if (dtype == FA_DTYPE_F32) {
@@ -168,13 +170,13 @@ fa_status_t dkdv_impl(const void* Q, const void* K, const void* V, const void* d
 }
 
 fa_status_t dq_impl(const void* Q, const void* K, const void* V, const void* dO, const float* L,
-                    const float* Dvec, float* dQ, int B, int T, int H, int HKV, int D,
+                    const float* Dvec, float* dQ, int B, int T, int Tk, int H, int HKV, int D,
                     float scale, int causal, int window, fa_dtype_t dtype, hipStream_t stream,
                     int bq, int bk, const fa_layout_t& lq, const fa_layout_t& lk) {
-    fa_status_t s = check_all({Q, K, V, dO, L, Dvec, dQ}, B, T, H, HKV, D, scale, causal, window,
+    fa_status_t s = check_all({Q, K, V, dO, L, Dvec, dQ}, B, T, Tk, H, HKV, D, scale, causal, window,
                               dtype, lq, lk);
     if (s != FA_OK) return s;
-    fa::AttnArgs a = make_args(B, T, H, HKV, D, scale, causal, window, stream, lq, lk, dtype);
+    fa::AttnArgs a = make_args(B, T, Tk, H, HKV, D, scale, causal, window, stream, lq, lk, dtype);
     a.Q = Q; a.K = K; a.V = V; a.dO = dO; a.Lin = L; a.Dvec = const_cast<float*>(Dvec);
     a.dQ = dQ;
     if (dtype == FA_DTYPE_F32) {
@@ -187,34 +189,34 @@ fa_status_t dq_impl(const void* Q, const void* K, const void* V, const void* dO,
 }
 
 fa_status_t dq_dvec_impl(const void* Q, const void* K, const void* V, const void* O,
-                         const void* dO, const float* L, float* Dvec, float* dQ, int B, int T,
+                         const void* dO, const float* L, float* Dvec, float* dQ, int B, int T, int Tk,
                          int H, int HKV, int D, float scale, int causal, int window,
                          fa_dtype_t dtype, hipStream_t stream, int bq, int bk,
                          const fa_layout_t& lq, const fa_layout_t& lk, int g16 = 0) {
-    fa_status_t s = check_all({Q, K, V, O, dO, L, Dvec, dQ}, B, T, H, HKV, D, scale, causal,
+    fa_status_t s = check_all({Q, K, V, O, dO, L, Dvec, dQ}, B, T, Tk, H, HKV, D, scale, causal,
                               window, dtype, lq, lk);
     if (s != FA_OK) return s;
     if (dtype == FA_DTYPE_F32) {
         if ((s = resolve_f32_tiles(bq, bk)) != FA_OK) return s;
         s = preprocess_impl(O, dO, Dvec, B, T, H, D, dtype, stream, lq);
         if (s != FA_OK) return s;
-        return dq_impl(Q, K, V, dO, L, Dvec, dQ, B, T, H, HKV, D, scale, causal, window, dtype,
+        return dq_impl(Q, K, V, dO, L, Dvec, dQ, B, T, Tk, H, HKV, D, scale, causal, window, dtype,
                        stream, bq, bk, lq, lk);
     }
     if (!((bq == 0 && bk == 0) || (bq == fa::kB16DqBq && bk == fa::kB16DqBk)))
         return FA_ERR_INVALID_ARG;
-    fa::AttnArgs a = make_args(B, T, H, HKV, D, scale, causal, window, stream, lq, lk, dtype);
+    fa::AttnArgs a = make_args(B, T, Tk, H, HKV, D, scale, causal, window, stream, lq, lk, dtype);
     a.Q = Q; a.K = K; a.V = V; a.O = O; a.dO = dO; a.Lin = L; a.Dvec = Dvec; a.dQ = dQ;
     a.g16 = g16;
     return hip_status(fa::launch_dq_b16_fused_d(a));
 }
 
 fa_status_t bwd_impl(const void* Q, const void* K, const void* V, const void* O, const float* L,
-                     const void* dO, float* dQ, float* dK, float* dV, int B, int T, int H,
+                     const void* dO, float* dQ, float* dK, float* dV, int B, int T, int Tk, int H,
                      int HKV, int D, float scale, int causal, int window, fa_dtype_t dtype,
                      hipStream_t stream, int bq, int bk, const fa_layout_t& lq,
                      const fa_layout_t& lk, int g16 = 0) {
-    fa_status_t s = check_all({Q, K, V, O, L, dO, dQ, dK, dV}, B, T, H, HKV, D, scale, causal,
+    fa_status_t s = check_all({Q, K, V, O, L, dO, dQ, dK, dV}, B, T, Tk, H, HKV, D, scale, causal,
                               window, dtype, lq, lk);
     if (s != FA_OK) return s;
     if (dtype == FA_DTYPE_F32) {
@@ -225,10 +227,10 @@ fa_status_t bwd_impl(const void* Q, const void* K, const void* V, const void* O,
     float* Dvec = nullptr;
     const size_t bytes = (size_t)B * H * T * sizeof(float);
     if (hipMallocAsync((void**)&Dvec, bytes, stream) != hipSuccess) return FA_ERR_HIP;
-    s = dq_dvec_impl(Q, K, V, O, dO, L, Dvec, dQ, B, T, H, HKV, D, scale, causal, window, dtype,
+    s = dq_dvec_impl(Q, K, V, O, dO, L, Dvec, dQ, B, T, Tk, H, HKV, D, scale, causal, window, dtype,
                      stream, bq, bk, lq, lk, g16);
     if (s == FA_OK)
-        s = dkdv_impl(Q, K, V, dO, L, Dvec, dK, dV, B, T, H, HKV, D, scale, causal, window,
+        s = dkdv_impl(Q, K, V, dO, L, Dvec, dK, dV, B, T, Tk, H, HKV, D, scale, causal, window,
                       dtype, stream, bq, bk, lq, lk, g16);
     const hipError_t fe = hipFreeAsync(Dvec, stream);
     if (s == FA_OK && fe != hipSuccess) s = FA_ERR_HIP;
@@ -263,7 +265,23 @@ int flash_attn_block_class(int T, int bq, int bk, int causal, int window, int i,
     if (T < 1 || bq < 1 || bk < 1 || window < 0 || i < 0 || j < 0) return -1;
     if ((long long)(i + 1) * bq > (1ll << 30) || (long long)(j + 1) * bk > (1ll << 30)) return -1;
     if (off) *off = i * bq - j * bk;
-    return fa::block_class(T, i * bq, i * bq + bq, j * bk, j * bk + bk, causal != 0, window);
+    return fa::block_class(T, T, i * bq, i * bq + bq, j * bk, j * bk + bk, causal != 0, window);
+}
+
+int flash_attn_block_class_qk(int Tq, int Tk, int bq, int bk, int causal, int window, int i,
+                              int j) {
+    if (Tq < 1 || Tk < 1 || bq < 1 || bk < 1 || window < 0 || i < 0 || j < 0) return -1;
+    if ((long long)(i + 1) * bq > (1ll << 30) || (long long)(j + 1) * bk > (1ll << 30)) return -1;
+    return fa::block_class(Tq, Tk, i * bq, i * bq + bq, j * bk, j * bk + bk, causal != 0, window);
+}
+
+fa_status_t flash_attn_kv_block_range_qk(int Tq, int Tk, int bq, int bk, int causal, int window,
+                                         int i, int* j_lo, int* j_hi) {
+    if (Tq < 1 || Tk < 1 || bq < 1 || bk < 1 || window < 0 || i < 0 || !j_lo || !j_hi)
+        return FA_ERR_INVALID_ARG;
+    if ((long long)(i + 1) * bq > (1ll << 30)) return FA_ERR_INVALID_ARG;
+    fa::kv_block_range(Tq, Tk, i * bq, i * bq + bq, bk, causal != 0, window, *j_lo, *j_hi);
+    return FA_OK;
 }
 
 fa_status_t flash_attn_kv_block_range(int T, int bq, int bk, int causal, int window, int i,
@@ -271,7 +289,7 @@ fa_status_t flash_attn_kv_block_range(int T, int bq, int bk, int causal, int win
     if (T < 1 || bq < 1 || bk < 1 || window < 0 || i < 0 || !j_lo || !j_hi)
         return FA_ERR_INVALID_ARG;
     if ((long long)(i + 1) * bq > (1ll << 30)) return FA_ERR_INVALID_ARG;
-    fa::kv_block_range(T, i * bq, i * bq + bq, bk, causal != 0, window, *j_lo, *j_hi);
+    fa::kv_block_range(T, T, i * bq, i * bq + bq, bk, causal != 0, window, *j_lo, *j_hi);
     return FA_OK;
 }
 
@@ -295,7 +313,7 @@ fa_status_t flash_attn_default_tiles(fa_dtype_t dtype, int D, int pass, int* bq,
 fa_status_t flash_attn_fwd_ex(const void* Q, const void* K, const void* V, void* O, float* L,
                               int B, int T, int H, int HKV, int D, float scale, int causal,
                               int window, fa_dtype_t dtype, hipStream_t stream, int bq, int bk) {
-    return fwd_impl(Q, K, V, O, L, B, T, H, HKV, D, scale, causal, window, dtype, stream, bq, bk,
+    return fwd_impl(Q, K, V, O, L, B, T, T, H, HKV, D, scale, causal, window, dtype, stream, bq, bk,
                     dense_layout(T, H, D), dense_layout(T, HKV, D));
 }
 
@@ -307,11 +325,12 @@ fa_status_t flash_attn_fwd(const void* Q, const void* K, const void* V, void* O,
 }
 
 fa_status_t flash_attn_fwd_strided(const void* Q, const void* K, const void* V, void* O,
-                                   float* L, int B, int T, int H, int HKV, int D, float scale,
-                                   int causal, int window, fa_dtype_t dtype, hipStream_t stream,
-                                   fa_layout_t q_layout, fa_layout_t kv_layout) {
-    return fwd_impl(Q, K, V, O, L, B, T, H, HKV, D, scale, causal, window, dtype, stream, 0, 0,
-                    q_layout, kv_layout);
+                                   float* L, int B, int T, int Tk, int H, int HKV, int D,
+                                   float scale, int causal, int window, fa_dtype_t dtype,
+                                   hipStream_t stream, fa_layout_t q_layout,
+                                   fa_layout_t kv_layout) {
+    return fwd_impl(Q, K, V, O, L, B, T, Tk, H, HKV, D, scale, causal, window, dtype, stream, 0,
+                    0, q_layout, kv_layout);
 }
 
 fa_status_t flash_attn_bwd_preprocess(const void* O, const void* dO, float* Dvec, int B, int T,
@@ -323,7 +342,7 @@ fa_status_t flash_attn_bwd_dkdv(const void* Q, const void* K, const void* V, con
                                 const float* L, const float* Dvec, float* dK, float* dV, int B,
                                 int T, int H, int HKV, int D, float scale, int causal, int window,
                                 fa_dtype_t dtype, hipStream_t stream, int bq, int bk) {
-    return dkdv_impl(Q, K, V, dO, L, Dvec, dK, dV, B, T, H, HKV, D, scale, causal, window, dtype,
+    return dkdv_impl(Q, K, V, dO, L, Dvec, dK, dV, B, T, T, H, HKV, D, scale, causal, window, dtype,
                      stream, bq, bk, dense_layout(T, H, D), dense_layout(T, HKV, D));
 }
 
@@ -331,7 +350,7 @@ fa_status_t flash_attn_bwd_dq(const void* Q, const void* K, const void* V, const
                               const float* L, const float* Dvec, float* dQ, int B, int T, int H,
                               int HKV, int D, float scale, int causal, int window,
                               fa_dtype_t dtype, hipStream_t stream, int bq, int bk) {
-    return dq_impl(Q, K, V, dO, L, Dvec, dQ, B, T, H, HKV, D, scale, causal, window, dtype,
+    return dq_impl(Q, K, V, dO, L, Dvec, dQ, B, T, T, H, HKV, D, scale, causal, window, dtype,
                    stream, bq, bk, dense_layout(T, H, D), dense_layout(T, HKV, D));
 }
 
@@ -340,7 +359,7 @@ fa_status_t flash_attn_bwd_dq_dvec(const void* Q, const void* K, const void* V, 
                                    int T, int H, int HKV, int D, float scale, int causal,
                                    int window, fa_dtype_t dtype, hipStream_t stream, int bq,
                                    int bk) {
-    return dq_dvec_impl(Q, K, V, O, dO, L, Dvec, dQ, B, T, H, HKV, D, scale, causal, window,
+    return dq_dvec_impl(Q, K, V, O, dO, L, Dvec, dQ, B, T, T, H, HKV, D, scale, causal, window,
                         dtype, stream, bq, bk, dense_layout(T, H, D), dense_layout(T, HKV, D));
 }
 
@@ -348,7 +367,7 @@ fa_status_t flash_attn_bwd_ex(const void* Q, const void* K, const void* V, const
                               const float* L, const void* dO, float* dQ, float* dK, float* dV,
                               int B, int T, int H, int HKV, int D, float scale, int causal,
                               int window, fa_dtype_t dtype, hipStream_t stream, int bq, int bk) {
-    return bwd_impl(Q, K, V, O, L, dO, dQ, dK, dV, B, T, H, HKV, D, scale, causal, window, dtype,
+    return bwd_impl(Q, K, V, O, L, dO, dQ, dK, dV, B, T, T, H, HKV, D, scale, causal, window, dtype,
                     stream, bq, bk, dense_layout(T, H, D), dense_layout(T, HKV, D));
 }
 
@@ -362,21 +381,22 @@ fa_status_t flash_attn_bwd(const void* Q, const void* K, const void* V, const vo
 
 fa_status_t flash_attn_bwd_strided(const void* Q, const void* K, const void* V, const void* O,
                                    const float* L, const void* dO, float* dQ, float* dK,
-                                   float* dV, int B, int T, int H, int HKV, int D, float scale,
-                                   int causal, int window, fa_dtype_t dtype, hipStream_t stream,
-                                   fa_layout_t q_layout, fa_layout_t kv_layout) {
-    return bwd_impl(Q, K, V, O, L, dO, dQ, dK, dV, B, T, H, HKV, D, scale, causal, window, dtype,
-                    stream, 0, 0, q_layout, kv_layout);
+                                   float* dV, int B, int T, int Tk, int H, int HKV, int D,
+                                   float scale, int causal, int window, fa_dtype_t dtype,
+                                   hipStream_t stream, fa_layout_t q_layout,
+                                   fa_layout_t kv_layout) {
+    return bwd_impl(Q, K, V, O, L, dO, dQ, dK, dV, B, T, Tk, H, HKV, D, scale, causal, window,
+                    dtype, stream, 0, 0, q_layout, kv_layout);
 }
 
 fa_status_t flash_attn_bwd_grad16(const void* Q, const void* K, const void* V, const void* O,
                                   const float* L, const void* dO, void* dQ, void* dK, void* dV,
-                                  int B, int T, int H, int HKV, int D, float scale, int causal,
-                                  int window, fa_dtype_t dtype, hipStream_t stream,
+                                  int B, int T, int Tk, int H, int HKV, int D, float scale,
+                                  int causal, int window, fa_dtype_t dtype, hipStream_t stream,
                                   fa_layout_t q_layout, fa_layout_t kv_layout) {
     if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return FA_ERR_INVALID_ARG;
     return bwd_impl(Q, K, V, O, L, dO, static_cast<float*>(dQ), static_cast<float*>(dK),
-                    static_cast<float*>(dV), B, T, H, HKV, D, scale, causal, window, dtype,
+                    static_cast<float*>(dV), B, T, Tk, H, HKV, D, scale, causal, window, dtype,
                     stream, 0, 0, q_layout, kv_layout, 1);
 }
 

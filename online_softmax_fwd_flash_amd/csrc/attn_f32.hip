@@ -52,7 +52,7 @@ __device__ __forceinline__ void stage_rows(float* __restrict__ dst, const float*
 template <int DP, int BQ, int BK>
 __global__ __launch_bounds__(BQ / 16 * 64) void fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-    float* __restrict__ O, float* __restrict__ L, int B, int T, int H, int HKV, int D,
+    float* __restrict__ O, float* __restrict__ L, int B, int T, int Tk, int H, int HKV, int D,
     float scale, int causal, int window, int nqt, Layout lq, Layout lk) {
     using Tl = F32Tile<DP>;
     constexpr int NW = BQ / 16, NT = NW * 64, KS = Tl::KS, LD = Tl::LD, NDB = Tl::NDB;
@@ -87,13 +87,13 @@ __global__ __launch_bounds__(BQ / 16 * 64) void fwd_f32_kernel(
     const bool cz = causal != 0;
 
     int jlo, jhi;
-    kv_block_range(T, qt * BQ, qt * BQ + BQ, BK, cz, window, jlo, jhi);
+    kv_block_range(T, Tk, qt * BQ, qt * BQ + BQ, BK, cz, window, jlo, jhi);
     for (int j = jlo; j < jhi; ++j) {
         __syncthreads();
-        stage_rows<DP, BK, NT>(Ks, Kh, ldk, j * BK, T, D);
-        stage_rows<DP, BK, NT>(Vs, Vh, ldk, j * BK, T, D);
+        stage_rows<DP, BK, NT>(Ks, Kh, ldk, j * BK, Tk, D);
+        stage_rows<DP, BK, NT>(Vs, Vh, ldk, j * BK, Tk, D);
         __syncthreads();
-        const int cls = block_class(T, wr0, wr0 + 16, j * BK, j * BK + BK, cz, window);
+        const int cls = block_class(T, Tk, wr0, wr0 + 16, j * BK, j * BK + BK, cz, window);
         if (cls == kSkip) continue;
 
         f32x4 s[BK / 16];
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(BQ / 16 * 64) void fwd_f32_kernel(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int key = j * BK + kb * 16 + 4 * g + r;
-                    if (!visible(q, key, T, cz, window)) s[kb][r] = -INFINITY;
+                    if (!visible(q, key, T, Tk, cz, window)) s[kb][r] = -INFINITY;
                 }
         }
         float mx = kNegMax;
@@ -168,7 +168,7 @@ template <int DP, int BQ, int BK>
 __global__ __launch_bounds__(BK / 16 * 64) void dkdv_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ L, const float* __restrict__ Dv,
-    float* __restrict__ dK, float* __restrict__ dV, int B, int T, int H, int HKV, int D,
+    float* __restrict__ dK, float* __restrict__ dV, int B, int T, int Tk, int H, int HKV, int D,
     float scale, int causal, int window, int nkt, Layout lq, Layout lk) {
     using Tl = F32Tile<DP>;
     constexpr int NW = BK / 16, NT = NW * 64, KS = Tl::KS, LD = Tl::LD, NDB = Tl::NDB;
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(BK / 16 * 64) void dkdv_f32_kernel(
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
         const int d = g * KS + s;
-        const bool ok = key < T && d < D;
+        const bool ok = key < Tk && d < D;
         kreg[s] = ok ? Kh[(int64_t)key * ldk + d] : 0.f;
         vreg[s] = ok ? Vh[(int64_t)key * ldk + d] : 0.f;
     }
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(BK / 16 * 64) void dkdv_f32_kernel(
     for (int i = 0; i < NDB; ++i) dka[i] = dva[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     int ilo, ihi;
-    q_block_range(T, kt * BK, kt * BK + BK, BQ, cz, window, ilo, ihi);
+    q_block_range(T, Tk, kt * BK, kt * BK + BK, BQ, cz, window, ilo, ihi);
     for (int hh = 0; hh < rep; ++hh) {
         const int h = hk * rep + hh;
         const float* Qh = Q + b * lq.b + h * lq.h;
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(BK / 16 * 64) void dkdv_f32_kernel(
 #pragma unroll 1
             for (int qs = 0; qs < BQ; qs += 16) {
                 const int qr0 = i * BQ + qs;
-                const int cls = block_class(T, qr0, qr0 + 16, kw0, kw0 + 16, cz, window);
+                const int cls = block_class(T, Tk, qr0, qr0 + 16, kw0, kw0 + 16, cz, window);
                 if (cls == kSkip) continue;
                 f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
                 const float* qrow = Qs + (qs + n) * LD + g * KS;
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(BK / 16 * 64) void dkdv_f32_kernel(
                 for (int r = 0; r < 4; ++r) {
                     const int qq = qs + 4 * g + r;
                     float pr = fast_exp2(fmaf(sc[r], c, -Ls[qq]));
-                    if (cls == kPartial && !visible(qr0 + 4 * g + r, key, T, cz, window)) pr = 0.f;
+                    if (cls == kPartial && !visible(qr0 + 4 * g + r, key, T, Tk, cz, window)) pr = 0.f;
                     p[r] = pr;
                     ds[r] = pr * (dp[r] - Ds[qq]);
                 }
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(BK / 16 * 64) void dkdv_f32_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int kk = kw0 + 4 * g + r;
-            if (kk < T && d < D) {
+            if (kk < Tk && d < D) {
                 dKh[(int64_t)kk * ldk + d] = dka[db][r] * scale;
                 dVh[(int64_t)kk * ldk + d] = dva[db][r];
             }
@@ -279,7 +279,7 @@ template <int DP, int BQ, int BK>
 __global__ __launch_bounds__(BQ / 16 * 64) void dq_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ L, const float* __restrict__ Dv,
-    float* __restrict__ dQ, int B, int T, int H, int HKV, int D, float scale, int causal,
+    float* __restrict__ dQ, int B, int T, int Tk, int H, int HKV, int D, float scale, int causal,
     int window, int nqt, Layout lq, Layout lk) {
     using Tl = F32Tile<DP>;
     constexpr int NW = BQ / 16, NT = NW * 64, KS = Tl::KS, LD = Tl::LD, NDB = Tl::NDB;
@@ -318,16 +318,16 @@ __global__ __launch_bounds__(BQ / 16 * 64) void dq_f32_kernel(
     for (int i = 0; i < NDB; ++i) dqa[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     int jlo, jhi;
-    kv_block_range(T, qt * BQ, qt * BQ + BQ, BK, cz, window, jlo, jhi);
+    kv_block_range(T, Tk, qt * BQ, qt * BQ + BQ, BK, cz, window, jlo, jhi);
     for (int j = jlo; j < jhi; ++j) {
         __syncthreads();
-        stage_rows<DP, BK, NT>(Ks, Kh, ldk, j * BK, T, D);
-        stage_rows<DP, BK, NT>(Vs, Vh, ldk, j * BK, T, D);
+        stage_rows<DP, BK, NT>(Ks, Kh, ldk, j * BK, Tk, D);
+        stage_rows<DP, BK, NT>(Vs, Vh, ldk, j * BK, Tk, D);
         __syncthreads();
 #pragma unroll 1
         for (int kb = 0; kb < BK / 16; ++kb) {
             const int kc0 = j * BK + kb * 16;
-            const int cls = block_class(T, wr0, wr0 + 16, kc0, kc0 + 16, cz, window);
+            const int cls = block_class(T, Tk, wr0, wr0 + 16, kc0, kc0 + 16, cz, window);
             if (cls == kSkip) continue;
             f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
             const float* krow = Ks + (kb * 16 + n) * LD + g * KS;
@@ -342,7 +342,7 @@ __global__ __launch_bounds__(BQ / 16 * 64) void dq_f32_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 float pr = fast_exp2(fmaf(sc[r], c, -l2));
-                if (cls == kPartial && !visible(q, kc0 + 4 * g + r, T, cz, window)) pr = 0.f;
+                if (cls == kPartial && !visible(q, kc0 + 4 * g + r, T, Tk, cz, window)) pr = 0.f;
                 ds[r] = pr * (dp[r] - dq_i);
             }
 #pragma unroll
@@ -372,18 +372,18 @@ hipError_t launch_fwd_f32_t(const AttnArgs& a) {
     const unsigned grid = (unsigned)nqt * a.B * a.H;
     hipLaunchKernelGGL((fwd_f32_kernel<DP, BQ, BK>), dim3(grid), dim3(BQ / 16 * 64), 0,
                        a.stream, (const float*)a.Q, (const float*)a.K, (const float*)a.V,
-                       (float*)a.Oout, a.L, a.B, a.T, a.H, a.HKV, a.D, a.scale, a.causal,
+                       (float*)a.Oout, a.L, a.B, a.T, a.Tk, a.H, a.HKV, a.D, a.scale, a.causal,
                        a.window, nqt, a.lq, a.lk);
     return hipGetLastError();
 }
 
 template <int DP, int BQ, int BK>
 hipError_t launch_dkdv_f32_t(const AttnArgs& a) {
-    const int nkt = (a.T + BK - 1) / BK;
+    const int nkt = (a.Tk + BK - 1) / BK;
     const unsigned grid = (unsigned)nkt * a.B * a.HKV;
     hipLaunchKernelGGL((dkdv_f32_kernel<DP, BQ, BK>), dim3(grid), dim3(BK / 16 * 64), 0,
                        a.stream, (const float*)a.Q, (const float*)a.K, (const float*)a.V,
-                       (const float*)a.dO, a.Lin, a.Dvec, a.dK, a.dV, a.B, a.T, a.H, a.HKV, a.D,
+                       (const float*)a.dO, a.Lin, a.Dvec, a.dK, a.dV, a.B, a.T, a.Tk, a.H, a.HKV, a.D,
                        a.scale, a.causal, a.window, nkt, a.lq, a.lk);
     return hipGetLastError();
 }
@@ -394,7 +394,7 @@ hipError_t launch_dq_f32_t(const AttnArgs& a) {
     const unsigned grid = (unsigned)nqt * a.B * a.H;
     hipLaunchKernelGGL((dq_f32_kernel<DP, BQ, BK>), dim3(grid), dim3(BQ / 16 * 64), 0,
                        a.stream, (const float*)a.Q, (const float*)a.K, (const float*)a.V,
-                       (const float*)a.dO, a.Lin, a.Dvec, a.dQ, a.B, a.T, a.H, a.HKV, a.D,
+                       (const float*)a.dO, a.Lin, a.Dvec, a.dQ, a.B, a.T, a.Tk, a.H, a.HKV, a.D,
                        a.scale, a.causal, a.window, nqt, a.lq, a.lk);
     return hipGetLastError();
 }

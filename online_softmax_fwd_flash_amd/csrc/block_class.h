@@ -1,7 +1,7 @@
 // Block classification for tiled causal / sliding-window attention, shared by every kernel
 // and by the host-side query entry points, so host tests see exactly what the device does.
 //
-// A block covers query rows [r0, r1) and keys [c0, c1) of a T x T problem.  A query row r
+// A block covers query rows [r0, r1) and keys [c0, c1).  In a T x T problem a query row r
 // sees key c when (no causal or c <= r) and (no window or c >= r - W + 1) and c < T.
 //   SKIP    nothing in the block is visible (never computed),
 //   FULL    every in-range element is visible and no key is past T (no mask test),
@@ -26,46 +26,85 @@ namespace fa {
 
 enum BlockClass : int { kSkip = 0, kFull = 1, kPartial = 2 };
 
-FA_HD int block_class(int T, int r0, int r1, int c0, int c1, bool causal, int window) {
-    if (r1 > T) r1 = T;
-    if (r0 >= r1 || c0 >= T || c0 >= c1) return kSkip;
-    const int R = r1 - 1;                      // last in-range row
-    const int C = (c1 < T ? c1 : T) - 1;       // last in-range key
-    // any visible pair: exists r in [r0,R] with [r-W+1, r] meeting [c0, C]
-    if (causal && c0 > R) return kSkip;
-    if (window > 0 && C < r0 - window + 1) return kSkip;
-    bool full = (c1 <= T);
-    if (causal && C > r0) full = false;
-    if (window > 0 && c0 < R - window + 1) full = false;
+// Query rows and keys may number differently (Tq, Tk).  Query row r then sits at key position
+// r + Tk - Tq (the rows are the last Tq positions, as when the keys start with a prefix), and
+// the rules above apply to that position: row r sees key c when c < Tk and (no causal or
+// c <= r + Tk - Tq) and (no window or c >= r + Tk - Tq - W + 1).  With Tq = Tk this is the
+// square rule.  Rows whose position is negative (Tq > Tk, causal) see no key.
+
+FA_HD int block_class(int Tq, int Tk, int r0, int r1, int c0, int c1, bool causal, int window) {
+    if (r1 > Tq) r1 = Tq;
+    if (r0 >= r1 || c0 >= Tk || c0 >= c1) return kSkip;
+    const int dq = Tk - Tq;
+    const int p0 = r0 + dq, P = r1 - 1 + dq;   // first and last row position
+    const int C = (c1 < Tk ? c1 : Tk) - 1;     // last in-range key
+    // any visible pair: exists p in [p0, P] with [p-W+1, p] meeting [c0, C]
+    if (causal && c0 > P) return kSkip;
+    if (window > 0 && C < p0 - window + 1) return kSkip;
+    bool full = (c1 <= Tk);
+    if (causal && C > p0) full = false;
+    if (window > 0 && c0 < P - window + 1) full = false;
     return full ? kFull : kPartial;
 }
 
 // Key-block range [lo, hi) (blocks of bk keys) that rows [r0, r1) may see.
-FA_HD void kv_block_range(int T, int r0, int r1, int bk, bool causal, int window, int& lo,
-                          int& hi) {
-    if (r1 > T) r1 = T;
-    if (r0 >= r1) { lo = hi = 0; return; }
-    int first = (window > 0 && r0 - window + 1 > 0) ? r0 - window + 1 : 0;
-    int last = causal ? r1 - 1 : T - 1;
+FA_HD void kv_block_range(int Tq, int Tk, int r0, int r1, int bk, bool causal, int window,
+                          int& lo, int& hi) {
+    if (r1 > Tq) r1 = Tq;
+    lo = hi = 0;
+    if (r0 >= r1) return;
+    const int dq = Tk - Tq;
+    const int p0 = r0 + dq, P = r1 - 1 + dq;
+    const int first = (window > 0 && p0 - window + 1 > 0) ? p0 - window + 1 : 0;
+    const int last = causal ? (P < Tk - 1 ? P : Tk - 1) : Tk - 1;
+    if (last < first) return;
     lo = first / bk;
     hi = last / bk + 1;
 }
 
 // Query-block range [lo, hi) (blocks of bq rows) whose rows may see keys [c0, c1).
-FA_HD void q_block_range(int T, int c0, int c1, int bq, bool causal, int window, int& lo,
-                         int& hi) {
-    if (c1 > T) c1 = T;
-    if (c0 >= c1) { lo = hi = 0; return; }
-    int first = causal ? c0 : 0;
-    int last = (window > 0 && c1 - 1 + window - 1 < T - 1) ? c1 - 1 + window - 1 : T - 1;
-    if (first > last) { lo = hi = 0; return; }
+FA_HD void q_block_range(int Tq, int Tk, int c0, int c1, int bq, bool causal, int window,
+                         int& lo, int& hi) {
+    if (c1 > Tk) c1 = Tk;
+    lo = hi = 0;
+    if (c0 >= c1) return;
+    const int dq = Tk - Tq;
+    // row positions p = r + dq that see some key of [c0, c1): p >= c0 (causal) and
+    // p <= c1 - 1 + W - 1 (window), with r in [0, Tq)
+    int first = causal ? c0 - dq : 0;
+    int last = (window > 0) ? c1 - 1 + window - 1 - dq : Tq - 1;
+    if (first < 0) first = 0;
+    if (last > Tq - 1) last = Tq - 1;
+    if (first > last) return;
     lo = first / bq;
     hi = last / bq + 1;
 }
 
 // Per-element keep test in global indices (used inside PARTIAL blocks).
-FA_HD bool visible(int r, int c, int T, bool causal, int window) {
-    return c < T && (!causal || c <= r) && (window <= 0 || c >= r - window + 1);
+FA_HD bool visible(int r, int c, int Tq, int Tk, bool causal, int window) {
+    const int p = r + Tk - Tq;
+    return r < Tq && c < Tk && (!causal || c <= p) && (window <= 0 || c >= p - window + 1);
+}
+
+// Number of keys row r sees, as the interval [lo, lo + n) (n = 0 when none): the kernels'
+// per-lane form of the rule, one unsigned compare per element.
+FA_HD void row_keys(int r, int Tq, int Tk, bool causal, int window, int& lo, int& n) {
+    const int p = r + Tk - Tq;
+    lo = window > 0 ? p - window + 1 : 0;
+    if (lo < 0) lo = 0;
+    int hi = causal ? p : Tk - 1;
+    if (hi > Tk - 1) hi = Tk - 1;
+    n = hi >= lo ? hi - lo + 1 : 0;
+}
+
+// Query rows that see key c, as [lo, lo + n): the transposed form for key-owned passes.
+FA_HD void key_rows(int c, int Tq, int Tk, bool causal, int window, int& lo, int& n) {
+    const int dq = Tk - Tq;
+    lo = causal ? c - dq : 0;
+    if (lo < 0) lo = 0;
+    int hi = window > 0 ? c - dq + window - 1 : Tq - 1;
+    if (hi > Tq - 1) hi = Tq - 1;
+    n = (c < Tk && hi >= lo) ? hi - lo + 1 : 0;
 }
 
 }  // namespace fa

@@ -136,8 +136,8 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv_b16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ L, const float* __restrict__ Dv, float* __restrict__ dK,
-    float* __restrict__ dV, int B, int T, int H, int HKV, float scale, int causal, int window,
-    Layout lq, Layout lk, int g16) {
+    float* __restrict__ dV, int B, int T, int Tk, int H, int HKV, float scale, int causal,
+    int window, Layout lq, Layout lk, int g16) {
     using C = Dkdv16Cfg<D>;
     using V8 = typename E::v8;
     using S16 = typename E::s;
@@ -158,14 +158,14 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv_b16_kernel(
     const bool cz = causal != 0;
     const float c = scale * kLog2e;
     // queries that see this lane's key: [qlo, qhi] (lanes of keys past T are never stored)
-    const int qlo = cz ? key : 0;
-    const int qhi = min(window > 0 ? key + window - 1 : T - 1, T - 1);
+    int qlo, qn;
+    key_rows(key, T, Tk, cz, window, qlo, qn);
 
     // B operands of S = Q K^T and dP = dO V^T: lane (n, g) holds K/V[key][32*ds + 8g .. +7]
     V8 kreg[C::DS], vreg[C::DS];
     {
-        const Buf kb = head_buf<D>(K + b * lk.b + hk * lk.h, ldk, T);
-        const Buf vb = head_buf<D>(V + b * lk.b + hk * lk.h, ldk, T);
+        const Buf kb = head_buf<D>(K + b * lk.b + hk * lk.h, ldk, Tk);
+        const Buf vb = head_buf<D>(V + b * lk.b + hk * lk.h, ldk, Tk);
         const uint32_t off = (uint32_t)key * (uint32_t)(ldk * 2) + 16 * g;
 #pragma unroll
         for (int ds = 0; ds < C::DS; ++ds) {
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv_b16_kernel(
     for (int i = 0; i < C::NDB; ++i) dka[i] = dva[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     int ilo, ihi;
-    q_block_range(T, kt * C::BKW, kt * C::BKW + C::BKW, C::BQ, cz, window, ilo, ihi);
+    q_block_range(T, Tk, kt * C::BKW, kt * C::BKW + C::BKW, C::BQ, cz, window, ilo, ihi);
     const int niter = rep * (ihi - ilo);
     // the group's first query head; head h2 of the group is h2 * lq.h elements further
     const uint32_t ldq_b = (uint32_t)(ldq * 2);
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv_b16_kernel(
         lds_barrier();
         if (it + 1 < niter) dkdv16_issue<D>(sm, qs, Lg, Dg, voff, w, rep, ihi, T, it + 1);
         const int qr0 = i * C::BQ;
-        const int cls = block_class(T, qr0, qr0 + C::BQ, kw0, kw0 + C::KPW, cz, window);
+        const int cls = block_class(T, Tk, qr0, qr0 + C::BQ, kw0, kw0 + C::KPW, cz, window);
         if (cls == kSkip) continue;
         const char* stg = sm + (it & 1) * C::STAGE;
         const uint16_t* Qn = reinterpret_cast<const uint16_t*>(stg);
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv_b16_kernel(
                 float p = fast_exp2(fmaf(sc[qb][r], c, -l4[r] * kLog2e));
                 if (cls == kPartial) {
                     const int qi = qr0 + qb * 16 + 4 * g + r;
-                    p = ((unsigned)(qi - qlo) > (unsigned)(qhi - qlo)) ? 0.f : p;
+                    p = ((unsigned)(qi - qlo) >= (unsigned)qn) ? 0.f : p;
                 }
                 // k-step kk = qb/2 takes rows of blocks 2kk (elements 0-3), 2kk+1 (4-7)
                 pp[qb >> 1][4 * (qb & 1) + r] = (S16)p;
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv_b16_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int kk = kw0 + 4 * g + r;
-        if (kk < T) {
+        if (kk < Tk) {
             const int64_t row = kbase + (int64_t)kk * ldk + n;
             if (g16) {
                 typename E::s* dKh = reinterpret_cast<typename E::s*>(dK) + row;
@@ -342,8 +342,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_b16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const uint16_t* __restrict__ O, const float* __restrict__ L, float* __restrict__ Dv,
-    float* __restrict__ dQ, int B, int T, int H, int HKV, float scale, int causal, int window,
-    int nqt, int xcd_group, Layout lq, Layout lk, int g16) {
+    float* __restrict__ dQ, int B, int T, int Tk, int H, int HKV, float scale, int causal,
+    int window, int nqt, int xcd_group, Layout lq, Layout lk, int g16) {
     using C = DqCfg<D, NW>;
     using V8 = typename E::v8;
     extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
@@ -359,8 +359,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_b16_kernel(
     const int q = wr0 + n;
     const int64_t ldq = lq.t, ldk = lk.t;   // row strides (elements)
     const uint32_t ldk_b = (uint32_t)(ldk * 2);
-    const Buf kbuf = head_buf<D>(K + b * lk.b + hk * lk.h, ldk, T);
-    const Buf vbuf = head_buf<D>(V + b * lk.b + hk * lk.h, ldk, T);
+    const Buf kbuf = head_buf<D>(K + b * lk.b + hk * lk.h, ldk, Tk);
+    const Buf vbuf = head_buf<D>(V + b * lk.b + hk * lk.h, ldk, Tk);
     // element offset of this lane's query row in Q, O, dO and dQ
     const int64_t qrow = b * lq.b + (int64_t)q * ldq + h * lq.h;
     const bool cz = causal != 0;
@@ -395,9 +395,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_b16_kernel(
     } else {
         dq_i = q < T ? Dv[((int64_t)b * H + h) * T + q] : 0.f;
     }
-    // keys this query row may see: [klo, khi]
-    const int klo = window > 0 ? q - window + 1 : 0;
-    const int khi = cz ? q : T - 1;
+    // keys this query row may see: [klo, klo + kn)
+    int klo, kn;
+    row_keys(q, T, Tk, cz, window, klo, kn);
     f32x16 dqa[C::NDB];
 #pragma unroll
     for (int i = 0; i < C::NDB; ++i)
@@ -405,7 +405,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_b16_kernel(
         for (int r = 0; r < 16; ++r) dqa[i][r] = 0.f;
 
     int jlo, jhi;
-    kv_block_range(T, qt * C::BQ, qt * C::BQ + C::BQ, C::BK, cz, window, jlo, jhi);
+    kv_block_range(T, Tk, qt * C::BQ, qt * C::BQ + C::BQ, C::BK, cz, window, jlo, jhi);
     uint32_t voff[C::PMAX];
 #pragma unroll
     for (int i = 0; i < C::PMAX; ++i)
@@ -418,7 +418,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_b16_kernel(
         // every wave's pieces are visible; every wave is done with the other stage
         lds_barrier();
         if (j + 1 < jhi) dq_issue<D, NW>(sm + (stg ^ 1) * C::STAGE, kbuf, vbuf, voff, w, ldk_b, j + 1);
-        const int cls = block_class(T, wr0, wr0 + 32, j * C::BK, j * C::BK + C::BK, cz, window);
+        const int cls = block_class(T, Tk, wr0, wr0 + 32, j * C::BK, j * C::BK + C::BK, cz, window);
         if (cls == kSkip) continue;
         const uint16_t* Kn = reinterpret_cast<const uint16_t*>(sm + stg * C::STAGE);
         const uint16_t* Vn = reinterpret_cast<const uint16_t*>(sm + stg * C::STAGE + C::OFF_V);
@@ -453,7 +453,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_b16_kernel(
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int kk = j * C::BK + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-                    if ((unsigned)(kk - klo) > (unsigned)(khi - klo)) sk[r] = 0.f;
+                    if ((unsigned)(kk - klo) >= (unsigned)kn) sk[r] = 0.f;
                 }
             }
             V8 pd[2];
@@ -519,11 +519,11 @@ hipError_t launch_dkdv_b16_t(const AttnArgs& a) {
     const size_t lds = 2 * (size_t)C::STAGE;
     hipError_t e = allow_lds(dkdv_b16_kernel<E, D>, lds, set);
     if (e != hipSuccess) return e;
-    const int nkt = (a.T + C::BKW - 1) / C::BKW;
+    const int nkt = (a.Tk + C::BKW - 1) / C::BKW;
     const unsigned grid = (unsigned)nkt * a.B * a.HKV;
     hipLaunchKernelGGL((dkdv_b16_kernel<E, D>), dim3(grid), dim3(C::NT), lds, a.stream,
                        (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
-                       (const uint16_t*)a.dO, a.Lin, a.Dvec, a.dK, a.dV, a.B, a.T, a.H, a.HKV,
+                       (const uint16_t*)a.dO, a.Lin, a.Dvec, a.dK, a.dV, a.B, a.T, a.Tk, a.H, a.HKV,
                        a.scale, a.causal, a.window, a.lq, a.lk, a.g16);
     return hipGetLastError();
 }
@@ -546,7 +546,7 @@ hipError_t launch_dq_b16_t(const AttnArgs& a) {
     hipLaunchKernelGGL((dq_b16_kernel<E, D, kDqWaves, FUSE_D>), dim3(grid), dim3(C::NT), lds,
                        a.stream, (const uint16_t*)a.Q, (const uint16_t*)a.K,
                        (const uint16_t*)a.V, (const uint16_t*)a.dO, (const uint16_t*)a.O, a.Lin,
-                       a.Dvec, a.dQ, a.B, a.T, a.H, a.HKV, a.scale, a.causal, a.window, nqt,
+                       a.Dvec, a.dQ, a.B, a.T, a.Tk, a.H, a.HKV, a.scale, a.causal, a.window, nqt,
                        xcd_group_for(nqt, a.B, a.H, a.HKV), a.lq, a.lk, a.g16);
     return hipGetLastError();
 }

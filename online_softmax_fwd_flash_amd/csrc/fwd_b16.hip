@@ -84,7 +84,7 @@ template <class E, int D>
 __global__ __launch_bounds__(kThreads, kWgs) void fwd_b16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ L, int B,
-    int T, int H, int HKV, float scale, int causal, int window, int nqt, int xcd_group,
+    int T, int Tk, int H, int HKV, float scale, int causal, int window, int nqt, int xcd_group,
     Layout lq, Layout lk) {
     using C = Bf16Fwd<D>;
     using V8 = typename E::v8;
@@ -100,13 +100,13 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_b16_kernel(
     const int q = wr0 + n;
     const int64_t ldq = lq.t, ldk = lk.t;   // row strides (elements)
     const uint32_t ldk_b = (uint32_t)(ldk * 2);
-    const Buf kbuf = head_buf<D>(K + b * lk.b + hk * lk.h, ldk, T);
-    const Buf vbuf = head_buf<D>(V + b * lk.b + hk * lk.h, ldk, T);
+    const Buf kbuf = head_buf<D>(K + b * lk.b + hk * lk.h, ldk, Tk);
+    const Buf vbuf = head_buf<D>(V + b * lk.b + hk * lk.h, ldk, Tk);
     const bool cz = causal != 0;
     const float c = scale * kLog2e;
-    // keys this query row may see: [klo, khi]
-    const int klo = window > 0 ? q - window + 1 : 0;
-    const int khi = cz ? q : T - 1;
+    // keys this query row may see: [klo, klo + kn)
+    int klo, kn;
+    row_keys(q, T, Tk, cz, window, klo, kn);
 
     // Q^T operand: lane (n, g) holds Q[q][16*dc + 8*g .. +7] (zero past T)
     V8 qreg[C::DC];
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_b16_kernel(
     float m = kNegMax, lsum = 0.f;
 
     int jlo, jhi;
-    kv_block_range(T, qt * kBQ, qt * kBQ + kBQ, kBK, cz, window, jlo, jhi);
+    kv_block_range(T, Tk, qt * kBQ, qt * kBQ + kBQ, kBK, cz, window, jlo, jhi);
 
     // LDS-DMA source offsets of this lane in its wave's pieces of a K / V tile
     const int wu = __builtin_amdgcn_readfirstlane(w);
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_b16_kernel(
         // all pieces visible; every wave is done with the other stage (block j - 1)
         lds_barrier();
         if (j + 1 < jhi) fwd_issue<D>(kbuf, vbuf, koff, voff, sm + (stg ^ 1) * C::STAGEB, wu, ldk_b, j + 1);
-        const int cls = block_class(T, wr0, wr0 + 32, j * kBK, j * kBK + kBK, cz, window);
+        const int cls = block_class(T, Tk, wr0, wr0 + 32, j * kBK, j * kBK + kBK, cz, window);
         if (cls == kSkip) continue;
         const char* sb = sm + stg * C::STAGEB;
         // S^T for the block's 32-key halves: entry r of lane (n, g) in s[hk] is key
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_b16_kernel(
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int k0 = j * kBK + 32 * hk + 8 * (r >> 2) + 4 * g + (r & 3);
-                    if ((unsigned)(k0 - klo) > (unsigned)(khi - klo)) s[hk][r] = -INFINITY;
+                    if ((unsigned)(k0 - klo) >= (unsigned)kn) s[hk][r] = -INFINITY;
                 }
         }
         float mx = s[0][0];
@@ -289,7 +289,7 @@ hipError_t launch_fwd_b16_t(const AttnArgs& a) {
     }
     hipLaunchKernelGGL((fwd_b16_kernel<E, D>), dim3(grid), dim3(kThreads), lds, a.stream,
                        (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
-                       (uint16_t*)a.Oout, a.L, a.B, a.T, a.H, a.HKV, a.scale, a.causal,
+                       (uint16_t*)a.Oout, a.L, a.B, a.T, a.Tk, a.H, a.HKV, a.scale, a.causal,
                        a.window, nqt, xcd_group, a.lq, a.lk);
     return hipGetLastError();
 }

@@ -25,7 +25,8 @@ struct AttnArgs {
     float* dQ;
     float* dK;
     float* dV;
-    int B, T, H, HKV, D;
+    int B, T, H, HKV, D;   // T: query rows
+    int Tk;                 // keys (T unless the two lengths differ)
     float scale;
     int causal, window;
     hipStream_t stream;

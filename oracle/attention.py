@@ -18,6 +18,10 @@ Sources (web pages, cited by title and section):
   * teeny-kernels "flash_attn2.rs", backward dQ and dK/dV doc comments: the same formulas.
   * Graphcore "flash_attention_qkv_packed.cpp", flashAttentionQKVPackedGrad: D = rowsum(O * dO),
     dV += P^T dO, dP = dO V^T, dS = P (dP - D), dQ += dS K, dK += dS^T Q.
+  * teeny-kernels "flash_attn2.rs", flash_attention2_forward: separate query and key lengths
+    (n_ctx_q, n_ctx_k).  No page states a causal rule for them.  Reading taken here: the T
+    query rows are the last T of the Tk key positions (row i sits at position i + Tk - T, as
+    after a cached key prefix), and the causal and window rules apply to that position.
 """
 import numpy as np
 
@@ -38,19 +42,22 @@ def group_of_head(h, H, HKV):
     return h // (H // HKV)
 
 
-def visible_mask(T, causal, window, rows=None):
-    """Boolean [len(rows), T] matrix: True where query row i may attend to key j.
+def visible_mask(T, causal, window, rows=None, Tk=None):
+    """Boolean [len(rows), Tk] matrix: True where query row i may attend to key j.
 
-    Causal keeps j <= i (the diagonal is kept).  A window W > 0 keeps j >= i - W + 1, i.e. the
-    W keys ending at the query, self included; without causal it is a lower bound only.
+    Query row i sits at key position p = i + Tk - T (p = i when Tk = T, the default).  Causal
+    keeps j <= p (the diagonal is kept).  A window W > 0 keeps j >= p - W + 1, i.e. the W keys
+    ending at the query, self included; without causal it is a lower bound only.
     """
+    Tk = T if Tk is None else Tk
     i = np.arange(T)[:, None] if rows is None else np.asarray(rows)[:, None]
-    j = np.arange(T)[None, :]
-    vis = np.ones((i.shape[0], T), dtype=bool)
+    p = i + (Tk - T)
+    j = np.arange(Tk)[None, :]
+    vis = np.ones((i.shape[0], Tk), dtype=bool)
     if causal:
-        vis &= j <= i
+        vis &= j <= p
     if window > 0:
-        vis &= j >= i - window + 1
+        vis &= j >= p - window + 1
     return vis
 
 
@@ -67,21 +74,22 @@ def _softmax_rows(S, vis):
 
 
 def _check_shapes(q, k, v=None):
+    """(B, T, Tk, H, HKV, D) of q [B,T,H,D] and k, v [B,Tk,HKV,D]."""
     B, T, H, D = q.shape
     Bk, Tk, HKV, Dk = k.shape
-    if (Bk, Tk, Dk) != (B, T, D) or H % HKV != 0:
+    if (Bk, Dk) != (B, D) or H % HKV != 0:
         raise ValueError(f"bad shapes q{q.shape} k{k.shape}")
     if v is not None and v.shape != k.shape:
         raise ValueError(f"bad shapes k{k.shape} v{v.shape}")
-    return B, T, H, HKV, D
+    return B, T, Tk, H, HKV, D
 
 
 def attn_probs(q, k, scale, causal, window):
-    """Full probability tensor P [B,H,T,T] in fp64 (small inputs only)."""
+    """Full probability tensor P [B,H,T,Tk] in fp64 (small inputs only)."""
     q, k = _f64(q), _f64(k)
-    B, T, H, HKV, D = _check_shapes(q, k)
-    vis = visible_mask(T, causal, window)
-    P = np.zeros((B, H, T, T))
+    B, T, Tk, H, HKV, D = _check_shapes(q, k)
+    vis = visible_mask(T, causal, window, Tk=Tk)
+    P = np.zeros((B, H, T, Tk))
     for b in range(B):
         for h in range(H):
             g = group_of_head(h, H, HKV)
@@ -98,7 +106,7 @@ def attn_fwd(q, k, v, scale, causal, window, row_chunk=1024, pairs=None):
     `pairs` optionally restricts the work to a list of (b, h); other entries are left NaN.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
-    B, T, H, HKV, D = _check_shapes(q, k, v)
+    B, T, Tk, H, HKV, D = _check_shapes(q, k, v)
     O = np.full((B, T, H, D), np.nan)
     L = np.full((B, H, T), np.nan)
     todo = [(b, h) for b in range(B) for h in range(H)] if pairs is None else pairs
@@ -107,7 +115,7 @@ def attn_fwd(q, k, v, scale, causal, window, row_chunk=1024, pairs=None):
         for r0 in range(0, T, row_chunk):
             rows = np.arange(r0, min(T, r0 + row_chunk))
             S = scale * (q[b, rows, h, :] @ k[b, :, g, :].T)
-            P, m, l = _softmax_rows(S, visible_mask(T, causal, window, rows))
+            P, m, l = _softmax_rows(S, visible_mask(T, causal, window, rows, Tk))
             O[b, rows, h, :] = P @ v[b, :, g, :]
             L[b, h, rows] = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), 0.0)
     return O, L
@@ -116,13 +124,13 @@ def attn_fwd(q, k, v, scale, causal, window, row_chunk=1024, pairs=None):
 def attn_fwd_rows(q, k, v, scale, causal, window, triples):
     """O rows and L values for a list of (b, h, i) triples, each computed on its own."""
     q, k, v = _f64(q), _f64(k), _f64(v)
-    B, T, H, HKV, D = _check_shapes(q, k, v)
+    B, T, Tk, H, HKV, D = _check_shapes(q, k, v)
     out_o = np.zeros((len(triples), D))
     out_l = np.zeros(len(triples))
     for n, (b, h, i) in enumerate(triples):
         g = group_of_head(h, H, HKV)
         S = scale * (q[b, i, h, :][None, :] @ k[b, :, g, :].T)
-        P, m, l = _softmax_rows(S, visible_mask(T, causal, window, [i]))
+        P, m, l = _softmax_rows(S, visible_mask(T, causal, window, [i], Tk))
         out_o[n] = (P @ v[b, :, g, :])[0]
         out_l[n] = m[0] + np.log(l[0]) if l[0] > 0 else 0.0
     return out_o, out_l
@@ -137,7 +145,7 @@ def attn_bwd(q, k, v, do, scale, causal, window, row_chunk=1024, groups=None):
     dK_j = scale sum_{h in group} sum_i dS_ij Q_i;  dV_j = sum_{h in group} sum_i P_ij dO_i.
     """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
-    B, T, H, HKV, D = _check_shapes(q, k, v)
+    B, T, Tk, H, HKV, D = _check_shapes(q, k, v)
     if do.shape != q.shape:
         raise ValueError("dO must have the shape of Q")
     rep = H // HKV
@@ -157,7 +165,7 @@ def attn_bwd(q, k, v, do, scale, causal, window, row_chunk=1024, groups=None):
                 rows = np.arange(r0, min(T, r0 + row_chunk))
                 Qc, dOc = q[b, rows, h, :], do[b, rows, h, :]
                 S = scale * (Qc @ Kg.T)
-                P, m, l = _softmax_rows(S, visible_mask(T, causal, window, rows))
+                P, m, l = _softmax_rows(S, visible_mask(T, causal, window, rows, Tk))
                 Oc = P @ Vg
                 Dc = (dOc * Oc).sum(axis=1)
                 dP = dOc @ Vg.T

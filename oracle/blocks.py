@@ -24,20 +24,22 @@ def _cdiv(a, b):
     return -(-a // b)
 
 
-def classify_blocks(T, Bq, Bk, causal, window):
-    """[ceil(T/Bq), ceil(T/Bk)] int array of SKIP/FULL/PARTIAL from the materialised mask.
+def classify_blocks(T, Bq, Bk, causal, window, Tk=None):
+    """[ceil(T/Bq), ceil(Tk/Bk)] int array of SKIP/FULL/PARTIAL from the materialised mask of
+    T query rows against Tk keys (Tk = T by default).
 
-    A block that sticks out past T counts as PARTIAL when any of its in-range elements are
+    A block that sticks out past Tk counts as PARTIAL when any of its in-range elements are
     visible, because the out-of-range keys must still be excluded."""
-    vis = visible_mask(T, causal, window)
-    nq, nk = _cdiv(T, Bq), _cdiv(T, Bk)
+    Tk = T if Tk is None else Tk
+    vis = visible_mask(T, causal, window, Tk=Tk)
+    nq, nk = _cdiv(T, Bq), _cdiv(Tk, Bk)
     out = np.zeros((nq, nk), dtype=np.int64)
     for i in range(nq):
         for j in range(nk):
             blk = vis[i * Bq:(i + 1) * Bq, j * Bk:(j + 1) * Bk]
             if not blk.any():
                 out[i, j] = SKIP
-            elif blk.all() and (j + 1) * Bk <= T:
+            elif blk.all() and (j + 1) * Bk <= Tk:
                 out[i, j] = FULL
             else:
                 out[i, j] = PARTIAL
@@ -58,10 +60,10 @@ def block_keep_mask(i, j, Bq, Bk, T, causal, window):
     return keep
 
 
-def kv_block_range(i, Bq, Bk, T, causal, window):
+def kv_block_range(i, Bq, Bk, T, causal, window, Tk=None):
     """(first, last+1) key blocks of query tile i that hold any visible element, read off the
     materialised mask; (0, 0) when the tile sees nothing."""
-    cls = classify_blocks(T, Bq, Bk, causal, window)[i]
+    cls = classify_blocks(T, Bq, Bk, causal, window, Tk)[i]
     live = np.nonzero(cls != SKIP)[0]
     if live.size == 0:
         return 0, 0

@@ -176,5 +176,71 @@ def check_invariants(ora):
                 assert np.allclose((P[b, hh] * dP).sum(-1), res["delta"][b, hh], atol=1e-12)
 
 
-ALL_FORWARD = [check_prob_rows, check_causal_row0, check_equal_scores, check_lse]
-ALL_BACKWARD = [check_sdpa, check_finite_differences, check_invariants]
+def check_rect_decode(ora):
+    """One query row against Tk keys (separate query and key lengths, teeny-kernels
+    flash_attn2.rs flash_attention2_forward's n_ctx_q / n_ctx_k; the reading that the rows are
+    the last positions): the row sits at position Tk - 1, so causal keeps every key and a
+    window W the last min(W, Tk).  With Q = 0 every score is 0, so O is the mean of those V rows
+    and L = ln(their count)."""
+    Tk, H, HKV, D = 7, 4, 2, 5
+    _, k, v, _ = _tiny(T=Tk, H=H, HKV=HKV, D=D, seed=23)
+    q = torch.zeros(1, 1, H, D, dtype=torch.float64)
+    for causal, window in MASKS:
+        O, L = ora.attn_fwd(q, k, v, 0.9, causal, window)
+        n = Tk if window <= 0 else min(window, Tk)
+        for h in range(H):
+            g = h // (H // HKV)
+            want = v[0, Tk - n:, g, :].numpy().mean(axis=0)
+            assert np.allclose(O[0, 0, h], want, atol=1e-14, rtol=0)
+            assert abs(L[0, h, 0] - math.log(n)) < 1e-14
+
+
+def check_rect_prefix(ora):
+    """T query rows against Tk > T keys are the last T rows of the square Tk problem, whatever
+    its first Tk - T query rows hold; with dO = 0 on those rows they add nothing to dK, dV, so
+    the gradients agree too (the reading of separate lengths)."""
+    Tk, T, H, HKV, D = 11, 4, 4, 2, 5
+    q, k, v, do = _tiny(T=Tk, H=H, HKV=HKV, D=D, seed=21)
+    do = do.clone()
+    do[:, :Tk - T] = 0
+    for causal, window in MASKS:
+        O_sq, L_sq = ora.attn_fwd(q, k, v, 0.6, causal, window)
+        O, L = ora.attn_fwd(q[:, Tk - T:], k, v, 0.6, causal, window)
+        assert np.allclose(O, O_sq[:, Tk - T:], atol=1e-13, rtol=0)
+        assert np.allclose(L, L_sq[:, :, Tk - T:], atol=1e-13, rtol=0)
+
+
+def check_rect_prefix_grads(ora):
+    Tk, T, H, HKV, D = 11, 4, 4, 2, 5
+    q, k, v, do = _tiny(T=Tk, H=H, HKV=HKV, D=D, seed=21)
+    do = do.clone()
+    do[:, :Tk - T] = 0
+    for causal, window in MASKS:
+        sq = ora.attn_bwd(q, k, v, do, 0.6, causal, window)
+        rc = ora.attn_bwd(q[:, Tk - T:], k, v, do[:, Tk - T:], 0.6, causal, window)
+        assert np.allclose(rc["dq"], sq["dq"][:, Tk - T:], atol=1e-13, rtol=0)
+        assert np.allclose(rc["dk"], sq["dk"], atol=1e-13, rtol=0)
+        assert np.allclose(rc["dv"], sq["dv"], atol=1e-13, rtol=0)
+
+
+def check_rect_more_queries(ora):
+    """T > Tk: under causal the first T - Tk rows sit before the first key and see nothing
+    (O = 0, L = 0, as for any row without a visible key) and the rest are the square Tk
+    problem's rows; without causal every row sees all keys (window: a lower bound)."""
+    T, Tk, H, HKV, D = 10, 6, 4, 2, 5
+    q, _, _, _ = _tiny(T=T, H=H, HKV=HKV, D=D, seed=25)
+    _, k, v, _ = _tiny(T=Tk, H=H, HKV=HKV, D=D, seed=26)
+    for window in (0, 3):
+        O, L = ora.attn_fwd(q, k, v, 0.8, True, window)
+        assert (O[:, :T - Tk] == 0).all() and (L[:, :, :T - Tk] == 0).all()
+        O_sq, L_sq = ora.attn_fwd(q[:, T - Tk:], k, v, 0.8, True, window)
+        assert np.allclose(O[:, T - Tk:], O_sq, atol=1e-13, rtol=0)
+        assert np.allclose(L[:, :, T - Tk:], L_sq, atol=1e-13, rtol=0)
+    O, L = ora.attn_fwd(q, k, v, 0.8, False, 0)
+    P = ora.attn_probs(q, k, 0.8, False, 0)
+    assert (P > 0).all()
+
+
+ALL_FORWARD = [check_prob_rows, check_causal_row0, check_equal_scores, check_lse,
+               check_rect_decode, check_rect_prefix, check_rect_more_queries]
+ALL_BACKWARD = [check_sdpa, check_finite_differences, check_invariants, check_rect_prefix_grads]

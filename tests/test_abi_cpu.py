@@ -109,8 +109,8 @@ def test_grad16_rejects_before_launch():
     L = _lib.lib()
     q = _lib.Layout(64 * 4 * 128, 4 * 128, 128)
     k = _lib.Layout(64 * 2 * 128, 2 * 128, 128)
-    dims = [1, 64, 4, 2, 128, 0.125, 1, 0, 1, S0]
-    dims32 = list(dims); dims32[8] = 0
+    dims = [1, 64, 64, 4, 2, 128, 0.125, 1, 0, 1, S0]
+    dims32 = list(dims); dims32[9] = 0
     assert L.flash_attn_bwd_grad16(*([A] * 9), *dims32, q, k) == 1          # f32 inputs
     assert L.flash_attn_bwd_grad16(*([A] * 8), NUL, *dims, q, k) == 1
     assert L.flash_attn_bwd_grad16(*([A] * 9), *dims, q, _lib.Layout(0, 64, 128)) == 1
@@ -167,7 +167,7 @@ def test_layout_check(strides, B, T, heads, D, dtype, code):
 
 def test_strided_entries_reject_before_launch():
     L = _lib.lib()
-    dims = (1, 64, 4, 2, 128, 0.125, 1, 0, 1, S0)
+    dims = (1, 64, 64, 4, 2, 128, 0.125, 1, 0, 1, S0)   # B T Tk H HKV D scale causal window dtype
     good_q = _lib.Layout(64 * 4 * 128, 4 * 128, 128)
     good_k = _lib.Layout(64 * 2 * 128, 2 * 128, 128)
     bad = _lib.Layout(64 * 4 * 128, 64, 128)                       # rows shorter than D
@@ -177,6 +177,8 @@ def test_strided_entries_reject_before_launch():
     assert L.flash_attn_bwd_strided(*([A] * 9), *dims, bad, good_k) == 1
     assert L.flash_attn_bwd_strided(*([A] * 9), *dims, good_q, bad) == 1
     assert L.flash_attn_bwd_strided(*([A] * 8), MIS, *dims, good_q, good_k) == 1
+    assert L.flash_attn_fwd_strided(A, A, A, A, A, 1, 64, 0, 4, 2, 128, 0.125, 1, 0, 1, S0,
+                                    good_q, good_k) == 1                      # Tk < 1
     # the KV layout is checked with HKV heads: a head stride that aliases only at 4 heads
     kv2 = _lib.Layout(64 * 2 * 128, 2 * 128, 128)
     assert fa.flash_attn_check_layout((kv2.batch, kv2.row, kv2.head), 1, 64, 2, 128, 1) == 0
@@ -215,3 +217,29 @@ def test_device_partial_offsets_cycle_like_the_graphcore_walk():
                     seq.append(off + 1)
         cyc = oracle.triu_offset_sequence(bq, bk)
         assert seq == [cyc[n % len(cyc)] for n in range(len(seq))]
+
+
+RECT_SWEEP = [(Tq, Tk, bq, bk, c, w)
+              for Tq, Tk in ((1, 7), (5, 64), (64, 5), (100, 129), (129, 100), (1, 300), (300, 17))
+              for bq, bk in ((32, 32), (64, 16), (128, 64), (32, 64), (5, 3))
+              for c, w in ((True, 0), (True, 9), (False, 0), (False, 5), (True, 1))]
+
+
+@pytest.mark.parametrize("Tq,Tk,bq,bk,causal,window", RECT_SWEEP)
+def test_rect_classifier_matches_oracle(Tq, Tk, bq, bk, causal, window):
+    """T query rows against Tk keys: the device classifier and key-block ranges equal the
+    oracle's brute force over the materialised mask."""
+    cls = oracle.classify_blocks(Tq, bq, bk, causal, window, Tk)
+    for i in range(cls.shape[0]):
+        for j in range(cls.shape[1]):
+            assert fa.flash_attn_block_class_qk(Tq, Tk, bq, bk, causal, window, i, j) == cls[i, j], (i, j)
+        want = oracle.kv_block_range(i, bq, bk, Tq, causal, window, Tk)
+        assert fa.flash_attn_kv_block_range_qk(Tq, Tk, bq, bk, causal, window, i) == want, i
+
+
+def test_square_helpers_equal_rect_helpers_at_equal_lengths():
+    for T, bq, bk, c, w in ((100, 32, 64, True, 0), (257, 128, 32, True, 7), (64, 16, 16, False, 3)):
+        for i in range(-(-T // bq)):
+            for j in range(-(-T // bk)):
+                assert (fa.flash_attn_block_class(T, bq, bk, c, w, i, j)[0]
+                        == fa.flash_attn_block_class_qk(T, T, bq, bk, c, w, i, j))

@@ -28,8 +28,10 @@ ATTN_MUTANTS = {
                          "dk[b, :, g, :] += scale * (dS.T @ dOc)"),
     "dv_transposed_P": ("dv[b, :, g, :] += P.T @ dOc", "dv[b, :, g, :] += P @ dOc"),
     "gqa_modulo_map": ("return h // (H // HKV)", "return h % HKV"),
-    "causal_drops_diagonal": ("vis &= j <= i", "vis &= j < i"),
-    "window_off_by_one": ("vis &= j >= i - window + 1", "vis &= j >= i - window"),
+    "causal_drops_diagonal": ("vis &= j <= p", "vis &= j < p"),
+    "window_off_by_one": ("vis &= j >= p - window + 1", "vis &= j >= p - window"),
+    "rect_rows_top_aligned": ("p = i + (Tk - T)", "p = i"),
+    "rect_offset_sign": ("p = i + (Tk - T)", "p = i + (T - Tk)"),
     "lse_log2": ("L[b, h, rows] = np.where(l > 0, m + np.log(",
                  "L[b, h, rows] = np.where(l > 0, m + np.log2("),
     "fwd_missing_scale": ("S = scale * (q[b, rows, h, :] @ k[b, :, g, :].T)",
