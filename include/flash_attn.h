@@ -16,6 +16,7 @@
  *               doc comments; the module comment on the tensor layout.
  *   [metal5]    "flashback.metal" (FlashMetal): backprop_attention, its batch and head
  *               offset arithmetic.
+ *   [rope]      "qkv_rope.py" (modded-nanogpt): the fused QK-norm + rotary forward.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -190,6 +191,29 @@ fa_status_t flash_attn_bwd_dq_dvec(const void* Q, const void* K, const void* V, 
                                    int T, int H, int HKV, int D, float scale, int causal,
                                    int window, fa_dtype_t dtype, hipStream_t stream, int bq,
                                    int bk);
+
+/* QK RMS-norm + rotary prologue ([rope] "qkv_rope.py": module docstring, qk_norm_rope_forward
+ * and its forward kernel): from one packed QK projection qk [tokens, 2*heads, qk_dim] (query
+ * heads first; element strides qk_stride_t per token and qk_stride_h per head, qk_dim
+ * contiguous), each row x is normalised in fp32 as x * rsqrt(mean(x^2) + 2^-23) (no weight)
+ * and mixed with its pair-swapped copy (elements 2i and 2i+1 exchanged) through per-token
+ * float32 factor tables: y = factor1[t] * x + factor2[t] * swap(x) (tables [tokens, qk_dim],
+ * row stride factor_stride_t elements; a rotation has factor1 = cos, factor2 = -sin / +sin on
+ * even / odd elements).  Query rows go to out_q, key rows to out_k, both contiguous
+ * [tokens, heads, qk_dim] in `dtype`.
+ *   paired: logical head h of token t goes to token 2t + h / (heads/2), head h % (heads/2)
+ *     (outputs [2*tokens, heads/2, qk_dim]); odd h read the second half of double-width
+ *     tables [tokens, 2*qk_dim].  Needs an even head count; not with key_offset.
+ *   key_offset: for key heads of tokens t > 0 the elements from rotary_dim on are the previous
+ *     token's normalised row instead (rotary_dim even, <= qk_dim).
+ * qk_dim in {16, 32, 64, 128, 256} (FA_ERR_UNSUPPORTED otherwise); dtype F32, BF16 or F16;
+ * every pointer 16-byte aligned, strides multiples of 16 bytes, qk_stride_h >= qk_dim and
+ * qk_stride_t >= (2*heads - 1) * qk_stride_h + qk_dim (a token's rows stored together). */
+fa_status_t flash_attn_qk_norm_rope(const void* qk, int64_t qk_stride_t, int64_t qk_stride_h,
+                                   const float* factor1, const float* factor2,
+                                   int64_t factor_stride_t, void* out_q, void* out_k, int tokens,
+                                   int heads, int qk_dim, int rotary_dim, int paired,
+                                   int key_offset, fa_dtype_t dtype, hipStream_t stream);
 
 /* ---- host-only helpers (no GPU needed) ---- */
 

@@ -7,6 +7,7 @@ this package is its thin Python binding.  Build with
 from .api import (FlashAttnError, flash_attn_fwd, flash_attn_bwd, flash_attn_bwd_preprocess,
                   flash_attn_bwd_dkdv, flash_attn_bwd_dq, flash_attn_bwd_dq_dvec,
                   flash_attn_fwd_strided, flash_attn_bwd_strided, flash_attn_bwd_grad16,
+                  flash_attn_qk_norm_rope,
                   flash_attn_block_class, flash_attn_block_class_qk, flash_attn_kv_block_range_qk,
                   flash_attn_kv_block_range, flash_attn_default_tiles, flash_attn_check_layout,
                   flash_attn_version)
@@ -15,6 +16,7 @@ from ._lib import LIB_PATH, EXPORTS
 __all__ = ["FlashAttnError", "flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_preprocess",
            "flash_attn_bwd_dkdv", "flash_attn_bwd_dq", "flash_attn_bwd_dq_dvec",
            "flash_attn_fwd_strided", "flash_attn_bwd_strided", "flash_attn_bwd_grad16",
+           "flash_attn_qk_norm_rope",
            "flash_attn_block_class", "flash_attn_block_class_qk", "flash_attn_kv_block_range_qk",
            "flash_attn_kv_block_range", "flash_attn_default_tiles", "flash_attn_check_layout",
            "flash_attn_version",

@@ -16,7 +16,7 @@ EXPORTS = [
     "flash_attn_bwd_preprocess", "flash_attn_bwd_dkdv", "flash_attn_bwd_dq",
     "flash_attn_bwd_dq_dvec", "flash_attn_fwd_strided", "flash_attn_bwd_strided",
     "flash_attn_check_layout", "flash_attn_bwd_grad16", "flash_attn_block_class_qk",
-    "flash_attn_kv_block_range_qk",
+    "flash_attn_kv_block_range_qk", "flash_attn_qk_norm_rope",
     "flash_attn_status_string", "flash_attn_block_class", "flash_attn_kv_block_range",
     "flash_attn_default_tiles", "flash_attn_version",
 ]
@@ -48,6 +48,8 @@ def _declare(lib):
         "flash_attn_fwd_strided": [P] * 5 + _DIMS_QK + [Layout, Layout],
         "flash_attn_bwd_strided": [P] * 9 + _DIMS_QK + [Layout, Layout],
         "flash_attn_block_class_qk": [I] * 8,
+        "flash_attn_qk_norm_rope": [P, ctypes.c_int64, ctypes.c_int64, P, P, ctypes.c_int64, P, P,
+                                    I, I, I, I, I, I, I, P],
         "flash_attn_kv_block_range_qk": [I] * 7 + [ctypes.POINTER(I), ctypes.POINTER(I)],
         "flash_attn_check_layout": [Layout, I, I, I, I, I],
         "flash_attn_bwd_grad16": [P] * 9 + _DIMS_QK + [Layout, Layout],

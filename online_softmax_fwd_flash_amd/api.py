@@ -264,6 +264,39 @@ def flash_attn_bwd_grad16(q, k, v, o, lse, do, causal=True, window=0, scale=None
     return dq, dk, dv
 
 
+def flash_attn_qk_norm_rope(qk, factor1, factor2, heads, rotary_dim=None, paired=False,
+                            key_offset=False, out_q=None, out_k=None, stream=None):
+    """(out_q, out_k) from a packed QK projection qk [tokens, 2*heads, D] (last axis
+    contiguous, any token / head strides) and float32 factor tables [tokens, D] ([tokens, 2D]
+    when paired): RMS-norm without weight, then y = factor1 * x + factor2 * pair_swap(x)."""
+    if qk.dim() != 3 or qk.stride(2) != 1 or not qk.is_cuda:
+        raise ValueError("qk: expected a cuda [tokens, 2*heads, D] tensor, last axis contiguous")
+    tokens, heads2, D = qk.shape
+    if heads2 != 2 * heads:
+        raise ValueError("qk: second axis must be 2 * heads")
+    rotary_dim = D if rotary_dim is None else rotary_dim
+    width = D * (2 if paired else 1)
+    for name, f in (("factor1", factor1), ("factor2", factor2)):
+        if (f.dtype != torch.float32 or not f.is_cuda or f.dim() != 2
+                or tuple(f.shape) != (tokens, width) or f.stride(1) != 1
+                or f.stride() != factor1.stride()):
+            raise ValueError(f"{name}: expected float32 cuda [{tokens}, {width}], last axis "
+                             "contiguous, both tables with the same strides")
+    shape = (2 * tokens, heads // 2, D) if paired else (tokens, heads, D)
+    out_q = torch.empty(shape, device=qk.device, dtype=qk.dtype) if out_q is None else out_q
+    out_k = torch.empty(shape, device=qk.device, dtype=qk.dtype) if out_k is None else out_k
+    _want(out_q, shape, qk.dtype, "out_q")
+    _want(out_k, shape, qk.dtype, "out_k")
+    code = _lib.lib().flash_attn_qk_norm_rope(_ptr(qk), qk.stride(0), qk.stride(1),
+                                              _ptr(factor1), _ptr(factor2), factor1.stride(0),
+                                              _ptr(out_q), _ptr(out_k), tokens, heads, D,
+                                              int(rotary_dim), int(bool(paired)),
+                                              int(bool(key_offset)), _DT[qk.dtype],
+                                              _stream(stream))
+    _check("flash_attn_qk_norm_rope", code)
+    return out_q, out_k
+
+
 def flash_attn_block_class(T, bq, bk, causal, window, i, j):
     """(class, off) of block (i, j): class 0 skip, 1 full, 2 masked; off = i*bq - j*bk."""
     off = ctypes.c_int(0)

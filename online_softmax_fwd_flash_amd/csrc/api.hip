@@ -400,4 +400,39 @@ fa_status_t flash_attn_bwd_grad16(const void* Q, const void* K, const void* V, c
                     stream, 0, 0, q_layout, kv_layout, 1);
 }
 
+fa_status_t flash_attn_qk_norm_rope(const void* qk, int64_t qk_stride_t, int64_t qk_stride_h,
+                                   const float* factor1, const float* factor2,
+                                   int64_t factor_stride_t, void* out_q, void* out_k, int tokens,
+                                   int heads, int qk_dim, int rotary_dim, int paired,
+                                   int key_offset, fa_dtype_t dtype, hipStream_t stream) {
+    fa_status_t s = check_ptrs({qk, factor1, factor2, out_q, out_k});
+    if (s != FA_OK) return s;
+    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16)
+        return FA_ERR_INVALID_ARG;
+    if (tokens < 1 || heads < 1 || (paired != 0 && paired != 1) ||
+        (key_offset != 0 && key_offset != 1) || (paired && key_offset) || (paired && heads % 2))
+        return FA_ERR_INVALID_ARG;
+    if (!(qk_dim == 16 || qk_dim == 32 || qk_dim == 64 || qk_dim == 128 || qk_dim == 256))
+        return FA_ERR_UNSUPPORTED;
+    if (rotary_dim < 0 || rotary_dim > qk_dim || rotary_dim % 2) return FA_ERR_INVALID_ARG;
+    const int64_t esz = dtype == FA_DTYPE_F32 ? 4 : 2, align = 16 / esz;
+    // rows of a token stored together, heads at least D apart, 16-byte aligned
+    if (qk_stride_h < qk_dim || qk_stride_h % align) return FA_ERR_INVALID_ARG;
+    if (qk_stride_t < (int64_t)(2 * heads - 1) * qk_stride_h + qk_dim || qk_stride_t % align)
+        return FA_ERR_INVALID_ARG;
+    if (factor_stride_t < (int64_t)qk_dim * (paired ? 2 : 1) || factor_stride_t % 4)
+        return FA_ERR_INVALID_ARG;
+    if ((double)tokens * qk_stride_t * esz > 9.0e18 || (double)tokens * 2 * heads * qk_dim > 4.0e12)
+        return FA_ERR_INVALID_ARG;
+    fa::RopeArgs a{};
+    a.qk = qk; a.st = qk_stride_t; a.sh = qk_stride_h;
+    a.f1 = factor1; a.f2 = factor2; a.fst = factor_stride_t;
+    a.out_q = out_q; a.out_k = out_k;
+    a.tokens = tokens; a.heads = heads; a.D = qk_dim; a.rotary_dim = rotary_dim;
+    a.paired = paired; a.key_offset = key_offset;
+    a.dtype = dtype == FA_DTYPE_F32 ? 0 : dtype == FA_DTYPE_BF16 ? 1 : 2;
+    a.stream = stream;
+    return hip_status(fa::launch_qk_norm_rope(a));
+}
+
 }  // extern "C"

@@ -54,6 +54,23 @@ hipError_t launch_dq_b16(const AttnArgs& a);
 // to a.Dvec (the dK/dV pass launched after it reads those values)
 hipError_t launch_dq_b16_fused_d(const AttnArgs& a);
 
+// QK RMS-norm + rotary prologue: qk [tokens, 2*heads, D] with element strides st (token),
+// sh (head); float32 factor tables [tokens, D * (paired ? 2 : 1)] with row stride fst;
+// out_q / out_k contiguous [tokens, heads, D] ([2*tokens, heads/2, D] when paired).
+struct RopeArgs {
+    const void* qk;
+    int64_t st, sh;
+    const float* f1;
+    const float* f2;
+    int64_t fst;
+    void* out_q;
+    void* out_k;
+    int tokens, heads, D, rotary_dim, paired, key_offset;
+    int dtype;   // 0 = f32, 1 = bf16, 2 = fp16
+    hipStream_t stream;
+};
+hipError_t launch_qk_norm_rope(const RopeArgs& a);
+
 // dtype: 0 = f32, 1 = bf16, 2 = fp16
 hipError_t launch_bwd_preprocess(const void* O, const void* dO, float* Dvec, int B, int T,
                                  int H, int D, int dtype, hipStream_t stream, Layout lq);

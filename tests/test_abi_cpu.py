@@ -243,3 +243,20 @@ def test_square_helpers_equal_rect_helpers_at_equal_lengths():
             for j in range(-(-T // bk)):
                 assert (fa.flash_attn_block_class(T, bq, bk, c, w, i, j)[0]
                         == fa.flash_attn_block_class_qk(T, T, bq, bk, c, w, i, j))
+
+
+def rope(qk=A, f1=A, f2=A, oq=A, ok=A, st=8 * 128, sh=128, fst=128, tokens=4, heads=4, D=128,
+         rd=128, paired=0, key_offset=0, dtype=1):
+    return _lib.lib().flash_attn_qk_norm_rope(qk, st, sh, f1, f2, fst, oq, ok, tokens, heads, D,
+                                              rd, paired, key_offset, dtype, S0)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(qk=NUL), 1), (dict(oq=MIS), 1), (dict(tokens=0), 1), (dict(heads=0), 1),
+    (dict(D=96), 2), (dict(D=512), 2), (dict(rd=130), 1), (dict(rd=7), 1), (dict(rd=-2), 1),
+    (dict(paired=1, key_offset=1), 1), (dict(paired=1, heads=3, st=6 * 128), 1),
+    (dict(paired=2), 1), (dict(sh=64), 1), (dict(sh=132), 1), (dict(st=7 * 128), 1),
+    (dict(fst=64), 1), (dict(fst=130), 1), (dict(paired=1, fst=128), 1), (dict(dtype=5), 1),
+])
+def test_rope_rejects_before_launch(kw, code):
+    assert rope(**kw) == code
