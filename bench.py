@@ -110,6 +110,38 @@ def cpu_baseline(cfg, budget_s=10.0):
                       f"{dt:.1f} s wall; host has {cores} usable cores"}
 
 
+def time_prologue(cfg, steps, warmup):
+    """flash_attn_qk_norm_rope on the workload's B*T tokens (packed QK of 2*H heads of D), the
+    average of `steps` launches by HIP events on the launch stream.  Algorithmic bytes: the QK
+    projection read once, Q and K written once, both factor tables read once."""
+    import torch
+    import online_softmax_fwd_flash_amd as fa
+    from workloads import make_qk_packed, rotary_tables
+    tokens, heads, D = cfg.B * cfg.T, cfg.H, cfg.D
+    dev = torch.device("cuda:0")
+    qk = make_qk_packed(tokens, heads, D, cfg.dtype, seed=cfg.seed).to(dev)
+    f1, f2 = (t.to(dev) for t in rotary_tables(tokens, D, D))
+    oq = torch.empty(tokens, heads, D, device=dev, dtype=qk.dtype)
+    ok = torch.empty_like(oq)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fa.flash_attn_qk_norm_rope(qk, f1, f2, heads, out_q=oq, out_k=ok)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for _ in range(steps):
+        fa.flash_attn_qk_norm_rope(qk, f1, f2, heads, out_q=oq, out_k=ok)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    esz = qk.element_size()
+    nbytes = 2 * tokens * 2 * heads * D * esz + 2 * tokens * D * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": f"qk_norm_rope {cfg.dtype} tokens={tokens} heads={heads} D={D}",
+            "ms": round(ms, 4), "bound": "hbm", "bytes": nbytes, "achieved": round(gbs, 1),
+            "unit": "GB/s", "peak": 8000.0, "frac": round(gbs / 8000.0, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -118,6 +150,10 @@ def main():
     ap.add_argument("--config", default="C4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--prologue", action="store_true",
+                    help="also time the QK RMS-norm + rotary prologue on the workload's tokens "
+                         "(B*T tokens, H heads, D, in the workload dtype) and report it in its "
+                         "own 'prologue' object")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, copy a 512 MiB device buffer once (a plain copy of known "
                          "size, for scaling hardware byte counters)")
@@ -239,6 +275,8 @@ def main():
         wa = 4.0 * D * vis
         out["fwd_tflops_window_aware"] = round(wa / (fwd_ms * 1e-3) / 1e12, 2)
         out["fwd_bwd_tflops_window_aware"] = round(3.5 * wa / (ms_step * 1e-3) / 1e12, 2)
+    if args.prologue:
+        out["prologue"] = time_prologue(cfg, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
     print(json.dumps(out), flush=True)
