@@ -35,7 +35,7 @@ struct AttnArgs {
     int g16;         // 16-bit kernels: 1 = dQ, dK, dV stored in the element type, 0 = float32
 };
 
-// Tilings of the bf16 kernels: query rows x keys handled per workgroup block.  Each kernel
+// Tilings of the 16-bit kernels: query rows x keys handled per workgroup block.  Each kernel
 // translation unit static_asserts its own constants against these.
 constexpr int kB16FwdBq = 128, kB16FwdBk = 32;    // forward: q-tile x staged key block
 constexpr int kB16DkdvBq = 32, kB16DkdvBk = 64;   // dK/dV: staged query block x key tile

@@ -1,5 +1,5 @@
-// Staging of bf16 [rows x D] tiles from HBM into row-major LDS tiles for the MFMA kernels,
-// plus the operand-read helpers that work on those tiles.
+// Staging of 16-bit (bf16 or fp16) [rows x D] tiles from HBM into row-major LDS tiles for the
+// MFMA kernels, plus the operand-read helpers that work on those tiles.
 //
 // gfx950 LDS has 128 four-byte banks.  Measured on MI355X: a 16-byte-per-lane read serves 32
 // lanes per cycle, and an 8-byte transpose read (ds_read_b64_tr_b16) 64 lanes; row strides
@@ -27,7 +27,7 @@ struct Buf {
     }
 };
 
-// Buffer over rows [0, T) of one head: rows of D bf16 elements, `ld` elements apart
+// Buffer over rows [0, T) of one head: rows of D 16-bit elements, `ld` elements apart
 // (ld >= D).  It ends with the last row's D elements, so reads at rows past T return zeros
 // whatever the layout puts there.
 template <int D>
@@ -51,7 +51,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 // after the barrier once that wave has waited for those loads (wait_vmcnt).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// Unpadded row-major [rows x D] bf16 tile in LDS whose 16-byte chunks are XOR-swizzled per
+// Unpadded row-major [rows x D] 16-bit tile in LDS whose 16-byte chunks are XOR-swizzled per
 // row, filled by LDS-DMA (buffer_load ... lds, 16 bytes per lane: a wave instruction writes
 // 1 KB of consecutive LDS bytes).  The swizzle serves tiles read with ds_read_b64_tr_b16
 // (8 consecutive rows x 4 adjacent chunks per wave): XOR with a multiple of 4 keeps the 4
@@ -74,7 +74,7 @@ __device__ __forceinline__ uint32_t dma_src_offset_swz(int p, int lane, uint32_t
     return (uint32_t)r * ld_bytes + 16u * (uint32_t)(pc ^ S::v(r));
 }
 
-// Padded row-major [rows x D] bf16 tile filled by LDS-DMA: rows are D + 8*PADC elements
+// Padded row-major [rows x D] 16-bit tile filled by LDS-DMA: rows are D + 8*PADC elements
 // apart.  Measured on gfx950 (128 banks, 32 lanes serviced together): 16-byte reads of 32
 // consecutive rows at one chunk are conflict-free at D + 8 and D + 24 (an odd number of
 // 16-byte slots per row whose product with 16 rows is not a multiple of the 512-byte bank
