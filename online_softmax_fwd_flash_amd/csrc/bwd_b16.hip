@@ -72,8 +72,8 @@ struct Dkdv16Cfg {
     static_assert(TPIECES * 1024 == BQ * PadT::ROWB, "tile must be whole pieces");
 };
 
-// LDS-DMA of the stage of iteration it (query block ihi - 1 - it / rep of head it % rep)
-// into buffer it % 2.  The first half of the waves fill the Q tile (pieces w, w + NW/2, ...),
+// LDS-DMA of the stage of query block i2 of head h2 (the group's h2-th query head) into
+// buffer `buf`.  The first half of the waves fill the Q tile (pieces w, w + NW/2, ...),
 // the second half the dO tile; wave 0 also moves the block's L values, wave 1 its D values.
 // Q / dO rows reach LDS through one descriptor for the whole KV group when the group's heads
 // lie inside each row (row stride >= (rep - 1) * head stride + D, as in [B, T, H, D]): rows
@@ -89,10 +89,9 @@ struct QdoSrc {
 template <int D>
 __device__ __forceinline__ void dkdv16_issue(char* sm, const QdoSrc& qs, const float* Lg,
                                              const float* Dg, const uint32_t* voff, int w,
-                                             int rep, int ihi, int T, int it) {
+                                             int h2, int i2, int T, int buf) {
     using C = Dkdv16Cfg<D>;
-    const int h2 = it % rep, i2 = ihi - 1 - it / rep;
-    char* st = sm + (it & 1) * C::STAGE;
+    char* st = sm + buf * C::STAGE;
     const uint32_t rows = (uint32_t)i2 * C::BQ * (uint32_t)(qs.ldq * 2);
     const int tso = __builtin_amdgcn_readfirstlane(
         (int)(qs.grp ? rows + (uint32_t)(h2 * qs.qh * 2) : rows));
@@ -198,13 +197,20 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv_b16_kernel(
     // Query blocks are walked last-first (heads inner): every key block of a KV group needs
     // the last query blocks, so the group's co-resident workgroups (same XCD) stream the same
     // Q / dO blocks at about the same time and share them in L2.
-    if (niter > 0) dkdv16_issue<D>(sm, qs, Lg, Dg, voff, w, rep, ihi, T, 0);
+    // iteration it takes query block ihi - 1 - it / rep of head it % rep; (h2n, in) steps
+    // through that sequence one iteration ahead (no divisions in the loop)
+    int h2n = 0, in = ihi - 1;
+    if (niter > 0) dkdv16_issue<D>(sm, qs, Lg, Dg, voff, w, h2n, in, T, 0);
     for (int it = 0; it < niter; ++it) {
-        const int i = ihi - 1 - it / rep;
+        const int i = in;
+        if (++h2n == rep) {
+            h2n = 0;
+            --in;
+        }
         wait_vmcnt<0>();   // this stage's pieces, the only loads in flight
         // every wave's pieces are visible; every wave is done with the other stage
         lds_barrier();
-        if (it + 1 < niter) dkdv16_issue<D>(sm, qs, Lg, Dg, voff, w, rep, ihi, T, it + 1);
+        if (it + 1 < niter) dkdv16_issue<D>(sm, qs, Lg, Dg, voff, w, h2n, in, T, (it + 1) & 1);
         const int qr0 = i * C::BQ;
         const int cls = block_class(T, Tk, qr0, qr0 + C::BQ, kw0, kw0 + C::KPW, cz, window);
         if (cls == kSkip) continue;
@@ -231,22 +237,32 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv_b16_kernel(
                 dp[qb] = mfma16x16x32(ao[ds], vreg[ds], dp[qb]);
             }
         }
-        V8 pp[C::KKS], pd[C::KKS];
+        // rows past T have L = D = 0 and zero Q / dO: they add nothing
 #pragma unroll
         for (int qb = 0; qb < C::QB16; ++qb) {
             const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + qb * 16 + 4 * g);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sc[qb][r] = fast_exp2(fmaf(sc[qb][r], c, -l4[r] * kLog2e));
+        }
+        if (cls == kPartial) {
+            keep_branch();
+#pragma unroll
+            for (int qb = 0; qb < C::QB16; ++qb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int qi = qr0 + qb * 16 + 4 * g + r;
+                    if ((unsigned)(qi - qlo) >= (unsigned)qn) sc[qb][r] = 0.f;
+                }
+        }
+        V8 pp[C::KKS], pd[C::KKS];
+#pragma unroll
+        for (int qb = 0; qb < C::QB16; ++qb) {
             const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + qb * 16 + 4 * g);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                // rows past T have L = D = 0 and zero Q / dO: they add nothing
-                float p = fast_exp2(fmaf(sc[qb][r], c, -l4[r] * kLog2e));
-                if (cls == kPartial) {
-                    const int qi = qr0 + qb * 16 + 4 * g + r;
-                    p = ((unsigned)(qi - qlo) >= (unsigned)qn) ? 0.f : p;
-                }
                 // k-step kk = qb/2 takes rows of blocks 2kk (elements 0-3), 2kk+1 (4-7)
-                pp[qb >> 1][4 * (qb & 1) + r] = (S16)p;
-                pd[qb >> 1][4 * (qb & 1) + r] = (S16)(p * (dp[qb][r] - d4[r]));
+                pp[qb >> 1][4 * (qb & 1) + r] = (S16)sc[qb][r];
+                pd[qb >> 1][4 * (qb & 1) + r] = (S16)(sc[qb][r] * (dp[qb][r] - d4[r]));
             }
         }
         // dV += P^T dO and dK += dS^T Q, 32 query rows per k-step
@@ -450,6 +466,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_b16_kernel(
                 dk[r] = dk[r] - dq_i;
             }
             if (cls == kPartial) {
+                keep_branch();
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int kk = j * C::BK + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);

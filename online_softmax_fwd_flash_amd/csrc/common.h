@@ -118,6 +118,11 @@ struct F16 {
     typedef f16x2 v2;
 };
 
+// Placed first in the body of a wave-uniform `if`, keeps it a branch: the compiler does not
+// speculate an asm statement with side effects, so it cannot flatten the body into selects
+// executed on every path (the diagonal-block masks would otherwise run on every block).
+__device__ __forceinline__ void keep_branch() { asm volatile(""); }
+
 // x unchanged, but opaque to the compiler: a float result rounded to 16 bits after this is
 // rounded from its float32 value (the compiler may otherwise fold the product feeding a
 // conversion into a mixed-precision multiply that rounds only once, to 16 bits).

@@ -96,7 +96,7 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_b16_kernel(
     const int hk = h / (H / HKV);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int n = lane & 31, g = lane >> 5;
-    const int wr0 = qt * kBQ + w * 32;
+    const int wr0 = qt * kBQ + __builtin_amdgcn_readfirstlane(w) * 32;   // wave-uniform: scalar block tests
     const int q = wr0 + n;
     const int64_t ldq = lq.t, ldk = lk.t;   // row strides (elements)
     const uint32_t ldk_b = (uint32_t)(ldk * 2);
@@ -189,6 +189,7 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_b16_kernel(
         }
         __builtin_amdgcn_sched_group_barrier(0x008, (kNH * C::DC) / 2, 0);
         if (cls == kPartial) {
+            keep_branch();
 #pragma unroll
             for (int hk = 0; hk < kNH; ++hk)
 #pragma unroll
@@ -216,12 +217,13 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_b16_kernel(
         float ps[kNH];
 #pragma unroll
         for (int hk = 0; hk < kNH; ++hk) {
-            ps[hk] = 0.f;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                s[hk][r] = fast_exp2(fmaf(s[hk][r], c, -mc));
-                ps[hk] += s[hk][r];
-            }
+            for (int r = 0; r < 16; ++r) s[hk][r] = fast_exp2(fmaf(s[hk][r], c, -mc));
+            // pairwise sum: a dependency chain of 4 adds instead of 16
+            float t4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) t4[i] = (s[hk][i] + s[hk][4 + i]) + (s[hk][8 + i] + s[hk][12 + i]);
+            ps[hk] = (t4[0] + t4[1]) + (t4[2] + t4[3]);
         }
 #pragma unroll
         for (int hk = 0; hk < kNH; ++hk) lsum += ps[hk];
