@@ -207,12 +207,13 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv_b16_kernel(
             h2n = 0;
             --in;
         }
+        // scalar block test before the wait, where it costs nothing
+        const int qr0 = i * C::BQ;
+        const int cls = block_class(T, Tk, qr0, qr0 + C::BQ, kw0, kw0 + C::KPW, cz, window);
         wait_vmcnt<0>();   // this stage's pieces, the only loads in flight
         // every wave's pieces are visible; every wave is done with the other stage
         lds_barrier();
         if (it + 1 < niter) dkdv16_issue<D>(sm, qs, Lg, Dg, voff, w, h2n, in, T, (it + 1) & 1);
-        const int qr0 = i * C::BQ;
-        const int cls = block_class(T, Tk, qr0, qr0 + C::BQ, kw0, kw0 + C::KPW, cz, window);
         if (cls == kSkip) continue;
         const char* stg = sm + (it & 1) * C::STAGE;
         const uint16_t* Qn = reinterpret_cast<const uint16_t*>(stg);
@@ -430,11 +431,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_b16_kernel(
     if (jlo < jhi) dq_issue<D, NW>(sm, kbuf, vbuf, voff, w, ldk_b, jlo);
     for (int j = jlo; j < jhi; ++j) {
         const int stg = (j - jlo) & 1;
+        // scalar block test before the wait, where it costs nothing
+        const int cls = block_class(T, Tk, wr0, wr0 + 32, j * C::BK, j * C::BK + C::BK, cz, window);
         wait_vmcnt<0>();   // block j's pieces, the only loads in flight
         // every wave's pieces are visible; every wave is done with the other stage
         lds_barrier();
         if (j + 1 < jhi) dq_issue<D, NW>(sm + (stg ^ 1) * C::STAGE, kbuf, vbuf, voff, w, ldk_b, j + 1);
-        const int cls = block_class(T, Tk, wr0, wr0 + 32, j * C::BK, j * C::BK + C::BK, cz, window);
         if (cls == kSkip) continue;
         const uint16_t* Kn = reinterpret_cast<const uint16_t*>(sm + stg * C::STAGE);
         const uint16_t* Vn = reinterpret_cast<const uint16_t*>(sm + stg * C::STAGE + C::OFF_V);

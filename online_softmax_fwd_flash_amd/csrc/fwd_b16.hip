@@ -155,11 +155,12 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_b16_kernel(
 
     for (int j = jlo; j < jhi; ++j) {
         const int stg = (j - jlo) & 1;
+        // scalar block test before the wait, where it costs nothing
+        const int cls = block_class(T, Tk, wr0, wr0 + 32, j * kBK, j * kBK + kBK, cz, window);
         wait_vmcnt<0>();   // block j's pieces, the only ones in flight
         // all pieces visible; every wave is done with the other stage (block j - 1)
         lds_barrier();
         if (j + 1 < jhi) fwd_issue<D>(kbuf, vbuf, koff, voff, sm + (stg ^ 1) * C::STAGEB, wu, ldk_b, j + 1);
-        const int cls = block_class(T, Tk, wr0, wr0 + 32, j * kBK, j * kBK + kBK, cz, window);
         if (cls == kSkip) continue;
         const char* sb = sm + stg * C::STAGEB;
         // S^T for the block's 32-key halves: entry r of lane (n, g) in s[hk] is key
