@@ -80,6 +80,53 @@ FA_HD void q_block_range(int Tq, int Tk, int c0, int c1, int bq, bool causal, in
     hi = last / bq + 1;
 }
 
+// floor(a / b) for b > 0 and any a.
+FA_HD int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+
+// Key blocks j (keys [j*bk, j*bk + bk)) that are FULL for rows [r0, r1), as [lo, hi) (empty
+// when hi <= lo): every key in range (c1 <= Tk), before the causal bound of the first row
+// and inside the window of the last row.  Inside it block_class returns kFull; the kernels
+// call block_class only outside it.
+FA_HD void full_kv_block_range(int Tq, int Tk, int r0, int r1, int bk, bool causal, int window,
+                               int& lo, int& hi) {
+    if (r1 > Tq) r1 = Tq;
+    lo = hi = 0;
+    if (r0 >= r1) return;
+    const int dq = Tk - Tq;
+    const int p0 = r0 + dq, P = r1 - 1 + dq;
+    int h = Tk / bk;                                          // (j + 1) bk <= Tk
+    if (causal) {                                             // (j + 1) bk - 1 <= p0
+        const int hc = floor_div(p0 + 1, bk);
+        if (hc < h) h = hc;
+    }
+    int l = 0;
+    if (window > 0 && P - window + 1 > 0) l = (P - window + 1 + bk - 1) / bk;   // j bk >= P - W + 1
+    if (h > l) {
+        lo = l;
+        hi = h;
+    }
+}
+
+// Query blocks i (rows [i*bq, i*bq + bq)) that are FULL for keys [c0, c1), as [lo, hi): the
+// transposed form for key-owned passes.
+FA_HD void full_q_block_range(int Tq, int Tk, int c0, int c1, int bq, bool causal, int window,
+                              int& lo, int& hi) {
+    lo = hi = 0;
+    if (c0 >= c1 || c1 > Tk) return;
+    const int dq = Tk - Tq;
+    int l = 0;
+    if (causal && c1 - 1 - dq > 0) l = (c1 - 1 - dq + bq - 1) / bq;   // i bq + dq >= c1 - 1
+    int h = (Tq + bq - 1) / bq;                                          // i bq < Tq
+    if (window > 0 && Tq > c0 + window - dq) {                           // last row inside
+        const int hw = floor_div(c0 + window - dq, bq);                  // (i + 1) bq <= c0 + W - dq
+        if (hw < h) h = hw;
+    }
+    if (h > l) {
+        lo = l;
+        hi = h;
+    }
+}
+
 // Per-element keep test in global indices (used inside PARTIAL blocks).
 FA_HD bool visible(int r, int c, int Tq, int Tk, bool causal, int window) {
     const int p = r + Tk - Tq;

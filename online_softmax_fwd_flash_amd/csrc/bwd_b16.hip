@@ -99,9 +99,11 @@ __device__ __forceinline__ void dkdv16_issue(char* sm, const QdoSrc& qs, const f
     char* dst = st + (w / C::QW) * C::OFF_DO;
     const Buf src = qs.grp ? (w < C::QW ? qs.q : qs.o)
                            : head_buf<D>((w < C::QW ? qs.Qg : qs.dOg) + h2 * qs.qh, qs.ldq, T);
+    // pieces wq + QW*i exist for every wave except possibly the last one
 #pragma unroll
     for (int i = 0; i < C::PMAX; ++i)
-        if (wq + C::QW * i < C::TPIECES) dma_piece(src, dst + (wq + C::QW * i) * 1024, voff[i], tso);
+        if (i < C::PMAX - 1 || wq + C::QW * i < C::TPIECES)
+            dma_piece(src, dst + (wq + C::QW * i) * 1024, voff[i], tso);
     if (w < 2) {
         const int rso = __builtin_amdgcn_readfirstlane(i2 * C::BQ * 4);
         // rows past T read as 0
@@ -178,6 +180,8 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv_b16_kernel(
 
     int ilo, ihi;
     q_block_range(T, Tk, kt * C::BKW, kt * C::BKW + C::BKW, C::BQ, cz, window, ilo, ihi);
+    int if0, if1;   // query blocks that are FULL for this wave's keys
+    full_q_block_range(T, Tk, kw0, kw0 + C::KPW, C::BQ, cz, window, if0, if1);
     const int niter = rep * (ihi - ilo);
     // the group's first query head; head h2 of the group is h2 * lq.h elements further
     const uint32_t ldq_b = (uint32_t)(ldq * 2);
@@ -207,9 +211,13 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv_b16_kernel(
             h2n = 0;
             --in;
         }
-        // scalar block test before the wait, where it costs nothing
+        // scalar block test before the wait, only outside the FULL range
         const int qr0 = i * C::BQ;
-        const int cls = block_class(T, Tk, qr0, qr0 + C::BQ, kw0, kw0 + C::KPW, cz, window);
+        int cls = kFull;
+        if (i < if0 || i >= if1) {
+            keep_branch();
+            cls = block_class(T, Tk, qr0, qr0 + C::BQ, kw0, kw0 + C::KPW, cz, window);
+        }
         wait_vmcnt<0>();   // this stage's pieces, the only loads in flight
         // every wave's pieces are visible; every wave is done with the other stage
         lds_barrier();
@@ -347,9 +355,11 @@ __device__ __forceinline__ void dq_issue(char* st, const Buf& kbuf, const Buf& v
     const int wt = w % C::TW;
     char* dst = st + (w / C::TW) * C::OFF_V;
     const Buf& src = w < C::TW ? kbuf : vbuf;
+    // pieces wt + TW*i exist for every wave except possibly the last one
 #pragma unroll
     for (int i = 0; i < C::PMAX; ++i)
-        if (wt + C::TW * i < C::TPIECES) dma_piece(src, dst + (wt + C::TW * i) * 1024, voff[i], soff);
+        if (i < C::PMAX - 1 || wt + C::TW * i < C::TPIECES)
+            dma_piece(src, dst + (wt + C::TW * i) * 1024, voff[i], soff);
 }
 
 }  // namespace
@@ -423,6 +433,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_b16_kernel(
 
     int jlo, jhi;
     kv_block_range(T, Tk, qt * C::BQ, qt * C::BQ + C::BQ, C::BK, cz, window, jlo, jhi);
+    int jf0, jf1;   // key blocks that are FULL for this wave's rows
+    full_kv_block_range(T, Tk, wr0, wr0 + 32, C::BK, cz, window, jf0, jf1);
     uint32_t voff[C::PMAX];
 #pragma unroll
     for (int i = 0; i < C::PMAX; ++i)
@@ -431,8 +443,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_b16_kernel(
     if (jlo < jhi) dq_issue<D, NW>(sm, kbuf, vbuf, voff, w, ldk_b, jlo);
     for (int j = jlo; j < jhi; ++j) {
         const int stg = (j - jlo) & 1;
-        // scalar block test before the wait, where it costs nothing
-        const int cls = block_class(T, Tk, wr0, wr0 + 32, j * C::BK, j * C::BK + C::BK, cz, window);
+        // scalar block test before the wait, only outside the FULL range
+        int cls = kFull;
+        if (j < jf0 || j >= jf1) {
+            keep_branch();
+            cls = block_class(T, Tk, wr0, wr0 + 32, j * C::BK, j * C::BK + C::BK, cz, window);
+        }
         wait_vmcnt<0>();   // block j's pieces, the only loads in flight
         // every wave's pieces are visible; every wave is done with the other stage
         lds_barrier();

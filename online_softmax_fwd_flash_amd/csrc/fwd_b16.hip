@@ -70,9 +70,11 @@ __device__ __forceinline__ void fwd_issue(const Buf& kb, const Buf& vb, const ui
                                           uint32_t ld_bytes, int jb) {
     using C = Bf16Fwd<D>;
     const int soff = __builtin_amdgcn_readfirstlane((int)((uint32_t)jb * kBK * ld_bytes));
+    // pieces wu + i*NW exist for every wave except possibly the last one
 #pragma unroll
     for (int i = 0; i < C::KMAX; ++i)
-        if (wu + i * C::NW < C::KPIECES) dma_piece(kb, stage + (wu + i * C::NW) * 1024, koff[i], soff);
+        if (i < C::KMAX - 1 || wu + i * C::NW < C::KPIECES)
+            dma_piece(kb, stage + (wu + i * C::NW) * 1024, koff[i], soff);
     char* vbase = stage + C::KTILEB + wu * C::VPW * 1024;
 #pragma unroll
     for (int i = 0; i < C::VPW; ++i) dma_piece(vb, vbase + i * 1024, voff[i], soff);
@@ -125,6 +127,8 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_b16_kernel(
 
     int jlo, jhi;
     kv_block_range(T, Tk, qt * kBQ, qt * kBQ + kBQ, kBK, cz, window, jlo, jhi);
+    int jf0, jf1;   // key blocks that are FULL for this wave's rows
+    full_kv_block_range(T, Tk, wr0, wr0 + 32, kBK, cz, window, jf0, jf1);
 
     // LDS-DMA source offsets of this lane in its wave's pieces of a K / V tile
     const int wu = __builtin_amdgcn_readfirstlane(w);
@@ -155,8 +159,12 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_b16_kernel(
 
     for (int j = jlo; j < jhi; ++j) {
         const int stg = (j - jlo) & 1;
-        // scalar block test before the wait, where it costs nothing
-        const int cls = block_class(T, Tk, wr0, wr0 + 32, j * kBK, j * kBK + kBK, cz, window);
+        // scalar block test before the wait, only outside the FULL range
+        int cls = kFull;
+        if (j < jf0 || j >= jf1) {
+            keep_branch();
+            cls = block_class(T, Tk, wr0, wr0 + 32, j * kBK, j * kBK + kBK, cz, window);
+        }
         wait_vmcnt<0>();   // block j's pieces, the only ones in flight
         // all pieces visible; every wave is done with the other stage (block j - 1)
         lds_barrier();
@@ -207,7 +215,8 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_b16_kernel(
         mx = halves_max(mx);
         const float mnew = vmax(m, mx);
         // a row whose max is still the -FLT_MAX start rescales on its first visible key
-        if (__any(mnew > m && (m == kNegMax || (mnew - m) * c > 8.0f))) {
+        // (bitwise operators: one vector-compare sequence, no branches)
+        if (__any((mnew > m) & ((m == kNegMax) | ((mnew - m) * c > 8.0f)))) {
             const float corr = fast_exp2((m - mnew) * c);
             m = mnew;
             lsum *= corr;
