@@ -21,6 +21,10 @@
 // row-major tiles through LDS transpose reads.  K and V of the wave's 16 keys stay in
 // registers.
 //
+// In both passes the dP accumulators start at -D of their query rows, so the MFMAs leave
+// dP - D and dS = P (dP - D) costs one multiply per score; the per-block class test runs only
+// outside each wave's precomputed range of FULL blocks, and the diagonal mask is a branch.
+//
 // dQ pass (32x32x16 MFMA).  Workgroup = 4 waves x 32 query rows of one (b, h), two
 // workgroups per CU, walking its key blocks of 64; K and V reach LDS by LDS-DMA (padded
 // rows, double-buffered).  S^T = K Q^T and dP^T = V dO^T keep a query per accumulator

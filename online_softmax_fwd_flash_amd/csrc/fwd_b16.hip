@@ -30,6 +30,10 @@
 //  * Work order: longest key ranges (last query tiles) first; with GQA the query heads of one
 //    KV head are placed on the same XCD (workgroup ids congruent mod 8) at the same time so
 //    they share its K/V in that XCD's L2.
+//  * Scalar and vector overhead per block is kept small, since a SIMD issues at most one
+//    instruction of each kind per 4-cycle slot: each wave computes once the range of key
+//    blocks that are FULL for its rows and runs the class test only outside it, and the
+//    diagonal mask is a real branch (keep_branch) rather than selects on every block.
 #include "common.h"
 #include "kernels.h"
 #include "stage_b16.h"
