@@ -84,3 +84,13 @@ def test_f16_forward_large_scale_value():
     """As the bf16 case: scale above 1, masked rows in the first key block (forward; the
     absolute bounds are set for the 1/sqrt(D) scale the workloads use)."""
     check_case(1, 200, 4, 2, 64, "f16", True, 3, seed=150, backward=False, scale=1.7)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 64)])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("window", [31, 32, 33, 63, 64, 65, 128, 129])
+def test_window_at_block_edges(dtype, D, causal, window):
+    """Windows one key shorter or longer than a block (32 keys in the forward and per dK/dV
+    query block, 64 in dQ): where each wave's precomputed FULL blocks, which skip the class
+    test and the mask, begin and end."""
+    check_case(1, 300, 4, 2, D, dtype, causal, window, seed=150 + window)
