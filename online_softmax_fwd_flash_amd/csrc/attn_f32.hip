@@ -162,16 +162,26 @@ __global__ __launch_bounds__(BQ / 16 * 64) void fwd_f32_kernel(
 }
 
 // ------------------------------------------------------------------------------ dK / dV
-// One workgroup per (b, kv head, key block of BK keys); wave w owns keys [w*16, w*16+16) of
-// the block and loops over the query heads of the group and the query blocks that see them.
+// Keys per workgroup: BK, or several key blocks of BK when BK < 64, so that a workgroup has
+// four waves (a one-wave workgroup per 16-key block left one wave per SIMD, the Q / dO stage
+// filling the LDS).  Each wave's 16 keys lie inside one BK block, and every query x key
+// class test is per wave, so the BK blocking itself is unchanged.
+template <int BK>
+struct DkdvF32Keys {
+    static constexpr int KW = BK < 64 ? 64 : BK;
+};
+
+// One workgroup per (b, kv head, KW keys); wave w owns keys [w*16, w*16+16) of them and loops
+// over the query heads of the group and the query blocks that see them.
 template <int DP, int BQ, int BK>
-__global__ __launch_bounds__(BK / 16 * 64) void dkdv_f32_kernel(
+__global__ __launch_bounds__(DkdvF32Keys<BK>::KW / 16 * 64) void dkdv_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ L, const float* __restrict__ Dv,
     float* __restrict__ dK, float* __restrict__ dV, int B, int T, int Tk, int H, int HKV, int D,
     float scale, int causal, int window, int nkt, Layout lq, Layout lk) {
     using Tl = F32Tile<DP>;
-    constexpr int NW = BK / 16, NT = NW * 64, KS = Tl::KS, LD = Tl::LD, NDB = Tl::NDB;
+    constexpr int KW = DkdvF32Keys<BK>::KW;
+    constexpr int NW = KW / 16, NT = NW * 64, KS = Tl::KS, LD = Tl::LD, NDB = Tl::NDB;
     __shared__ __attribute__((aligned(16))) float Qs[BQ * LD];
     __shared__ __attribute__((aligned(16))) float dOs[BQ * LD];
     __shared__ float Ls[BQ], Ds[BQ];
@@ -183,7 +193,7 @@ __global__ __launch_bounds__(BK / 16 * 64) void dkdv_f32_kernel(
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index (uniform)
     const int n = lane & 15, g = lane >> 4;
-    const int kw0 = kt * BK + w * 16;
+    const int kw0 = kt * KW + w * 16;
     const int key = kw0 + n;
     const int64_t ldq = lq.t, ldk = lk.t;   // row strides (elements)
     const float* Kh = K + b * lk.b + hk * lk.h;
@@ -204,7 +214,7 @@ __global__ __launch_bounds__(BK / 16 * 64) void dkdv_f32_kernel(
     for (int i = 0; i < NDB; ++i) dka[i] = dva[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     int ilo, ihi;
-    q_block_range(T, Tk, kt * BK, kt * BK + BK, BQ, cz, window, ilo, ihi);
+    q_block_range(T, Tk, kt * KW, kt * KW + KW, BQ, cz, window, ilo, ihi);
     for (int hh = 0; hh < rep; ++hh) {
         const int h = hk * rep + hh;
         const float* Qh = Q + b * lq.b + h * lq.h;
@@ -379,9 +389,10 @@ hipError_t launch_fwd_f32_t(const AttnArgs& a) {
 
 template <int DP, int BQ, int BK>
 hipError_t launch_dkdv_f32_t(const AttnArgs& a) {
-    const int nkt = (a.Tk + BK - 1) / BK;
+    constexpr int KW = DkdvF32Keys<BK>::KW;
+    const int nkt = (a.Tk + KW - 1) / KW;
     const unsigned grid = (unsigned)nkt * a.B * a.HKV;
-    hipLaunchKernelGGL((dkdv_f32_kernel<DP, BQ, BK>), dim3(grid), dim3(BK / 16 * 64), 0,
+    hipLaunchKernelGGL((dkdv_f32_kernel<DP, BQ, BK>), dim3(grid), dim3(KW / 16 * 64), 0,
                        a.stream, (const float*)a.Q, (const float*)a.K, (const float*)a.V,
                        (const float*)a.dO, a.Lin, a.Dvec, a.dK, a.dV, a.B, a.T, a.Tk, a.H, a.HKV, a.D,
                        a.scale, a.causal, a.window, nkt, a.lq, a.lk);
