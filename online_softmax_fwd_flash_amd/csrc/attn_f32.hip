@@ -46,6 +46,37 @@ __device__ __forceinline__ void stage_rows(float* __restrict__ dst, const float*
     }
 }
 
+// The same ROWS x DP tile through registers: load() issues the global loads of the next block
+// while the current one is computed, store() writes them to LDS after the next barrier.  Used
+// by the dQ pass, where it measured 6.5% faster at 64 x 16 tiles, D = 64; the forward and
+// dK/dV passes measured 1-2% slower with it (more registers, no latency left to hide).
+template <int DP, int ROWS, int NT>
+struct RowPrefetch {
+    static constexpr int C4 = DP / 4;
+    static constexpr int PER = (ROWS * C4 + NT - 1) / NT;   // float4 per thread
+    f32x4 v[PER];
+    __device__ __forceinline__ void load(const float* __restrict__ base, int64_t ld, int row0,
+                                         int T, int D) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = (int)threadIdx.x + i * NT;
+            const int r = e / C4, d = (e % C4) * 4;
+            const int row = row0 + r;
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+            if (e < ROWS * C4 && row < T && d < D) x = *reinterpret_cast<const f32x4*>(base + (int64_t)row * ld + d);
+            v[i] = x;
+        }
+    }
+    __device__ __forceinline__ void store(float* __restrict__ dst) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = (int)threadIdx.x + i * NT;
+            if (e < ROWS * C4)
+                *reinterpret_cast<f32x4*>(dst + (e / C4) * F32Tile<DP>::LD + (e % C4) * 4) = v[i];
+        }
+    }
+};
+
 }  // namespace
 
 // ------------------------------------------------------------------------------ forward
@@ -329,11 +360,20 @@ __global__ __launch_bounds__(BQ / 16 * 64) void dq_f32_kernel(
 
     int jlo, jhi;
     kv_block_range(T, Tk, qt * BQ, qt * BQ + BQ, BK, cz, window, jlo, jhi);
+    RowPrefetch<DP, BK, NT> pk, pv;
+    if (jlo < jhi) {
+        pk.load(Kh, ldk, jlo * BK, Tk, D);
+        pv.load(Vh, ldk, jlo * BK, Tk, D);
+    }
     for (int j = jlo; j < jhi; ++j) {
         __syncthreads();
-        stage_rows<DP, BK, NT>(Ks, Kh, ldk, j * BK, Tk, D);
-        stage_rows<DP, BK, NT>(Vs, Vh, ldk, j * BK, Tk, D);
+        pk.store(Ks);
+        pv.store(Vs);
         __syncthreads();
+        if (j + 1 < jhi) {   // next block's loads in flight while this one is computed
+            pk.load(Kh, ldk, (j + 1) * BK, Tk, D);
+            pv.load(Vh, ldk, (j + 1) * BK, Tk, D);
+        }
 #pragma unroll 1
         for (int kb = 0; kb < BK / 16; ++kb) {
             const int kc0 = j * BK + kb * 16;
