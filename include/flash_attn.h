@@ -27,7 +27,8 @@
  *  scale multiplies q.k ([forge] flash_attn_fwd, [teeny] forward); must be finite and > 0.
  *  causal != 0 keeps keys j <= i (diagonal kept).  window > 0 keeps keys j >= i - window + 1
  *  (window counts keys including self; 0 = off; without causal it is a lower bound only),
- *  as in [forge] FlashParams and the per-row bounds of its kernels.
+ *  as in [forge] FlashParams and the per-row bounds of its kernels.  A window of T keys or
+ *  more keeps every key, exactly as no window.
  *  L = m + ln(l) in natural-log units ([ipu] forward epilogue, [forge] forward epilogue);
  *  a row with no visible key gets O = 0 and L = 0 ([forge] forward epilogue guard).
  *  dtype selects the element type of Q, K, V, O and dO: FA_DTYPE_F32 (float),
@@ -43,8 +44,9 @@
  *
  *  Errors: arguments are validated on the host before anything is enqueued.
  *    FA_ERR_INVALID_ARG  null pointer, B/T/H/HKV/D < 1, H % HKV != 0, window < 0,
- *                        scale not finite or <= 0, misaligned pointer, size overflow
- *                        (B*T*H*D > 2^40 elements, or for bf16 the T rows of one head
+ *                        scale not finite or <= 0, dtype not one of the values below,
+ *                        misaligned pointer, size overflow (T or Tk above 2^30 rows,
+ *                        B*T*H*D > 2^40 elements, or for bf16 the T rows of one head
  *                        spanning 2 GiB), an unusable layout (flash_attn_*_strided), tile
  *                        sizes that are not supported values;
  *    FA_ERR_UNSUPPORTED  a valid request this build has no kernel for (head dim);
@@ -65,14 +67,25 @@
 extern "C" {
 #endif
 
+/* Both enums span the whole int range (the _RANGE_ markers are not values to pass): any int a
+ * caller puts in an fa_dtype_t is a valid object, and the library answers unknown values with
+ * FA_ERR_INVALID_ARG. */
 typedef enum {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = 1,
     FA_ERR_UNSUPPORTED = 2,
-    FA_ERR_HIP = 3
+    FA_ERR_HIP = 3,
+    FA_STATUS_RANGE_MIN_ = -2147483647 - 1,
+    FA_STATUS_RANGE_MAX_ = 2147483647
 } fa_status_t;
 
-typedef enum { FA_DTYPE_F32 = 0, FA_DTYPE_BF16 = 1, FA_DTYPE_F16 = 2 } fa_dtype_t;
+typedef enum {
+    FA_DTYPE_F32 = 0,
+    FA_DTYPE_BF16 = 1,
+    FA_DTYPE_F16 = 2,
+    FA_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+    FA_DTYPE_RANGE_MAX_ = 2147483647
+} fa_dtype_t;
 
 /* Forward ([forge] flash_attn_fwd; [ipu] flashAttentionQKVPackedWithStash; [teeny] forward):
  * O = softmax(scale * Q K^T, masked) V per (b, h), and L = row log-sum-exp of the masked,

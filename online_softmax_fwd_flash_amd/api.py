@@ -46,7 +46,8 @@ def _dims(q, k):
 
 def _dims_qk(q, k):
     """(B, T, Tk, H, HKV, D) of q [B,T,H,D] and k [B,Tk,HKV,D]."""
-    if q.dim() != 4 or k.dim() != 4:
+    if (not isinstance(q, torch.Tensor) or not isinstance(k, torch.Tensor) or q.dim() != 4
+            or k.dim() != 4):
         raise ValueError("expected q [B,T,H,D] and k/v [B,Tk,HKV,D]")
     B, T, H, D = q.shape
     Bk, Tk, HKV, Dk = k.shape
@@ -55,9 +56,31 @@ def _dims_qk(q, k):
     return B, T, Tk, H, HKV, D
 
 
-def _want(t, shape, dtype, name):
-    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous() or not t.is_cuda:
-        raise ValueError(f"{name}: expected contiguous {dtype} cuda tensor of shape {tuple(shape)}")
+def _want(t, shape, dtype, name, device=None):
+    if (not isinstance(t, torch.Tensor) or tuple(t.shape) != tuple(shape) or t.dtype != dtype
+            or not t.is_contiguous() or not t.is_cuda
+            or (device is not None and t.device != device)):
+        where = f" on {device}" if device is not None else ""
+        raise ValueError(f"{name}: expected contiguous {dtype} cuda tensor of shape "
+                         f"{tuple(shape)}{where}")
+
+
+def _dtype_code(dtype):
+    if dtype not in _DT:
+        raise ValueError(f"unsupported dtype {dtype}: expected float32, bfloat16 or float16")
+    return _DT[dtype]
+
+
+def _want_inputs(q, k, v, **more):
+    """q [B,T,H,D], k and v [B,Tk,HKV,D] contiguous, on one device, in one supported dtype;
+    each tensor of `more` contiguous with q's shape and dtype on that device."""
+    _dtype_code(q.dtype)
+    dev = q.device
+    _want(q, q.shape, q.dtype, "q", dev)
+    _want(k, k.shape, q.dtype, "k", dev)
+    _want(v, k.shape, q.dtype, "v", dev)
+    for name, t in more.items():
+        _want(t, q.shape, q.dtype, name, dev)
 
 
 def _scale(scale, D):
@@ -68,14 +91,12 @@ def flash_attn_fwd(q, k, v, causal=True, window=0, scale=None, out=None, lse=Non
                    stream=None):
     """O [B,T,H,D] (q.dtype) and L [B,H,T] (float32) for q [B,T,H,D], k, v [B,T,HKV,D]."""
     B, T, H, HKV, D = _dims(q, k)
+    _want_inputs(q, k, v)
     dt = _DT[q.dtype]
-    for t, name in ((q, "q"), (k, "k"), (v, "v")):
-        _want(t, t.shape, q.dtype, name)
-    _want(v, k.shape, q.dtype, "v")
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty(B, H, T, device=q.device, dtype=torch.float32) if lse is None else lse
-    _want(out, q.shape, q.dtype, "out")
-    _want(lse, (B, H, T), torch.float32, "lse")
+    _want(out, q.shape, q.dtype, "out", q.device)
+    _want(lse, (B, H, T), torch.float32, "lse", q.device)
     code = _lib.lib().flash_attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, T, H,
                                         HKV, D, _scale(scale, D), int(bool(causal)), int(window),
                                         dt, _stream(stream), int(tiles[0]), int(tiles[1]))
@@ -84,10 +105,14 @@ def flash_attn_fwd(q, k, v, causal=True, window=0, scale=None, out=None, lse=Non
 
 
 def flash_attn_bwd_preprocess(o, do, dvec=None, stream=None):
+    if not isinstance(o, torch.Tensor) or o.dim() != 4:
+        raise ValueError("o: expected a [B, T, H, D] tensor")
     B, T, H, D = o.shape
-    _want(do, o.shape, o.dtype, "do")
+    _dtype_code(o.dtype)
+    _want(o, o.shape, o.dtype, "o", o.device)
+    _want(do, o.shape, o.dtype, "do", o.device)
     dvec = torch.empty(B, H, T, device=o.device, dtype=torch.float32) if dvec is None else dvec
-    _want(dvec, (B, H, T), torch.float32, "dvec")
+    _want(dvec, (B, H, T), torch.float32, "dvec", o.device)
     code = _lib.lib().flash_attn_bwd_preprocess(_ptr(o), _ptr(do), _ptr(dvec), B, T, H, D,
                                                 _DT[o.dtype], _stream(stream))
     _check("flash_attn_bwd_preprocess", code)
@@ -99,20 +124,23 @@ def _grads(q, k, dq, dk, dv):
     dq = torch.empty(q.shape, device=q.device, dtype=f) if dq is None else dq
     dk = torch.empty(k.shape, device=q.device, dtype=f) if dk is None else dk
     dv = torch.empty(k.shape, device=q.device, dtype=f) if dv is None else dv
-    _want(dq, q.shape, f, "dq")
-    _want(dk, k.shape, f, "dk")
-    _want(dv, k.shape, f, "dv")
+    _want(dq, q.shape, f, "dq", q.device)
+    _want(dk, k.shape, f, "dk", q.device)
+    _want(dv, k.shape, f, "dv", q.device)
     return dq, dk, dv
 
 
 def flash_attn_bwd_dkdv(q, k, v, do, lse, dvec, causal=True, window=0, scale=None, dk=None,
                         dv=None, tiles=(0, 0), stream=None):
     B, T, H, HKV, D = _dims(q, k)
+    _want_inputs(q, k, v, do=do)
     f = torch.float32
+    _want(lse, (B, H, T), f, "lse", q.device)
+    _want(dvec, (B, H, T), f, "dvec", q.device)
     dk = torch.empty(k.shape, device=q.device, dtype=f) if dk is None else dk
     dv = torch.empty(k.shape, device=q.device, dtype=f) if dv is None else dv
-    _want(dk, k.shape, f, "dk")
-    _want(dv, k.shape, f, "dv")
+    _want(dk, k.shape, f, "dk", q.device)
+    _want(dv, k.shape, f, "dv", q.device)
     code = _lib.lib().flash_attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse),
                                           _ptr(dvec), _ptr(dk), _ptr(dv), B, T, H, HKV, D,
                                           _scale(scale, D), int(bool(causal)), int(window),
@@ -125,8 +153,11 @@ def flash_attn_bwd_dkdv(q, k, v, do, lse, dvec, causal=True, window=0, scale=Non
 def flash_attn_bwd_dq(q, k, v, do, lse, dvec, causal=True, window=0, scale=None, dq=None,
                       tiles=(0, 0), stream=None):
     B, T, H, HKV, D = _dims(q, k)
+    _want_inputs(q, k, v, do=do)
+    _want(lse, (B, H, T), torch.float32, "lse", q.device)
+    _want(dvec, (B, H, T), torch.float32, "dvec", q.device)
     dq = torch.empty(q.shape, device=q.device, dtype=torch.float32) if dq is None else dq
-    _want(dq, q.shape, torch.float32, "dq")
+    _want(dq, q.shape, torch.float32, "dq", q.device)
     code = _lib.lib().flash_attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse),
                                         _ptr(dvec), _ptr(dq), B, T, H, HKV, D, _scale(scale, D),
                                         int(bool(causal)), int(window), _DT[q.dtype],
@@ -139,13 +170,12 @@ def flash_attn_bwd_dq_dvec(q, k, v, o, do, lse, dvec=None, causal=True, window=0
                            dq=None, tiles=(0, 0), stream=None):
     """dQ (float32) and Dvec = rowsum(dO * O) ([B,H,T] float32) in one pass; returns (dq, dvec)."""
     B, T, H, HKV, D = _dims(q, k)
-    _want(o, q.shape, q.dtype, "o")
-    _want(do, q.shape, q.dtype, "do")
-    _want(lse, (B, H, T), torch.float32, "lse")
+    _want_inputs(q, k, v, o=o, do=do)
+    _want(lse, (B, H, T), torch.float32, "lse", q.device)
     dq = torch.empty(q.shape, device=q.device, dtype=torch.float32) if dq is None else dq
     dvec = torch.empty(B, H, T, device=q.device, dtype=torch.float32) if dvec is None else dvec
-    _want(dq, q.shape, torch.float32, "dq")
-    _want(dvec, (B, H, T), torch.float32, "dvec")
+    _want(dq, q.shape, torch.float32, "dq", q.device)
+    _want(dvec, (B, H, T), torch.float32, "dvec", q.device)
     code = _lib.lib().flash_attn_bwd_dq_dvec(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
                                              _ptr(lse), _ptr(dvec), _ptr(dq), B, T, H, HKV, D,
                                              _scale(scale, D), int(bool(causal)), int(window),
@@ -159,9 +189,8 @@ def flash_attn_bwd(q, k, v, o, lse, do, causal=True, window=0, scale=None, dq=No
                    dv=None, tiles=(0, 0), stream=None):
     """dQ, dK, dV (float32) of sum(O * dO); O, L from flash_attn_fwd on the same inputs."""
     B, T, H, HKV, D = _dims(q, k)
-    _want(o, q.shape, q.dtype, "o")
-    _want(do, q.shape, q.dtype, "do")
-    _want(lse, (B, H, T), torch.float32, "lse")
+    _want_inputs(q, k, v, o=o, do=do)
+    _want(lse, (B, H, T), torch.float32, "lse", q.device)
     dq, dk, dv = _grads(q, k, dq, dk, dv)
     code = _lib.lib().flash_attn_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
                                         _ptr(dq), _ptr(dk), _ptr(dv), B, T, H, HKV, D,
@@ -180,9 +209,11 @@ def _layout(t, name):
 
 
 def _want_view(t, like, dtype, name):
-    """t must be a cuda tensor of like's shape and strides (elements) in dtype."""
-    if (tuple(t.shape) != tuple(like.shape) or tuple(t.stride()) != tuple(like.stride())
-            or t.dtype != dtype or not t.is_cuda):
+    """t must be a cuda tensor on like's device with like's shape and strides (elements), in
+    dtype."""
+    if (not isinstance(t, torch.Tensor) or tuple(t.shape) != tuple(like.shape)
+            or tuple(t.stride()) != tuple(like.stride()) or t.dtype != dtype or not t.is_cuda
+            or t.device != like.device):
         raise ValueError(f"{name}: expected a {dtype} cuda view with shape {tuple(like.shape)} "
                          f"and strides {tuple(like.stride())}")
 
@@ -197,12 +228,14 @@ def flash_attn_fwd_strided(q, k, v, causal=True, window=0, scale=None, out=None,
     x.transpose(1, 2) of a [B, H, T, D] tensor or of a third of a packed QKV buffer.  k and v
     share strides; O takes q's strides."""
     B, T, Tk, H, HKV, D = _dims_qk(q, k)
+    _dtype_code(q.dtype)
+    _want_view(q, q, q.dtype, "q")
     _want_view(k, k, q.dtype, "k")
     _want_view(v, k, q.dtype, "v")
     out = _empty_like_view(q, q.dtype) if out is None else out
     _want_view(out, q, q.dtype, "out")
     lse = torch.empty(B, H, T, device=q.device, dtype=torch.float32) if lse is None else lse
-    _want(lse, (B, H, T), torch.float32, "lse")
+    _want(lse, (B, H, T), torch.float32, "lse", q.device)
     code = _lib.lib().flash_attn_fwd_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                                              B, T, Tk, H, HKV, D, _scale(scale, D),
                                              int(bool(causal)), int(window), _DT[q.dtype],
@@ -216,11 +249,13 @@ def flash_attn_bwd_strided(q, k, v, o, lse, do, causal=True, window=0, scale=Non
     """flash_attn_bwd on strided views: o, do and dq (float32) take q's strides, dk and dv
     (float32) take k's."""
     B, T, Tk, H, HKV, D = _dims_qk(q, k)
+    _dtype_code(q.dtype)
+    _want_view(q, q, q.dtype, "q")
     _want_view(k, k, q.dtype, "k")
     _want_view(v, k, q.dtype, "v")
     _want_view(o, q, q.dtype, "o")
     _want_view(do, q, q.dtype, "do")
-    _want(lse, (B, H, T), torch.float32, "lse")
+    _want(lse, (B, H, T), torch.float32, "lse", q.device)
     f32 = torch.float32
     dq = _empty_like_view(q, f32) if dq is None else dq
     dk = _empty_like_view(k, f32) if dk is None else dk
@@ -244,11 +279,12 @@ def flash_attn_bwd_grad16(q, k, v, o, lse, do, causal=True, window=0, scale=None
     B, T, Tk, H, HKV, D = _dims_qk(q, k)
     if q.dtype not in (torch.bfloat16, torch.float16):
         raise ValueError("flash_attn_bwd_grad16 needs bfloat16 or float16 inputs")
+    _want_view(q, q, q.dtype, "q")
     _want_view(k, k, q.dtype, "k")
     _want_view(v, k, q.dtype, "v")
     _want_view(o, q, q.dtype, "o")
     _want_view(do, q, q.dtype, "do")
-    _want(lse, (B, H, T), torch.float32, "lse")
+    _want(lse, (B, H, T), torch.float32, "lse", q.device)
     dq = _empty_like_view(q, q.dtype) if dq is None else dq
     dk = _empty_like_view(k, q.dtype) if dk is None else dk
     dv = _empty_like_view(k, q.dtype) if dv is None else dv
@@ -269,15 +305,18 @@ def flash_attn_qk_norm_rope(qk, factor1, factor2, heads, rotary_dim=None, paired
     """(out_q, out_k) from a packed QK projection qk [tokens, 2*heads, D] (last axis
     contiguous, any token / head strides) and float32 factor tables [tokens, D] ([tokens, 2D]
     when paired): RMS-norm without weight, then y = factor1 * x + factor2 * pair_swap(x)."""
-    if qk.dim() != 3 or qk.stride(2) != 1 or not qk.is_cuda:
+    if (not isinstance(qk, torch.Tensor) or qk.dim() != 3 or qk.stride(2) != 1
+            or not qk.is_cuda):
         raise ValueError("qk: expected a cuda [tokens, 2*heads, D] tensor, last axis contiguous")
+    _dtype_code(qk.dtype)
     tokens, heads2, D = qk.shape
     if heads2 != 2 * heads:
         raise ValueError("qk: second axis must be 2 * heads")
     rotary_dim = D if rotary_dim is None else rotary_dim
     width = D * (2 if paired else 1)
     for name, f in (("factor1", factor1), ("factor2", factor2)):
-        if (f.dtype != torch.float32 or not f.is_cuda or f.dim() != 2
+        if (not isinstance(f, torch.Tensor) or f.dtype != torch.float32 or not f.is_cuda
+                or f.device != qk.device or f.dim() != 2
                 or tuple(f.shape) != (tokens, width) or f.stride(1) != 1
                 or f.stride() != factor1.stride()):
             raise ValueError(f"{name}: expected float32 cuda [{tokens}, {width}], last axis "
@@ -285,8 +324,8 @@ def flash_attn_qk_norm_rope(qk, factor1, factor2, heads, rotary_dim=None, paired
     shape = (2 * tokens, heads // 2, D) if paired else (tokens, heads, D)
     out_q = torch.empty(shape, device=qk.device, dtype=qk.dtype) if out_q is None else out_q
     out_k = torch.empty(shape, device=qk.device, dtype=qk.dtype) if out_k is None else out_k
-    _want(out_q, shape, qk.dtype, "out_q")
-    _want(out_k, shape, qk.dtype, "out_k")
+    _want(out_q, shape, qk.dtype, "out_q", qk.device)
+    _want(out_k, shape, qk.dtype, "out_k", qk.device)
     code = _lib.lib().flash_attn_qk_norm_rope(_ptr(qk), qk.stride(0), qk.stride(1),
                                               _ptr(factor1), _ptr(factor2), factor1.stride(0),
                                               _ptr(out_q), _ptr(out_k), tokens, heads, D,

@@ -10,6 +10,13 @@
 namespace {
 
 constexpr int kF32DefaultBq = 64, kF32DefaultBk = 64;
+// Longest query or key sequence: row and block indices (plus a tile) stay far inside int.
+constexpr int kMaxRows = 1 << 30;
+
+// A window of at least Tk keys constrains no row (row positions are below Tk), so it is the
+// same as no window; the kernels and helpers take it as 0, which keeps their index arithmetic
+// (row + window) inside int.
+int effective_window(int window, int Tk) { return window >= Tk ? 0 : window; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -17,6 +24,7 @@ fa_status_t check_dims(int B, int T, int H, int HKV, int D, float scale, int cau
                        fa_dtype_t dtype, int Tk = -1) {
     if (Tk < 0) Tk = T;
     if (B < 1 || T < 1 || Tk < 1 || H < 1 || HKV < 1 || D < 1) return FA_ERR_INVALID_ARG;
+    if (T > kMaxRows || Tk > kMaxRows) return FA_ERR_INVALID_ARG;
     if (H % HKV != 0) return FA_ERR_INVALID_ARG;
     if (window < 0 || (causal != 0 && causal != 1)) return FA_ERR_INVALID_ARG;
     if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
@@ -25,7 +33,8 @@ fa_status_t check_dims(int B, int T, int H, int HKV, int D, float scale, int cau
     // every element offset and every grid stays far inside its integer type
     const double elems = (double)B * (T > Tk ? T : Tk) * H * D;
     if (elems > (double)(1ll << 40)) return FA_ERR_INVALID_ARG;
-    if ((double)B * H * (((T > Tk ? T : Tk) + 15) / 16) > 2147483647.0) return FA_ERR_INVALID_ARG;
+    if ((double)B * H * (((int64_t)(T > Tk ? T : Tk) + 15) / 16) > 2147483647.0)
+        return FA_ERR_INVALID_ARG;
     if (dtype == FA_DTYPE_F32) {
         if (D % 8 != 0 || D > 128) return FA_ERR_UNSUPPORTED;
     } else {
@@ -69,11 +78,18 @@ fa_status_t check_layout(const fa_layout_t& l, int B, int T, int heads, int D, f
     return FA_OK;
 }
 
+// a * b, saturated at INT64_MAX (the sizes are not validated yet when the layouts of the
+// contiguous entry points are formed; a saturated stride fails the layout check)
+int64_t sat_mul(int64_t a, int64_t b) {
+    int64_t r;
+    return __builtin_mul_overflow(a, b, &r) ? INT64_MAX : r;
+}
+
 // The layouts of contiguous [B, T, H, D] (queries) and [B, T, HKV, D] (keys) tensors.
 fa_layout_t dense_layout(int T, int heads, int D) {
     fa_layout_t l;
-    l.batch = (int64_t)T * heads * D;
-    l.row = (int64_t)heads * D;
+    l.batch = sat_mul(sat_mul(T, heads), D);
+    l.row = sat_mul(heads, D);
     l.head = D;
     return l;
 }
@@ -104,7 +120,8 @@ fa::AttnArgs make_args(int B, int T, int Tk, int H, int HKV, int D, float scale,
     fa::AttnArgs a{};
     a.f16 = dtype == FA_DTYPE_F16 ? 1 : 0;
     a.B = B; a.T = T; a.Tk = Tk; a.H = H; a.HKV = HKV; a.D = D;
-    a.scale = scale; a.causal = causal; a.window = window; a.stream = stream;
+    a.scale = scale; a.causal = causal; a.window = effective_window(window, Tk);
+    a.stream = stream;
     a.lq = to_layout(lq); a.lk = to_layout(lk);
     return a;
 }
@@ -247,6 +264,7 @@ const char* flash_attn_status_string(fa_status_t s) {
         case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG";
         case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
         case FA_ERR_HIP: return "FA_ERR_HIP";
+        default: break;
     }
     return "FA_UNKNOWN_STATUS";
 }
@@ -262,34 +280,41 @@ fa_status_t flash_attn_check_layout(fa_layout_t layout, int B, int T, int heads,
 }
 
 int flash_attn_block_class(int T, int bq, int bk, int causal, int window, int i, int j, int* off) {
-    if (T < 1 || bq < 1 || bk < 1 || window < 0 || i < 0 || j < 0) return -1;
-    if ((long long)(i + 1) * bq > (1ll << 30) || (long long)(j + 1) * bk > (1ll << 30)) return -1;
+    if (T < 1 || T > kMaxRows || bq < 1 || bk < 1 || window < 0 || i < 0 || j < 0) return -1;
+    if (((long long)i + 1) * bq > (1ll << 30) || ((long long)j + 1) * bk > (1ll << 30)) return -1;
     if (off) *off = i * bq - j * bk;
-    return fa::block_class(T, T, i * bq, i * bq + bq, j * bk, j * bk + bk, causal != 0, window);
+    return fa::block_class(T, T, i * bq, i * bq + bq, j * bk, j * bk + bk, causal != 0,
+                           effective_window(window, T));
 }
 
 int flash_attn_block_class_qk(int Tq, int Tk, int bq, int bk, int causal, int window, int i,
                               int j) {
-    if (Tq < 1 || Tk < 1 || bq < 1 || bk < 1 || window < 0 || i < 0 || j < 0) return -1;
-    if ((long long)(i + 1) * bq > (1ll << 30) || (long long)(j + 1) * bk > (1ll << 30)) return -1;
-    return fa::block_class(Tq, Tk, i * bq, i * bq + bq, j * bk, j * bk + bk, causal != 0, window);
+    if (Tq < 1 || Tk < 1 || Tq > kMaxRows || Tk > kMaxRows || bq < 1 || bk < 1 || window < 0 ||
+        i < 0 || j < 0)
+        return -1;
+    if (((long long)i + 1) * bq > (1ll << 30) || ((long long)j + 1) * bk > (1ll << 30)) return -1;
+    return fa::block_class(Tq, Tk, i * bq, i * bq + bq, j * bk, j * bk + bk, causal != 0,
+                           effective_window(window, Tk));
 }
 
 fa_status_t flash_attn_kv_block_range_qk(int Tq, int Tk, int bq, int bk, int causal, int window,
                                          int i, int* j_lo, int* j_hi) {
-    if (Tq < 1 || Tk < 1 || bq < 1 || bk < 1 || window < 0 || i < 0 || !j_lo || !j_hi)
+    if (Tq < 1 || Tk < 1 || Tq > kMaxRows || Tk > kMaxRows || bq < 1 || bk < 1 || window < 0 ||
+        i < 0 || !j_lo || !j_hi)
         return FA_ERR_INVALID_ARG;
-    if ((long long)(i + 1) * bq > (1ll << 30)) return FA_ERR_INVALID_ARG;
-    fa::kv_block_range(Tq, Tk, i * bq, i * bq + bq, bk, causal != 0, window, *j_lo, *j_hi);
+    if (((long long)i + 1) * bq > (1ll << 30)) return FA_ERR_INVALID_ARG;
+    fa::kv_block_range(Tq, Tk, i * bq, i * bq + bq, bk, causal != 0, effective_window(window, Tk),
+                       *j_lo, *j_hi);
     return FA_OK;
 }
 
 fa_status_t flash_attn_kv_block_range(int T, int bq, int bk, int causal, int window, int i,
                                       int* j_lo, int* j_hi) {
-    if (T < 1 || bq < 1 || bk < 1 || window < 0 || i < 0 || !j_lo || !j_hi)
+    if (T < 1 || T > kMaxRows || bq < 1 || bk < 1 || window < 0 || i < 0 || !j_lo || !j_hi)
         return FA_ERR_INVALID_ARG;
-    if ((long long)(i + 1) * bq > (1ll << 30)) return FA_ERR_INVALID_ARG;
-    fa::kv_block_range(T, T, i * bq, i * bq + bq, bk, causal != 0, window, *j_lo, *j_hi);
+    if (((long long)i + 1) * bq > (1ll << 30)) return FA_ERR_INVALID_ARG;
+    fa::kv_block_range(T, T, i * bq, i * bq + bq, bk, causal != 0, effective_window(window, T),
+                       *j_lo, *j_hi);
     return FA_OK;
 }
 

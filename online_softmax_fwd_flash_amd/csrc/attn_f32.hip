@@ -420,6 +420,12 @@ template <int DP, int BQ, int BK>
 hipError_t launch_fwd_f32_t(const AttnArgs& a) {
     const int nqt = (a.T + BQ - 1) / BQ;
     const unsigned grid = (unsigned)nqt * a.B * a.H;
+    if (log_enabled()) {
+        char nm[64];
+        snprintf(nm, sizeof nm, "fwd_f32_kernel<DP=%d,BQ=%d,BK=%d>", DP, BQ, BK);
+        log_launch(nm, "f32", a.D, grid, BQ / 16 * 64, 0, a.B, a.T, a.Tk, a.H, a.HKV, a.causal,
+                   a.window);
+    }
     hipLaunchKernelGGL((fwd_f32_kernel<DP, BQ, BK>), dim3(grid), dim3(BQ / 16 * 64), 0,
                        a.stream, (const float*)a.Q, (const float*)a.K, (const float*)a.V,
                        (float*)a.Oout, a.L, a.B, a.T, a.Tk, a.H, a.HKV, a.D, a.scale, a.causal,
@@ -432,6 +438,12 @@ hipError_t launch_dkdv_f32_t(const AttnArgs& a) {
     constexpr int KW = DkdvF32Keys<BK>::KW;
     const int nkt = (a.Tk + KW - 1) / KW;
     const unsigned grid = (unsigned)nkt * a.B * a.HKV;
+    if (log_enabled()) {
+        char nm[64];
+        snprintf(nm, sizeof nm, "dkdv_f32_kernel<DP=%d,BQ=%d,BK=%d>", DP, BQ, BK);
+        log_launch(nm, "f32", a.D, grid, KW / 16 * 64, 0, a.B, a.T, a.Tk, a.H, a.HKV, a.causal,
+                   a.window);
+    }
     hipLaunchKernelGGL((dkdv_f32_kernel<DP, BQ, BK>), dim3(grid), dim3(KW / 16 * 64), 0,
                        a.stream, (const float*)a.Q, (const float*)a.K, (const float*)a.V,
                        (const float*)a.dO, a.Lin, a.Dvec, a.dK, a.dV, a.B, a.T, a.Tk, a.H, a.HKV, a.D,
@@ -443,6 +455,12 @@ template <int DP, int BQ, int BK>
 hipError_t launch_dq_f32_t(const AttnArgs& a) {
     const int nqt = (a.T + BQ - 1) / BQ;
     const unsigned grid = (unsigned)nqt * a.B * a.H;
+    if (log_enabled()) {
+        char nm[64];
+        snprintf(nm, sizeof nm, "dq_f32_kernel<DP=%d,BQ=%d,BK=%d>", DP, BQ, BK);
+        log_launch(nm, "f32", a.D, grid, BQ / 16 * 64, 0, a.B, a.T, a.Tk, a.H, a.HKV, a.causal,
+                   a.window);
+    }
     hipLaunchKernelGGL((dq_f32_kernel<DP, BQ, BK>), dim3(grid), dim3(BQ / 16 * 64), 0,
                        a.stream, (const float*)a.Q, (const float*)a.K, (const float*)a.V,
                        (const float*)a.dO, a.Lin, a.Dvec, a.dQ, a.B, a.T, a.Tk, a.H, a.HKV, a.D,

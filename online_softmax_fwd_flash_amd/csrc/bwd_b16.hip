@@ -540,30 +540,17 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_b16_kernel(
 // ------------------------------------------------------------------------------ launchers
 namespace {
 
-template <typename Kern>
-hipError_t allow_lds(Kern kern, size_t lds, bool* set_flags) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-    if (!set_flags[dev]) {
-        e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)lds);
-        if (e != hipSuccess) return e;
-        set_flags[dev] = true;
-    }
-    return hipSuccess;
-}
-
 template <class E, int D>
 hipError_t launch_dkdv_b16_t(const AttnArgs& a) {
     using C = Dkdv16Cfg<D>;
-    static bool set[kMaxDevices] = {};
+    static std::atomic<bool> set[kMaxDeviceSlots];
     const size_t lds = 2 * (size_t)C::STAGE;
-    hipError_t e = allow_lds(dkdv_b16_kernel<E, D>, lds, set);
+    hipError_t e = allow_dynamic_lds((const void*)dkdv_b16_kernel<E, D>, lds, set);
     if (e != hipSuccess) return e;
     const int nkt = (a.Tk + C::BKW - 1) / C::BKW;
     const unsigned grid = (unsigned)nkt * a.B * a.HKV;
+    log_launch("dkdv_b16_kernel", ElemName<E>::value, D, grid, C::NT, lds, a.B, a.T, a.Tk, a.H,
+               a.HKV, a.causal, a.window);
     hipLaunchKernelGGL((dkdv_b16_kernel<E, D>), dim3(grid), dim3(C::NT), lds, a.stream,
                        (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
                        (const uint16_t*)a.dO, a.Lin, a.Dvec, a.dK, a.dV, a.B, a.T, a.Tk, a.H, a.HKV,
@@ -580,12 +567,14 @@ static_assert(Dkdv16Cfg<128>::BQ == kB16DkdvBq && Dkdv16Cfg<128>::BKW == kB16Dkd
 template <class E, int D, bool FUSE_D>
 hipError_t launch_dq_b16_t(const AttnArgs& a) {
     using C = DqCfg<D, kDqWaves>;
-    static bool set[kMaxDevices] = {};
+    static std::atomic<bool> set[kMaxDeviceSlots];
     const size_t lds = 2 * (size_t)C::STAGE;
-    hipError_t e = allow_lds(dq_b16_kernel<E, D, kDqWaves, FUSE_D>, lds, set);
+    hipError_t e = allow_dynamic_lds((const void*)dq_b16_kernel<E, D, kDqWaves, FUSE_D>, lds, set);
     if (e != hipSuccess) return e;
     const int nqt = (a.T + C::BQ - 1) / C::BQ;
     const unsigned grid = (unsigned)nqt * a.B * a.H;
+    log_launch(FUSE_D ? "dq_b16_kernel(+Dvec)" : "dq_b16_kernel", ElemName<E>::value, D, grid,
+               C::NT, lds, a.B, a.T, a.Tk, a.H, a.HKV, a.causal, a.window);
     hipLaunchKernelGGL((dq_b16_kernel<E, D, kDqWaves, FUSE_D>), dim3(grid), dim3(C::NT), lds,
                        a.stream, (const uint16_t*)a.Q, (const uint16_t*)a.K,
                        (const uint16_t*)a.V, (const uint16_t*)a.dO, (const uint16_t*)a.O, a.Lin,

@@ -74,6 +74,8 @@ hipError_t launch_bwd_preprocess(const void* O, const void* dO, float* Dvec, int
     const int64_t rows = (int64_t)B * T * H;
     const int64_t per = kThreads / kTeam;
     const unsigned grid = (unsigned)((rows + per - 1) / per);
+    log_launch("bwd_preprocess_kernel", dtype == 0 ? "f32" : dtype == 1 ? "bf16" : "f16", D, grid,
+               kThreads, 0, B, T, T, H, H, 0, 0);
     if (dtype == 0)
         hipLaunchKernelGGL(bwd_preprocess_kernel<float>, dim3(grid), dim3(kThreads), 0, stream,
                            O, dO, Dvec, B, T, H, D, lq);

@@ -20,7 +20,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kMaxDevices = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegMax = -3.402823466e+38f;  // running max starts here, never at -inf
@@ -117,6 +116,11 @@ struct F16 {
     typedef f16x4 v4;
     typedef f16x2 v2;
 };
+
+// Name of an element type in launch logs.
+template <class E> struct ElemName;
+template <> struct ElemName<Bf16> { static constexpr const char* value = "bf16"; };
+template <> struct ElemName<F16> { static constexpr const char* value = "f16"; };
 
 // Placed first in the body of a wave-uniform `if`, keeps it a branch: the compiler does not
 // speculate an asm statement with side effects, so it cannot flatten the body into selects

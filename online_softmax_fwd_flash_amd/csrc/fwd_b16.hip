@@ -292,17 +292,11 @@ hipError_t launch_fwd_b16_t(const AttnArgs& a) {
     const unsigned grid = (unsigned)nqt * a.B * a.H;
     const int xcd_group = xcd_group_for(nqt, a.B, a.H, a.HKV);
     const size_t lds = 2 * C::STAGEB;
-    static bool attr_set[kMaxDevices] = {};
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
+    static std::atomic<bool> attr_set[kMaxDeviceSlots];
+    hipError_t e = allow_dynamic_lds((const void*)fwd_b16_kernel<E, D>, lds, attr_set);
     if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-    if (!attr_set[dev]) {
-        e = hipFuncSetAttribute((const void*)fwd_b16_kernel<E, D>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        attr_set[dev] = true;
-    }
+    log_launch("fwd_b16_kernel", ElemName<E>::value, D, grid, kThreads, lds, a.B, a.T, a.Tk,
+               a.H, a.HKV, a.causal, a.window);
     hipLaunchKernelGGL((fwd_b16_kernel<E, D>), dim3(grid), dim3(kThreads), lds, a.stream,
                        (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
                        (uint16_t*)a.Oout, a.L, a.B, a.T, a.Tk, a.H, a.HKV, a.scale, a.causal,

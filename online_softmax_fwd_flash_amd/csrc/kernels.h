@@ -2,9 +2,53 @@
 // units.  Arguments have been validated before any of these is called.
 #pragma once
 
+#include <atomic>
+#include <stdio.h>
+#include <stdlib.h>
+
 #include <hip/hip_runtime.h>
 
 namespace fa {
+
+constexpr int kMaxDeviceSlots = 64;
+
+// Raises a kernel's dynamic-LDS limit to `bytes` on the current device, once per device.  The
+// per-device flags are atomics, so host threads making their first calls at the same time do
+// not race (the attribute call itself is idempotent; the flag only saves repeating it).
+inline hipError_t allow_dynamic_lds(const void* kernel, size_t bytes,
+                                    std::atomic<bool>* flags) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDeviceSlots) return hipErrorInvalidDevice;
+    if (!flags[dev].load(std::memory_order_acquire)) {
+        e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+        if (e != hipSuccess) return e;
+        flags[dev].store(true, std::memory_order_release);
+    }
+    return hipSuccess;
+}
+
+// With the environment variable FA_LOG set to a non-empty value other than "0" (read once per
+// process), every launch prints the kernel instantiation it chose and its launch shape to
+// stderr.
+inline bool log_enabled() {
+    static const bool on = [] {
+        const char* v = getenv("FA_LOG");
+        return v != nullptr && v[0] != '\0' && !(v[0] == '0' && v[1] == '\0');
+    }();
+    return on;
+}
+
+inline void log_launch(const char* kernel, const char* elem, int D, unsigned grid,
+                       unsigned block, size_t lds, int B, int T, int Tk, int H, int HKV,
+                       int causal, int window) {
+    if (!log_enabled()) return;
+    fprintf(stderr,
+            "flash_attn: %s elem=%s D=%d grid=%u block=%u lds=%zu B=%d T=%d Tk=%d H=%d "
+            "HKV=%d causal=%d window=%d\n",
+            kernel, elem, D, grid, block, lds, B, T, Tk, H, HKV, causal, window);
+}
 
 // Element strides of a [B, T, heads, D] view (batch, row, head); the D axis is contiguous.
 // Q, O, dO and dQ share one layout, K, V, dK and dV another.

@@ -149,6 +149,8 @@ hipError_t launch_rope_t(const RopeArgs& a) {
     const int64_t rows = (int64_t)a.tokens * 2 * a.heads;
     const int64_t threads = rows * LPR;
     const unsigned grid = (unsigned)((threads + kRopeThreads - 1) / kRopeThreads);
+    log_launch("qk_norm_rope_kernel", a.dtype == 0 ? "f32" : a.dtype == 1 ? "bf16" : "f16", D,
+               grid, kRopeThreads, 0, 1, a.tokens, a.tokens, a.heads, a.heads, 0, 0);
     hipLaunchKernelGGL((qk_norm_rope_kernel<E, D>), dim3(grid), dim3(kRopeThreads), 0, a.stream,
                        (const char*)a.qk, a.st, a.sh, a.f1, a.f2, a.fst, (char*)a.out_q,
                        (char*)a.out_k, a.tokens, a.heads, a.rotary_dim, a.paired, a.key_offset);
