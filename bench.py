@@ -1,15 +1,29 @@
 """Benchmark of the fused attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C4] [--no-cpu-baseline]
+                    [--no-extra-workloads] [--no-mfma-probe] [--prologue] [--calibrate-copy]
 
 A step is one pass of the whole path over one batch of synthetic input already resident in
-HBM: forward (flash_attn_fwd) and backward (flash_attn_bwd_dq_dvec, then flash_attn_bwd_dkdv —
-the two kernels flash_attn_bwd runs, called through their own entry points so each can be
-timed with HIP events on the launch stream).  Prints one JSON line.
+HBM: flash_attn_fwd, then flash_attn_bwd (the public entry points; the backward includes its
+stream-ordered Dvec workspace).  W untimed steps, then exactly K timed steps between device
+synchronisations give `ms_per_step` and `value`; HIP events recorded on the launch stream
+around each call give the per-call medians `fwd_ms` and `bwd_ms`.  A second run of K steps
+calls the three kernels through their stage entry points (flash_attn_fwd,
+flash_attn_bwd_dq_dvec, flash_attn_bwd_dkdv, the kernels flash_attn_bwd runs) with events
+between them, for the per-kernel medians in `kernels` and the dominant kernel's `roofline`.
+Prints one JSON line.
 
 FLOP convention: forward 4*B*H*T^2*D (halved when causal), backward 2.5x that; the metric is
 fwd+bwd TFLOP/s, with the forward alone and the fraction of the MI355X dense bf16 MFMA peak
-(2516.6 TFLOP/s = 256 CU x 2.4 GHz x 4096 FLOP/clk) reported beside it.
+(2516.6 TFLOP/s = 256 CU x 2.4 GHz x 4096 FLOP/clk) reported beside it.  Per kernel, the
+algorithmic work is FLOP per visible (query, key) pair times the visible pairs.
+
+`workloads` carries the same figures for the other bf16 workloads (D=64 MHA and the sliding
+window; the window one also counted by its visible pairs) unless --no-extra-workloads.
+
+`roofline.measured_peak` is the bf16 MFMA rate the chip sustains in the library's MFMA probe
+(flash_attn_mfma_rate_probe) on N(0,1) operands, the distribution of this workload's inputs;
+`mfma_probe` lists it beside the rates on uniform [0,1) and constant operands.
 
 roofline.traffic is the HBM byte count (read + write) per launch of the dominant kernel, taken
 from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary scaled by a plain device copy of
@@ -17,13 +31,13 @@ known size (`--calibrate-copy` adds that copy to a profiled run); it is null for
 workloads and whenever the kernel sources no longer match the ones the counters were taken on.
 
 The CPU baseline times the fp64 oracle (a plain materialised-softmax reference) on the host
-cores on a bounded sample of the same workload: whole (batch, KV-head) groups, forward and
-backward, until about 10 s have elapsed.
+cores on a bounded sample of the same workload: whole (batch, KV-head) groups, the forward for
+about a third of the budget, then forward + backward for the rest.
 """
 import argparse
 import json
-import math
 import os
+import statistics
 import sys
 import time
 
@@ -36,6 +50,9 @@ COPY_BYTES = 512 * 1024 * 1024
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_c4_hbm_traffic.md")
 CSRC = os.path.join(ROOT, "online_softmax_fwd_flash_amd", "csrc")
 METRIC = "causal attn TFLOP/s fwd & fwd+bwd (bf16, GQA, T=4096, D=128); % MFMA peak"
+EXTRA_WORKLOADS = ("C3", "C5")
+PROBE_GRID, PROBE_ITERS = 2048, 1000   # MFMA probe launch: grid * 4 * iters * 16 MFMAs
+MFMA_FLOP = 2 * 32 * 32 * 16           # one bf16 32x32x16 MFMA
 
 
 def visible_pairs(T, causal, window):
@@ -81,33 +98,49 @@ def measured_traffic(kernel):
     return None
 
 
-def cpu_baseline(cfg, budget_s=10.0):
-    """Time the fp64 oracle (fwd + bwd of whole (b, kv-head) groups) on the host cores."""
-    import numpy as np
+def cpu_baseline(cfg, budget_s=15.0):
+    """Time the fp64 oracle on the host cores: whole (b, kv-head) groups, the forward for a
+    third of the budget, then forward + backward for the rest.  BLAS runs on every core the
+    process may use."""
+    import contextlib
     import oracle
     from workloads import make_inputs, fwd_flops
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover - threadpoolctl missing
-        threads = None
-    q, k, v, do = make_inputs(cfg)
-    groups = [(b, g) for b in range(cfg.B) for g in range(cfg.HKV)]
-    done, t0 = 0, time.perf_counter()
-    for grp in groups:
-        oracle.attn_bwd(q, k, v, do, cfg.scale, cfg.causal, cfg.window, groups=[grp])
-        done += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    per_group = 3.5 * fwd_flops(cfg) / (cfg.B * cfg.HKV)
     cores = len(os.sched_getaffinity(0))
-    return {"value": per_group * done / dt / 1e12, "unit": "TFLOP/s", "cores": threads or cores,
-            "kind": "oracle",
-            "sample": f"{done} of {len(groups)} (batch, kv-head) groups of the "
-                      f"{cfg.describe()} workload "
-                      f"({cfg.H // cfg.HKV} query heads each), fwd+bwd in fp64 numpy, "
-                      f"{dt:.1f} s wall; host has {cores} usable cores"}
+    try:
+        from threadpoolctl import threadpool_limits, threadpool_info
+        limits = threadpool_limits(limits=cores)
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threadpool_info, limits = None, contextlib.nullcontext()
+    with limits:
+        blas = (max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+                if threadpool_info else None)
+        q, k, v, do = make_inputs(cfg)
+        groups = [(b, g) for b in range(cfg.B) for g in range(cfg.HKV)]
+        rep = cfg.H // cfg.HKV
+
+        def timed(fn, budget):
+            done, t0 = 0, time.perf_counter()
+            for grp in groups:
+                fn(grp)
+                done += 1
+                if time.perf_counter() - t0 >= budget:
+                    break
+            return done, time.perf_counter() - t0
+
+        n_f, t_f = timed(lambda grp: oracle.attn_fwd(
+            q, k, v, cfg.scale, cfg.causal, cfg.window,
+            pairs=[(grp[0], h) for h in range(grp[1] * rep, (grp[1] + 1) * rep)]), budget_s / 3)
+        n_fb, t_fb = timed(lambda grp: oracle.attn_bwd(
+            q, k, v, do, cfg.scale, cfg.causal, cfg.window, groups=[grp]), budget_s * 2 / 3)
+    per_group = fwd_flops(cfg) / (cfg.B * cfg.HKV)
+    return {"value": 3.5 * per_group * n_fb / t_fb / 1e12, "unit": "TFLOP/s",
+            "cores": blas or cores, "kind": "oracle",
+            "fwd_value": per_group * n_f / t_f / 1e12,
+            "host_cores": cores, "blas_threads": blas,
+            "sample": f"{n_f} (forward) then {n_fb} (forward + backward) of the {len(groups)} "
+                      f"(batch, kv-head) groups of the {cfg.describe()} workload "
+                      f"({rep} query heads each) in fp64 numpy, {t_f:.1f} s + {t_fb:.1f} s wall; "
+                      f"BLAS threads {blas} of {cores} usable cores"}
 
 
 def time_prologue(cfg, steps, warmup):
@@ -142,6 +175,158 @@ def time_prologue(cfg, steps, warmup):
             "unit": "GB/s", "peak": 8000.0, "frac": round(gbs / 8000.0, 4)}
 
 
+def mfma_probe(steps=10, warmup=3):
+    """bf16 MFMA rate (TFLOP/s, median of `steps` launches) of the library's probe kernel on
+    three operand distributions."""
+    import torch
+    import online_softmax_fwd_flash_amd as fa
+    dev = torch.device("cuda:0")
+    g = torch.Generator("cpu").manual_seed(1234)
+    dists = {
+        "normal": torch.randn(4096, generator=g),
+        "uniform01": torch.rand(4096, generator=g),
+        "constant": torch.ones(4096),
+    }
+    out = torch.empty(PROBE_GRID * 256, device=dev, dtype=torch.float32)
+    stream = torch.cuda.current_stream()
+    flop = PROBE_GRID * 4 * PROBE_ITERS * 16 * MFMA_FLOP
+    res = {}
+    for name, vals in dists.items():
+        ops = vals.to(torch.bfloat16).to(dev)
+        for _ in range(warmup):
+            fa.flash_attn_mfma_rate_probe(ops, out, PROBE_GRID, PROBE_ITERS)
+        ts = []
+        for _ in range(steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fa.flash_attn_mfma_rate_probe(ops, out, PROBE_GRID, PROBE_ITERS)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        res[name] = round(flop / (statistics.median(ts) * 1e-3) / 1e12, 1)
+    return {"unit": "TFLOP/s", "kernel": "mfma_probe_kernel (bf16 32x32x16, 4 independent "
+            "accumulators per wave)", "grid": PROBE_GRID, "iters": PROBE_ITERS, **res}
+
+
+def run_workload(cfg, steps, warmup):
+    """Time one workload: the public entry points (headline) and the stage entry points
+    (per-kernel breakdown).  Returns a dict of timings in ms."""
+    import torch
+    import online_softmax_fwd_flash_amd as fa
+    from workloads import make_inputs
+
+    dev = torch.device("cuda:0")
+    q, k, v, do = (t.to(dev) for t in make_inputs(cfg))
+    B, T, H = cfg.B, cfg.T, cfg.H
+    f32 = torch.float32
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, T, device=dev, dtype=f32)
+    dvec = torch.empty(B, H, T, device=dev, dtype=f32)
+    dq = torch.empty(q.shape, device=dev, dtype=f32)
+    dk = torch.empty(k.shape, device=dev, dtype=f32)
+    dv = torch.empty(k.shape, device=dev, dtype=f32)
+    kw = dict(causal=cfg.causal, window=cfg.window, scale=cfg.scale, tiles=cfg.tiles)
+    stream = torch.cuda.current_stream()
+
+    def public(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.flash_attn_fwd(q, k, v, out=o, lse=lse, **kw)
+        if ev is not None:
+            ev[1].record(stream)
+        fa.flash_attn_bwd(q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, **kw)
+        if ev is not None:
+            ev[2].record(stream)
+
+    def stages(ev):
+        ev[0].record(stream)
+        fa.flash_attn_fwd(q, k, v, out=o, lse=lse, **kw)
+        ev[1].record(stream)
+        fa.flash_attn_bwd_dq_dvec(q, k, v, o, do, lse, dvec=dvec, dq=dq, **kw)
+        ev[2].record(stream)
+        fa.flash_attn_bwd_dkdv(q, k, v, do, lse, dvec, dk=dk, dv=dv, **kw)
+        ev[3].record(stream)
+
+    def events(n):
+        return [[torch.cuda.Event(enable_timing=True) for _ in range(n)] for _ in range(steps)]
+
+    for _ in range(warmup):
+        public()
+    ev_pub = events(3)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        public(ev_pub[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ev_st = events(4)
+    for s in range(steps):
+        stages(ev_st[s])
+    torch.cuda.synchronize()
+
+    def med(evs, i):
+        return statistics.median(e[i].elapsed_time(e[i + 1]) for e in evs)
+
+    def mean(evs, i):
+        return sum(e[i].elapsed_time(e[i + 1]) for e in evs) / len(evs)
+
+    out = {"ms_per_step": wall * 1e3 / steps,
+           "fwd_ms": med(ev_pub, 0), "bwd_ms": med(ev_pub, 1),
+           "fwd_ms_mean": mean(ev_pub, 0), "bwd_ms_mean": mean(ev_pub, 1),
+           "kernels_ms": {"fwd": med(ev_st, 0), "bwd_dq_dvec": med(ev_st, 1),
+                          "bwd_dkdv": med(ev_st, 2)},
+           "kernels_ms_mean": {"fwd": mean(ev_st, 0), "bwd_dq_dvec": mean(ev_st, 1),
+                               "bwd_dkdv": mean(ev_st, 2)}}
+    del q, k, v, do, o, lse, dvec, dq, dk, dv
+    torch.cuda.empty_cache()
+    return out
+
+
+def kernel_table(cfg, kernels_ms, peak):
+    """Per-kernel achieved TFLOP/s from algorithmic work: FLOP per visible score x visible
+    scores (forward 4D: QK^T, PV; dQ pass 6D: QK^T, dO V^T, dS K; dK/dV pass 8D: QK^T, dO V^T,
+    P^T dO, dS^T Q)."""
+    vis = cfg.B * cfg.H * visible_pairs(cfg.T, cfg.causal, cfg.window)
+    work = {"fwd": 4.0 * cfg.D * vis, "bwd_dq_dvec": 6.0 * cfg.D * vis,
+            "bwd_dkdv": 8.0 * cfg.D * vis}
+    table = {}
+    for n, ms in kernels_ms.items():
+        ach = work[n] / (ms * 1e-3) / 1e12
+        table[n] = {"ms": round(ms, 4), "bound": "mfma", "achieved": round(ach, 1),
+                    "unit": "TFLOP/s", "frac": round(ach / peak, 4)}
+    return table, vis
+
+
+def summarize(cfg, r, peak):
+    """Metric figures of one workload's timings."""
+    from workloads import fwd_flops, bwd_flops
+    ff, bf = fwd_flops(cfg), bwd_flops(cfg)
+    kernels, vis = kernel_table(cfg, r["kernels_ms"], peak)
+    s = {
+        "workload": cfg.describe(),
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "fwd_bwd_tflops": round((ff + bf) / (r["ms_per_step"] * 1e-3) / 1e12, 2),
+        "fwd_ms": round(r["fwd_ms"], 4),
+        "bwd_ms": round(r["bwd_ms"], 4),
+        "fwd_tflops": round(ff / (r["fwd_ms"] * 1e-3) / 1e12, 2),
+        "fwd_frac_peak": round(ff / (r["fwd_ms"] * 1e-3) / 1e12 / peak, 4),
+        "fwd_bwd_frac_peak": round((ff + bf) / (r["ms_per_step"] * 1e-3) / 1e12 / peak, 4),
+        "kernels": kernels,
+    }
+    if cfg.window:
+        # the metric's formula counts T^2/2 pairs per head; a window keeps far fewer, so the
+        # formula's fractions of peak exceed 1 and only the window-aware ones are meaningful
+        wa = 4.0 * cfg.D * vis
+        fwa = wa / (r["fwd_ms"] * 1e-3) / 1e12
+        fbwa = 3.5 * wa / (r["ms_per_step"] * 1e-3) / 1e12
+        s["fwd_tflops_window_aware"] = round(fwa, 2)
+        s["fwd_frac_peak_window_aware"] = round(fwa / peak, 4)
+        s["fwd_bwd_tflops_window_aware"] = round(fbwa, 2)
+        s["fwd_bwd_frac_peak_window_aware"] = round(fbwa / peak, 4)
+    return s
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -149,7 +334,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="C4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-extra-workloads", action="store_true",
+                    help="skip the D=64 MHA and sliding-window workloads")
+    ap.add_argument("--no-mfma-probe", action="store_true",
+                    help="skip the MFMA-rate probe (roofline.measured_peak)")
     ap.add_argument("--prologue", action="store_true",
                     help="also time the QK RMS-norm + rotary prologue on the workload's tokens "
                          "(B*T tokens, H heads, D, in the workload dtype) and report it in its "
@@ -164,55 +353,14 @@ def main():
         sys.exit(2)
 
     import torch
-    import online_softmax_fwd_flash_amd as fa
-    from workloads import get_config, make_inputs, fwd_flops, bwd_flops
+    from workloads import get_config, fwd_flops, bwd_flops
 
     cfg = get_config(args.config)
-    dev = torch.device("cuda:0")
-    q, k, v, do = (t.to(dev) for t in make_inputs(cfg))
-    B, T, H, HKV, D = cfg.B, cfg.T, cfg.H, cfg.HKV, cfg.D
-    f32 = torch.float32
-    o = torch.empty_like(q)
-    lse = torch.empty(B, H, T, device=dev, dtype=f32)
-    dvec = torch.empty(B, H, T, device=dev, dtype=f32)
-    dq = torch.empty(q.shape, device=dev, dtype=f32)
-    dk = torch.empty(k.shape, device=dev, dtype=f32)
-    dv = torch.empty(k.shape, device=dev, dtype=f32)
-    kw = dict(causal=cfg.causal, window=cfg.window, scale=cfg.scale, tiles=cfg.tiles)
-    stream = torch.cuda.current_stream()
-    names = ["fwd", "bwd_dq_dvec", "bwd_dkdv"]
-
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        fa.flash_attn_fwd(q, k, v, out=o, lse=lse, **kw)
-        if ev is not None:
-            ev[1].record(stream)
-        fa.flash_attn_bwd_dq_dvec(q, k, v, o, do, lse, dvec=dvec, dq=dq, **kw)
-        if ev is not None:
-            ev[2].record(stream)
-        fa.flash_attn_bwd_dkdv(q, k, v, do, lse, dvec, dk=dk, dv=dv, **kw)
-        if ev is not None:
-            ev[3].record(stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-              for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(events[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_kernel = {n: 0.0 for n in names}
-    for ev in events:
-        for i, n in enumerate(names):
-            per_kernel[n] += ev[i].elapsed_time(ev[i + 1])
-    per_kernel = {n: t / args.steps for n, t in per_kernel.items()}   # ms per launch
+    peak = PEAK_BF16 if cfg.dtype == "bf16" else PEAK_FP32
+    r = run_workload(cfg, args.steps, args.warmup)
 
     if args.calibrate_copy:
+        dev = torch.device("cuda:0")
         src = torch.empty(COPY_BYTES // 4, device=dev, dtype=torch.float32).fill_(1.0)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
@@ -220,32 +368,21 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    ms_step = wall * 1e3 / args.steps
+    s = summarize(cfg, r, peak)
     ff, bf = fwd_flops(cfg), bwd_flops(cfg)
-    fwd_ms = per_kernel["fwd"]
-    bwd_ms = per_kernel["bwd_dq_dvec"] + per_kernel["bwd_dkdv"]
-    value = (ff + bf) / (ms_step * 1e-3) / 1e12
-    peak = PEAK_BF16 if cfg.dtype == "bf16" else PEAK_FP32
-
-    # algorithmic work per launch: FLOP per visible score x visible scores
-    vis = B * H * visible_pairs(T, cfg.causal, cfg.window)
-    algo = {
-        "fwd": ("mfma", 4.0 * D * vis),                    # Q K^T and P V
-        "bwd_dkdv": ("mfma", 8.0 * D * vis),               # Q K^T, dO V^T, P^T dO, dS^T Q
-        "bwd_dq_dvec": ("mfma", 6.0 * D * vis),            # Q K^T, dO V^T, dS K (+ rowsum(dO O))
-    }
-    kernels = {}
-    for n in names:
-        bound, work = algo[n]
-        ach = work / (per_kernel[n] * 1e-3) / 1e12
-        kernels[n] = {"ms": round(per_kernel[n], 4), "bound": bound, "achieved": round(ach, 1),
-                      "unit": "TFLOP/s", "frac": round(ach / peak, 4)}
-    dom = max(names, key=lambda n: per_kernel[n])
+    value = (ff + bf) / (r["ms_per_step"] * 1e-3) / 1e12
+    kernels = s["kernels"]
+    dom = max(kernels, key=lambda n: kernels[n]["ms"])
     dk_ = kernels[dom]
-    roofline = {"bound": dk_["bound"], "achieved": dk_["achieved"],
-                "peak": peak, "unit": dk_["unit"],
-                "frac": dk_["frac"], "kernel": dom,
+    roofline = {"bound": dk_["bound"], "achieved": dk_["achieved"], "peak": peak,
+                "unit": dk_["unit"], "frac": dk_["frac"], "kernel": dom,
                 "traffic": measured_traffic(dom) if cfg.name == "C4" else None}
+    probe = None
+    if not args.no_mfma_probe and cfg.dtype == "bf16":
+        probe = mfma_probe()
+        roofline["measured_peak"] = probe["normal"]
+        roofline["measured_peak_operands"] = "N(0,1) bf16 (the workload's input distribution)"
+        roofline["frac_measured_peak"] = round(dk_["achieved"] / probe["normal"], 4)
 
     out = {
         "metric": METRIC,
@@ -254,33 +391,41 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": round(r["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic (seeded i.i.d. N(0,1) Q, K, V, dO)",
-        "config": {"workload": cfg.describe(), "B": B, "H": H, "HKV": HKV, "T": T, "D": D,
-                   "causal": cfg.causal, "window": cfg.window, "seed": cfg.seed},
-        "fwd_tflops": round(ff / (fwd_ms * 1e-3) / 1e12, 2),
-        "fwd_frac_peak": round(ff / (fwd_ms * 1e-3) / 1e12 / peak, 4),
-        "fwd_bwd_tflops_events": round((ff + bf) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12, 2),
+        "config": {"workload": cfg.describe(), "B": cfg.B, "H": cfg.H, "HKV": cfg.HKV,
+                   "T": cfg.T, "D": cfg.D, "causal": cfg.causal, "window": cfg.window,
+                   "seed": cfg.seed},
+        "fwd_tflops": s["fwd_tflops"],
+        "fwd_frac_peak": s["fwd_frac_peak"],
         "fwd_bwd_frac_peak": round(value / peak, 4),
-        "fwd_ms": round(fwd_ms, 4),
-        "bwd_ms": round(bwd_ms, 4),
+        "fwd_ms": s["fwd_ms"],
+        "bwd_ms": s["bwd_ms"],
+        "timing": "fwd_ms / bwd_ms: medians of per-call HIP events on flash_attn_fwd and "
+                  "flash_attn_bwd over the timed steps; kernels: medians of the stage entry "
+                  "points over a second run of as many steps",
+        "fwd_ms_mean": round(r["fwd_ms_mean"], 4),
+        "bwd_ms_mean": round(r["bwd_ms_mean"], 4),
         "kernels": kernels,
         "roofline": roofline,
     }
-    if cfg.window:
-        # the metric's formula counts T^2/2 pairs per head; a window keeps far fewer, so the
-        # formula's fractions of peak exceed 1 and only the window-aware ones are meaningful
-        wa = 4.0 * D * vis
-        fwa = wa / (fwd_ms * 1e-3) / 1e12
-        fbwa = 3.5 * wa / (ms_step * 1e-3) / 1e12
-        out["fwd_tflops_window_aware"] = round(fwa, 2)
-        out["fwd_frac_peak_window_aware"] = round(fwa / peak, 4)
-        out["fwd_bwd_tflops_window_aware"] = round(fbwa, 2)
-        out["fwd_bwd_frac_peak_window_aware"] = round(fbwa / peak, 4)
+    for key in ("fwd_tflops_window_aware", "fwd_frac_peak_window_aware",
+                "fwd_bwd_tflops_window_aware", "fwd_bwd_frac_peak_window_aware"):
+        if key in s:
+            out[key] = s[key]
+    if probe is not None:
+        out["mfma_probe"] = probe
+    if not args.no_extra_workloads and cfg.name == "C4":
+        extra = {}
+        for name in EXTRA_WORKLOADS:
+            c = get_config(name)
+            rr = run_workload(c, min(args.steps, 10), min(args.warmup, 3))
+            extra[name] = summarize(c, rr, PEAK_BF16 if c.dtype == "bf16" else PEAK_FP32)
+        out["workloads"] = extra
     if args.prologue:
         out["prologue"] = time_prologue(cfg, args.steps, args.warmup)
     if not args.no_cpu_baseline:

@@ -107,6 +107,24 @@ fa_status_t flash_attn_bwd(const void* Q, const void* K, const void* V, const vo
                            int B, int T, int H, int HKV, int D, float scale, int causal,
                            int window, fa_dtype_t dtype, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): flash_attn_bwd without the per-call
+ * workspace.  Same arguments, kernels and results (bit for bit) as flash_attn_bwd; the Dvec
+ * workspace is instead a fixed array of FA_NOALLOC_MAX_DVEC floats (16 MiB) in device memory
+ * that the library holds on each device it runs on until the process ends.  The call makes no
+ * allocation (no hipMalloc / hipMallocAsync / hipFree) and enqueues only the two kernels.
+ * B * H * T above FA_NOALLOC_MAX_DVEC returns FA_ERR_UNSUPPORTED before anything is enqueued.
+ * Every call on one device shares that device's array: calls that may run at the same time on
+ * one device (other streams, other host threads) race on it and must be ordered by the caller.
+ * The array keeps the last call's contents; nothing in it needs clearing (each call writes
+ * every Dvec value it reads).  The first call on a device looks up the array's address
+ * (hipGetSymbolAddress); later calls reuse it. */
+#define FA_NOALLOC_MAX_DVEC 4194304
+fa_status_t flash_attn_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O,
+                                   const float* L, const void* dO, float* dQ, float* dK,
+                                   float* dV, int B, int T, int H, int HKV, int D, float scale,
+                                   int causal, int window, fa_dtype_t dtype, hipStream_t stream);
+
 /* As flash_attn_fwd / flash_attn_bwd, with the block tiling forced: bq query rows by bk keys
  * per block (0, 0 = the library's choice).  FA_DTYPE_F32 accepts bq in {32, 64} and
  * bk in {16, 32, 64}; the 16-bit types accept (0, 0) or their one tiling.  The tiling decides which blocks
@@ -263,6 +281,17 @@ fa_status_t flash_attn_default_tiles(fa_dtype_t dtype, int D, int pass, int* bq,
  * spanning under 2 GiB), FA_ERR_INVALID_ARG otherwise. */
 fa_status_t flash_attn_check_layout(fa_layout_t layout, int B, int T, int heads, int D,
                                     fa_dtype_t dtype);
+
+/* Measurement helper (not part of the attention path): a kernel of `grid` workgroups of 256
+ * threads (four waves) in which every wave issues iters * 16 bf16 MFMA 32x32x16 operations
+ * (32768 FLOP each) on fixed operands, so the launch performs grid * 4 * iters * 16 * 32768
+ * FLOP.  `operands` holds 4096 bf16 values (lane l's 16-byte fragments at element offsets
+ * (i*64 + l)*8, i < 8), loaded once per wave; their distribution decides the rate, since the
+ * chip's power limit depends on the bits the MFMA units switch.  `out` receives grid * 256
+ * floats (sums of the accumulators, so the work is not optimised away).  Device pointers,
+ * 16-byte aligned; 1 <= grid <= 2^20, 1 <= iters <= 2^24. */
+fa_status_t flash_attn_mfma_rate_probe(const void* operands, float* out, int grid, int iters,
+                                       hipStream_t stream);
 
 /* Library ABI version (major * 100 + minor). */
 int flash_attn_version(void);

@@ -10,15 +10,17 @@ LIB_PATH = os.environ.get("FLASHATTN_LIB", os.path.join(_HERE, "libflashattn.so"
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 FA_DTYPE_F32, FA_DTYPE_BF16, FA_DTYPE_F16 = 0, 1, 2
+FA_NOALLOC_MAX_DVEC = 4194304    # B * H * T limit of flash_attn_bwd_noalloc (include/flash_attn.h)
 
 EXPORTS = [
-    "flash_attn_fwd", "flash_attn_bwd", "flash_attn_fwd_ex", "flash_attn_bwd_ex",
+    "flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_noalloc", "flash_attn_fwd_ex",
+    "flash_attn_bwd_ex",
     "flash_attn_bwd_preprocess", "flash_attn_bwd_dkdv", "flash_attn_bwd_dq",
     "flash_attn_bwd_dq_dvec", "flash_attn_fwd_strided", "flash_attn_bwd_strided",
     "flash_attn_check_layout", "flash_attn_bwd_grad16", "flash_attn_block_class_qk",
     "flash_attn_kv_block_range_qk", "flash_attn_qk_norm_rope",
     "flash_attn_status_string", "flash_attn_block_class", "flash_attn_kv_block_range",
-    "flash_attn_default_tiles", "flash_attn_version",
+    "flash_attn_default_tiles", "flash_attn_version", "flash_attn_mfma_rate_probe",
 ]
 
 _lib = None
@@ -40,6 +42,7 @@ def _declare(lib):
         "flash_attn_fwd": [P, P, P, P, P] + _DIMS,
         "flash_attn_fwd_ex": [P, P, P, P, P] + _DIMS + [I, I],
         "flash_attn_bwd": [P] * 9 + _DIMS,
+        "flash_attn_bwd_noalloc": [P] * 9 + _DIMS,
         "flash_attn_bwd_ex": [P] * 9 + _DIMS + [I, I],
         "flash_attn_bwd_preprocess": [P, P, P, I, I, I, I, I, P],
         "flash_attn_bwd_dkdv": [P] * 8 + _DIMS + [I, I],
@@ -57,6 +60,7 @@ def _declare(lib):
         "flash_attn_kv_block_range": [I, I, I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)],
         "flash_attn_default_tiles": [I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)],
         "flash_attn_version": [],
+        "flash_attn_mfma_rate_probe": [P, P, I, I, P],
         "flash_attn_status_string": [I],
     }
     for name, args in sig.items():

@@ -201,6 +201,23 @@ def flash_attn_bwd(q, k, v, o, lse, do, causal=True, window=0, scale=None, dq=No
     return dq, dk, dv
 
 
+def flash_attn_bwd_noalloc(q, k, v, o, lse, do, causal=True, window=0, scale=None, dq=None,
+                           dk=None, dv=None, stream=None):
+    """flash_attn_bwd with its Dvec workspace in the library's fixed per-device scratch instead
+    of a per-call allocation (B*H*T up to FA_NOALLOC_MAX_DVEC).  Pass dq, dk, dv to keep the
+    whole call free of allocations; calls that may overlap on one device race on the scratch."""
+    B, T, H, HKV, D = _dims(q, k)
+    _want_inputs(q, k, v, o=o, do=do)
+    _want(lse, (B, H, T), torch.float32, "lse", q.device)
+    dq, dk, dv = _grads(q, k, dq, dk, dv)
+    code = _lib.lib().flash_attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                             _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), B, T, H, HKV,
+                                             D, _scale(scale, D), int(bool(causal)), int(window),
+                                             _DT[q.dtype], _stream(stream))
+    _check("flash_attn_bwd_noalloc", code)
+    return dq, dk, dv
+
+
 def _layout(t, name):
     if t.dim() != 4 or t.stride(3) != 1:
         raise ValueError(f"{name}: expected a [B, T, heads, D] view with a contiguous last axis")
@@ -379,6 +396,17 @@ def flash_attn_check_layout(strides, B, T, heads, D, dtype):
     """Status code (0 = usable) of the library's check of element strides (batch, row, head)
     for a [B, T, heads, D] view; dtype 0 = f32, 1 = bf16."""
     return _lib.lib().flash_attn_check_layout(_lib.Layout(*strides), B, T, heads, D, dtype)
+
+
+def flash_attn_mfma_rate_probe(operands, out, grid, iters, stream=None):
+    """Launch the library's MFMA throughput probe (grid * 4 * iters * 16 bf16 32x32x16 MFMAs)
+    on `operands` (4096 bfloat16 values, cuda) writing grid * 256 floats to `out`."""
+    _want(operands, (4096,), torch.bfloat16, "operands")
+    _want(out, (grid * 256,), torch.float32, "out", operands.device)
+    _check("flash_attn_mfma_rate_probe",
+           _lib.lib().flash_attn_mfma_rate_probe(_ptr(operands), _ptr(out), int(grid),
+                                                 int(iters), _stream(stream)))
+    return out
 
 
 def flash_attn_version():

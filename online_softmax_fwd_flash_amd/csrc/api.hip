@@ -12,6 +12,7 @@ namespace {
 constexpr int kF32DefaultBq = 64, kF32DefaultBk = 64;
 // Longest query or key sequence: row and block indices (plus a tile) stay far inside int.
 constexpr int kMaxRows = 1 << 30;
+static_assert(FA_NOALLOC_MAX_DVEC == fa::kNoAllocDvecFloats, "no-alloc scratch size differs");
 
 // A window of at least Tk keys constrains no row (row positions are below Tk), so it is the
 // same as no window; the kernels and helpers take it as 0, which keeps their index arithmetic
@@ -228,11 +229,16 @@ fa_status_t dq_dvec_impl(const void* Q, const void* K, const void* V, const void
     return hip_status(fa::launch_dq_b16_fused_d(a));
 }
 
+// Where the backward's Dvec workspace comes from: allocated stream-ordered per call, or the
+// library's fixed per-device scratch (no allocation).
+enum class Workspace { kStreamOrdered, kFixedScratch };
+
 fa_status_t bwd_impl(const void* Q, const void* K, const void* V, const void* O, const float* L,
                      const void* dO, float* dQ, float* dK, float* dV, int B, int T, int Tk, int H,
                      int HKV, int D, float scale, int causal, int window, fa_dtype_t dtype,
                      hipStream_t stream, int bq, int bk, const fa_layout_t& lq,
-                     const fa_layout_t& lk, int g16 = 0) {
+                     const fa_layout_t& lk, int g16 = 0,
+                     Workspace ws = Workspace::kStreamOrdered) {
     fa_status_t s = check_all({Q, K, V, O, L, dO, dQ, dK, dV}, B, T, Tk, H, HKV, D, scale, causal,
                               window, dtype, lq, lk);
     if (s != FA_OK) return s;
@@ -242,15 +248,24 @@ fa_status_t bwd_impl(const void* Q, const void* K, const void* V, const void* O,
         return FA_ERR_INVALID_ARG;
     }
     float* Dvec = nullptr;
-    const size_t bytes = (size_t)B * H * T * sizeof(float);
-    if (hipMallocAsync((void**)&Dvec, bytes, stream) != hipSuccess) return FA_ERR_HIP;
+    const size_t floats = (size_t)B * H * T;
+    if (ws == Workspace::kFixedScratch) {
+        // every Dvec row the dK/dV pass reads (rows < T) is written by the dQ pass first, so
+        // the scratch needs no clearing between calls
+        if (floats > (size_t)fa::kNoAllocDvecFloats) return FA_ERR_UNSUPPORTED;
+        if (fa::noalloc_dvec(floats, &Dvec) != hipSuccess) return FA_ERR_HIP;
+    } else if (hipMallocAsync((void**)&Dvec, floats * sizeof(float), stream) != hipSuccess) {
+        return FA_ERR_HIP;
+    }
     s = dq_dvec_impl(Q, K, V, O, dO, L, Dvec, dQ, B, T, Tk, H, HKV, D, scale, causal, window, dtype,
                      stream, bq, bk, lq, lk, g16);
     if (s == FA_OK)
         s = dkdv_impl(Q, K, V, dO, L, Dvec, dK, dV, B, T, Tk, H, HKV, D, scale, causal, window,
                       dtype, stream, bq, bk, lq, lk, g16);
-    const hipError_t fe = hipFreeAsync(Dvec, stream);
-    if (s == FA_OK && fe != hipSuccess) s = FA_ERR_HIP;
+    if (ws == Workspace::kStreamOrdered) {
+        const hipError_t fe = hipFreeAsync(Dvec, stream);
+        if (s == FA_OK && fe != hipSuccess) s = FA_ERR_HIP;
+    }
     return s;
 }
 
@@ -269,7 +284,15 @@ const char* flash_attn_status_string(fa_status_t s) {
     return "FA_UNKNOWN_STATUS";
 }
 
-int flash_attn_version(void) { return 101; }
+int flash_attn_version(void) { return 102; }
+
+fa_status_t flash_attn_mfma_rate_probe(const void* operands, float* out, int grid, int iters,
+                                       hipStream_t stream) {
+    fa_status_t s = check_ptrs({operands, out});
+    if (s != FA_OK) return s;
+    if (grid < 1 || grid > (1 << 20) || iters < 1 || iters > (1 << 24)) return FA_ERR_INVALID_ARG;
+    return hip_status(fa::launch_mfma_probe(operands, out, grid, iters, stream));
+}
 
 fa_status_t flash_attn_check_layout(fa_layout_t layout, int B, int T, int heads, int D,
                                     fa_dtype_t dtype) {
@@ -402,6 +425,15 @@ fa_status_t flash_attn_bwd(const void* Q, const void* K, const void* V, const vo
                            fa_dtype_t dtype, hipStream_t stream) {
     return flash_attn_bwd_ex(Q, K, V, O, L, dO, dQ, dK, dV, B, T, H, HKV, D, scale, causal,
                              window, dtype, stream, 0, 0);
+}
+
+fa_status_t flash_attn_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O,
+                                   const float* L, const void* dO, float* dQ, float* dK,
+                                   float* dV, int B, int T, int H, int HKV, int D, float scale,
+                                   int causal, int window, fa_dtype_t dtype, hipStream_t stream) {
+    return bwd_impl(Q, K, V, O, L, dO, dQ, dK, dV, B, T, T, H, HKV, D, scale, causal, window, dtype,
+                    stream, 0, 0, dense_layout(T, H, D), dense_layout(T, HKV, D), 0,
+                    Workspace::kFixedScratch);
 }
 
 fa_status_t flash_attn_bwd_strided(const void* Q, const void* K, const void* V, const void* O,

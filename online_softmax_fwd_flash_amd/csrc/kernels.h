@@ -115,6 +115,20 @@ struct RopeArgs {
 };
 hipError_t launch_qk_norm_rope(const RopeArgs& a);
 
+// Capacity of the fixed device scratch that flash_attn_bwd_noalloc uses for Dvec, in floats
+// (16 MiB per device): B * H * T may not exceed it.
+constexpr int64_t kNoAllocDvecFloats = int64_t(1) << 22;
+
+// Device address of the current device's fixed Dvec scratch (at least `floats` floats); looked
+// up on the first call per device.  No allocation.  hipErrorInvalidValue if `floats` exceeds
+// kNoAllocDvecFloats.
+hipError_t noalloc_dvec(size_t floats, float** out);
+
+// MFMA throughput probe: grid workgroups of 256 threads, each wave running iters x 16
+// bf16 32x32x16 MFMAs on the 4096 bf16 operand values at ops; out gets grid * 256 floats.
+hipError_t launch_mfma_probe(const void* ops, float* out, int grid, int iters,
+                             hipStream_t stream);
+
 // dtype: 0 = f32, 1 = bf16, 2 = fp16
 hipError_t launch_bwd_preprocess(const void* O, const void* dO, float* Dvec, int B, int T,
                                  int H, int D, int dtype, hipStream_t stream, Layout lq);

@@ -1,10 +1,13 @@
 """fp64 reference for exact scaled-dot-product attention with causal / sliding-window masks and
 grouped-query heads.  TEST INFRASTRUCTURE ONLY (see the package docstring).
 
-Everything is the plain definition, materialised: the full score matrix of a (batch, head)
-is formed (in chunks of query rows, which are independent), masked, soft-maxed and multiplied
-by V.  There is no online softmax here, no tiling of the key axis and no recomputation trick;
-those belong to the method under test, not to the oracle.
+Everything is the plain definition, materialised: the score matrix of a (batch, head) is
+formed (in chunks of query rows, which are independent), masked, soft-maxed and multiplied by
+V.  Each chunk of rows is formed against the span of keys that some row of the chunk sees:
+every key outside that span is masked for every row of the chunk, so it would add exactly zero
+to each sum over visible keys that the definition takes.  There is no online softmax here, no
+tiling of the key axis and no recomputation trick; those belong to the method under test, not
+to the oracle.
 
 Sources (web pages, cited by title and section):
   * forge "flash_attention.metal" (S.-P. Boucher), header comment and the forward kernel
@@ -61,6 +64,13 @@ def visible_mask(T, causal, window, rows=None, Tk=None):
     return vis
 
 
+def _key_span(vis):
+    """Slice of the keys that at least one row of the boolean mask `vis` sees (empty when no
+    row sees any)."""
+    seen = np.flatnonzero(vis.any(axis=0))
+    return slice(0, 0) if seen.size == 0 else slice(int(seen[0]), int(seen[-1]) + 1)
+
+
 def _softmax_rows(S, vis):
     """Masked row softmax of S (fp64).  Returns P, m, l; rows with no visible key give P=0,
     m=0, l=0."""
@@ -114,9 +124,11 @@ def attn_fwd(q, k, v, scale, causal, window, row_chunk=1024, pairs=None):
         g = group_of_head(h, H, HKV)
         for r0 in range(0, T, row_chunk):
             rows = np.arange(r0, min(T, r0 + row_chunk))
-            S = scale * (q[b, rows, h, :] @ k[b, :, g, :].T)
-            P, m, l = _softmax_rows(S, visible_mask(T, causal, window, rows, Tk))
-            O[b, rows, h, :] = P @ v[b, :, g, :]
+            vis = visible_mask(T, causal, window, rows, Tk)
+            keys = _key_span(vis)
+            S = scale * (q[b, rows, h, :] @ k[b, keys, g, :].T)
+            P, m, l = _softmax_rows(S, vis[:, keys])
+            O[b, rows, h, :] = P @ v[b, keys, g, :]
             L[b, h, rows] = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), 0.0)
     return O, L
 
@@ -163,16 +175,19 @@ def attn_bwd(q, k, v, do, scale, causal, window, row_chunk=1024, groups=None):
         for h in range(g * rep, (g + 1) * rep):
             for r0 in range(0, T, row_chunk):
                 rows = np.arange(r0, min(T, r0 + row_chunk))
+                vis = visible_mask(T, causal, window, rows, Tk)
+                keys = _key_span(vis)
                 Qc, dOc = q[b, rows, h, :], do[b, rows, h, :]
-                S = scale * (Qc @ Kg.T)
-                P, m, l = _softmax_rows(S, visible_mask(T, causal, window, rows, Tk))
-                Oc = P @ Vg
+                Kc, Vc = Kg[keys], Vg[keys]
+                S = scale * (Qc @ Kc.T)
+                P, m, l = _softmax_rows(S, vis[:, keys])
+                Oc = P @ Vc
                 Dc = (dOc * Oc).sum(axis=1)
-                dP = dOc @ Vg.T
+                dP = dOc @ Vc.T
                 dS = P * (dP - Dc[:, None])
-                dq[b, rows, h, :] = scale * (dS @ Kg)
-                dk[b, :, g, :] += scale * (dS.T @ Qc)
-                dv[b, :, g, :] += P.T @ dOc
+                dq[b, rows, h, :] = scale * (dS @ Kc)
+                dk[b, keys, g, :] += scale * (dS.T @ Qc)
+                dv[b, keys, g, :] += P.T @ dOc
                 O[b, rows, h, :] = Oc
                 L[b, h, rows] = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), 0.0)
                 Dv[b, h, rows] = Dc

@@ -59,6 +59,18 @@ hipError_t launch_bwd_preprocess(const void*, const void*, float*, int, int, int
     g_calls.push_back("preprocess");
     return hipSuccess;
 }
+hipError_t launch_mfma_probe(const void*, float*, int, int, hipStream_t) {
+    g_calls.push_back("mfma_probe");
+    return hipSuccess;
+}
+alignas(256) float g_fake_scratch[64];
+size_t g_scratch_request = 0;
+hipError_t noalloc_dvec(size_t floats, float** out) {
+    g_calls.push_back("scratch");
+    g_scratch_request = floats;
+    *out = floats <= (size_t)kNoAllocDvecFloats ? g_fake_scratch : nullptr;
+    return floats <= (size_t)kNoAllocDvecFloats ? hipSuccess : hipErrorInvalidValue;
+}
 }  // namespace fa
 
 namespace {
@@ -236,6 +248,29 @@ void test_dispatch() {
         CHECK(s == FA_ERR_HIP);
         CHECK(g_calls.empty());
     }
+    // no-allocation backward: the fixed scratch replaces hipMallocAsync (which has no device
+    // to allocate on here), so the two passes run and both see the scratch as Dvec
+    g_calls.clear();
+    CHECK(flash_attn_bwd_noalloc(P(0), P(1), P(2), P(3), (const float*)P(4), P(5), (float*)P(6),
+                                 (float*)P(7), (float*)P(8), d.B, d.T, d.H, d.HKV, d.D, d.scale,
+                                 d.causal, d.window, d.dt, nullptr) == FA_OK);
+    CHECK(g_calls.size() == 3 && g_calls[0] == "scratch" && g_calls[1] == "dq_b16_fused_d" &&
+          g_calls[2] == "dkdv_b16");
+    CHECK(g_last.Dvec == fa::g_fake_scratch && fa::g_scratch_request == (size_t)d.B * d.H * d.T);
+    g_calls.clear();
+    CHECK(flash_attn_bwd_noalloc(P(0), P(1), P(2), P(3), (const float*)P(4), P(5), (float*)P(6),
+                                 (float*)P(7), (float*)P(8), d.B, d.T, d.H, d.HKV, d.D, d.scale,
+                                 d.causal, d.window, FA_DTYPE_F32, nullptr) == FA_OK);
+    CHECK(g_calls.size() == 4 && g_calls[1] == "preprocess" && g_calls[3] == "dkdv_f32");
+    // beyond the scratch: refused before anything is looked up or launched
+    g_calls.clear();
+    CHECK(flash_attn_bwd_noalloc(P(0), P(1), P(2), P(3), (const float*)P(4), P(5), (float*)P(6),
+                                 (float*)P(7), (float*)P(8), 2, FA_NOALLOC_MAX_DVEC / 16 + 1, 8,
+                                 2, 64, d.scale, 1, 0, d.dt, nullptr) == FA_ERR_UNSUPPORTED);
+    CHECK(flash_attn_bwd_noalloc(P(0), P(1), P(2), P(3), (const float*)P(4), P(5), nullptr,
+                                 (float*)P(7), (float*)P(8), d.B, d.T, d.H, d.HKV, d.D, d.scale,
+                                 d.causal, d.window, d.dt, nullptr) == FA_ERR_INVALID_ARG);
+    CHECK(g_calls.empty());
     // strided, Tq != Tk
     fa_layout_t lq{(int64_t)d.H * 24 * d.D, d.D, (int64_t)24 * d.D};
     fa_layout_t lk{(int64_t)d.HKV * 56 * d.D, d.D, (int64_t)56 * d.D};
@@ -249,6 +284,13 @@ void test_dispatch() {
                                   P(3), P(4), 16, 4, 64, 64, 0, 1, FA_DTYPE_BF16, nullptr) ==
           FA_OK);
     CHECK(g_calls.size() == 1 && g_calls[0] == "rope");
+    g_calls.clear();
+    CHECK(flash_attn_mfma_rate_probe(P(0), (float*)P(1), 0, 10, nullptr) == FA_ERR_INVALID_ARG);
+    CHECK(flash_attn_mfma_rate_probe(P(0), (float*)P(1), 8, 0, nullptr) == FA_ERR_INVALID_ARG);
+    CHECK(flash_attn_mfma_rate_probe(MIS, (float*)P(1), 8, 10, nullptr) == FA_ERR_INVALID_ARG);
+    CHECK(g_calls.empty());
+    CHECK(flash_attn_mfma_rate_probe(P(0), (float*)P(1), 8, 10, nullptr) == FA_OK);
+    CHECK(g_calls.size() == 1 && g_calls[0] == "mfma_probe");
 }
 
 // Visibility of (row r, key c) by the definition in flash_attn.h.

@@ -4,6 +4,7 @@ Each check takes an oracle-like module (attn_fwd, attn_bwd, attn_probs, group_of
 raises AssertionError on failure, so the same checks run against the real oracle
 (test_oracle_pins.py) and against copies with a planted mistake (test_oracle_mutants.py).
 """
+import itertools
 import math
 
 import numpy as np
@@ -96,16 +97,19 @@ def check_lse(ora):
         assert np.allclose(L, want, atol=1e-13, rtol=0)
 
 
-def check_sdpa(ora, shapes=((2, 10, 4, 2, 6), (1, 17, 3, 3, 8), (1, 8, 8, 1, 4))):
+def check_sdpa(ora, shapes=((2, 10, 4, 2, 6), (1, 17, 3, 3, 8), (1, 8, 8, 1, 4)),
+               row_chunks=(1024, 3)):
     """O, dQ, dK, dV against CPU fp64 torch scaled_dot_product_attention with autograd
-    (GQA through repeat_interleave, i.e. contiguous head groups; masks as explicit booleans)."""
-    for n, (B, T, H, HKV, D) in enumerate(shapes):
+    (GQA through repeat_interleave, i.e. contiguous head groups; masks as explicit booleans).
+    Row chunks of 3 make the oracle form most chunks against a strict sub-span of the keys
+    (the causal bound, the window), so that path is held to the library routine too."""
+    for (n, (B, T, H, HKV, D)), chunk in itertools.product(enumerate(shapes), row_chunks):
         q, k, v, do = make_inputs_like(B, T, H, HKV, D, "f32", 100 + n)
         q, k, v, do = (t.double() for t in (q, k, v, do))
         for causal, window in MASKS:
             scale = 1.0 / math.sqrt(D) * (1.5 if n == 1 else 1.0)
-            res = ora.attn_bwd(q, k, v, do, scale, causal, window)
-            O, L = ora.attn_fwd(q, k, v, scale, causal, window)
+            res = ora.attn_bwd(q, k, v, do, scale, causal, window, row_chunk=chunk)
+            O, L = ora.attn_fwd(q, k, v, scale, causal, window, row_chunk=chunk)
             qt = q.permute(0, 2, 1, 3).clone().requires_grad_()
             kt = k.permute(0, 2, 1, 3).clone().requires_grad_()
             vt = v.permute(0, 2, 1, 3).clone().requires_grad_()

@@ -32,7 +32,7 @@ def test_header_and_exports_agree():
 
 
 def test_version_and_strings():
-    assert fa.flash_attn_version() == 101
+    assert fa.flash_attn_version() == 102
     assert _lib.status_string(0) == "FA_OK"
     assert _lib.status_string(2) == "FA_ERR_UNSUPPORTED"
 

@@ -33,6 +33,7 @@ CHILD = textwrap.dedent('''
         dims = (1, 16, 4, 2, D, 0.125, 1, 0, dt, S0)
         print("fwd", dt, D, L.flash_attn_fwd(A, A, A, A, A, *dims))
         print("bwd", dt, D, L.flash_attn_bwd(*([A] * 9), *dims))
+        print("bwd_noalloc", dt, D, L.flash_attn_bwd_noalloc(*([A] * 9), *dims))
         print("dkdv", dt, D, L.flash_attn_bwd_dkdv(*([A] * 8), *dims, 0, 0))
         print("dq_dvec", dt, D, L.flash_attn_bwd_dq_dvec(*([A] * 8), *dims, 0, 0))
     print("pre", L.flash_attn_bwd_preprocess(A, A, A, 1, 16, 4, 64, 1, S0))
@@ -40,6 +41,9 @@ CHILD = textwrap.dedent('''
                                                   0, 1, S0, lay_q, lay_k))
     print("rope", L.flash_attn_qk_norm_rope(A, 8 * 64, 64, A, A, 64, A, A, 16, 4, 64, 64, 0, 0,
                                             1, S0))
+    # beyond the fixed scratch: refused (FA_ERR_UNSUPPORTED) before any HIP call
+    print("noalloc_too_big", L.flash_attn_bwd_noalloc(*([A] * 9), 2, _lib.FA_NOALLOC_MAX_DVEC // 16
+                                                       + 1, 8, 2, 64, 0.125, 1, 0, 1, S0))
     print("DONE")
 ''')
 
@@ -60,9 +64,11 @@ def run_child(env_extra):
 
 def test_runtime_failures_map_to_fa_err_hip():
     r = run_child({})
-    codes = [line.split()[-1] for line in r.stdout.splitlines() if line and line != "DONE"]
-    assert len(codes) == 19
-    assert set(codes) == {"3"}, r.stdout
+    lines = [line.split() for line in r.stdout.splitlines() if line and line != "DONE"]
+    codes = {" ".join(x[:-1]): x[-1] for x in lines}
+    assert len(codes) == 24
+    assert codes.pop("noalloc_too_big") == "2"
+    assert set(codes.values()) == {"3"}, r.stdout
     assert "flash_attn:" not in r.stderr
 
 

@@ -23,10 +23,10 @@ def _load(fname, old, new, extra_subs=()):
 
 ATTN_MUTANTS = {
     "dropped_D_term": ("dS = P * (dP - Dc[:, None])", "dS = P * dP"),
-    "dq_without_scale": ("dq[b, rows, h, :] = scale * (dS @ Kg)", "dq[b, rows, h, :] = dS @ Kg"),
-    "dk_wrong_operand": ("dk[b, :, g, :] += scale * (dS.T @ Qc)",
-                         "dk[b, :, g, :] += scale * (dS.T @ dOc)"),
-    "dv_transposed_P": ("dv[b, :, g, :] += P.T @ dOc", "dv[b, :, g, :] += P @ dOc"),
+    "dq_without_scale": ("dq[b, rows, h, :] = scale * (dS @ Kc)", "dq[b, rows, h, :] = dS @ Kc"),
+    "dk_wrong_operand": ("dk[b, keys, g, :] += scale * (dS.T @ Qc)",
+                         "dk[b, keys, g, :] += scale * (dS.T @ dOc)"),
+    "dv_transposed_P": ("dv[b, keys, g, :] += P.T @ dOc", "dv[b, keys, g, :] += P @ dOc"),
     "gqa_modulo_map": ("return h // (H // HKV)", "return h % HKV"),
     "causal_drops_diagonal": ("vis &= j <= p", "vis &= j < p"),
     "window_off_by_one": ("vis &= j >= p - window + 1", "vis &= j >= p - window"),
@@ -34,8 +34,14 @@ ATTN_MUTANTS = {
     "rect_offset_sign": ("p = i + (Tk - T)", "p = i + (T - Tk)"),
     "lse_log2": ("L[b, h, rows] = np.where(l > 0, m + np.log(",
                  "L[b, h, rows] = np.where(l > 0, m + np.log2("),
-    "fwd_missing_scale": ("S = scale * (q[b, rows, h, :] @ k[b, :, g, :].T)",
-                          "S = (q[b, rows, h, :] @ k[b, :, g, :].T)"),
+    "fwd_missing_scale": ("S = scale * (q[b, rows, h, :] @ k[b, keys, g, :].T)",
+                          "S = (q[b, rows, h, :] @ k[b, keys, g, :].T)"),
+    "key_span_drops_last_key": ("slice(int(seen[0]), int(seen[-1]) + 1)",
+                                "slice(int(seen[0]), int(seen[-1]))"),
+    "key_span_skips_first_key": ("slice(int(seen[0]), int(seen[-1]) + 1)",
+                                 "slice(int(seen[0]) + 1, int(seen[-1]) + 1)"),
+    "key_span_misaligned_mask": ("P, m, l = _softmax_rows(S, vis[:, keys])",
+                                 "P, m, l = _softmax_rows(S, vis[:, :S.shape[1]])"),
     "softmax_without_max_shift_sign": ("np.exp(Sm - m[:, None])", "np.exp(Sm + m[:, None])"),
 }
 
