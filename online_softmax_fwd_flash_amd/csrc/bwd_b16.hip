@@ -136,6 +136,136 @@ __device__ __forceinline__ typename E::v8 tr_operand(const uint16_t* tile, int k
 
 }  // namespace
 
+// Loop-invariant values of one wave's walk over its (query head, query block) pairs.
+template <int D>
+struct DkdvCtx {
+    using C = Dkdv16Cfg<D>;
+    QdoSrc qs;
+    const float *Lg, *Dg;                    // the group's first head's L and Dvec rows
+    uint32_t voff[C::PMAX + 1];              // LDS-DMA source offsets of this lane
+    uint32_t aq;      // A-operand reads of the Q tile (stage 0; the dO tile is OFF_DO further)
+    uint32_t tr;      // transpose reads of the Q tile (stage 0; dO likewise)
+    uint32_t ld;      // this lane's L values (stage 0; its D values are 256 bytes further)
+    int w, rep, niter, if0, if1, T, Tk, kw0, window, qlo, qn, g;
+    bool cz;
+    float c;          // scale * log2(e)
+    __device__ __forceinline__ DkdvCtx(const QdoSrc& q) : qs(q) {}
+};
+
+// Accumulators and operands of one wave: K and -V of its keys (the B operands of S = Q K^T
+// and of D - dP = D - dO V^T), and its dK (negated, see below) and dV columns.
+template <class E, int D>
+struct DkdvState {
+    using C = Dkdv16Cfg<D>;
+    typename E::v8 kreg[C::DS], vneg[C::DS];
+    f32x4 dka[C::NDB], dva[C::NDB];
+};
+
+// One (query head h2, query block i) pair, staged in LDS stage STG (a compile-time constant:
+// every LDS address is a pinned per-lane base plus an immediate offset).  (h2n, in) is the
+// pair after it, whose LDS-DMA goes into the other stage after the barrier.
+//
+// The dP accumulators start at +D with -V as operand, so the MFMAs leave D - dP; P (D - dP)
+// is then -dS and dK accumulates -dS^T Q, negated again (with the scale) at the store.  Each
+// negation is exact, so the stored dK equals the one from dS itself bit for bit.
+template <class E, int D, int STG>
+__device__ __forceinline__ void dkdv_block(DkdvState<E, D>& st, const DkdvCtx<D>& x, char* sm,
+                                           int it, int i, int h2n, int in) {
+    using C = Dkdv16Cfg<D>;
+    using V8 = typename E::v8;
+    using V4 = typename E::v4;
+    using S16 = typename E::s;
+    // scalar block test before the wait, only outside the FULL range
+    const int qr0 = i * C::BQ;
+    int cls = kFull;
+    if (i < x.if0 || i >= x.if1) {
+        keep_branch();
+        cls = block_class(x.T, x.Tk, qr0, qr0 + C::BQ, x.kw0, x.kw0 + C::KPW, x.cz, x.window);
+    }
+    wait_vmcnt<0>();   // this stage's pieces, the only loads in flight
+    // every wave's pieces are visible; every wave is done with the other stage
+    lds_barrier();
+    if (it + 1 < x.niter) dkdv16_issue<D>(sm, x.qs, x.Lg, x.Dg, x.voff, x.w, h2n, in, x.T, STG ^ 1);
+    if (cls == kSkip) return;
+    constexpr uint32_t SO = STG * C::STAGE;
+    // S and D - dP for the 16-row blocks; entry r of lane (n, g): row 16qb + 4g + r, key n
+    f32x4 sc[C::QB16], dp[C::QB16];
+#pragma unroll
+    for (int qb = 0; qb < C::QB16; ++qb) {
+        sc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dp[qb] = lds_load<f32x4>(x.ld + SO + 256 + qb * 64);
+        V8 aq[C::DS], ao[C::DS];
+#pragma unroll
+        for (int ds = 0; ds < C::DS; ++ds) {
+            const uint32_t off = SO + 2 * (qb * 16 * C::LDN + ds * 32);
+            aq[ds] = lds_load<V8>(x.aq + off);
+            ao[ds] = lds_load<V8>(x.aq + C::OFF_DO + off);
+        }
+#pragma unroll
+        for (int ds = 0; ds < C::DS; ++ds) {
+            sc[qb] = mfma16x16x32(aq[ds], st.kreg[ds], sc[qb]);
+            dp[qb] = mfma16x16x32(ao[ds], st.vneg[ds], dp[qb]);
+        }
+    }
+    // rows past T have L = D = 0 and zero Q / dO: they add nothing
+#pragma unroll
+    for (int qb = 0; qb < C::QB16; ++qb) {
+        const f32x4 l4 = lds_load<f32x4>(x.ld + SO + qb * 64);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[qb][r] = fast_exp2(fmaf(sc[qb][r], x.c, -l4[r] * kLog2e));
+    }
+    if (cls == kPartial) {
+        keep_branch();
+#pragma unroll
+        for (int qb = 0; qb < C::QB16; ++qb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int qi = qr0 + qb * 16 + 4 * x.g + r;
+                if ((unsigned)(qi - x.qlo) >= (unsigned)x.qn) sc[qb][r] = 0.f;
+            }
+    }
+    V8 pp[C::KKS], pd[C::KKS];
+#pragma unroll
+    for (int qb = 0; qb < C::QB16; ++qb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            // k-step kk = qb/2 takes rows of blocks 2kk (elements 0-3), 2kk+1 (4-7)
+            pp[qb >> 1][4 * (qb & 1) + r] = (S16)sc[qb][r];
+            pd[qb >> 1][4 * (qb & 1) + r] = (S16)(sc[qb][r] * dp[qb][r]);   // -dS
+        }
+    // dV += P^T dO and -dK += (-dS)^T Q, 32 query rows per k-step; raised wave priority
+    // while these MFMAs issue (measured about 1% faster).  B operands: rows 32kk +
+    // 16*(e/4) + 4g + e%4 of column 16db + i, two transpose reads of 4 rows each.
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int kk = 0; kk < C::KKS; ++kk)
+#pragma unroll
+        for (int d0 = 0; d0 < C::NDB; d0 += 4) {
+            V8 bo[4], bq[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t off = SO + 2 * (32 * kk * C::LDN + 16 * (d0 + u));
+                const V4 ol = lds_load_tr4<E>(x.tr + C::OFF_DO + off);
+                const V4 oh = lds_load_tr4<E>(x.tr + C::OFF_DO + off + 32 * C::LDN);
+                const V4 ql = lds_load_tr4<E>(x.tr + off);
+                const V4 qh = lds_load_tr4<E>(x.tr + off + 32 * C::LDN);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    bo[u][e] = ol[e];
+                    bo[u][4 + e] = oh[e];
+                    bq[u][e] = ql[e];
+                    bq[u][4 + e] = qh[e];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                st.dva[d0 + u] = mfma16x16x32(pp[kk], bo[u], st.dva[d0 + u]);
+                st.dka[d0 + u] = mfma16x16x32(pd[kk], bq[u], st.dka[d0 + u]);
+            }
+        }
+    __builtin_amdgcn_s_setprio(0);
+}
+
 template <class E, int D>
 __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv_b16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -145,7 +275,6 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv_b16_kernel(
     int window, Layout lq, Layout lk, int g16) {
     using C = Dkdv16Cfg<D>;
     using V8 = typename E::v8;
-    using S16 = typename E::s;
     extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
     char* sm = reinterpret_cast<char*>(smem);
 
@@ -160,148 +289,99 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv_b16_kernel(
     const int kw0 = kt * C::BKW + w * C::KPW;
     const int key = kw0 + n;
     const int64_t ldq = lq.t, ldk = lk.t;   // row strides (elements)
-    const bool cz = causal != 0;
-    const float c = scale * kLog2e;
-    // queries that see this lane's key: [qlo, qhi] (lanes of keys past T are never stored)
-    int qlo, qn;
-    key_rows(key, T, Tk, cz, window, qlo, qn);
 
-    // B operands of S = Q K^T and dP = dO V^T: lane (n, g) holds K/V[key][32*ds + 8g .. +7]
-    V8 kreg[C::DS], vreg[C::DS];
-    {
-        const Buf kb = head_buf<D>(K + b * lk.b + hk * lk.h, ldk, Tk);
-        const Buf vb = head_buf<D>(V + b * lk.b + hk * lk.h, ldk, Tk);
-        const uint32_t off = (uint32_t)key * (uint32_t)(ldk * 2) + 16 * g;
-#pragma unroll
-        for (int ds = 0; ds < C::DS; ++ds) {
-            kreg[ds] = __builtin_bit_cast(V8, kb.load16(off + ds * 64));
-            vreg[ds] = __builtin_bit_cast(V8, vb.load16(off + ds * 64));
-        }
-    }
-    f32x4 dka[C::NDB], dva[C::NDB];
-#pragma unroll
-    for (int i = 0; i < C::NDB; ++i) dka[i] = dva[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    int ilo, ihi;
-    q_block_range(T, Tk, kt * C::BKW, kt * C::BKW + C::BKW, C::BQ, cz, window, ilo, ihi);
-    int if0, if1;   // query blocks that are FULL for this wave's keys
-    full_q_block_range(T, Tk, kw0, kw0 + C::KPW, C::BQ, cz, window, if0, if1);
-    const int niter = rep * (ihi - ilo);
     // the group's first query head; head h2 of the group is h2 * lq.h elements further
     const uint32_t ldq_b = (uint32_t)(ldq * 2);
     const uint16_t* Qg = Q + b * lq.b + (int64_t)hk * rep * lq.h;
     const uint16_t* dOg = dO + b * lq.b + (int64_t)hk * rep * lq.h;
     const uint32_t gspan = (uint32_t)(((int64_t)(rep - 1) * lq.h + (int64_t)(T - 1) * ldq + D) * 2);
-    const QdoSrc qs{Buf(Qg, gspan), Buf(dOg, gspan), Qg, dOg, ldq, lq.h,
-                    ldq >= (int64_t)(rep - 1) * lq.h + D};
-    const float* Lg = L + ((int64_t)b * H + (int64_t)hk * rep) * T;
-    const float* Dg = Dv + ((int64_t)b * H + (int64_t)hk * rep) * T;
-    uint32_t voff[C::PMAX + 1];
+    DkdvCtx<D> x(QdoSrc{Buf(Qg, gspan), Buf(dOg, gspan), Qg, dOg, ldq, lq.h,
+                        ldq >= (int64_t)(rep - 1) * lq.h + D});
+    x.Lg = L + ((int64_t)b * H + (int64_t)hk * rep) * T;
+    x.Dg = Dv + ((int64_t)b * H + (int64_t)hk * rep) * T;
+    x.w = w;
+    x.rep = rep;
+    x.T = T;
+    x.Tk = Tk;
+    x.kw0 = kw0;
+    x.window = window;
+    x.g = g;
+    x.cz = causal != 0;
+    x.c = scale * kLog2e;
+    // queries that see this lane's key: [qlo, qlo + qn) (lanes of keys past T are never stored)
+    key_rows(key, T, Tk, x.cz, window, x.qlo, x.qn);
+
+    DkdvState<E, D> st;
+    // B operands of S = Q K^T and D - dP = D - dO V^T: lane (n, g) holds K[key][32*ds + 8g ..
+    // +7] and the same elements of V negated (sign bits flipped: exact)
+    {
+        const Buf kb = head_buf<D>(K + b * lk.b + hk * lk.h, ldk, Tk);
+        const Buf vb = head_buf<D>(V + b * lk.b + hk * lk.h, ldk, Tk);
+        const uint32_t off = (uint32_t)key * (uint32_t)(ldk * 2) + 16 * g;
+        const u32x4 sign = {0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+#pragma unroll
+        for (int ds = 0; ds < C::DS; ++ds) {
+            st.kreg[ds] = __builtin_bit_cast(V8, kb.load16(off + ds * 64));
+            st.vneg[ds] = __builtin_bit_cast(V8, vb.load16(off + ds * 64) ^ sign);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < C::NDB; ++i) st.dka[i] = st.dva[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    int ilo, ihi;
+    q_block_range(T, Tk, kt * C::BKW, kt * C::BKW + C::BKW, C::BQ, x.cz, window, ilo, ihi);
+    // query blocks that are FULL for this wave's keys
+    full_q_block_range(T, Tk, kw0, kw0 + C::KPW, C::BQ, x.cz, window, x.if0, x.if1);
+    x.niter = rep * (ihi - ilo);
 #pragma unroll
     for (int i = 0; i < C::PMAX; ++i)
-        voff[i] = dma_src_offset_padded<D, 2>(w % C::QW + C::QW * i, lane, ldq_b);
-    voff[C::PMAX] = 4u * (uint32_t)lane;
+        x.voff[i] = dma_src_offset_padded<D, 2>(w % C::QW + C::QW * i, lane, ldq_b);
+    x.voff[C::PMAX] = 4u * (uint32_t)lane;
+    // per-lane LDS read bases in stage 0 (Q tile; dO is OFF_DO further): A-operand row n at
+    // column 8g; transpose-read row 4g + j/4 at column 4*(j%4) (j = lane % 16); L / D of rows
+    // 4g .. 4g + 3
+    {
+        const int j = lane & 15;
+        x.aq = pinned_lds_addr(lds_addr(sm + 2 * (n * C::LDN + 8 * g)));
+        x.tr = pinned_lds_addr(lds_addr(sm + 2 * ((4 * g + (j >> 2)) * C::LDN + 4 * (j & 3))));
+        x.ld = pinned_lds_addr(lds_addr(sm + C::OFF_L + 16 * g));
+    }
 
     // Query blocks are walked last-first (heads inner): every key block of a KV group needs
     // the last query blocks, so the group's co-resident workgroups (same XCD) stream the same
     // Q / dO blocks at about the same time and share them in L2.
     // iteration it takes query block ihi - 1 - it / rep of head it % rep; (h2n, in) steps
-    // through that sequence one iteration ahead (no divisions in the loop)
+    // through that sequence one iteration ahead (no divisions in the loop).  Iterations
+    // alternate between the two LDS stages: two per trip, stage 0 then stage 1.
     int h2n = 0, in = ihi - 1;
-    if (niter > 0) dkdv16_issue<D>(sm, qs, Lg, Dg, voff, w, h2n, in, T, 0);
-    for (int it = 0; it < niter; ++it) {
+    if (x.niter > 0) dkdv16_issue<D>(sm, x.qs, x.Lg, x.Dg, x.voff, w, h2n, in, T, 0);
+    int it = 0;
+    for (; it + 1 < x.niter; it += 2) {
+        int i = in;
+        if (++h2n == rep) {
+            h2n = 0;
+            --in;
+        }
+        dkdv_block<E, D, 0>(st, x, sm, it, i, h2n, in);
+        i = in;
+        if (++h2n == rep) {
+            h2n = 0;
+            --in;
+        }
+        dkdv_block<E, D, 1>(st, x, sm, it + 1, i, h2n, in);
+    }
+    if (it < x.niter) {
         const int i = in;
         if (++h2n == rep) {
             h2n = 0;
             --in;
         }
-        // scalar block test before the wait, only outside the FULL range
-        const int qr0 = i * C::BQ;
-        int cls = kFull;
-        if (i < if0 || i >= if1) {
-            keep_branch();
-            cls = block_class(T, Tk, qr0, qr0 + C::BQ, kw0, kw0 + C::KPW, cz, window);
-        }
-        wait_vmcnt<0>();   // this stage's pieces, the only loads in flight
-        // every wave's pieces are visible; every wave is done with the other stage
-        lds_barrier();
-        if (it + 1 < niter) dkdv16_issue<D>(sm, qs, Lg, Dg, voff, w, h2n, in, T, (it + 1) & 1);
-        if (cls == kSkip) continue;
-        const char* stg = sm + (it & 1) * C::STAGE;
-        const uint16_t* Qn = reinterpret_cast<const uint16_t*>(stg);
-        const uint16_t* dOn = reinterpret_cast<const uint16_t*>(stg + C::OFF_DO);
-        const float* Ls = reinterpret_cast<const float*>(stg + C::OFF_L);
-        const float* Ds = Ls + 64;
-        // S, dP - D for the 16-row blocks; entry r of lane (n, g): row 16qb + 4g + r, key n.
-        // The dP accumulators start at -D of their rows, so the MFMAs leave dP - D.
-        f32x4 sc[C::QB16], dp[C::QB16];
-#pragma unroll
-        for (int qb = 0; qb < C::QB16; ++qb) {
-            sc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            dp[qb] = -*reinterpret_cast<const f32x4*>(Ds + qb * 16 + 4 * g);
-            V8 aq[C::DS], ao[C::DS];
-#pragma unroll
-            for (int ds = 0; ds < C::DS; ++ds) {
-                const int off = (qb * 16 + n) * C::LDN + ds * 32 + 8 * g;
-                aq[ds] = *reinterpret_cast<const V8*>(Qn + off);
-                ao[ds] = *reinterpret_cast<const V8*>(dOn + off);
-            }
-#pragma unroll
-            for (int ds = 0; ds < C::DS; ++ds) {
-                sc[qb] = mfma16x16x32(aq[ds], kreg[ds], sc[qb]);
-                dp[qb] = mfma16x16x32(ao[ds], vreg[ds], dp[qb]);
-            }
-        }
-        // rows past T have L = D = 0 and zero Q / dO: they add nothing
-#pragma unroll
-        for (int qb = 0; qb < C::QB16; ++qb) {
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + qb * 16 + 4 * g);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sc[qb][r] = fast_exp2(fmaf(sc[qb][r], c, -l4[r] * kLog2e));
-        }
-        if (cls == kPartial) {
-            keep_branch();
-#pragma unroll
-            for (int qb = 0; qb < C::QB16; ++qb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int qi = qr0 + qb * 16 + 4 * g + r;
-                    if ((unsigned)(qi - qlo) >= (unsigned)qn) sc[qb][r] = 0.f;
-                }
-        }
-        V8 pp[C::KKS], pd[C::KKS];
-#pragma unroll
-        for (int qb = 0; qb < C::QB16; ++qb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                // k-step kk = qb/2 takes rows of blocks 2kk (elements 0-3), 2kk+1 (4-7)
-                pp[qb >> 1][4 * (qb & 1) + r] = (S16)sc[qb][r];
-                pd[qb >> 1][4 * (qb & 1) + r] = (S16)(sc[qb][r] * dp[qb][r]);
-            }
-        // dV += P^T dO and dK += dS^T Q, 32 query rows per k-step; raised wave priority
-        // while these MFMAs issue (measured about 1% faster)
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int kk = 0; kk < C::KKS; ++kk)
-#pragma unroll
-            for (int d0 = 0; d0 < C::NDB; d0 += 4) {
-                V8 bo[4], bq[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    bo[u] = tr_operand<E, C::LDN>(dOn, kk, d0 + u, lane);
-                    bq[u] = tr_operand<E, C::LDN>(Qn, kk, d0 + u, lane);
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    dva[d0 + u] = mfma16x16x32(pp[kk], bo[u], dva[d0 + u]);
-                    dka[d0 + u] = mfma16x16x32(pd[kk], bq[u], dka[d0 + u]);
-                }
-            }
-        __builtin_amdgcn_s_setprio(0);
+        dkdv_block<E, D, 0>(st, x, sm, it, i, h2n, in);
     }
 
-    // entry r of lane (n, g) in block db: key kw0 + 4g + r, column db*16 + n.  Stored as
-    // float32, or (g16) rounded to the element type.
+    // entry r of lane (n, g) in block db: key kw0 + 4g + r, column db*16 + n.  dka holds -dK /
+    // scale.  Stored as float32, or (g16) rounded to the element type.
+    const float nscale = -scale;
     const int64_t kbase = b * lk.b + hk * lk.h;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -313,14 +393,14 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv_b16_kernel(
                 typename E::s* dVh = reinterpret_cast<typename E::s*>(dV) + row;
 #pragma unroll
                 for (int db = 0; db < C::NDB; ++db) {
-                    dKh[db * 16] = (typename E::s)opaque(dka[db][r] * scale);
-                    dVh[db * 16] = (typename E::s)opaque(dva[db][r]);
+                    dKh[db * 16] = (typename E::s)opaque(st.dka[db][r] * nscale);
+                    dVh[db * 16] = (typename E::s)opaque(st.dva[db][r]);
                 }
             } else {
 #pragma unroll
                 for (int db = 0; db < C::NDB; ++db) {
-                    dK[row + db * 16] = dka[db][r] * scale;
-                    dV[row + db * 16] = dva[db][r];
+                    dK[row + db * 16] = st.dka[db][r] * nscale;
+                    dV[row + db * 16] = st.dva[db][r];
                 }
             }
         }

@@ -71,13 +71,14 @@ struct Bf16Fwd {
 template <int D>
 __device__ __forceinline__ void fwd_issue(const Buf& kb, const Buf& vb, const uint32_t* koff,
                                           const uint32_t* voff, char* stage, int wu,
-                                          uint32_t ld_bytes, int jb) {
+                                          uint32_t ld_bytes, int jb, int klast) {
     using C = Bf16Fwd<D>;
     const int soff = __builtin_amdgcn_readfirstlane((int)((uint32_t)jb * kBK * ld_bytes));
-    // pieces wu + i*NW exist for every wave except possibly the last one
+    // pieces wu + i*NW exist for every wave except possibly the last one (klast: this wave's
+    // last piece exists; a wave-uniform value)
 #pragma unroll
     for (int i = 0; i < C::KMAX; ++i)
-        if (i < C::KMAX - 1 || wu + i * C::NW < C::KPIECES)
+        if (i < C::KMAX - 1 || klast)
             dma_piece(kb, stage + (wu + i * C::NW) * 1024, koff[i], soff);
     char* vbase = stage + C::KTILEB + wu * C::VPW * 1024;
 #pragma unroll
@@ -85,6 +86,164 @@ __device__ __forceinline__ void fwd_issue(const Buf& kb, const Buf& vb, const ui
 }
 
 }  // namespace
+
+// Loop-invariant values of one wave's walk over its key blocks.
+template <int D>
+struct FwdCtx {
+    using C = Bf16Fwd<D>;
+    Buf kbuf, vbuf;
+    uint32_t koff[C::KMAX], voff[C::VPW];   // LDS-DMA source offsets of this lane's pieces
+    uint32_t kp;                             // K operand reads: stage-0 LDS address
+    uint32_t vp[C::NDB];                     // V^T operand transpose reads: stage-0 addresses
+    uint32_t ldk_b;                          // key row stride (bytes)
+    int wu;                                  // wave index (uniform)
+    int klast;                               // this wave fills the last K piece (uniform)
+    int jhi, jf0, jf1;                       // block range end; FULL blocks [jf0, jf1)
+    int T, Tk, wr0, window;
+    bool cz;
+    int klo, kn;                             // keys this lane's query row sees
+    int g;                                   // lane half
+    float c;                                 // scale * log2(e)
+    float inv8c;                             // 8 / c: rescale threshold above the running max
+    __device__ __forceinline__ FwdCtx(const Buf& k, const Buf& v) : kbuf(k), vbuf(v) {}
+};
+
+// Online-softmax state of one wave: Q^T operands, O^T accumulators, and per query row the
+// running max m (raw score units), the rescale threshold thr = m + 8/c, m*c (clamped finite)
+// and the running sum.
+template <class E, int D>
+struct FwdState {
+    using C = Bf16Fwd<D>;
+    typename E::v8 qreg[C::DC];
+    f32x16 oacc[C::NDB];
+    float m, thr, mc, lsum;
+};
+
+// One key block j, staged in LDS stage STG (a compile-time constant, so every LDS address is
+// a per-lane base plus an immediate offset).  Issues the next block's LDS-DMA into the other
+// stage after the barrier.
+template <class E, int D, int STG>
+__device__ __forceinline__ void fwd_block(FwdState<E, D>& st, const FwdCtx<D>& x, char* sm,
+                                          int j) {
+    using C = Bf16Fwd<D>;
+    using V8 = typename E::v8;
+    using V4 = typename E::v4;
+    // scalar block test before the wait, only outside the FULL range
+    int cls = kFull;
+    if (j < x.jf0 || j >= x.jf1) {
+        keep_branch();
+        cls = block_class(x.T, x.Tk, x.wr0, x.wr0 + 32, j * kBK, j * kBK + kBK, x.cz, x.window);
+    }
+    wait_vmcnt<0>();   // block j's pieces, the only ones in flight
+    // all pieces visible; every wave is done with the other stage (block j - 1)
+    lds_barrier();
+    if (j + 1 < x.jhi)
+        fwd_issue<D>(x.kbuf, x.vbuf, x.koff, x.voff, sm + (STG ^ 1) * C::STAGEB, x.wu, x.ldk_b,
+                     j + 1, x.klast);
+    if (cls == kSkip) return;
+    // S^T for the block's 32-key halves: entry r of lane (n, g) in s[hk] is key
+    // j*BK + 32*hk + 8*(r/4) + 4g + r%4 of query n
+    f32x16 s[kNH];
+#pragma unroll
+    for (int hk = 0; hk < kNH; ++hk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[hk][r] = 0.f;
+    V8 ka[C::DC][kNH];
+#pragma unroll
+    for (int dc = 0; dc < C::DC; ++dc)
+#pragma unroll
+        for (int hk = 0; hk < kNH; ++hk)
+            ka[dc][hk] = lds_load<V8>(x.kp + STG * C::STAGEB + 32 * dc + 32 * hk * C::KROWB);
+#pragma unroll
+    for (int dc = 0; dc < C::DC; ++dc)
+#pragma unroll
+        for (int hk = 0; hk < kNH; ++hk) s[hk] = mfma32x32x16(ka[dc][hk], st.qreg[dc], s[hk]);
+    // schedule: the first DC K reads up front, then one read per MFMA, so the LDS
+    // latency hides behind the MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, C::DC, 0);
+#pragma unroll
+    for (int i = 0; i < (kNH * C::DC) / 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, (kNH * C::DC) / 2, 0);
+    if (cls == kPartial) {
+        keep_branch();
+#pragma unroll
+        for (int hk = 0; hk < kNH; ++hk)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int k0 = j * kBK + 32 * hk + 8 * (r >> 2) + 4 * x.g + (r & 3);
+                if ((unsigned)(k0 - x.klo) >= (unsigned)x.kn) s[hk][r] = -INFINITY;
+            }
+    }
+    // block max of each query row: three-input maxima over the lane's 16 * kNH entries, then
+    // the other wave half's
+    float mx;
+    {
+        float t[kNH];
+#pragma unroll
+        for (int hk = 0; hk < kNH; ++hk) {
+            const f32x16& v = s[hk];
+            const float a0 = vmax(vmax(v[0], v[1]), v[2]), a1 = vmax(vmax(v[3], v[4]), v[5]);
+            const float a2 = vmax(vmax(v[6], v[7]), v[8]), a3 = vmax(vmax(v[9], v[10]), v[11]);
+            const float a4 = vmax(vmax(v[12], v[13]), v[14]);
+            t[hk] = vmax(vmax(vmax(a0, a1), a2), vmax(vmax(a3, a4), v[15]));
+        }
+        mx = t[0];
+#pragma unroll
+        for (int hk = 1; hk < kNH; ++hk) mx = vmax(mx, t[hk]);
+    }
+    mx = halves_max(mx);
+    // lazy rescale: only when some row's block max passed its threshold (the first visible
+    // key of a row always does: thr starts at -inf).  Otherwise the stale max keeps every
+    // exp2 argument below 8.
+    if (__any(mx > st.thr)) {
+        const float mnew = vmax(st.m, mx);
+        const float corr = fast_exp2((st.m - mnew) * x.c);
+        st.m = mnew;
+        st.thr = mnew + x.inv8c;
+        st.mc = vmax(mnew * x.c, kNegMax);   // finite even while m = -FLT_MAX
+        st.lsum *= corr;
+#pragma unroll
+        for (int i = 0; i < C::NDB; ++i) st.oacc[i] *= corr;
+    }
+    float ps[kNH];
+#pragma unroll
+    for (int hk = 0; hk < kNH; ++hk) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[hk][r] = fast_exp2(fmaf(s[hk][r], x.c, -st.mc));
+        // pairwise sum: a dependency chain of 4 adds instead of 16
+        float t4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t4[i] = (s[hk][i] + s[hk][4 + i]) + (s[hk][8 + i] + s[hk][12 + i]);
+        ps[hk] = (t4[0] + t4[1]) + (t4[2] + t4[3]);
+    }
+#pragma unroll
+    for (int hk = 0; hk < kNH; ++hk) st.lsum += ps[hk];
+    // P^T operand of 16-key quarter kh: element e <-> accumulator entry 8*(kh % 2) + e of
+    // s[kh / 2]
+    V8 pb[2 * kNH];
+#pragma unroll
+    for (int kh = 0; kh < 2 * kNH; ++kh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[kh][e] = (typename E::s)s[kh >> 1][8 * (kh & 1) + e];
+#pragma unroll
+    for (int kh = 0; kh < 2 * kNH; ++kh)
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+            const uint32_t pv = x.vp[db] + STG * C::STAGEB + 16 * kh * C::VROWB;
+            const V4 lo = lds_load_tr4<E>(pv);
+            const V4 hi = lds_load_tr4<E>(pv + 8 * C::VROWB);
+            V8 av;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                av[e] = lo[e];
+                av[4 + e] = hi[e];
+            }
+            st.oacc[db] = mfma32x32x16(av, pb[kh], st.oacc[db]);
+        }
+}
 
 template <class E, int D>
 __global__ __launch_bounds__(kThreads, kWgs) void fwd_b16_kernel(
@@ -94,7 +253,6 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_b16_kernel(
     Layout lq, Layout lk) {
     using C = Bf16Fwd<D>;
     using V8 = typename E::v8;
-    using V4 = typename E::v4;
     extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
 
     int qt, b, h;
@@ -102,51 +260,58 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_b16_kernel(
     const int hk = h / (H / HKV);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int n = lane & 31, g = lane >> 5;
-    const int wr0 = qt * kBQ + __builtin_amdgcn_readfirstlane(w) * 32;   // wave-uniform: scalar block tests
-    const int q = wr0 + n;
     const int64_t ldq = lq.t, ldk = lk.t;   // row strides (elements)
-    const uint32_t ldk_b = (uint32_t)(ldk * 2);
-    const Buf kbuf = head_buf<D>(K + b * lk.b + hk * lk.h, ldk, Tk);
-    const Buf vbuf = head_buf<D>(V + b * lk.b + hk * lk.h, ldk, Tk);
-    const bool cz = causal != 0;
-    const float c = scale * kLog2e;
-    // keys this query row may see: [klo, klo + kn)
-    int klo, kn;
-    row_keys(q, T, Tk, cz, window, klo, kn);
 
+    FwdCtx<D> x(head_buf<D>(K + b * lk.b + hk * lk.h, ldk, Tk),
+                head_buf<D>(V + b * lk.b + hk * lk.h, ldk, Tk));
+    x.wr0 = qt * kBQ + __builtin_amdgcn_readfirstlane(w) * 32;   // wave-uniform: scalar block tests
+    const int q = x.wr0 + n;
+    x.ldk_b = (uint32_t)(ldk * 2);
+    x.cz = causal != 0;
+    x.T = T;
+    x.Tk = Tk;
+    x.window = window;
+    x.g = g;
+    x.c = scale * kLog2e;
+    x.inv8c = 8.0f / x.c;
+    // keys this query row may see: [klo, klo + kn)
+    row_keys(q, T, Tk, x.cz, window, x.klo, x.kn);
+
+    FwdState<E, D> st;
     // Q^T operand: lane (n, g) holds Q[q][16*dc + 8*g .. +7] (zero past T)
-    V8 qreg[C::DC];
     {
         const Buf qbuf = head_buf<D>(Q + b * lq.b + h * lq.h, ldq, T);
         const uint32_t off = (uint32_t)q * (uint32_t)(ldq * 2) + 16 * g;
 #pragma unroll
-        for (int dc = 0; dc < C::DC; ++dc) qreg[dc] = __builtin_bit_cast(V8, qbuf.load16(off + dc * 32));
+        for (int dc = 0; dc < C::DC; ++dc)
+            st.qreg[dc] = __builtin_bit_cast(V8, qbuf.load16(off + dc * 32));
     }
-    f32x16 oacc[C::NDB];
 #pragma unroll
     for (int i = 0; i < C::NDB; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
-    float m = kNegMax, lsum = 0.f;
+        for (int r = 0; r < 16; ++r) st.oacc[i][r] = 0.f;
+    st.m = kNegMax;
+    st.thr = -INFINITY;
+    st.mc = kNegMax;
+    st.lsum = 0.f;
 
-    int jlo, jhi;
-    kv_block_range(T, Tk, qt * kBQ, qt * kBQ + kBQ, kBK, cz, window, jlo, jhi);
-    int jf0, jf1;   // key blocks that are FULL for this wave's rows
-    full_kv_block_range(T, Tk, wr0, wr0 + 32, kBK, cz, window, jf0, jf1);
+    int jlo;
+    kv_block_range(T, Tk, qt * kBQ, qt * kBQ + kBQ, kBK, x.cz, window, jlo, x.jhi);
+    // key blocks that are FULL for this wave's rows
+    full_kv_block_range(T, Tk, x.wr0, x.wr0 + 32, kBK, x.cz, window, x.jf0, x.jf1);
 
     // LDS-DMA source offsets of this lane in its wave's pieces of a K / V tile
-    const int wu = __builtin_amdgcn_readfirstlane(w);
-    uint32_t koff[C::KMAX], voff[C::VPW];
+    x.wu = __builtin_amdgcn_readfirstlane(w);
 #pragma unroll
-    for (int i = 0; i < C::KMAX; ++i) koff[i] = dma_src_offset_padded<D>(w + i * C::NW, lane, ldk_b);
+    for (int i = 0; i < C::KMAX; ++i) x.koff[i] = dma_src_offset_padded<D>(w + i * C::NW, lane, x.ldk_b);
 #pragma unroll
-    for (int i = 0; i < C::VPW; ++i) voff[i] = dma_src_offset_swz<D>(w * C::VPW + i, lane, ldk_b);
+    for (int i = 0; i < C::VPW; ++i) x.voff[i] = dma_src_offset_swz<D>(w * C::VPW + i, lane, x.ldk_b);
     // LDS read offsets inside a stage.  K operand: rows n and 32 + n, chunk 2*dc + g (padded
     // rows: consecutive k-steps are 32 bytes apart).  V^T operand via transpose reads: lane
     // 16*cq + jj reads 8 bytes of row 16*kh + 4*(cq/2) + jj/4 (and 8 rows further) at
     // column 32*db + 16*(cq%2) + 4*(jj%4).
-    const uint32_t kaddr = (uint32_t)(n * C::KROWB + 16 * g);
-    uint32_t vaddr[C::NDB];
+    char* sm = reinterpret_cast<char*>(smem);
+    x.kp = pinned_lds_addr(lds_addr(sm + n * C::KROWB + 16 * g));
     {
         const int jj = lane & 15, cq = lane >> 4;
         const int vr = 4 * (cq >> 1) + (jj >> 2);
@@ -154,118 +319,22 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_b16_kernel(
         const int lo2 = 2 * (cq & 1) + ((jj & 3) >> 1);
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db)
-            vaddr[db] = (uint32_t)(C::KTILEB + vr * C::VROWB + 16 * (4 * (db ^ vx) + lo2) +
-                                   8 * (jj & 1));
+            x.vp[db] = pinned_lds_addr(lds_addr(sm + C::KTILEB + vr * C::VROWB +
+                                                16 * (4 * (db ^ vx) + lo2) + 8 * (jj & 1)));
     }
 
-    char* sm = reinterpret_cast<char*>(smem);
-    if (jlo < jhi) fwd_issue<D>(kbuf, vbuf, koff, voff, sm, wu, ldk_b, jlo);
+    x.klast = __builtin_amdgcn_readfirstlane((int)(x.wu + (C::KMAX - 1) * C::NW < C::KPIECES));
+    if (jlo < x.jhi) fwd_issue<D>(x.kbuf, x.vbuf, x.koff, x.voff, sm, x.wu, x.ldk_b, jlo, x.klast);
 
-    for (int j = jlo; j < jhi; ++j) {
-        const int stg = (j - jlo) & 1;
-        // scalar block test before the wait, only outside the FULL range
-        int cls = kFull;
-        if (j < jf0 || j >= jf1) {
-            keep_branch();
-            cls = block_class(T, Tk, wr0, wr0 + 32, j * kBK, j * kBK + kBK, cz, window);
-        }
-        wait_vmcnt<0>();   // block j's pieces, the only ones in flight
-        // all pieces visible; every wave is done with the other stage (block j - 1)
-        lds_barrier();
-        if (j + 1 < jhi) fwd_issue<D>(kbuf, vbuf, koff, voff, sm + (stg ^ 1) * C::STAGEB, wu, ldk_b, j + 1);
-        if (cls == kSkip) continue;
-        const char* sb = sm + stg * C::STAGEB;
-        // S^T for the block's 32-key halves: entry r of lane (n, g) in s[hk] is key
-        // j*BK + 32*hk + 8*(r/4) + 4g + r%4 of query n
-        f32x16 s[kNH];
-#pragma unroll
-        for (int hk = 0; hk < kNH; ++hk)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[hk][r] = 0.f;
-        V8 ka[C::DC][kNH];
-#pragma unroll
-        for (int dc = 0; dc < C::DC; ++dc)
-#pragma unroll
-            for (int hk = 0; hk < kNH; ++hk)
-                ka[dc][hk] = *reinterpret_cast<const V8*>(sb + kaddr + 32 * dc + 32 * hk * C::KROWB);
-#pragma unroll
-        for (int dc = 0; dc < C::DC; ++dc)
-#pragma unroll
-            for (int hk = 0; hk < kNH; ++hk) s[hk] = mfma32x32x16(ka[dc][hk], qreg[dc], s[hk]);
-        // schedule: the first DC K reads up front, then one read per MFMA, so the LDS
-        // latency hides behind the MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, C::DC, 0);
-#pragma unroll
-        for (int i = 0; i < (kNH * C::DC) / 2; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, (kNH * C::DC) / 2, 0);
-        if (cls == kPartial) {
-            keep_branch();
-#pragma unroll
-            for (int hk = 0; hk < kNH; ++hk)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int k0 = j * kBK + 32 * hk + 8 * (r >> 2) + 4 * g + (r & 3);
-                    if ((unsigned)(k0 - klo) >= (unsigned)kn) s[hk][r] = -INFINITY;
-                }
-        }
-        float mx = s[0][0];
-#pragma unroll
-        for (int hk = 0; hk < kNH; ++hk)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) mx = vmax(mx, vmax(s[hk][r], s[hk][r + 1]));
-        mx = halves_max(mx);
-        const float mnew = vmax(m, mx);
-        // a row whose max is still the -FLT_MAX start rescales on its first visible key
-        // (bitwise operators: one vector-compare sequence, no branches)
-        if (__any((mnew > m) & ((m == kNegMax) | ((mnew - m) * c > 8.0f)))) {
-            const float corr = fast_exp2((m - mnew) * c);
-            m = mnew;
-            lsum *= corr;
-#pragma unroll
-            for (int i = 0; i < C::NDB; ++i) oacc[i] *= corr;
-        }
-        const float mc = vmax(m * c, kNegMax);   // finite even while m = -FLT_MAX
-        float ps[kNH];
-#pragma unroll
-        for (int hk = 0; hk < kNH; ++hk) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[hk][r] = fast_exp2(fmaf(s[hk][r], c, -mc));
-            // pairwise sum: a dependency chain of 4 adds instead of 16
-            float t4[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) t4[i] = (s[hk][i] + s[hk][4 + i]) + (s[hk][8 + i] + s[hk][12 + i]);
-            ps[hk] = (t4[0] + t4[1]) + (t4[2] + t4[3]);
-        }
-#pragma unroll
-        for (int hk = 0; hk < kNH; ++hk) lsum += ps[hk];
-        // P^T operand of 16-key quarter kh: element e <-> accumulator entry 8*(kh % 2) + e of
-        // s[kh / 2]
-        V8 pb[2 * kNH];
-#pragma unroll
-        for (int kh = 0; kh < 2 * kNH; ++kh)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pb[kh][e] = (typename E::s)s[kh >> 1][8 * (kh & 1) + e];
-#pragma unroll
-        for (int kh = 0; kh < 2 * kNH; ++kh)
-#pragma unroll
-            for (int db = 0; db < C::NDB; ++db) {
-                const char* pv = sb + vaddr[db] + 16 * kh * C::VROWB;
-                const V4 lo = lds_read_tr4e<E>(reinterpret_cast<const uint16_t*>(pv));
-                const V4 hi = lds_read_tr4e<E>(reinterpret_cast<const uint16_t*>(pv + 8 * C::VROWB));
-                V8 av;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    av[e] = lo[e];
-                    av[4 + e] = hi[e];
-                }
-                oacc[db] = mfma32x32x16(av, pb[kh], oacc[db]);
-            }
+    // blocks alternate between the two LDS stages: two per trip, stage 0 then stage 1
+    int j = jlo;
+    for (; j + 1 < x.jhi; j += 2) {
+        fwd_block<E, D, 0>(st, x, sm, j);
+        fwd_block<E, D, 1>(st, x, sm, j + 1);
     }
+    if (j < x.jhi) fwd_block<E, D, 0>(st, x, sm, j);
 
-    lsum += swap_halves(lsum);
+    float lsum = st.lsum + swap_halves(st.lsum);
     if (q >= T) return;
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     uint16_t* Oq = O + b * lq.b + (int64_t)q * ldq + h * lq.h;
@@ -275,12 +344,12 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_b16_kernel(
 #pragma unroll
         for (int t4 = 0; t4 < 4; ++t4) {
             u32x2 wv;
-            wv[0] = pack2<E>(oacc[db][4 * t4 + 0] * inv, oacc[db][4 * t4 + 1] * inv);
-            wv[1] = pack2<E>(oacc[db][4 * t4 + 2] * inv, oacc[db][4 * t4 + 3] * inv);
+            wv[0] = pack2<E>(st.oacc[db][4 * t4 + 0] * inv, st.oacc[db][4 * t4 + 1] * inv);
+            wv[1] = pack2<E>(st.oacc[db][4 * t4 + 2] * inv, st.oacc[db][4 * t4 + 3] * inv);
             *reinterpret_cast<u32x2*>(Oq + db * 32 + 8 * t4 + 4 * g) = wv;
         }
     if (g == 0)
-        L[((int64_t)b * H + h) * T + q] = lsum > 0.f ? m * scale + fast_log2(lsum) * kLn2 : 0.f;
+        L[((int64_t)b * H + h) * T + q] = lsum > 0.f ? st.m * scale + fast_log2(lsum) * kLn2 : 0.f;
 }
 
 namespace {

@@ -37,6 +37,32 @@ __device__ __forceinline__ Buf head_buf(const uint16_t* base, int64_t ld, int T)
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// 32-bit LDS address of a pointer into shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(lds_ptr_t)p;
+}
+
+// The same address, opaque to the compiler: it stays in one register as computed, instead of
+// being rebuilt from its parts by a vector add in every loop iteration (which the compiler
+// does for addresses it can recompute, to save a register).
+__device__ __forceinline__ uint32_t pinned_lds_addr(uint32_t a) {
+    asm volatile("" : "+v"(a));
+    return a;
+}
+
+// Typed loads at a 32-bit LDS address (constant displacements fold into the instruction's
+// offset field).
+template <class T>
+__device__ __forceinline__ T lds_load(uint32_t a) {
+    return *(const __attribute__((address_space(3))) T*)(a);
+}
+template <class E>
+__device__ __forceinline__ typename E::v4 lds_load_tr4(uint32_t a) {
+    typedef __bf16 v4bf16 __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(typename E::v4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                                  (__attribute__((address_space(3))) v4bf16*)(a)));
+}
+
 // s_waitcnt vmcnt(N) only (gfx9 encoding: vmcnt in [3:0] and [15:14]; expcnt [6:4] and
 // lgkmcnt [11:8] left at their "no wait" maxima)
 template <int N>
