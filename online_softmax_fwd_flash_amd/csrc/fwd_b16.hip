@@ -335,9 +335,17 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_b16_kernel(
     if (j < x.jhi) fwd_block<E, D, 0>(st, x, sm, j);
 
     float lsum = st.lsum + swap_halves(st.lsum);
-    if (q >= T) return;
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    uint16_t* Oq = O + b * lq.b + (int64_t)q * ldq + h * lq.h;
+    if (g == 0 && q < T)
+        L[((int64_t)b * H + h) * T + q] = lsum > 0.f ? st.m * scale + fast_log2(lsum) * kLn2 : 0.f;
+    // O leaves through LDS, so that every store instruction writes whole rows: each wave puts
+    // its 32 x D tile, row-major, in its quarter of the two stages (free once every wave is
+    // past its last block), then reads it back 16 bytes per lane, 16 lanes per row.  Row
+    // stride D + 8 elements: the 8-byte writes of 32 rows at one column hit distinct banks.
+    lds_barrier();
+    constexpr uint32_t OROW = 2 * D + 16;
+    static_assert(kThreads / 64 * 32 * OROW <= 2 * C::STAGEB, "O tiles must fit the stages");
+    const uint32_t ot = lds_addr(sm) + (uint32_t)w * 32 * OROW;
     // lane (n, g), entry r of block db: O^T[db*32 + 8*(r/4) + 4g + r%4][query n]
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
@@ -346,10 +354,19 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_b16_kernel(
             u32x2 wv;
             wv[0] = pack2<E>(st.oacc[db][4 * t4 + 0] * inv, st.oacc[db][4 * t4 + 1] * inv);
             wv[1] = pack2<E>(st.oacc[db][4 * t4 + 2] * inv, st.oacc[db][4 * t4 + 3] * inv);
-            *reinterpret_cast<u32x2*>(Oq + db * 32 + 8 * t4 + 4 * g) = wv;
+            *(__attribute__((address_space(3))) u32x2*)(ot + n * OROW + 2 * (db * 32 + 8 * t4 + 4 * g)) = wv;
         }
-    if (g == 0)
-        L[((int64_t)b * H + h) * T + q] = lsum > 0.f ? st.m * scale + fast_log2(lsum) * kLn2 : 0.f;
+    // lane l: row 4i + l/16 of the wave's 32, elements 8*(l%16) .. +7 (rows past T not stored)
+    constexpr int LPR = D / 8;                  // lanes per row
+    constexpr int RPI = 64 / LPR;               // rows per instruction
+    const int rr = lane / LPR, ch = lane % LPR;
+    uint16_t* Ow = O + b * lq.b + h * lq.h + 8 * ch;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+        const int row = RPI * i + rr;
+        const u32x4 v = lds_load<u32x4>(ot + row * OROW + 16 * ch);
+        if (x.wr0 + row < T) *reinterpret_cast<u32x4*>(Ow + (int64_t)(x.wr0 + row) * ldq) = v;
+    }
 }
 
 namespace {
