@@ -1,8 +1,10 @@
 // fp32 attention kernels for gfx950: forward, dK/dV and dQ, on the 16x16x4 fp32 MFMA
 // (true fp32 products, fp32 accumulation).  Head dim D is a runtime multiple of 8 up to 128,
-// padded to DP in {16, 32, 64, 128} for the register tiles; a workgroup's tiling (BQ query
-// rows x BK keys per block) is a template parameter so the tilings the pages use (32 x 32,
-// 64 x 16) run as such.
+// padded to DP in {8, 16, 32, 64, 128} for the contractions over the head dim (S = Q K^T,
+// dP = dO V^T); the products whose output has head-dim columns (O, dQ, dK, dV) come in
+// 16-column MFMA blocks, so their operand tiles are staged at least 16 columns wide (zeros
+// past D).  A workgroup's tiling (BQ query rows x BK keys per block) is a template parameter
+// so the tilings the pages use (32 x 32, 64 x 16) run as such.
 //
 // Orientation.  Scores are formed transposed, S^T = K Q^T, so MFMA column n (lane l % 16) is a
 // query row: a query's running max / sum live in its own lanes and only the four 16-lane
@@ -23,17 +25,27 @@ namespace {
 
 template <int DP>
 struct F32Tile {
-    static constexpr int KS = DP / 4;   // MFMA k-steps over the (padded) head dim
-    static constexpr int LD = DP + 4;   // padded LDS row (floats): conflict-free column reads
-    static constexpr int NDB = DP / 16; // 16-wide blocks of the head dim in O / dQ / dK / dV
+    static constexpr int KS = DP / 4;                // MFMA k-steps over the (padded) head dim
+    static constexpr int DW = DP < 16 ? 16 : DP;     // staged columns (16-column output blocks)
+    static constexpr int LD = DW + 4;                // padded LDS row (floats): conflict-free
+    static constexpr int NDB = DW / 16;              // 16-wide blocks of O / dQ / dK / dV
+};
+
+// Keys staged per barrier pair in the query-owned passes (forward, dQ): several key blocks of
+// BK when BK is small (each block keeps its own class test and online-softmax update, in the
+// same order, so results do not change), as long as the K and V tiles fit static LDS.
+template <int DP, int BK>
+struct F32KeyStage {
+    static constexpr int SB = (BK < 64 && DP <= 64) ? 64 : BK;
+    static constexpr int NSB = SB / BK;   // key blocks per stage
 };
 
 // Stage rows [row0, row0 + ROWS) of a [*, ld] matrix (head slice at `base`) into LDS
-// (ROWS x DP, zero outside [0, T) x [0, D)).
+// (ROWS x DW, zero outside [0, T) x [0, D)).
 template <int DP, int ROWS, int NT>
 __device__ __forceinline__ void stage_rows(float* __restrict__ dst, const float* __restrict__ base,
                                            int64_t ld, int row0, int T, int D) {
-    constexpr int C4 = DP / 4;
+    constexpr int C4 = F32Tile<DP>::DW / 4;
     for (int e = threadIdx.x; e < ROWS * C4; e += NT) {
         const int r = e / C4, d = (e % C4) * 4;
         const int row = row0 + r;
@@ -52,7 +64,7 @@ __device__ __forceinline__ void stage_rows(float* __restrict__ dst, const float*
 // dK/dV passes measured 1-2% slower with it (more registers, no latency left to hide).
 template <int DP, int ROWS, int NT>
 struct RowPrefetch {
-    static constexpr int C4 = DP / 4;
+    static constexpr int C4 = F32Tile<DP>::DW / 4;
     static constexpr int PER = (ROWS * C4 + NT - 1) / NT;   // float4 per thread
     f32x4 v[PER];
     __device__ __forceinline__ void load(const float* __restrict__ base, int64_t ld, int row0,
@@ -87,8 +99,9 @@ __global__ __launch_bounds__(BQ / 16 * 64) void fwd_f32_kernel(
     float scale, int causal, int window, int nqt, Layout lq, Layout lk) {
     using Tl = F32Tile<DP>;
     constexpr int NW = BQ / 16, NT = NW * 64, KS = Tl::KS, LD = Tl::LD, NDB = Tl::NDB;
-    __shared__ __attribute__((aligned(16))) float Ks[BK * LD];
-    __shared__ __attribute__((aligned(16))) float Vs[BK * LD];
+    constexpr int SB = F32KeyStage<DP, BK>::SB, NSB = F32KeyStage<DP, BK>::NSB;
+    __shared__ __attribute__((aligned(16))) float Ks[SB * LD];
+    __shared__ __attribute__((aligned(16))) float Vs[SB * LD];
 
     const int BH = B * H;
     const int qt = nqt - 1 - (int)(blockIdx.x / BH);   // longest key ranges first
@@ -119,63 +132,69 @@ __global__ __launch_bounds__(BQ / 16 * 64) void fwd_f32_kernel(
 
     int jlo, jhi;
     kv_block_range(T, Tk, qt * BQ, qt * BQ + BQ, BK, cz, window, jlo, jhi);
-    for (int j = jlo; j < jhi; ++j) {
+    for (int j0 = jlo; j0 < jhi; j0 += NSB) {
         __syncthreads();
-        stage_rows<DP, BK, NT>(Ks, Kh, ldk, j * BK, Tk, D);
-        stage_rows<DP, BK, NT>(Vs, Vh, ldk, j * BK, Tk, D);
+        stage_rows<DP, SB, NT>(Ks, Kh, ldk, j0 * BK, Tk, D);
+        stage_rows<DP, SB, NT>(Vs, Vh, ldk, j0 * BK, Tk, D);
         __syncthreads();
-        const int cls = block_class(T, Tk, wr0, wr0 + 16, j * BK, j * BK + BK, cz, window);
-        if (cls == kSkip) continue;
+#pragma unroll 1
+        for (int jj = 0; jj < NSB && j0 + jj < jhi; ++jj) {
+            const int j = j0 + jj;
+            const float* Kb = Ks + jj * BK * LD;
+            const float* Vb = Vs + jj * BK * LD;
+            const int cls = block_class(T, Tk, wr0, wr0 + 16, j * BK, j * BK + BK, cz, window);
+            if (cls == kSkip) continue;
 
-        f32x4 s[BK / 16];
+            f32x4 s[BK / 16];
 #pragma unroll
-        for (int kb = 0; kb < BK / 16; ++kb) {
-            s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const float* krow = Ks + (kb * 16 + n) * LD + g * KS;
+            for (int kb = 0; kb < BK / 16; ++kb) {
+                s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                const float* krow = Kb + (kb * 16 + n) * LD + g * KS;
 #pragma unroll
-            for (int st = 0; st < KS; ++st) s[kb] = mfma16x16x4f32(krow[st], qreg[st], s[kb]);
-        }
-        if (cls == kPartial) {
+                for (int st = 0; st < KS; ++st) s[kb] = mfma16x16x4f32(krow[st], qreg[st], s[kb]);
+            }
+            if (cls == kPartial) {
+#pragma unroll
+                for (int kb = 0; kb < BK / 16; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int key = j * BK + kb * 16 + 4 * g + r;
+                        if (!visible(q, key, T, Tk, cz, window)) s[kb][r] = -INFINITY;
+                    }
+            }
+            float mx = kNegMax;
+#pragma unroll
+            for (int kb = 0; kb < BK / 16; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][r]);
+            mx = fmaxf(mx, xor_shfl(mx, 16));
+            mx = fmaxf(mx, xor_shfl(mx, 32));
+            const float mnew = fmaxf(m, mx);
+            const float corr = fast_exp2((m - mnew) * c);
+            m = mnew;
+            const float mc = fmaxf(m * c, kNegMax);   // finite even while m = -FLT_MAX
+            float ps = 0.f;
 #pragma unroll
             for (int kb = 0; kb < BK / 16; ++kb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int key = j * BK + kb * 16 + 4 * g + r;
-                    if (!visible(q, key, T, Tk, cz, window)) s[kb][r] = -INFINITY;
+                    const float p = fast_exp2(fmaf(s[kb][r], c, -mc));
+                    s[kb][r] = p;
+                    ps += p;
+                }
+            lsum = lsum * corr + ps;
+#pragma unroll
+            for (int i = 0; i < NDB; ++i) oacc[i] *= corr;
+#pragma unroll
+            for (int kb = 0; kb < BK / 16; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float* vrow = Vb + (kb * 16 + 4 * g + r) * LD + n;
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+                        oacc[db] = mfma16x16x4f32(vrow[db * 16], s[kb][r], oacc[db]);
                 }
         }
-        float mx = kNegMax;
-#pragma unroll
-        for (int kb = 0; kb < BK / 16; ++kb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = fmaxf(mx, xor_shfl(mx, 16));
-        mx = fmaxf(mx, xor_shfl(mx, 32));
-        const float mnew = fmaxf(m, mx);
-        const float corr = fast_exp2((m - mnew) * c);
-        m = mnew;
-        const float mc = fmaxf(m * c, kNegMax);   // finite even while m = -FLT_MAX
-        float ps = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < BK / 16; ++kb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float p = fast_exp2(fmaf(s[kb][r], c, -mc));
-                s[kb][r] = p;
-                ps += p;
-            }
-        lsum = lsum * corr + ps;
-#pragma unroll
-        for (int i = 0; i < NDB; ++i) oacc[i] *= corr;
-#pragma unroll
-        for (int kb = 0; kb < BK / 16; ++kb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float* vrow = Vs + (kb * 16 + 4 * g + r) * LD + n;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    oacc[db] = mfma16x16x4f32(vrow[db * 16], s[kb][r], oacc[db]);
-            }
     }
 
     lsum += xor_shfl(lsum, 16);
@@ -324,8 +343,9 @@ __global__ __launch_bounds__(BQ / 16 * 64) void dq_f32_kernel(
     int window, int nqt, Layout lq, Layout lk) {
     using Tl = F32Tile<DP>;
     constexpr int NW = BQ / 16, NT = NW * 64, KS = Tl::KS, LD = Tl::LD, NDB = Tl::NDB;
-    __shared__ __attribute__((aligned(16))) float Ks[BK * LD];
-    __shared__ __attribute__((aligned(16))) float Vs[BK * LD];
+    constexpr int SB = F32KeyStage<DP, BK>::SB, NSB = F32KeyStage<DP, BK>::NSB;
+    __shared__ __attribute__((aligned(16))) float Ks[SB * LD];
+    __shared__ __attribute__((aligned(16))) float Vs[SB * LD];
 
     const int BH = B * H;
     const int qt = nqt - 1 - (int)(blockIdx.x / BH);
@@ -360,23 +380,25 @@ __global__ __launch_bounds__(BQ / 16 * 64) void dq_f32_kernel(
 
     int jlo, jhi;
     kv_block_range(T, Tk, qt * BQ, qt * BQ + BQ, BK, cz, window, jlo, jhi);
-    RowPrefetch<DP, BK, NT> pk, pv;
+    RowPrefetch<DP, SB, NT> pk, pv;
     if (jlo < jhi) {
         pk.load(Kh, ldk, jlo * BK, Tk, D);
         pv.load(Vh, ldk, jlo * BK, Tk, D);
     }
-    for (int j = jlo; j < jhi; ++j) {
+    for (int j0 = jlo; j0 < jhi; j0 += NSB) {
         __syncthreads();
         pk.store(Ks);
         pv.store(Vs);
         __syncthreads();
-        if (j + 1 < jhi) {   // next block's loads in flight while this one is computed
-            pk.load(Kh, ldk, (j + 1) * BK, Tk, D);
-            pv.load(Vh, ldk, (j + 1) * BK, Tk, D);
+        if (j0 + NSB < jhi) {   // next stage's loads in flight while this one is computed
+            pk.load(Kh, ldk, (j0 + NSB) * BK, Tk, D);
+            pv.load(Vh, ldk, (j0 + NSB) * BK, Tk, D);
         }
+        // the 16-key blocks of the staged key blocks j0 .. (up to jhi)
+        const int nkb = ((jhi - j0 < NSB ? jhi - j0 : NSB) * BK) / 16;
 #pragma unroll 1
-        for (int kb = 0; kb < BK / 16; ++kb) {
-            const int kc0 = j * BK + kb * 16;
+        for (int kb = 0; kb < nkb; ++kb) {
+            const int kc0 = j0 * BK + kb * 16;
             const int cls = block_class(T, Tk, wr0, wr0 + 16, kc0, kc0 + 16, cz, window);
             if (cls == kSkip) continue;
             f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
@@ -481,6 +503,7 @@ hipError_t by_tiles(const AttnArgs& a, int bq, int bk) {
 
 template <template <int, int, int> class Fn>
 hipError_t by_dim(const AttnArgs& a, int bq, int bk) {
+    if (a.D <= 8) return by_tiles<Fn, 8>(a, bq, bk);
     if (a.D <= 16) return by_tiles<Fn, 16>(a, bq, bk);
     if (a.D <= 32) return by_tiles<Fn, 32>(a, bq, bk);
     if (a.D <= 64) return by_tiles<Fn, 64>(a, bq, bk);
