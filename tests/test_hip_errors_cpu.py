@@ -77,6 +77,6 @@ def test_fa_log_names_the_instantiation():
     # the f32 kernels need no LDS attribute, so their launch is attempted (and fails) and
     # logged; the log names the tiling and head-dim instantiation chosen for D = 64 and D = 8
     assert "flash_attn: fwd_f32_kernel<DP=64,BQ=64,BK=64> elem=f32 D=64" in r.stderr
-    assert "flash_attn: fwd_f32_kernel<DP=16,BQ=64,BK=64> elem=f32 D=8" in r.stderr
+    assert "flash_attn: fwd_f32_kernel<DP=8,BQ=64,BK=64> elem=f32 D=8" in r.stderr
     assert "flash_attn: bwd_preprocess_kernel elem=bf16 D=64" in r.stderr
     assert "flash_attn: qk_norm_rope_kernel elem=bf16 D=64" in r.stderr
