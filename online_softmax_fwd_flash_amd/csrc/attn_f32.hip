@@ -126,8 +126,12 @@ __global__ __launch_bounds__(BQ / 16 * 64) void fwd_f32_kernel(
     f32x4 oacc[NDB];
 #pragma unroll
     for (int i = 0; i < NDB; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = kNegMax, lsum = 0.f;
+    // running max m (raw score units), lazily moved: O and the sum are rescaled only when a
+    // row's max passes thr = m + 8/c (the first visible key always does), so every exp2
+    // argument stays below 8
+    float m = kNegMax, thr = -INFINITY, mc = kNegMax, lsum = 0.f;
     const float c = scale * kLog2e;
+    const float inv8c = 8.0f / c;
     const bool cz = causal != 0;
 
     int jlo, jhi;
@@ -137,62 +141,68 @@ __global__ __launch_bounds__(BQ / 16 * 64) void fwd_f32_kernel(
         stage_rows<DP, SB, NT>(Ks, Kh, ldk, j0 * BK, Tk, D);
         stage_rows<DP, SB, NT>(Vs, Vh, ldk, j0 * BK, Tk, D);
         __syncthreads();
-#pragma unroll 1
-        for (int jj = 0; jj < NSB && j0 + jj < jhi; ++jj) {
+        // S^T of the staged key blocks (each block skipped or masked by its own class); one
+        // online-softmax update for all of them
+        int cls[NSB];
+        f32x4 s[NSB][BK / 16];
+#pragma unroll
+        for (int jj = 0; jj < NSB; ++jj) {
             const int j = j0 + jj;
-            const float* Kb = Ks + jj * BK * LD;
-            const float* Vb = Vs + jj * BK * LD;
-            const int cls = block_class(T, Tk, wr0, wr0 + 16, j * BK, j * BK + BK, cz, window);
-            if (cls == kSkip) continue;
-
-            f32x4 s[BK / 16];
+            cls[jj] = j < jhi ? block_class(T, Tk, wr0, wr0 + 16, j * BK, j * BK + BK, cz, window)
+                              : (int)kSkip;
+#pragma unroll
+            for (int kb = 0; kb < BK / 16; ++kb) s[jj][kb] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+            if (cls[jj] == kSkip) continue;
 #pragma unroll
             for (int kb = 0; kb < BK / 16; ++kb) {
-                s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                const float* krow = Kb + (kb * 16 + n) * LD + g * KS;
+                f32x4 a = {0.f, 0.f, 0.f, 0.f};
+                const float* krow = Ks + (jj * BK + kb * 16 + n) * LD + g * KS;
 #pragma unroll
-                for (int st = 0; st < KS; ++st) s[kb] = mfma16x16x4f32(krow[st], qreg[st], s[kb]);
+                for (int st = 0; st < KS; ++st) a = mfma16x16x4f32(krow[st], qreg[st], a);
+                s[jj][kb] = a;
             }
-            if (cls == kPartial) {
+            if (cls[jj] == kPartial) {
 #pragma unroll
                 for (int kb = 0; kb < BK / 16; ++kb)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int key = j * BK + kb * 16 + 4 * g + r;
-                        if (!visible(q, key, T, Tk, cz, window)) s[kb][r] = -INFINITY;
+                        if (!visible(q, key, T, Tk, cz, window)) s[jj][kb][r] = -INFINITY;
                     }
             }
-            float mx = kNegMax;
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int jj = 0; jj < NSB; ++jj)
 #pragma unroll
             for (int kb = 0; kb < BK / 16; ++kb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][r]);
-            mx = fmaxf(mx, xor_shfl(mx, 16));
-            mx = fmaxf(mx, xor_shfl(mx, 32));
+                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[jj][kb][r]);
+        mx = fmaxf(mx, xor_shfl(mx, 16));
+        mx = fmaxf(mx, xor_shfl(mx, 32));
+        if (__any(mx > thr)) {
             const float mnew = fmaxf(m, mx);
             const float corr = fast_exp2((m - mnew) * c);
             m = mnew;
-            const float mc = fmaxf(m * c, kNegMax);   // finite even while m = -FLT_MAX
-            float ps = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < BK / 16; ++kb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float p = fast_exp2(fmaf(s[kb][r], c, -mc));
-                    s[kb][r] = p;
-                    ps += p;
-                }
-            lsum = lsum * corr + ps;
+            thr = mnew + inv8c;
+            mc = fmaxf(mnew * c, kNegMax);   // finite even while m = -FLT_MAX
+            lsum *= corr;
 #pragma unroll
             for (int i = 0; i < NDB; ++i) oacc[i] *= corr;
+        }
+#pragma unroll
+        for (int jj = 0; jj < NSB; ++jj) {
+            if (cls[jj] == kSkip) continue;
 #pragma unroll
             for (int kb = 0; kb < BK / 16; ++kb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float* vrow = Vb + (kb * 16 + 4 * g + r) * LD + n;
+                    const float p = fast_exp2(fmaf(s[jj][kb][r], c, -mc));
+                    lsum += p;
+                    const float* vrow = Vs + (jj * BK + kb * 16 + 4 * g + r) * LD + n;
 #pragma unroll
                     for (int db = 0; db < NDB; ++db)
-                        oacc[db] = mfma16x16x4f32(vrow[db * 16], s[kb][r], oacc[db]);
+                        oacc[db] = mfma16x16x4f32(vrow[db * 16], p, oacc[db]);
                 }
         }
     }

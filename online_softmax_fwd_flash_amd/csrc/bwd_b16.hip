@@ -58,6 +58,9 @@ struct Dkdv16Cfg {
     static constexpr int KPW = 16, BKW = NW * KPW;   // keys per wave / workgroup
     static constexpr int BQ = 32;                     // query rows per staged block
     static constexpr int WGS = 3;                     // workgroups per CU
+    // column blocks of the first dV / dK k-step whose B operands are read before the softmax
+    // arithmetic (more would spill registers at D = 128)
+    static constexpr int HOIST = D == 128 ? 2 : 4;
     static constexpr int QB16 = BQ / 16, KKS = BQ / 32;   // 16-row blocks, 32-row k-steps
     static constexpr int DS = D / 32;                 // 32-wide k-steps of S and dP
     static constexpr int NDB = D / 16;                // 16-wide column blocks of dK / dV
@@ -207,6 +210,27 @@ __device__ __forceinline__ void dkdv_block(DkdvState<E, D>& st, const DkdvCtx<D>
             dp[qb] = mfma16x16x32(ao[ds], st.vneg[ds], dp[qb]);
         }
     }
+    // B operands of dV += P^T dO and -dK += (-dS)^T Q: rows 32kk + 16*(e/4) + 4g + e%4 of
+    // column 16db + i, two transpose reads of 4 rows each.  The operands of the first HOIST
+    // column blocks are read before the softmax arithmetic, which then hides the reads'
+    // latency.
+    auto tr_b = [&](int kk, int db, V8& bo, V8& bq) {
+        const uint32_t off = SO + 2 * (32 * kk * C::LDN + 16 * db);
+        const V4 ol = lds_load_tr4<E>(x.tr + C::OFF_DO + off);
+        const V4 oh = lds_load_tr4<E>(x.tr + C::OFF_DO + off + 32 * C::LDN);
+        const V4 ql = lds_load_tr4<E>(x.tr + off);
+        const V4 qh = lds_load_tr4<E>(x.tr + off + 32 * C::LDN);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            bo[e] = ol[e];
+            bo[4 + e] = oh[e];
+            bq[e] = ql[e];
+            bq[4 + e] = qh[e];
+        }
+    };
+    V8 bo[4], bq[4];
+#pragma unroll
+    for (int u = 0; u < C::HOIST; ++u) tr_b(0, u, bo[u], bq[u]);
     // rows past T have L = D = 0 and zero Q / dO: they add nothing
 #pragma unroll
     for (int qb = 0; qb < C::QB16; ++qb) {
@@ -234,29 +258,15 @@ __device__ __forceinline__ void dkdv_block(DkdvState<E, D>& st, const DkdvCtx<D>
             pd[qb >> 1][4 * (qb & 1) + r] = (S16)(sc[qb][r] * dp[qb][r]);   // -dS
         }
     // dV += P^T dO and -dK += (-dS)^T Q, 32 query rows per k-step; raised wave priority
-    // while these MFMAs issue (measured about 1% faster).  B operands: rows 32kk +
-    // 16*(e/4) + 4g + e%4 of column 16db + i, two transpose reads of 4 rows each.
+    // while these MFMAs issue (measured about 1% faster)
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < C::KKS; ++kk)
 #pragma unroll
         for (int d0 = 0; d0 < C::NDB; d0 += 4) {
-            V8 bo[4], bq[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint32_t off = SO + 2 * (32 * kk * C::LDN + 16 * (d0 + u));
-                const V4 ol = lds_load_tr4<E>(x.tr + C::OFF_DO + off);
-                const V4 oh = lds_load_tr4<E>(x.tr + C::OFF_DO + off + 32 * C::LDN);
-                const V4 ql = lds_load_tr4<E>(x.tr + off);
-                const V4 qh = lds_load_tr4<E>(x.tr + off + 32 * C::LDN);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    bo[u][e] = ol[e];
-                    bo[u][4 + e] = oh[e];
-                    bq[u][e] = ql[e];
-                    bq[u][4 + e] = qh[e];
-                }
-            }
+            for (int u = 0; u < 4; ++u)
+                if (kk > 0 || d0 > 0 || u >= C::HOIST) tr_b(kk, d0 + u, bo[u], bq[u]);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 st.dva[d0 + u] = mfma16x16x32(pp[kk], bo[u], st.dva[d0 + u]);
