@@ -11,19 +11,18 @@
 // formulas); Graphcore "flash_attention_qkv_packed.cpp", flashAttentionQKVPackedGrad
 // (key-chunk-outer loop with dV += P^T dO, dP = dO V^T, dS, dK += dS^T Q).
 //
-// dK/dV pass (16x16x32 MFMA).  Workgroup = 4 waves x 16 keys of one (b, kv head), three
-// workgroups per CU (one's barrier waits are covered by the others' work); it walks every
-// (query head of the group, 32-row query block) pair that sees its keys, last query block
-// first.  Q, dO (row-major, padded rows) and L, D of a block reach LDS by LDS-DMA,
-// double-buffered.  S = Q K^T and dP = dO V^T keep a key per accumulator column, so P and dS
-// leave the accumulators already in the A-operand layout of dV += P^T dO and dK += dS^T Q;
-// the B operands of those (dO and Q with rows in the accumulator's order) come from the
-// row-major tiles through LDS transpose reads.  K and V of the wave's 16 keys stay in
-// registers.
+// dK/dV pass (16x16x32 MFMA).  Workgroup = 4 waves x 32 keys of one (b, kv head), two
+// workgroups per CU; it walks every (query head of the group, 32-row query block) pair that
+// sees its keys, last query block first.  Q, dO (row-major, padded rows) and L, D of a block
+// reach LDS by LDS-DMA, double-buffered.  S = Q K^T and dP = dO V^T keep a key per
+// accumulator column, so P and dS leave the accumulators already in the A-operand layout of
+// dV += P^T dO and dK += dS^T Q; the B operands of those (dO and Q with rows in the
+// accumulator's order) come from the row-major tiles through LDS transpose reads.
 //
-// In both passes the dP accumulators start at -D of their query rows, so the MFMAs leave
-// dP - D and dS = P (dP - D) costs one multiply per score; the per-block class test runs only
-// outside each wave's precomputed range of FULL blocks, and the diagonal mask is a branch.
+// In both passes the dP accumulators start at D of their query rows (dK/dV: with -V as the
+// operand, so the MFMAs leave D - dP; dQ: at -D, leaving dP - D), so dS = P (dP - D) costs one
+// multiply per score; the per-block class test runs only outside each wave's precomputed range
+// of FULL blocks, and the diagonal mask is a branch.
 //
 // dQ pass (32x32x16 MFMA).  Workgroup = 4 waves x 32 query rows of one (b, h), two
 // workgroups per CU, walking its key blocks of 64; K and V reach LDS by LDS-DMA (padded
@@ -44,23 +43,17 @@ constexpr float kBigLse = 3.0e38f;   // L of a padding row: exp2(s*c - big) = 0
 }  // namespace
 
 // ------------------------------------------------------------------------------ dK / dV
-// Workgroup = 4 waves x 16 keys of one (b, kv head), three workgroups per CU.  16x16x32
-// MFMAs: S = Q K^T puts the wave's 16 keys on the accumulator columns and 4 query rows per
-// lane, so P and dS of two 16-row blocks concatenate into the A operand of dV += P^T dO and
+// 16x16x32 MFMAs: S = Q K^T puts 16 keys on the accumulator columns and 4 query rows per lane,
+// so P and dS of two 16-row blocks concatenate into the A operand of dV += P^T dO and
 // dK += dS^T Q (32 query rows per k-step), whose B operands come from the same row-major
-// Q / dO tiles through LDS transpose reads.  Per wave: K / V operands 32 registers, dK / dV
-// accumulators 64.
+// Q / dO tiles through LDS transpose reads.
 namespace {
 
+// The staged (query head, query block) pair: Q and dO tiles of 32 rows, and their L and D.
 template <int D>
-struct Dkdv16Cfg {
+struct DkdvStage {
     static constexpr int NW = 4, NT = 256;
-    static constexpr int KPW = 16, BKW = NW * KPW;   // keys per wave / workgroup
     static constexpr int BQ = 32;                     // query rows per staged block
-    static constexpr int WGS = 3;                     // workgroups per CU
-    // column blocks of the first dV / dK k-step whose B operands are read before the softmax
-    // arithmetic (more would spill registers at D = 128)
-    static constexpr int HOIST = D == 128 ? 2 : 4;
     static constexpr int QB16 = BQ / 16, KKS = BQ / 32;   // 16-row blocks, 32-row k-steps
     static constexpr int DS = D / 32;                 // 32-wide k-steps of S and dP
     static constexpr int NDB = D / 16;                // 16-wide column blocks of dK / dV
@@ -94,10 +87,10 @@ struct QdoSrc {
 };
 
 template <int D>
-__device__ __forceinline__ void dkdv16_issue(char* sm, const QdoSrc& qs, const float* Lg,
+__device__ __forceinline__ void dkdv_issue(char* sm, const QdoSrc& qs, const float* Lg,
                                              const float* Dg, const uint32_t* voff, int w,
                                              int h2, int i2, int T, int buf) {
-    using C = Dkdv16Cfg<D>;
+    using C = DkdvStage<D>;
     char* st = sm + buf * C::STAGE;
     const uint32_t rows = (uint32_t)i2 * C::BQ * (uint32_t)(qs.ldq * 2);
     const int tso = __builtin_amdgcn_readfirstlane(
@@ -119,49 +112,54 @@ __device__ __forceinline__ void dkdv16_issue(char* sm, const QdoSrc& qs, const f
     }
 }
 
-// B operand of dV += P^T dO / dK += dS^T Q (K = 32 query rows, N = 16 columns) straight from
-// a row-major tile: lane (i, g) element e holds row 32kk + 16*(e/4) + 4g + e%4 of column
-// 16db + i, matching the order P / dS take as A operand.  Two transpose reads of 4 rows.
-template <class E, int LDN>
-__device__ __forceinline__ typename E::v8 tr_operand(const uint16_t* tile, int kk, int db, int lane) {
-    const int j = lane & 15, g = lane >> 4;
-    const uint16_t* p = tile + (32 * kk + 4 * g + (j >> 2)) * LDN + 16 * db + 4 * (j & 3);
-    const typename E::v4 lo = lds_read_tr4e<E>(p);
-    const typename E::v4 hi = lds_read_tr4e<E>(p + 16 * LDN);
-    typename E::v8 r;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        r[e] = lo[e];
-        r[4 + e] = hi[e];
-    }
-    return r;
-}
-
 }  // namespace
 
-// Loop-invariant values of one wave's walk over its (query head, query block) pairs.
+// Workgroup = 4 waves x 32 keys (two 16-key halves per wave) of one (b, kv head), two
+// workgroups per CU.  Every A operand read from the Q / dO tiles and every transpose-read B
+// operand of dV / dK feeds both key halves, so a wave moves about 40% fewer LDS bytes per MFMA
+// than with 16 keys per wave (measured 16% faster at B=4 H=32 HKV=8 T=4096 D=128 than 16 keys
+// per wave at three workgroups per CU), and the workgroup stages each Q / dO block for 128
+// keys (half the barriers and L2 -> LDS traffic per FLOP).  K of the wave's keys stays in
+// registers; -V of the workgroup's 128 keys is staged in LDS once (negated while staged), the
+// B operand of D - dP = D - dO V^T; the dK and dV accumulators take 128 registers per wave.
+namespace {
+
+template <int D>
+struct DkdvCfg : DkdvStage<D> {
+    using Base = DkdvStage<D>;
+    static constexpr int KH = 2;                          // 16-key halves per wave
+    static constexpr int KPW = 16 * KH, BKW = Base::NW * KPW;
+    static constexpr int WGS = 2;                         // workgroups per CU
+    // column blocks of the dV / dK products whose B operands are read before the softmax
+    // arithmetic, which then hides the reads' latency (more would spill at D = 128)
+    static constexpr int HOIST = D == 128 ? 2 : 4;
+    static constexpr int VOFF = 2 * Base::STAGE;          // -V tile: BKW rows, padded
+    static constexpr int LDS = VOFF + BKW * Base::PadT::ROWB;
+};
+
 template <int D>
 struct DkdvCtx {
-    using C = Dkdv16Cfg<D>;
+    using C = DkdvCfg<D>;
     QdoSrc qs;
-    const float *Lg, *Dg;                    // the group's first head's L and Dvec rows
-    uint32_t voff[C::PMAX + 1];              // LDS-DMA source offsets of this lane
-    uint32_t aq;      // A-operand reads of the Q tile (stage 0; the dO tile is OFF_DO further)
-    uint32_t tr;      // transpose reads of the Q tile (stage 0; dO likewise)
-    uint32_t ld;      // this lane's L values (stage 0; its D values are 256 bytes further)
-    int w, rep, niter, if0, if1, T, Tk, kw0, window, qlo, qn, g;
+    const float *Lg, *Dg;
+    uint32_t voff[C::PMAX + 1];
+    // per-lane LDS read bases in stage 0 (the dO tile is OFF_DO after the Q tile): A-operand
+    // row n at column 8g; transpose-read row 4g + j/4 at column 4*(j%4) (j = lane % 16); L / D
+    // of rows 4g .. 4g + 3 (D 256 bytes after L)
+    uint32_t aq, tr, ld;
+    uint32_t va;           // -V operand reads: row w*32 + n of the -V tile at column 8g
+    int w, rep, niter, if0, if1, T, Tk, kw0, window, g;
+    int qlo[C::KH], qn[C::KH];   // query rows that see this lane's key of each half
     bool cz;
-    float c;          // scale * log2(e)
+    float c;
     __device__ __forceinline__ DkdvCtx(const QdoSrc& q) : qs(q) {}
 };
 
-// Accumulators and operands of one wave: K and -V of its keys (the B operands of S = Q K^T
-// and of D - dP = D - dO V^T), and its dK (negated, see below) and dV columns.
 template <class E, int D>
 struct DkdvState {
-    using C = Dkdv16Cfg<D>;
-    typename E::v8 kreg[C::DS], vneg[C::DS];
-    f32x4 dka[C::NDB], dva[C::NDB];
+    using C = DkdvCfg<D>;
+    typename E::v8 kreg[C::KH][C::DS];
+    f32x4 dka[C::KH][C::NDB], dva[C::KH][C::NDB];
 };
 
 // One (query head h2, query block i) pair, staged in LDS stage STG (a compile-time constant:
@@ -174,11 +172,10 @@ struct DkdvState {
 template <class E, int D, int STG>
 __device__ __forceinline__ void dkdv_block(DkdvState<E, D>& st, const DkdvCtx<D>& x, char* sm,
                                            int it, int i, int h2n, int in) {
-    using C = Dkdv16Cfg<D>;
+    using C = DkdvCfg<D>;
     using V8 = typename E::v8;
     using V4 = typename E::v4;
     using S16 = typename E::s;
-    // scalar block test before the wait, only outside the FULL range
     const int qr0 = i * C::BQ;
     int cls = kFull;
     if (i < x.if0 || i >= x.if1) {
@@ -188,32 +185,39 @@ __device__ __forceinline__ void dkdv_block(DkdvState<E, D>& st, const DkdvCtx<D>
     wait_vmcnt<0>();   // this stage's pieces, the only loads in flight
     // every wave's pieces are visible; every wave is done with the other stage
     lds_barrier();
-    if (it + 1 < x.niter) dkdv16_issue<D>(sm, x.qs, x.Lg, x.Dg, x.voff, x.w, h2n, in, x.T, STG ^ 1);
+    if (it + 1 < x.niter) dkdv_issue<D>(sm, x.qs, x.Lg, x.Dg, x.voff, x.w, h2n, in, x.T, STG ^ 1);
     if (cls == kSkip) return;
     constexpr uint32_t SO = STG * C::STAGE;
-    // S and D - dP for the 16-row blocks; entry r of lane (n, g): row 16qb + 4g + r, key n
-    f32x4 sc[C::QB16], dp[C::QB16];
+    // S and D - dP of both key halves; entry r of lane (n, g): row 16qb + 4g + r, key 16h + n
+    f32x4 sc[C::KH][C::QB16], dp[C::KH][C::QB16];
 #pragma unroll
     for (int qb = 0; qb < C::QB16; ++qb) {
-        sc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dp[qb] = lds_load<f32x4>(x.ld + SO + 256 + qb * 64);
-        V8 aq[C::DS], ao[C::DS];
+        const f32x4 d4 = lds_load<f32x4>(x.ld + SO + 256 + qb * 64);
 #pragma unroll
-        for (int ds = 0; ds < C::DS; ++ds) {
-            const uint32_t off = SO + 2 * (qb * 16 * C::LDN + ds * 32);
-            aq[ds] = lds_load<V8>(x.aq + off);
-            ao[ds] = lds_load<V8>(x.aq + C::OFF_DO + off);
-        }
-#pragma unroll
-        for (int ds = 0; ds < C::DS; ++ds) {
-            sc[qb] = mfma16x16x32(aq[ds], st.kreg[ds], sc[qb]);
-            dp[qb] = mfma16x16x32(ao[ds], st.vneg[ds], dp[qb]);
+        for (int h = 0; h < C::KH; ++h) {
+            sc[h][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            dp[h][qb] = d4;
         }
     }
-    // B operands of dV += P^T dO and -dK += (-dS)^T Q: rows 32kk + 16*(e/4) + 4g + e%4 of
-    // column 16db + i, two transpose reads of 4 rows each.  The operands of the first HOIST
-    // column blocks are read before the softmax arithmetic, which then hides the reads'
-    // latency.
+#pragma unroll
+    for (int ds = 0; ds < C::DS; ++ds) {
+        V8 aq[C::QB16], ao[C::QB16], vb[C::KH];
+#pragma unroll
+        for (int qb = 0; qb < C::QB16; ++qb) {
+            const uint32_t off = SO + 2 * (qb * 16 * C::LDN + ds * 32);
+            aq[qb] = lds_load<V8>(x.aq + off);
+            ao[qb] = lds_load<V8>(x.aq + C::OFF_DO + off);
+        }
+#pragma unroll
+        for (int h = 0; h < C::KH; ++h) vb[h] = lds_load<V8>(x.va + 2 * (16 * h * C::LDN + ds * 32));
+#pragma unroll
+        for (int qb = 0; qb < C::QB16; ++qb)
+#pragma unroll
+            for (int h = 0; h < C::KH; ++h) {
+                sc[h][qb] = mfma16x16x32(aq[qb], st.kreg[h][ds], sc[h][qb]);
+                dp[h][qb] = mfma16x16x32(ao[qb], vb[h], dp[h][qb]);
+            }
+    }
     auto tr_b = [&](int kk, int db, V8& bo, V8& bq) {
         const uint32_t off = SO + 2 * (32 * kk * C::LDN + 16 * db);
         const V4 ol = lds_load_tr4<E>(x.tr + C::OFF_DO + off);
@@ -236,55 +240,63 @@ __device__ __forceinline__ void dkdv_block(DkdvState<E, D>& st, const DkdvCtx<D>
     for (int qb = 0; qb < C::QB16; ++qb) {
         const f32x4 l4 = lds_load<f32x4>(x.ld + SO + qb * 64);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sc[qb][r] = fast_exp2(fmaf(sc[qb][r], x.c, -l4[r] * kLog2e));
+        for (int r = 0; r < 4; ++r) {
+            const float ml = -l4[r] * kLog2e;
+#pragma unroll
+            for (int h = 0; h < C::KH; ++h) sc[h][qb][r] = fast_exp2(fmaf(sc[h][qb][r], x.c, ml));
+        }
     }
     if (cls == kPartial) {
         keep_branch();
 #pragma unroll
+        for (int h = 0; h < C::KH; ++h)
+#pragma unroll
+            for (int qb = 0; qb < C::QB16; ++qb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int qi = qr0 + qb * 16 + 4 * x.g + r;
+                    if ((unsigned)(qi - x.qlo[h]) >= (unsigned)x.qn[h]) sc[h][qb][r] = 0.f;
+                }
+    }
+    V8 pp[C::KH], pd[C::KH];
+#pragma unroll
+    for (int h = 0; h < C::KH; ++h)
+#pragma unroll
         for (int qb = 0; qb < C::QB16; ++qb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int qi = qr0 + qb * 16 + 4 * x.g + r;
-                if ((unsigned)(qi - x.qlo) >= (unsigned)x.qn) sc[qb][r] = 0.f;
+                pp[h][4 * qb + r] = (S16)sc[h][qb][r];
+                pd[h][4 * qb + r] = (S16)(sc[h][qb][r] * dp[h][qb][r]);   // -dS
             }
-    }
-    V8 pp[C::KKS], pd[C::KKS];
-#pragma unroll
-    for (int qb = 0; qb < C::QB16; ++qb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            // k-step kk = qb/2 takes rows of blocks 2kk (elements 0-3), 2kk+1 (4-7)
-            pp[qb >> 1][4 * (qb & 1) + r] = (S16)sc[qb][r];
-            pd[qb >> 1][4 * (qb & 1) + r] = (S16)(sc[qb][r] * dp[qb][r]);   // -dS
-        }
-    // dV += P^T dO and -dK += (-dS)^T Q, 32 query rows per k-step; raised wave priority
-    // while these MFMAs issue (measured about 1% faster)
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int kk = 0; kk < C::KKS; ++kk)
+    for (int d0 = 0; d0 < C::NDB; d0 += 4) {
 #pragma unroll
-        for (int d0 = 0; d0 < C::NDB; d0 += 4) {
+        for (int u = 0; u < 4; ++u)
+            if (d0 > 0 || u >= C::HOIST) tr_b(0, d0 + u, bo[u], bq[u]);
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (kk > 0 || d0 > 0 || u >= C::HOIST) tr_b(kk, d0 + u, bo[u], bq[u]);
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                st.dva[d0 + u] = mfma16x16x32(pp[kk], bo[u], st.dva[d0 + u]);
-                st.dka[d0 + u] = mfma16x16x32(pd[kk], bq[u], st.dka[d0 + u]);
+            for (int h = 0; h < C::KH; ++h) {
+                st.dva[h][d0 + u] = mfma16x16x32(pp[h], bo[u], st.dva[h][d0 + u]);
+                st.dka[h][d0 + u] = mfma16x16x32(pd[h], bq[u], st.dka[h][d0 + u]);
             }
-        }
+    }
     __builtin_amdgcn_s_setprio(0);
 }
 
+}  // namespace
+
 template <class E, int D>
-__global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv_b16_kernel(
+__global__ __launch_bounds__(256, DkdvCfg<D>::WGS) void dkdv_b16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ L, const float* __restrict__ Dv, float* __restrict__ dK,
     float* __restrict__ dV, int B, int T, int Tk, int H, int HKV, float scale, int causal,
     int window, Layout lq, Layout lk, int g16) {
-    using C = Dkdv16Cfg<D>;
+    using C = DkdvCfg<D>;
     using V8 = typename E::v8;
+    static_assert(C::BQ == 32 && C::KKS == 1, "one 32-row k-step per query block");
     extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
     char* sm = reinterpret_cast<char*>(smem);
 
@@ -297,16 +309,27 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv_b16_kernel(
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index (uniform)
     const int n = lane & 15, g = lane >> 4;
     const int kw0 = kt * C::BKW + w * C::KPW;
-    const int key = kw0 + n;
     const int64_t ldq = lq.t, ldk = lk.t;   // row strides (elements)
 
-    // the group's first query head; head h2 of the group is h2 * lq.h elements further
+    // -V of the workgroup's keys into LDS, row-major with padded rows (zeros past Tk)
+    {
+        const Buf vb = head_buf<D>(V + b * lk.b + hk * lk.h, ldk, Tk);
+        constexpr int CPR = D / 8;   // 16-byte chunks per row
+        const u32x4 sign = {0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+#pragma unroll
+        for (int e = threadIdx.x; e < C::BKW * CPR; e += 256) {
+            const int r = e / CPR, ch = e % CPR;
+            const u32x4 v = vb.load16((uint32_t)(kt * C::BKW + r) * (uint32_t)(ldk * 2) + 16 * ch) ^ sign;
+            *(__attribute__((address_space(3))) u32x4*)(lds_addr(sm) + C::VOFF + r * C::PadT::ROWB + 16 * ch) = v;
+        }
+    }
+
     const uint32_t ldq_b = (uint32_t)(ldq * 2);
     const uint16_t* Qg = Q + b * lq.b + (int64_t)hk * rep * lq.h;
     const uint16_t* dOg = dO + b * lq.b + (int64_t)hk * rep * lq.h;
     const uint32_t gspan = (uint32_t)(((int64_t)(rep - 1) * lq.h + (int64_t)(T - 1) * ldq + D) * 2);
     DkdvCtx<D> x(QdoSrc{Buf(Qg, gspan), Buf(dOg, gspan), Qg, dOg, ldq, lq.h,
-                        ldq >= (int64_t)(rep - 1) * lq.h + D});
+                          ldq >= (int64_t)(rep - 1) * lq.h + D});
     x.Lg = L + ((int64_t)b * H + (int64_t)hk * rep) * T;
     x.Dg = Dv + ((int64_t)b * H + (int64_t)hk * rep) * T;
     x.w = w;
@@ -318,53 +341,44 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv_b16_kernel(
     x.g = g;
     x.cz = causal != 0;
     x.c = scale * kLog2e;
-    // queries that see this lane's key: [qlo, qlo + qn) (lanes of keys past T are never stored)
-    key_rows(key, T, Tk, x.cz, window, x.qlo, x.qn);
+#pragma unroll
+    for (int h = 0; h < C::KH; ++h) key_rows(kw0 + 16 * h + n, T, Tk, x.cz, window, x.qlo[h], x.qn[h]);
 
     DkdvState<E, D> st;
-    // B operands of S = Q K^T and D - dP = D - dO V^T: lane (n, g) holds K[key][32*ds + 8g ..
-    // +7] and the same elements of V negated (sign bits flipped: exact)
     {
         const Buf kb = head_buf<D>(K + b * lk.b + hk * lk.h, ldk, Tk);
-        const Buf vb = head_buf<D>(V + b * lk.b + hk * lk.h, ldk, Tk);
-        const uint32_t off = (uint32_t)key * (uint32_t)(ldk * 2) + 16 * g;
-        const u32x4 sign = {0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
 #pragma unroll
-        for (int ds = 0; ds < C::DS; ++ds) {
-            st.kreg[ds] = __builtin_bit_cast(V8, kb.load16(off + ds * 64));
-            st.vneg[ds] = __builtin_bit_cast(V8, vb.load16(off + ds * 64) ^ sign);
+        for (int h = 0; h < C::KH; ++h) {
+            const uint32_t off = (uint32_t)(kw0 + 16 * h + n) * (uint32_t)(ldk * 2) + 16 * g;
+#pragma unroll
+            for (int ds = 0; ds < C::DS; ++ds)
+                st.kreg[h][ds] = __builtin_bit_cast(V8, kb.load16(off + ds * 64));
         }
     }
 #pragma unroll
-    for (int i = 0; i < C::NDB; ++i) st.dka[i] = st.dva[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < C::KH; ++h)
+#pragma unroll
+        for (int i = 0; i < C::NDB; ++i) st.dka[h][i] = st.dva[h][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     int ilo, ihi;
     q_block_range(T, Tk, kt * C::BKW, kt * C::BKW + C::BKW, C::BQ, x.cz, window, ilo, ihi);
-    // query blocks that are FULL for this wave's keys
     full_q_block_range(T, Tk, kw0, kw0 + C::KPW, C::BQ, x.cz, window, x.if0, x.if1);
     x.niter = rep * (ihi - ilo);
 #pragma unroll
     for (int i = 0; i < C::PMAX; ++i)
         x.voff[i] = dma_src_offset_padded<D, 2>(w % C::QW + C::QW * i, lane, ldq_b);
     x.voff[C::PMAX] = 4u * (uint32_t)lane;
-    // per-lane LDS read bases in stage 0 (Q tile; dO is OFF_DO further): A-operand row n at
-    // column 8g; transpose-read row 4g + j/4 at column 4*(j%4) (j = lane % 16); L / D of rows
-    // 4g .. 4g + 3
     {
         const int j = lane & 15;
         x.aq = pinned_lds_addr(lds_addr(sm + 2 * (n * C::LDN + 8 * g)));
         x.tr = pinned_lds_addr(lds_addr(sm + 2 * ((4 * g + (j >> 2)) * C::LDN + 4 * (j & 3))));
         x.ld = pinned_lds_addr(lds_addr(sm + C::OFF_L + 16 * g));
+        x.va = pinned_lds_addr(lds_addr(sm + C::VOFF + (w * C::KPW + n) * C::PadT::ROWB + 16 * g));
     }
+    __syncthreads();   // the -V tile is complete
 
-    // Query blocks are walked last-first (heads inner): every key block of a KV group needs
-    // the last query blocks, so the group's co-resident workgroups (same XCD) stream the same
-    // Q / dO blocks at about the same time and share them in L2.
-    // iteration it takes query block ihi - 1 - it / rep of head it % rep; (h2n, in) steps
-    // through that sequence one iteration ahead (no divisions in the loop).  Iterations
-    // alternate between the two LDS stages: two per trip, stage 0 then stage 1.
     int h2n = 0, in = ihi - 1;
-    if (x.niter > 0) dkdv16_issue<D>(sm, x.qs, x.Lg, x.Dg, x.voff, w, h2n, in, T, 0);
+    if (x.niter > 0) dkdv_issue<D>(sm, x.qs, x.Lg, x.Dg, x.voff, w, h2n, in, T, 0);
     int it = 0;
     for (; it + 1 < x.niter; it += 2) {
         int i = in;
@@ -389,32 +403,34 @@ __global__ __launch_bounds__(256, Dkdv16Cfg<D>::WGS) void dkdv_b16_kernel(
         dkdv_block<E, D, 0>(st, x, sm, it, i, h2n, in);
     }
 
-    // entry r of lane (n, g) in block db: key kw0 + 4g + r, column db*16 + n.  dka holds -dK /
-    // scale.  Stored as float32, or (g16) rounded to the element type.
+    // entry r of lane (n, g) in block db of half h: key kw0 + 16h + 4g + r, column db*16 + n.
+    // dka holds -dK / scale.  Stored as float32, or (g16) rounded to the element type.
     const float nscale = -scale;
     const int64_t kbase = b * lk.b + hk * lk.h;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int kk = kw0 + 4 * g + r;
-        if (kk < Tk) {
-            const int64_t row = kbase + (int64_t)kk * ldk + n;
-            if (g16) {
-                typename E::s* dKh = reinterpret_cast<typename E::s*>(dK) + row;
-                typename E::s* dVh = reinterpret_cast<typename E::s*>(dV) + row;
+    for (int h = 0; h < C::KH; ++h)
 #pragma unroll
-                for (int db = 0; db < C::NDB; ++db) {
-                    dKh[db * 16] = (typename E::s)opaque(st.dka[db][r] * nscale);
-                    dVh[db * 16] = (typename E::s)opaque(st.dva[db][r]);
-                }
-            } else {
+        for (int r = 0; r < 4; ++r) {
+            const int kk = kw0 + 16 * h + 4 * g + r;
+            if (kk < Tk) {
+                const int64_t row = kbase + (int64_t)kk * ldk + n;
+                if (g16) {
+                    typename E::s* dKh = reinterpret_cast<typename E::s*>(dK) + row;
+                    typename E::s* dVh = reinterpret_cast<typename E::s*>(dV) + row;
 #pragma unroll
-                for (int db = 0; db < C::NDB; ++db) {
-                    dK[row + db * 16] = st.dka[db][r] * nscale;
-                    dV[row + db * 16] = st.dva[db][r];
+                    for (int db = 0; db < C::NDB; ++db) {
+                        dKh[db * 16] = (typename E::s)opaque(st.dka[h][db][r] * nscale);
+                        dVh[db * 16] = (typename E::s)opaque(st.dva[h][db][r]);
+                    }
+                } else {
+#pragma unroll
+                    for (int db = 0; db < C::NDB; ++db) {
+                        dK[row + db * 16] = st.dka[h][db][r] * nscale;
+                        dV[row + db * 16] = st.dva[h][db][r];
+                    }
                 }
             }
         }
-    }
 }
 
 // ------------------------------------------------------------------------------ dQ
@@ -632,9 +648,9 @@ namespace {
 
 template <class E, int D>
 hipError_t launch_dkdv_b16_t(const AttnArgs& a) {
-    using C = Dkdv16Cfg<D>;
+    using C = DkdvCfg<D>;
     static std::atomic<bool> set[kMaxDeviceSlots];
-    const size_t lds = 2 * (size_t)C::STAGE;
+    const size_t lds = (size_t)C::LDS;
     hipError_t e = allow_dynamic_lds((const void*)dkdv_b16_kernel<E, D>, lds, set);
     if (e != hipSuccess) return e;
     const int nkt = (a.Tk + C::BKW - 1) / C::BKW;
@@ -651,7 +667,7 @@ hipError_t launch_dkdv_b16_t(const AttnArgs& a) {
 constexpr int kDqWaves = 4;
 static_assert(DqCfg<128, kDqWaves>::BQ == kB16DqBq && DqCfg<128, kDqWaves>::BK == kB16DqBk,
               "dQ tiling differs from kernels.h");
-static_assert(Dkdv16Cfg<128>::BQ == kB16DkdvBq && Dkdv16Cfg<128>::BKW == kB16DkdvBk,
+static_assert(DkdvCfg<128>::BQ == kB16DkdvBq && DkdvCfg<128>::BKW == kB16DkdvBk,
               "dK/dV tiling differs from kernels.h");
 
 template <class E, int D, bool FUSE_D>

@@ -82,7 +82,7 @@ struct AttnArgs {
 // Tilings of the 16-bit kernels: query rows x keys handled per workgroup block.  Each kernel
 // translation unit static_asserts its own constants against these.
 constexpr int kB16FwdBq = 128, kB16FwdBk = 32;    // forward: q-tile x staged key block
-constexpr int kB16DkdvBq = 32, kB16DkdvBk = 64;   // dK/dV: staged query block x key tile
+constexpr int kB16DkdvBq = 32, kB16DkdvBk = 128;  // dK/dV: staged query block x key tile
 constexpr int kB16DqBq = 128, kB16DqBk = 64;      // dQ: q-tile x staged key block
 
 bool f32_tiles_supported(int bq, int bk);

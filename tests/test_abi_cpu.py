@@ -130,7 +130,7 @@ def test_f16_dtype():
 
 def test_default_tiles():
     assert fa.flash_attn_default_tiles(1, 128, 0) == (128, 32)
-    assert fa.flash_attn_default_tiles(1, 128, 1) == (32, 64)
+    assert fa.flash_attn_default_tiles(1, 128, 1) == (32, 128)
     assert fa.flash_attn_default_tiles(1, 128, 2) == (128, 64)
     assert fa.flash_attn_default_tiles(0, 8, 0) == (64, 64)
     with pytest.raises(fa.FlashAttnError):
