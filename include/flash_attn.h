@@ -100,8 +100,15 @@ fa_status_t flash_attn_fwd(const void* Q, const void* K, const void* V, void* O,
  *   dS = P * (dP - Dvec);  dQ = scale dS K;  dK = scale dS^T Q;  dV = P^T dO,
  * dK and dV summed over the H/HKV query heads of each KV head.  O and L must be the forward's
  * outputs for the same inputs.  Outputs dQ, dK, dV are float32.  Runs flash_attn_bwd_dq_dvec
- * and then flash_attn_bwd_dkdv on `stream`; the Dvec workspace (B*H*T floats) is allocated
- * stream-ordered (hipMallocAsync) and released the same way. */
+ * and then flash_attn_bwd_dkdv on `stream`.  The Dvec workspace (B*H*T floats) comes from a
+ * per-device cache of at most 4 buffers that the library keeps until the process ends: a
+ * call allocates (hipMalloc) only on a device's first calls and when a larger problem comes,
+ * and never makes the host wait for the GPU except on such growth.  Reuse of a buffer that
+ * another call may still read is ordered on the GPU (hipStreamWaitEvent), so calls on any
+ * streams and host threads are safe; concurrent calls on one device take the cache's lock for
+ * the few microseconds of their enqueueing.  Under stream capture the workspace is allocated
+ * stream-ordered (hipMallocAsync / hipFreeAsync) instead, which a graph records as memory
+ * nodes. */
 fa_status_t flash_attn_bwd(const void* Q, const void* K, const void* V, const void* O,
                            const float* L, const void* dO, float* dQ, float* dK, float* dV,
                            int B, int T, int H, int HKV, int D, float scale, int causal,

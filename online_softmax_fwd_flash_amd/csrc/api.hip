@@ -6,6 +6,7 @@
 #include "flash_attn.h"
 #include "block_class.h"
 #include "kernels.h"
+#include "workspace.h"
 
 namespace {
 
@@ -229,16 +230,17 @@ fa_status_t dq_dvec_impl(const void* Q, const void* K, const void* V, const void
     return hip_status(fa::launch_dq_b16_fused_d(a));
 }
 
-// Where the backward's Dvec workspace comes from: allocated stream-ordered per call, or the
-// library's fixed per-device scratch (no allocation).
-enum class Workspace { kStreamOrdered, kFixedScratch };
+// Where the backward's Dvec workspace comes from: the library's per-device workspace cache
+// (allocates on first use and on growth only), or its fixed per-device scratch (never
+// allocates).
+enum class Workspace { kCached, kFixedScratch };
 
 fa_status_t bwd_impl(const void* Q, const void* K, const void* V, const void* O, const float* L,
                      const void* dO, float* dQ, float* dK, float* dV, int B, int T, int Tk, int H,
                      int HKV, int D, float scale, int causal, int window, fa_dtype_t dtype,
                      hipStream_t stream, int bq, int bk, const fa_layout_t& lq,
                      const fa_layout_t& lk, int g16 = 0,
-                     Workspace ws = Workspace::kStreamOrdered) {
+                     Workspace ws = Workspace::kCached) {
     fa_status_t s = check_all({Q, K, V, O, L, dO, dQ, dK, dV}, B, T, Tk, H, HKV, D, scale, causal,
                               window, dtype, lq, lk);
     if (s != FA_OK) return s;
@@ -249,23 +251,22 @@ fa_status_t bwd_impl(const void* Q, const void* K, const void* V, const void* O,
     }
     float* Dvec = nullptr;
     const size_t floats = (size_t)B * H * T;
+    fa::WorkspaceLease lease;
     if (ws == Workspace::kFixedScratch) {
         // every Dvec row the dK/dV pass reads (rows < T) is written by the dQ pass first, so
         // the scratch needs no clearing between calls
         if (floats > (size_t)fa::kNoAllocDvecFloats) return FA_ERR_UNSUPPORTED;
         if (fa::noalloc_dvec(floats, &Dvec) != hipSuccess) return FA_ERR_HIP;
-    } else if (hipMallocAsync((void**)&Dvec, floats * sizeof(float), stream) != hipSuccess) {
-        return FA_ERR_HIP;
+    } else {
+        if (lease.acquire(floats * sizeof(float), stream) != hipSuccess) return FA_ERR_HIP;
+        Dvec = lease.ptr();
     }
     s = dq_dvec_impl(Q, K, V, O, dO, L, Dvec, dQ, B, T, Tk, H, HKV, D, scale, causal, window, dtype,
                      stream, bq, bk, lq, lk, g16);
     if (s == FA_OK)
         s = dkdv_impl(Q, K, V, dO, L, Dvec, dK, dV, B, T, Tk, H, HKV, D, scale, causal, window,
                       dtype, stream, bq, bk, lq, lk, g16);
-    if (ws == Workspace::kStreamOrdered) {
-        const hipError_t fe = hipFreeAsync(Dvec, stream);
-        if (s == FA_OK && fe != hipSuccess) s = FA_ERR_HIP;
-    }
+    if (lease.release() != hipSuccess && s == FA_OK) s = FA_ERR_HIP;
     return s;
 }
 

@@ -238,8 +238,8 @@ void test_dispatch() {
     CHECK(fwd(big) == FA_OK && g_calls.size() == 1 && g_last.T == (1 << 30));
     g_calls.clear();
     CHECK(dkdv(d) == FA_OK && g_calls.size() == 1 && g_calls[0] == "dkdv_b16");
-    // full backward: the Dvec workspace comes from hipMallocAsync.  Without a device that
-    // fails and nothing is launched (FA_ERR_HIP); with one, dQ+Dvec then dK/dV run.
+    // full backward: the Dvec workspace comes from the library's workspace cache.  Without a
+    // device that fails and nothing is launched (FA_ERR_HIP); with one, dQ+Dvec then dK/dV run.
     g_calls.clear();
     const fa_status_t s = bwd(d);
     if (s == FA_OK) {
@@ -248,8 +248,8 @@ void test_dispatch() {
         CHECK(s == FA_ERR_HIP);
         CHECK(g_calls.empty());
     }
-    // no-allocation backward: the fixed scratch replaces hipMallocAsync (which has no device
-    // to allocate on here), so the two passes run and both see the scratch as Dvec
+    // no-allocation backward: the fixed scratch replaces the workspace cache (which has no
+    // device to allocate on here), so the two passes run and both see the scratch as Dvec
     g_calls.clear();
     CHECK(flash_attn_bwd_noalloc(P(0), P(1), P(2), P(3), (const float*)P(4), P(5), (float*)P(6),
                                  (float*)P(7), (float*)P(8), d.B, d.T, d.H, d.HKV, d.D, d.scale,

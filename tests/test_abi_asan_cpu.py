@@ -1,4 +1,5 @@
-"""The C-ABI layer (csrc/api.hip) built for the host alone with AddressSanitizer and
+"""The C-ABI layer (csrc/api.hip, with the workspace cache csrc/workspace.hip) built for the
+host alone with AddressSanitizer and
 UndefinedBehaviorSanitizer, its kernel launchers replaced by recording stubs
 (tests/native/abi_asan.cpp): every validation path, the dispatch to each launcher, the
 window normalisation and the host-side block classifier run under the sanitizers, which
@@ -24,7 +25,8 @@ def test_abi_layer_under_asan_and_ubsan(tmp_path):
     exe = str(tmp_path / "abi_asan")
     cmd = ([HIPCC, "-x", "hip", "--offload-host-only", "-O1", "-g", "-fno-omit-frame-pointer"]
            + SANITIZE + ["-I", os.path.join(ROOT, "include"), "-I", CSRC,
-                         os.path.join(CSRC, "api.hip"), os.path.join(HERE, "native", "abi_asan.cpp"),
+                         os.path.join(CSRC, "api.hip"), os.path.join(CSRC, "workspace.hip"),
+                         os.path.join(HERE, "native", "abi_asan.cpp"),
                          "-o", exe])
     r = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
