@@ -208,9 +208,14 @@ def mfma_probe(steps=10, warmup=3):
             "accumulators per wave)", "grid": PROBE_GRID, "iters": PROBE_ITERS, **res}
 
 
-def run_workload(cfg, steps, warmup):
+PREWARM_S = 0.2
+
+
+def run_workload(cfg, steps, warmup, prewarm_s=PREWARM_S):
     """Time one workload: the public entry points (headline) and the stage entry points
-    (per-kernel breakdown).  Returns a dict of timings in ms."""
+    (per-kernel breakdown).  Before the `warmup` steps, untimed steps run for `prewarm_s`
+    seconds, so the GPU's clocks have settled at this workload's load whatever ran before it.
+    Returns a dict of timings in ms."""
     import torch
     import online_softmax_fwd_flash_amd as fa
     from workloads import make_inputs
@@ -250,6 +255,10 @@ def run_workload(cfg, steps, warmup):
     def events(n):
         return [[torch.cuda.Event(enable_timing=True) for _ in range(n)] for _ in range(steps)]
 
+    t_end = time.perf_counter() + prewarm_s
+    while time.perf_counter() < t_end:
+        public()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         public()
     ev_pub = events(3)
@@ -379,6 +388,14 @@ def main():
     roofline = {"bound": dk_["bound"], "achieved": dk_["achieved"], "peak": peak,
                 "unit": dk_["unit"], "frac": dk_["frac"], "kernel": dom,
                 "traffic": measured_traffic(dom) if cfg.name == "C4" else None}
+    # the other workloads before the probe: each is timed after its own clock settling
+    extra = None
+    if not args.no_extra_workloads and cfg.name == "C4":
+        extra = {}
+        for name in EXTRA_WORKLOADS:
+            c = get_config(name)
+            rr = run_workload(c, args.steps, args.warmup)
+            extra[name] = summarize(c, rr, PEAK_BF16 if c.dtype == "bf16" else PEAK_FP32)
     probe = None
     if not args.no_mfma_probe and cfg.dtype == "bf16":
         probe = mfma_probe()
@@ -407,10 +424,12 @@ def main():
         "fwd_bwd_frac_peak": round(value / peak, 4),
         "fwd_ms": s["fwd_ms"],
         "bwd_ms": s["bwd_ms"],
-        "timing": "fwd_ms / bwd_ms: medians of per-call HIP events on flash_attn_fwd and "
-                  "flash_attn_bwd over the timed steps; kernels: the stage entry points over a "
-                  "second run of as many steps, HIP events on the launch stream (ms: median, "
-                  "ms_mean: mean; achieved = work FLOP / mean)",
+        "timing": ("each workload: untimed steps for %.1f s (clock settling), the warmup "
+                   "steps, then the timed steps; fwd_ms / bwd_ms: medians of per-call HIP "
+                   "events on flash_attn_fwd and flash_attn_bwd over the timed steps; kernels: "
+                   "the stage entry points over a second run of as many steps, HIP events on "
+                   "the launch stream (ms: median, ms_mean: mean; achieved = work FLOP / mean)"
+                   % PREWARM_S),
         "fwd_ms_mean": round(r["fwd_ms_mean"], 4),
         "bwd_ms_mean": round(r["bwd_ms_mean"], 4),
         "kernels": kernels,
@@ -422,12 +441,7 @@ def main():
             out[key] = s[key]
     if probe is not None:
         out["mfma_probe"] = probe
-    if not args.no_extra_workloads and cfg.name == "C4":
-        extra = {}
-        for name in EXTRA_WORKLOADS:
-            c = get_config(name)
-            rr = run_workload(c, min(args.steps, 10), min(args.warmup, 3))
-            extra[name] = summarize(c, rr, PEAK_BF16 if c.dtype == "bf16" else PEAK_FP32)
+    if extra is not None:
         out["workloads"] = extra
     if args.prologue:
         out["prologue"] = time_prologue(cfg, args.steps, args.warmup)

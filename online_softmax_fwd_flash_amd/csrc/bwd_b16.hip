@@ -129,7 +129,8 @@ struct DkdvCfg : DkdvStage<D> {
     using Base = DkdvStage<D>;
     static constexpr int KH = 2;                          // 16-key halves per wave
     static constexpr int KPW = 16 * KH, BKW = Base::NW * KPW;
-    static constexpr int WGS = 2;                         // workgroups per CU
+    // workgroups per CU: at D = 64 the registers (168) and LDS (41 KB) allow three
+    static constexpr int WGS = D == 64 ? 3 : 2;
     // column blocks of the dV / dK products whose B operands are read before the softmax
     // arithmetic, which then hides the reads' latency (more would spill at D = 128)
     static constexpr int HOIST = D == 128 ? 2 : 4;
