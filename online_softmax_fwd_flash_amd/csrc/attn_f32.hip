@@ -19,6 +19,13 @@
 #include "common.h"
 #include "kernels.h"
 
+// At least two waves per SIMD.  That caps a wave at 256 registers, so the compiler keeps MFMA
+// results in ordinary VGPRs; with room for more it allocates them in AGPRs and copies every
+// score to VGPRs for the softmax arithmetic, extra vector instructions that cost time here
+// because the fp32 MFMA does not overlap with vector instructions (7-13% per kernel at D = 8
+// and 64).
+#define kTwoWavesPerSimd __attribute__((amdgpu_waves_per_eu(2)))
+
 namespace fa {
 
 namespace {
@@ -89,11 +96,12 @@ struct RowPrefetch {
     }
 };
 
+
 }  // namespace
 
 // ------------------------------------------------------------------------------ forward
 template <int DP, int BQ, int BK>
-__global__ __launch_bounds__(BQ / 16 * 64) void fwd_f32_kernel(
+__global__ __launch_bounds__(BQ / 16 * 64) kTwoWavesPerSimd void fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ L, int B, int T, int Tk, int H, int HKV, int D,
     float scale, int causal, int window, int nqt, Layout lq, Layout lk) {
@@ -136,6 +144,9 @@ __global__ __launch_bounds__(BQ / 16 * 64) void fwd_f32_kernel(
 
     int jlo, jhi;
     kv_block_range(T, Tk, qt * BQ, qt * BQ + BQ, BK, cz, window, jlo, jhi);
+    // key blocks FULL for this wave's rows: the class test runs only outside them
+    int jf0, jf1;
+    full_kv_block_range(T, Tk, wr0, wr0 + 16, BK, cz, window, jf0, jf1);
     for (int j0 = jlo; j0 < jhi; j0 += NSB) {
         __syncthreads();
         stage_rows<DP, SB, NT>(Ks, Kh, ldk, j0 * BK, Tk, D);
@@ -148,8 +159,13 @@ __global__ __launch_bounds__(BQ / 16 * 64) void fwd_f32_kernel(
 #pragma unroll
         for (int jj = 0; jj < NSB; ++jj) {
             const int j = j0 + jj;
-            cls[jj] = j < jhi ? block_class(T, Tk, wr0, wr0 + 16, j * BK, j * BK + BK, cz, window)
-                              : (int)kSkip;
+            cls[jj] = kFull;
+            if (j >= jhi) {
+                cls[jj] = kSkip;
+            } else if (j < jf0 || j >= jf1) {
+                keep_branch();
+                cls[jj] = block_class(T, Tk, wr0, wr0 + 16, j * BK, j * BK + BK, cz, window);
+            }
 #pragma unroll
             for (int kb = 0; kb < BK / 16; ++kb) s[jj][kb] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
             if (cls[jj] == kSkip) continue;
@@ -234,7 +250,7 @@ struct DkdvF32Keys {
 // One workgroup per (b, kv head, KW keys); wave w owns keys [w*16, w*16+16) of them and loops
 // over the query heads of the group and the query blocks that see them.
 template <int DP, int BQ, int BK>
-__global__ __launch_bounds__(DkdvF32Keys<BK>::KW / 16 * 64) void dkdv_f32_kernel(
+__global__ __launch_bounds__(DkdvF32Keys<BK>::KW / 16 * 64) kTwoWavesPerSimd void dkdv_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ L, const float* __restrict__ Dv,
     float* __restrict__ dK, float* __restrict__ dV, int B, int T, int Tk, int H, int HKV, int D,
@@ -275,6 +291,9 @@ __global__ __launch_bounds__(DkdvF32Keys<BK>::KW / 16 * 64) void dkdv_f32_kernel
 
     int ilo, ihi;
     q_block_range(T, Tk, kt * KW, kt * KW + KW, BQ, cz, window, ilo, ihi);
+    // 16-row query blocks FULL for this wave's keys: the class test runs only outside them
+    int if0, if1;
+    full_q_block_range(T, Tk, kw0, kw0 + 16, 16, cz, window, if0, if1);
     for (int hh = 0; hh < rep; ++hh) {
         const int h = hk * rep + hh;
         const float* Qh = Q + b * lq.b + h * lq.h;
@@ -294,7 +313,11 @@ __global__ __launch_bounds__(DkdvF32Keys<BK>::KW / 16 * 64) void dkdv_f32_kernel
 #pragma unroll 1
             for (int qs = 0; qs < BQ; qs += 16) {
                 const int qr0 = i * BQ + qs;
-                const int cls = block_class(T, Tk, qr0, qr0 + 16, kw0, kw0 + 16, cz, window);
+                int cls = kFull;
+                if (qr0 < if0 * 16 || qr0 >= if1 * 16) {
+                    keep_branch();
+                    cls = block_class(T, Tk, qr0, qr0 + 16, kw0, kw0 + 16, cz, window);
+                }
                 if (cls == kSkip) continue;
                 f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
                 const float* qrow = Qs + (qs + n) * LD + g * KS;
@@ -346,7 +369,7 @@ __global__ __launch_bounds__(DkdvF32Keys<BK>::KW / 16 * 64) void dkdv_f32_kernel
 
 // ------------------------------------------------------------------------------ dQ
 template <int DP, int BQ, int BK>
-__global__ __launch_bounds__(BQ / 16 * 64) void dq_f32_kernel(
+__global__ __launch_bounds__(BQ / 16 * 64) kTwoWavesPerSimd void dq_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ L, const float* __restrict__ Dv,
     float* __restrict__ dQ, int B, int T, int Tk, int H, int HKV, int D, float scale, int causal,
@@ -390,6 +413,9 @@ __global__ __launch_bounds__(BQ / 16 * 64) void dq_f32_kernel(
 
     int jlo, jhi;
     kv_block_range(T, Tk, qt * BQ, qt * BQ + BQ, BK, cz, window, jlo, jhi);
+    // 16-key blocks FULL for this wave's rows: the class test runs only outside them
+    int kf0, kf1;
+    full_kv_block_range(T, Tk, wr0, wr0 + 16, 16, cz, window, kf0, kf1);
     RowPrefetch<DP, SB, NT> pk, pv;
     if (jlo < jhi) {
         pk.load(Kh, ldk, jlo * BK, Tk, D);
@@ -409,7 +435,11 @@ __global__ __launch_bounds__(BQ / 16 * 64) void dq_f32_kernel(
 #pragma unroll 1
         for (int kb = 0; kb < nkb; ++kb) {
             const int kc0 = j0 * BK + kb * 16;
-            const int cls = block_class(T, Tk, wr0, wr0 + 16, kc0, kc0 + 16, cz, window);
+            int cls = kFull;
+            if (kc0 < kf0 * 16 || kc0 >= kf1 * 16) {
+                keep_branch();
+                cls = block_class(T, Tk, wr0, wr0 + 16, kc0, kc0 + 16, cz, window);
+            }
             if (cls == kSkip) continue;
             f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
             const float* krow = Ks + (kb * 16 + n) * LD + g * KS;
