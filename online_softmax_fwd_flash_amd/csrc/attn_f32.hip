@@ -48,11 +48,13 @@ struct F32KeyStage {
 };
 
 // Stage rows [row0, row0 + ROWS) of a [*, ld] matrix (head slice at `base`) into LDS
-// (ROWS x DW, zero outside [0, T) x [0, D)).
-template <int DP, int ROWS, int NT>
+// (ROWS x DW, zero outside [0, T) x [0, D)).  With ONES (DP < DW, so D = DP and column DP is
+// padding) column DP holds 1 in every row instead.
+template <int DP, int ROWS, int NT, bool ONES = false>
 __device__ __forceinline__ void stage_rows(float* __restrict__ dst, const float* __restrict__ base,
                                            int64_t ld, int row0, int T, int D) {
     constexpr int C4 = F32Tile<DP>::DW / 4;
+    static_assert(!ONES || (DP < F32Tile<DP>::DW && DP % 4 == 0), "no padding column");
     for (int e = threadIdx.x; e < ROWS * C4; e += NT) {
         const int r = e / C4, d = (e % C4) * 4;
         const int row = row0 + r;
@@ -61,8 +63,19 @@ __device__ __forceinline__ void stage_rows(float* __restrict__ dst, const float*
             // D is a multiple of 8, so a float4 never straddles D
             x = *reinterpret_cast<const f32x4*>(base + (int64_t)row * ld + d);
         }
+        if (ONES && d == DP) x[0] = 1.f;
         *reinterpret_cast<f32x4*>(dst + r * F32Tile<DP>::LD + d) = x;
     }
+}
+
+// max(v[l], v[l ^ 16]) for every lane l, in VALU (v_permlane16_swap_b32 exchanges the odd
+// 16-lane rows of one copy of v with the even rows of another: the two results hold v[l] and
+// v[l ^ 16] in some order, and max does not care which)
+__device__ __forceinline__ float rows16_max(float v) {
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const unsigned r0 = r[0], r1 = r[1];
+    return __builtin_elementwise_maximum(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
 }
 
 // The same ROWS x DP tile through registers: load() issues the global loads of the next block
@@ -108,6 +121,10 @@ __global__ __launch_bounds__(BQ / 16 * 64) kTwoWavesPerSimd void fwd_f32_kernel(
     using Tl = F32Tile<DP>;
     constexpr int NW = BQ / 16, NT = NW * 64, KS = Tl::KS, LD = Tl::LD, NDB = Tl::NDB;
     constexpr int SB = F32KeyStage<DP, BK>::SB, NSB = F32KeyStage<DP, BK>::NSB;
+    // When the V tile has a padding column (DP < DW, i.e. D = 8), that column holds ones, so
+    // the PV products also leave each query's sum of P in O^T row DP: no per-score adds, and
+    // the rescale of O covers the sum.
+    constexpr bool kSumInPV = DP < Tl::DW;
     __shared__ __attribute__((aligned(16))) float Ks[SB * LD];
     __shared__ __attribute__((aligned(16))) float Vs[SB * LD];
 
@@ -150,7 +167,7 @@ __global__ __launch_bounds__(BQ / 16 * 64) kTwoWavesPerSimd void fwd_f32_kernel(
     for (int j0 = jlo; j0 < jhi; j0 += NSB) {
         __syncthreads();
         stage_rows<DP, SB, NT>(Ks, Kh, ldk, j0 * BK, Tk, D);
-        stage_rows<DP, SB, NT>(Vs, Vh, ldk, j0 * BK, Tk, D);
+        stage_rows<DP, SB, NT, kSumInPV>(Vs, Vh, ldk, j0 * BK, Tk, D);
         __syncthreads();
         // S^T of the staged key blocks (each block skipped or masked by its own class); one
         // online-softmax update for all of them
@@ -194,15 +211,14 @@ __global__ __launch_bounds__(BQ / 16 * 64) kTwoWavesPerSimd void fwd_f32_kernel(
             for (int kb = 0; kb < BK / 16; ++kb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[jj][kb][r]);
-        mx = fmaxf(mx, xor_shfl(mx, 16));
-        mx = fmaxf(mx, xor_shfl(mx, 32));
+        mx = halves_max(rows16_max(mx));
         if (__any(mx > thr)) {
             const float mnew = fmaxf(m, mx);
             const float corr = fast_exp2((m - mnew) * c);
             m = mnew;
             thr = mnew + inv8c;
             mc = fmaxf(mnew * c, kNegMax);   // finite even while m = -FLT_MAX
-            lsum *= corr;
+            if constexpr (!kSumInPV) lsum *= corr;
 #pragma unroll
             for (int i = 0; i < NDB; ++i) oacc[i] *= corr;
         }
@@ -214,7 +230,7 @@ __global__ __launch_bounds__(BQ / 16 * 64) kTwoWavesPerSimd void fwd_f32_kernel(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float p = fast_exp2(fmaf(s[jj][kb][r], c, -mc));
-                    lsum += p;
+                    if constexpr (!kSumInPV) lsum += p;
                     const float* vrow = Vs + (jj * BK + kb * 16 + 4 * g + r) * LD + n;
 #pragma unroll
                     for (int db = 0; db < NDB; ++db)
@@ -223,8 +239,13 @@ __global__ __launch_bounds__(BQ / 16 * 64) kTwoWavesPerSimd void fwd_f32_kernel(
         }
     }
 
-    lsum += xor_shfl(lsum, 16);
-    lsum += xor_shfl(lsum, 32);
+    if constexpr (kSumInPV) {
+        // O^T row DP of query n: element DP % 4 of block DP / 16 in lane (n, (DP % 16) / 4)
+        lsum = __shfl(oacc[DP / 16][DP % 4], 16 * ((DP % 16) / 4) + n, 64);
+    } else {
+        lsum += xor_shfl(lsum, 16);
+        lsum += xor_shfl(lsum, 32);
+    }
     if (q >= T) return;
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     float* Oq = O + b * lq.b + (int64_t)q * ldq + h * lq.h;

@@ -26,6 +26,19 @@ def test_f32_every_head_dim(D):
     check_case(1, 129, 2, 1, D, "f32", True, 0, seed=40 + D, tiles=(64, 16))
 
 
+@pytest.mark.parametrize("tiles", [(32, 32), (64, 16), (64, 64), (32, 16)])
+@pytest.mark.parametrize("causal,window", MASKS)
+def test_f32_d8_tiles_and_masks(tiles, causal, window):
+    """D = 8: the forward's V tile carries ones in its padding column, so the row sums come
+    out of the PV products (rescaled with O)."""
+    check_case(1, 100, 4, 2, 8, "f32", causal, window, seed=36, tiles=tiles)
+
+
+@pytest.mark.parametrize("T", [1, 2, 17, 130])
+def test_f32_d8_ragged_lengths(T):
+    check_case(2, T, 4, 1, 8, "f32", True, 3 if T > 17 else 0, seed=37 + T, tiles=(64, 16))
+
+
 @pytest.mark.parametrize("T", [1, 2, 17, 257])
 def test_f32_ragged_lengths(T):
     check_case(2, T, 8, 2, 32, "f32", True, 5 if T > 17 else 0, seed=50 + T)
