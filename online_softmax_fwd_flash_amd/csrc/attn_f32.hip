@@ -142,21 +142,24 @@ __global__ __launch_bounds__(BQ / 16 * 64) kTwoWavesPerSimd void fwd_f32_kernel(
     const float* Kh = K + b * lk.b + hk * lk.h;
     const float* Vh = V + b * lk.b + hk * lk.h;
 
+    // Q * scale * log2(e) (fp32: one rounding of 2^-24 relative), so S^T comes out of the
+    // MFMAs in exp2 units
+    const float c = scale * kLog2e;
     float qreg[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
         const int d = g * KS + s;
-        qreg[s] = (q < T && d < D) ? Qh[(int64_t)q * ldq + d] : 0.f;
+        qreg[s] = (q < T && d < D) ? Qh[(int64_t)q * ldq + d] * c : 0.f;
     }
     f32x4 oacc[NDB];
 #pragma unroll
     for (int i = 0; i < NDB; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // running max m (raw score units), lazily moved: O and the sum are rescaled only when a
-    // row's max passes thr = m + 8/c (the first visible key always does), so every exp2
-    // argument stays below 8
-    float m = kNegMax, thr = -INFINITY, mc = kNegMax, lsum = 0.f;
-    const float c = scale * kLog2e;
-    const float inv8c = 8.0f / c;
+    // Running reference mc (exp2 units), lazily moved: the S^T MFMAs start from -mc, so their
+    // results are the exp2 arguments themselves; O and the sum are rescaled only when a row's
+    // block max passes mc + 8 (thr = 8 once the row has seen a key, -inf before, so the first
+    // visible key always does), so every exp2 argument stays below 8.
+    float mc = 0.f, thr = -INFINITY, lsum = 0.f;
+    f32x4 negmc = {0.f, 0.f, 0.f, 0.f};
     const bool cz = causal != 0;
 
     int jlo, jhi;
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(BQ / 16 * 64) kTwoWavesPerSimd void fwd_f32_kernel(
             if (cls[jj] == kSkip) continue;
 #pragma unroll
             for (int kb = 0; kb < BK / 16; ++kb) {
-                f32x4 a = {0.f, 0.f, 0.f, 0.f};
+                f32x4 a = negmc;
                 const float* krow = Ks + (jj * BK + kb * 16 + n) * LD + g * KS;
 #pragma unroll
                 for (int st = 0; st < KS; ++st) a = mfma16x16x4f32(krow[st], qreg[st], a);
@@ -213,14 +216,22 @@ __global__ __launch_bounds__(BQ / 16 * 64) kTwoWavesPerSimd void fwd_f32_kernel(
                 for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[jj][kb][r]);
         mx = halves_max(rows16_max(mx));
         if (__any(mx > thr)) {
-            const float mnew = fmaxf(m, mx);
-            const float corr = fast_exp2((m - mnew) * c);
-            m = mnew;
-            thr = mnew + inv8c;
-            mc = fmaxf(mnew * c, kNegMax);   // finite even while m = -FLT_MAX
+            // d: how far the row's reference moves up (a row that has seen no key yet jumps
+            // to this stage's max; its O and sum are still zero)
+            const bool seen = thr > 0.f;
+            const bool now = seen || mx > -INFINITY;
+            const float d = seen ? fmaxf(mx, 0.f) : (now ? mx : 0.f);
+            const float corr = seen ? fast_exp2(-d) : 0.f;
+            mc += d;
+            thr = now ? 8.f : -INFINITY;
+            negmc = f32x4{-mc, -mc, -mc, -mc};
             if constexpr (!kSumInPV) lsum *= corr;
 #pragma unroll
             for (int i = 0; i < NDB; ++i) oacc[i] *= corr;
+#pragma unroll
+            for (int jj = 0; jj < NSB; ++jj)
+#pragma unroll
+                for (int kb = 0; kb < BK / 16; ++kb) s[jj][kb] -= d;
         }
 #pragma unroll
         for (int jj = 0; jj < NSB; ++jj) {
@@ -229,7 +240,7 @@ __global__ __launch_bounds__(BQ / 16 * 64) kTwoWavesPerSimd void fwd_f32_kernel(
             for (int kb = 0; kb < BK / 16; ++kb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float p = fast_exp2(fmaf(s[jj][kb][r], c, -mc));
+                    const float p = fast_exp2(s[jj][kb][r]);
                     if constexpr (!kSumInPV) lsum += p;
                     const float* vrow = Vs + (jj * BK + kb * 16 + 4 * g + r) * LD + n;
 #pragma unroll
@@ -255,7 +266,7 @@ __global__ __launch_bounds__(BQ / 16 * 64) kTwoWavesPerSimd void fwd_f32_kernel(
         if (d < D) *reinterpret_cast<f32x4*>(Oq + d) = oacc[db] * inv;
     }
     if (g == 0)
-        L[((int64_t)b * H + h) * T + q] = lsum > 0.f ? m * scale + fast_log2(lsum) * kLn2 : 0.f;
+        L[((int64_t)b * H + h) * T + q] = lsum > 0.f ? (mc + fast_log2(lsum)) * kLn2 : 0.f;
 }
 
 // ------------------------------------------------------------------------------ dK / dV
@@ -281,7 +292,8 @@ __global__ __launch_bounds__(DkdvF32Keys<BK>::KW / 16 * 64) kTwoWavesPerSimd voi
     constexpr int NW = KW / 16, NT = NW * 64, KS = Tl::KS, LD = Tl::LD, NDB = Tl::NDB;
     __shared__ __attribute__((aligned(16))) float Qs[BQ * LD];
     __shared__ __attribute__((aligned(16))) float dOs[BQ * LD];
-    __shared__ float Ls[BQ], Ds[BQ];
+    __shared__ __attribute__((aligned(16))) float Ls[BQ];
+    __shared__ __attribute__((aligned(16))) float Ds[BQ];
 
     const int BG = B * HKV;
     const int kt = (int)(blockIdx.x / BG);
@@ -298,12 +310,15 @@ __global__ __launch_bounds__(DkdvF32Keys<BK>::KW / 16 * 64) kTwoWavesPerSimd voi
     const bool cz = causal != 0;
     const float c = scale * kLog2e;
 
+    // K * scale * log2(e) (fp32), so S comes out of the MFMAs in exp2 units; the S and dP
+    // MFMAs start from -L*log2(e) and -Dvec of each query row, leaving P's exp2 argument and
+    // dP - Dvec
     float kreg[KS], vreg[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
         const int d = g * KS + s;
         const bool ok = key < Tk && d < D;
-        kreg[s] = ok ? Kh[(int64_t)key * ldk + d] : 0.f;
+        kreg[s] = ok ? Kh[(int64_t)key * ldk + d] * c : 0.f;
         vreg[s] = ok ? Vh[(int64_t)key * ldk + d] : 0.f;
     }
     f32x4 dka[NDB], dva[NDB];
@@ -327,8 +342,8 @@ __global__ __launch_bounds__(DkdvF32Keys<BK>::KW / 16 * 64) kTwoWavesPerSimd voi
             stage_rows<DP, BQ, NT>(dOs, dOh, ldq, i * BQ, T, D);
             for (int e = threadIdx.x; e < BQ; e += NT) {
                 const int row = i * BQ + e;
-                Ls[e] = row < T ? Lh[row] * kLog2e : 0.f;
-                Ds[e] = row < T ? Dh[row] : 0.f;
+                Ls[e] = row < T ? -Lh[row] * kLog2e : 0.f;
+                Ds[e] = row < T ? -Dh[row] : 0.f;
             }
             __syncthreads();
 #pragma unroll 1
@@ -340,7 +355,9 @@ __global__ __launch_bounds__(DkdvF32Keys<BK>::KW / 16 * 64) kTwoWavesPerSimd voi
                     cls = block_class(T, Tk, qr0, qr0 + 16, kw0, kw0 + 16, cz, window);
                 }
                 if (cls == kSkip) continue;
-                f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+                // lane (n, g), element r: query qr0 + 4g + r, key kw0 + n
+                f32x4 sc = *reinterpret_cast<const f32x4*>(Ls + qs + 4 * g);
+                f32x4 dp = *reinterpret_cast<const f32x4*>(Ds + qs + 4 * g);
                 const float* qrow = Qs + (qs + n) * LD + g * KS;
                 const float* orow = dOs + (qs + n) * LD + g * KS;
 #pragma unroll
@@ -348,15 +365,13 @@ __global__ __launch_bounds__(DkdvF32Keys<BK>::KW / 16 * 64) kTwoWavesPerSimd voi
                     sc = mfma16x16x4f32(qrow[st], kreg[st], sc);
                     dp = mfma16x16x4f32(orow[st], vreg[st], dp);
                 }
-                // lane (n, g), element r: query qr0 + 4g + r, key kw0 + n
                 f32x4 p, ds;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int qq = qs + 4 * g + r;
-                    float pr = fast_exp2(fmaf(sc[r], c, -Ls[qq]));
+                    float pr = fast_exp2(sc[r]);
                     if (cls == kPartial && !visible(qr0 + 4 * g + r, key, T, Tk, cz, window)) pr = 0.f;
                     p[r] = pr;
-                    ds[r] = pr * (dp[r] - Ds[qq]);
+                    ds[r] = pr * dp[r];
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -418,16 +433,20 @@ __global__ __launch_bounds__(BQ / 16 * 64) kTwoWavesPerSimd void dq_f32_kernel(
     const bool cz = causal != 0;
     const float c = scale * kLog2e;
 
+    // Q * scale * log2(e) (fp32), so S^T comes out of the MFMAs in exp2 units; the S^T and
+    // dP^T MFMAs start from this lane's -L*log2(e) and -Dvec, leaving P's exp2 argument and
+    // dP - Dvec
     float qreg[KS], doreg[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
         const int d = g * KS + s;
         const bool ok = q < T && d < D;
-        qreg[s] = ok ? Qh[(int64_t)q * ldq + d] : 0.f;
+        qreg[s] = ok ? Qh[(int64_t)q * ldq + d] * c : 0.f;
         doreg[s] = ok ? dOh[(int64_t)q * ldq + d] : 0.f;
     }
     const float l2 = q < T ? L[((int64_t)b * H + h) * T + q] * kLog2e : 0.f;
     const float dq_i = q < T ? Dv[((int64_t)b * H + h) * T + q] : 0.f;
+    const f32x4 negl = {-l2, -l2, -l2, -l2}, negd = {-dq_i, -dq_i, -dq_i, -dq_i};
     f32x4 dqa[NDB];
 #pragma unroll
     for (int i = 0; i < NDB; ++i) dqa[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -462,7 +481,7 @@ __global__ __launch_bounds__(BQ / 16 * 64) kTwoWavesPerSimd void dq_f32_kernel(
                 cls = block_class(T, Tk, wr0, wr0 + 16, kc0, kc0 + 16, cz, window);
             }
             if (cls == kSkip) continue;
-            f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+            f32x4 sc = negl, dp = negd;
             const float* krow = Ks + (kb * 16 + n) * LD + g * KS;
             const float* vrow = Vs + (kb * 16 + n) * LD + g * KS;
 #pragma unroll
@@ -474,9 +493,9 @@ __global__ __launch_bounds__(BQ / 16 * 64) kTwoWavesPerSimd void dq_f32_kernel(
             f32x4 ds;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                float pr = fast_exp2(fmaf(sc[r], c, -l2));
+                float pr = fast_exp2(sc[r]);
                 if (cls == kPartial && !visible(q, kc0 + 4 * g + r, T, Tk, cz, window)) pr = 0.f;
-                ds[r] = pr * (dp[r] - dq_i);
+                ds[r] = pr * dp[r];
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
