@@ -345,6 +345,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="C4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prewarm", type=float, default=PREWARM_S,
+                    help="seconds of untimed steps before each workload's warmup steps")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-extra-workloads", action="store_true",
                     help="skip the D=64 MHA and sliding-window workloads")
@@ -368,7 +370,7 @@ def main():
 
     cfg = get_config(args.config)
     peak = PEAK_BF16 if cfg.dtype == "bf16" else PEAK_FP32
-    r = run_workload(cfg, args.steps, args.warmup)
+    r = run_workload(cfg, args.steps, args.warmup, args.prewarm)
 
     if args.calibrate_copy:
         dev = torch.device("cuda:0")
@@ -394,7 +396,7 @@ def main():
         extra = {}
         for name in EXTRA_WORKLOADS:
             c = get_config(name)
-            rr = run_workload(c, args.steps, args.warmup)
+            rr = run_workload(c, args.steps, args.warmup, args.prewarm)
             extra[name] = summarize(c, rr, PEAK_BF16 if c.dtype == "bf16" else PEAK_FP32)
     probe = None
     if not args.no_mfma_probe and cfg.dtype == "bf16":
@@ -429,7 +431,7 @@ def main():
                    "events on flash_attn_fwd and flash_attn_bwd over the timed steps; kernels: "
                    "the stage entry points over a second run of as many steps, HIP events on "
                    "the launch stream (ms: median, ms_mean: mean; achieved = work FLOP / mean)"
-                   % PREWARM_S),
+                   % args.prewarm),
         "fwd_ms_mean": round(r["fwd_ms_mean"], 4),
         "bwd_ms_mean": round(r["bwd_ms_mean"], 4),
         "kernels": kernels,
