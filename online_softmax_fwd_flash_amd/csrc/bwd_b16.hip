@@ -378,20 +378,29 @@ __global__ __launch_bounds__(256, DkdvCfg<D>::WGS) void dkdv_b16_kernel(
     }
     __syncthreads();   // the -V tile is complete
 
-    int h2n = 0, in = ihi - 1;
+    // (query head, query block) pairs, heads innermost.  Under causal masking the first half
+    // of the key tiles walks its query blocks from the last one down and the second half from
+    // its first one up.  Workgroups start in key-tile order, the first half at once and each
+    // later one on the slot an earlier one frees (tile nkt - 1 - k after tile k, which sees as
+    // many fewer blocks as the later one sees more), on the XCD of its (b, kv head) group.  So
+    // at any moment the first-half tiles of a group read the same query block, and so do its
+    // second-half tiles, which shares each block through that XCD's L2.
+    const int nkt = (Tk + C::BKW - 1) / C::BKW;
+    const int di = (x.cz && 2 * kt >= nkt) ? 1 : -1;
+    int h2n = 0, in = di > 0 ? ilo : ihi - 1;
     if (x.niter > 0) dkdv_issue<D>(sm, x.qs, x.Lg, x.Dg, x.voff, w, h2n, in, T, 0);
     int it = 0;
     for (; it + 1 < x.niter; it += 2) {
         int i = in;
         if (++h2n == rep) {
             h2n = 0;
-            --in;
+            in += di;
         }
         dkdv_block<E, D, 0>(st, x, sm, it, i, h2n, in);
         i = in;
         if (++h2n == rep) {
             h2n = 0;
-            --in;
+            in += di;
         }
         dkdv_block<E, D, 1>(st, x, sm, it + 1, i, h2n, in);
     }
@@ -399,7 +408,7 @@ __global__ __launch_bounds__(256, DkdvCfg<D>::WGS) void dkdv_b16_kernel(
         const int i = in;
         if (++h2n == rep) {
             h2n = 0;
-            --in;
+            in += di;
         }
         dkdv_block<E, D, 0>(st, x, sm, it, i, h2n, in);
     }
