@@ -39,7 +39,7 @@ class WorkspaceLease {
     WorkspaceLease() = default;
     WorkspaceLease(const WorkspaceLease&) = delete;
     WorkspaceLease& operator=(const WorkspaceLease&) = delete;
-    ~WorkspaceLease() { release(); }
+    ~WorkspaceLease() { (void)release(); }
 
     // A buffer of at least `bytes` bytes (bytes > 0) on the current device, usable by work
     // enqueued on `stream` after this returns.  On error nothing is held.
