@@ -64,20 +64,32 @@ def visible_pairs(T, causal, window):
     return int(np.maximum(0, hi - lo + 1).sum())
 
 
+TRAFFIC_TUS = ("fwd_b16.hip", "bwd_b16.hip")   # define the kernels the traffic lines cover
+
+
 def kernel_source_hash():
-    """sha256 over the kernel sources (csrc/*.hip and *.h, sorted by name), with comments and
-    whitespace removed so that edits to comments alone keep the hash."""
+    """sha256 over the sources of the measured attention kernels: their translation units and
+    the csrc headers these include (transitively), sorted by name, with comments and whitespace
+    removed so that edits to comments alone, or to code outside these kernels (the C ABI, the
+    workspace cache), keep the hash."""
     import hashlib
     import re
+    files, todo = set(), list(TRAFFIC_TUS)
+    while todo:
+        f = todo.pop()
+        if f in files or not os.path.exists(os.path.join(CSRC, f)):
+            continue
+        files.add(f)
+        with open(os.path.join(CSRC, f)) as fh:
+            todo += re.findall(r'^\s*#include\s+"([^"]+)"', fh.read(), flags=re.M)
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
-        if f.endswith((".hip", ".h")):
-            with open(os.path.join(CSRC, f)) as fh:
-                code = fh.read()
-            code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)
-            code = re.sub(r"//[^\n]*", " ", code)
-            h.update(f.encode())
-            h.update(" ".join(code.split()).encode())
+    for f in sorted(files):
+        with open(os.path.join(CSRC, f)) as fh:
+            code = fh.read()
+        code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
+        h.update(f.encode())
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()
 
 
