@@ -579,54 +579,67 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_b16_kernel(
         if (cls == kSkip) continue;
         const uint16_t* Kn = reinterpret_cast<const uint16_t*>(sm + stg * C::STAGE);
         const uint16_t* Vn = reinterpret_cast<const uint16_t*>(sm + stg * C::STAGE + C::OFF_V);
+        // NF of the two 32-key halves at a time: their S^T and dP^T MFMAs first, then each
+        // one's softmax arithmetic and dQ^T MFMAs.  With NF = 2 (D = 128) the second half's
+        // MFMAs run while the first half's exp2 and products issue (2% faster); at D = 64 the
+        // extra accumulators cost more than they hide (NF = 1).
+        constexpr int NF = D == 128 ? 2 : 1;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb0 = 0; kb0 < 2; kb0 += NF) {
             // dP^T starts at -D of this lane's query row, so the MFMAs leave dP^T - D
-            f32x16 sk, dk;
+            f32x16 sk[NF], dk[NF];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                sk[r] = 0.f;
-                dk[r] = -dq_i;
-            }
-            // A operands of S^T and dP^T for this 32-key half, four k-steps ahead
-#pragma unroll
-            for (int d0 = 0; d0 < C::DC; d0 += 4) {
-                V8 ak[4], av[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int off = (kb * 32 + n) * C::LDN + (d0 + u) * 16 + 8 * g;
-                    ak[u] = *reinterpret_cast<const V8*>(Kn + off);
-                    av[u] = *reinterpret_cast<const V8*>(Vn + off);
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    sk = mfma32x32x16(ak[u], qreg[d0 + u], sk);
-                    dk = mfma32x32x16(av[u], oreg[d0 + u], dk);
-                }
-            }
-            // entry r of lane (n, g): key j*64 + 32kb + 8*(r/4) + 4g + r%4, query q
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sk[r] = fast_exp2(fmaf(sk[r], c, -l2));
-            if (cls == kPartial) {
-                keep_branch();
+            for (int f = 0; f < NF; ++f)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int kk = j * C::BK + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-                    if ((unsigned)(kk - klo) >= (unsigned)kn) sk[r] = 0.f;
+                    sk[f][r] = 0.f;
+                    dk[f][r] = -dq_i;
                 }
-            }
-            V8 pd[2];
+            // A operands of S^T and dP^T for each 32-key half, four k-steps ahead
 #pragma unroll
-            for (int r = 0; r < 16; ++r) pd[r >> 3][r & 7] = (typename E::s)(sk[r] * dk[r]);
-            // dQ^T += K^T dS^T over this half's 32 keys, 16 per k-step
+            for (int f = 0; f < NF; ++f)
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                V8 at[C::NDB];
+                for (int d0 = 0; d0 < C::DC; d0 += 4) {
+                    V8 ak[4], av[4];
 #pragma unroll
-                for (int db = 0; db < C::NDB; ++db)
-                    at[db] = tr_operand32<E, C::LDN>(Kn, kb * 32 + hf * 16, db * 32, lane);
+                    for (int u = 0; u < 4; ++u) {
+                        const int off = ((kb0 + f) * 32 + n) * C::LDN + (d0 + u) * 16 + 8 * g;
+                        ak[u] = *reinterpret_cast<const V8*>(Kn + off);
+                        av[u] = *reinterpret_cast<const V8*>(Vn + off);
+                    }
 #pragma unroll
-                for (int db = 0; db < C::NDB; ++db) dqa[db] = mfma32x32x16(at[db], pd[hf], dqa[db]);
+                    for (int u = 0; u < 4; ++u) {
+                        sk[f] = mfma32x32x16(ak[u], qreg[d0 + u], sk[f]);
+                        dk[f] = mfma32x32x16(av[u], oreg[d0 + u], dk[f]);
+                    }
+                }
+#pragma unroll
+            for (int f = 0; f < NF; ++f) {
+                const int kb = kb0 + f;
+                // entry r of lane (n, g): key j*64 + 32kb + 8*(r/4) + 4g + r%4, query q
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sk[f][r] = fast_exp2(fmaf(sk[f][r], c, -l2));
+                if (cls == kPartial) {
+                    keep_branch();
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int kk = j * C::BK + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+                        if ((unsigned)(kk - klo) >= (unsigned)kn) sk[f][r] = 0.f;
+                    }
+                }
+                V8 pd[2];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) pd[r >> 3][r & 7] = (typename E::s)(sk[f][r] * dk[f][r]);
+                // dQ^T += K^T dS^T over this half's 32 keys, 16 per k-step
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    V8 at[C::NDB];
+#pragma unroll
+                    for (int db = 0; db < C::NDB; ++db)
+                        at[db] = tr_operand32<E, C::LDN>(Kn, kb * 32 + hf * 16, db * 32, lane);
+#pragma unroll
+                    for (int db = 0; db < C::NDB; ++db) dqa[db] = mfma32x32x16(at[db], pd[hf], dqa[db]);
+                }
             }
         }
     }
