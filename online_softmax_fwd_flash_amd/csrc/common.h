@@ -90,18 +90,6 @@ __device__ __forceinline__ float xor_shfl(float v, int mask) {
     return __shfl_xor(v, mask, 64);
 }
 
-// Round-to-nearest-even float -> bf16 pair (v_cvt_pk_bf16_f32 on gfx950).
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    bf16x2 r;
-    r[0] = (__bf16)lo;
-    r[1] = (__bf16)hi;
-    return __builtin_bit_cast(uint32_t, r);
-}
-
-__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
-    return __builtin_bit_cast(float, (uint32_t)h << 16);
-}
-
 // The 16-bit element types of the MFMA kernels (the I/O type of Q, K, V, O and dO; products
 // accumulate in fp32): scalar, and the 8-, 4- and 2-element vectors the kernels move.
 struct Bf16 {
