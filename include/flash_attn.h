@@ -37,9 +37,9 @@
  *  (flash_attn_bwd_grad16 aside).
  *
  *  Pointers are DEVICE pointers (HIP device memory of the current device), 16-byte aligned.
- *  The caller owns every buffer; the library keeps no pointer after a call returns.  Calls
- *  are asynchronous on `stream` (0 = the null stream): they return after enqueueing, and
- *  errors raised while the kernels run surface at the caller's next synchronisation.
+ *  The caller owns every buffer; the library keeps no pointer to them after a call returns.
+ *  Calls are asynchronous on `stream` (0 = the null stream): they return after enqueueing,
+ *  and errors raised while the kernels run surface at the caller's next synchronisation.
  *  Every output is overwritten (never accumulated into).
  *
  *  Errors: arguments are validated on the host before anything is enqueued.
@@ -50,7 +50,8 @@
  *                        spanning 2 GiB), an unusable layout (flash_attn_*_strided), tile
  *                        sizes that are not supported values;
  *    FA_ERR_UNSUPPORTED  a valid request this build has no kernel for (head dim);
- *    FA_ERR_HIP          a HIP runtime error while enqueueing (hipGetLastError).
+ *    FA_ERR_HIP          a HIP runtime error while enqueueing (hipGetLastError) or while
+ *                        taking the backward's workspace.
  *  No C++ exception crosses this interface.
  *
  *  Supported head dims: FA_DTYPE_F32: D a multiple of 8 in [8, 128];
@@ -134,9 +135,9 @@ fa_status_t flash_attn_bwd_noalloc(const void* Q, const void* K, const void* V, 
 
 /* As flash_attn_fwd / flash_attn_bwd, with the block tiling forced: bq query rows by bk keys
  * per block (0, 0 = the library's choice).  FA_DTYPE_F32 accepts bq in {32, 64} and
- * bk in {16, 32, 64}; the 16-bit types accept (0, 0) or their one tiling.  The tiling decides which blocks
- * are skipped, computed without a mask, or masked (causal diagonal, window edge, ragged T);
- * results agree with the automatic tiling up to rounding order. */
+ * bk in {16, 32, 64}; the 16-bit types accept (0, 0) or their one tiling.  The tiling decides
+ * which blocks are skipped, computed without a mask, or masked (causal diagonal, window edge,
+ * ragged T); results agree with the automatic tiling up to rounding order. */
 fa_status_t flash_attn_fwd_ex(const void* Q, const void* K, const void* V, void* O, float* L,
                               int B, int T, int H, int HKV, int D, float scale, int causal,
                               int window, fa_dtype_t dtype, hipStream_t stream, int bq, int bk);
@@ -167,9 +168,9 @@ typedef struct fa_layout {
  * 2 GiB.
  * Query and key lengths ([teeny] flash_attention2_forward, its n_ctx_q and n_ctx_k; no page
  * states a causal rule for them): query row i sits at key position i + Tk - T, the last T
- * positions, as when the keys start with a cached prefix.  causal keeps keys j <= i + Tk - T, window keeps
- * j >= i + Tk - T - window + 1; a row with no visible key gets O = 0 and L = 0 (when T > Tk
- * under causal, the first T - Tk rows). */
+ * positions, as when the keys start with a cached prefix.  causal keeps keys j <= i + Tk - T,
+ * window keeps j >= i + Tk - T - window + 1; a row with no visible key gets O = 0 and L = 0
+ * (when T > Tk under causal, the first T - Tk rows). */
 fa_status_t flash_attn_fwd_strided(const void* Q, const void* K, const void* V, void* O,
                                    float* L, int B, int T, int Tk, int H, int HKV, int D,
                                    float scale, int causal, int window, fa_dtype_t dtype,
