@@ -350,6 +350,68 @@ def summarize(cfg, r, peak):
     return s
 
 
+def make_line(cfg, r, steps, warmup, prewarm, traffic, probe=None, extra=None):
+    """The JSON line (without cpu_baseline / prologue) from one workload's timings `r` (as
+    run_workload returns them): `traffic(kernel)` gives the committed HBM bytes per launch or
+    None, `probe` the MFMA probe's rates, `extra` the other workloads' summaries."""
+    from workloads import fwd_flops, bwd_flops
+    peak = PEAK_BF16 if cfg.dtype == "bf16" else PEAK_FP32
+    s = summarize(cfg, r, peak)
+    ff, bf = fwd_flops(cfg), bwd_flops(cfg)
+    value = (ff + bf) / (r["ms_per_step"] * 1e-3) / 1e12
+    kernels = s["kernels"]
+    dom = max(kernels, key=lambda n: kernels[n]["ms"])
+    dk_ = kernels[dom]
+    roofline = {"bound": dk_["bound"], "achieved": dk_["achieved"], "peak": peak,
+                "unit": dk_["unit"], "frac": dk_["frac"], "kernel": dom,
+                "traffic": traffic(dom) if cfg.name == "C4" else None}
+    if probe is not None:
+        roofline["measured_peak"] = probe["normal"]
+        roofline["measured_peak_operands"] = "N(0,1) bf16 (the workload's input distribution)"
+        roofline["frac_measured_peak"] = round(dk_["achieved"] / probe["normal"], 4)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded i.i.d. N(0,1) Q, K, V, dO)",
+        "config": {"workload": cfg.describe(), "B": cfg.B, "H": cfg.H, "HKV": cfg.HKV,
+                   "T": cfg.T, "D": cfg.D, "causal": cfg.causal, "window": cfg.window,
+                   "seed": cfg.seed},
+        "fwd_tflops": s["fwd_tflops"],
+        "fwd_frac_peak": s["fwd_frac_peak"],
+        "fwd_bwd_frac_peak": round(value / peak, 4),
+        "fwd_ms": s["fwd_ms"],
+        "bwd_ms": s["bwd_ms"],
+        "timing": ("each workload: untimed steps for %.1f s (clock settling), the warmup "
+                   "steps, then the timed steps; fwd_ms / bwd_ms: medians of per-call HIP "
+                   "events on flash_attn_fwd and flash_attn_bwd over the timed steps; kernels: "
+                   "the stage entry points over a second run of as many steps, HIP events on "
+                   "the launch stream (ms: median, ms_mean: mean; achieved = work FLOP / mean)"
+                   % prewarm),
+        "fwd_ms_mean": round(r["fwd_ms_mean"], 4),
+        "bwd_ms_mean": round(r["bwd_ms_mean"], 4),
+        "kernels": kernels,
+        "roofline": roofline,
+    }
+    for key in ("fwd_tflops_window_aware", "fwd_frac_peak_window_aware",
+                "fwd_bwd_tflops_window_aware", "fwd_bwd_frac_peak_window_aware"):
+        if key in s:
+            out[key] = s[key]
+    if probe is not None:
+        out["mfma_probe"] = probe
+    if extra is not None:
+        out["workloads"] = extra
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -378,10 +440,9 @@ def main():
         sys.exit(2)
 
     import torch
-    from workloads import get_config, fwd_flops, bwd_flops
+    from workloads import get_config
 
     cfg = get_config(args.config)
-    peak = PEAK_BF16 if cfg.dtype == "bf16" else PEAK_FP32
     r = run_workload(cfg, args.steps, args.warmup, args.prewarm)
 
     if args.calibrate_copy:
@@ -393,15 +454,6 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    s = summarize(cfg, r, peak)
-    ff, bf = fwd_flops(cfg), bwd_flops(cfg)
-    value = (ff + bf) / (r["ms_per_step"] * 1e-3) / 1e12
-    kernels = s["kernels"]
-    dom = max(kernels, key=lambda n: kernels[n]["ms"])
-    dk_ = kernels[dom]
-    roofline = {"bound": dk_["bound"], "achieved": dk_["achieved"], "peak": peak,
-                "unit": dk_["unit"], "frac": dk_["frac"], "kernel": dom,
-                "traffic": measured_traffic(dom) if cfg.name == "C4" else None}
     # the other workloads before the probe: each is timed after its own clock settling
     extra = None
     if not args.no_extra_workloads and cfg.name == "C4":
@@ -410,53 +462,9 @@ def main():
             c = get_config(name)
             rr = run_workload(c, args.steps, args.warmup, args.prewarm)
             extra[name] = summarize(c, rr, PEAK_BF16 if c.dtype == "bf16" else PEAK_FP32)
-    probe = None
-    if not args.no_mfma_probe and cfg.dtype == "bf16":
-        probe = mfma_probe()
-        roofline["measured_peak"] = probe["normal"]
-        roofline["measured_peak_operands"] = "N(0,1) bf16 (the workload's input distribution)"
-        roofline["frac_measured_peak"] = round(dk_["achieved"] / probe["normal"], 4)
-
-    out = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(r["ms_per_step"], 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": cfg.dtype,
-        "data": "synthetic (seeded i.i.d. N(0,1) Q, K, V, dO)",
-        "config": {"workload": cfg.describe(), "B": cfg.B, "H": cfg.H, "HKV": cfg.HKV,
-                   "T": cfg.T, "D": cfg.D, "causal": cfg.causal, "window": cfg.window,
-                   "seed": cfg.seed},
-        "fwd_tflops": s["fwd_tflops"],
-        "fwd_frac_peak": s["fwd_frac_peak"],
-        "fwd_bwd_frac_peak": round(value / peak, 4),
-        "fwd_ms": s["fwd_ms"],
-        "bwd_ms": s["bwd_ms"],
-        "timing": ("each workload: untimed steps for %.1f s (clock settling), the warmup "
-                   "steps, then the timed steps; fwd_ms / bwd_ms: medians of per-call HIP "
-                   "events on flash_attn_fwd and flash_attn_bwd over the timed steps; kernels: "
-                   "the stage entry points over a second run of as many steps, HIP events on "
-                   "the launch stream (ms: median, ms_mean: mean; achieved = work FLOP / mean)"
-                   % args.prewarm),
-        "fwd_ms_mean": round(r["fwd_ms_mean"], 4),
-        "bwd_ms_mean": round(r["bwd_ms_mean"], 4),
-        "kernels": kernels,
-        "roofline": roofline,
-    }
-    for key in ("fwd_tflops_window_aware", "fwd_frac_peak_window_aware",
-                "fwd_bwd_tflops_window_aware", "fwd_bwd_frac_peak_window_aware"):
-        if key in s:
-            out[key] = s[key]
-    if probe is not None:
-        out["mfma_probe"] = probe
-    if extra is not None:
-        out["workloads"] = extra
+    probe = mfma_probe() if (not args.no_mfma_probe and cfg.dtype == "bf16") else None
+    out = make_line(cfg, r, args.steps, args.warmup, args.prewarm, measured_traffic, probe,
+                    extra)
     if args.prologue:
         out["prologue"] = time_prologue(cfg, args.steps, args.warmup)
     if not args.no_cpu_baseline:
