@@ -6,8 +6,9 @@
 A step is one pass of the whole path over one batch of synthetic input already resident in
 HBM: flash_attn_fwd, then flash_attn_bwd (the public entry points; the backward includes its
 stream-ordered Dvec workspace).  W untimed steps, then exactly K timed steps between device
-synchronisations give `ms_per_step` and `value`; HIP events recorded on the launch stream
-around each call give the per-call medians `fwd_ms` and `bwd_ms`.  A second run of K steps
+synchronisations give `ms_per_step` and `value`.  A second run of K steps with HIP events
+recorded on the launch stream around each call gives the per-call medians `fwd_ms` and
+`bwd_ms` (and `ms_per_step_with_events`, its wall time per step).  A third run of K steps
 calls the three kernels through their stage entry points (flash_attn_fwd,
 flash_attn_bwd_dq_dvec, flash_attn_bwd_dkdv, the kernels flash_attn_bwd runs) with events
 between them, for the per-kernel medians in `kernels` and the dominant kernel's `roofline`.
@@ -273,13 +274,19 @@ def run_workload(cfg, steps, warmup, prewarm_s=PREWARM_S):
         torch.cuda.synchronize()
     for _ in range(warmup):
         public()
-    ev_pub = events(3)
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        public()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ev_pub = events(3)
     t0 = time.perf_counter()
     for s in range(steps):
         public(ev_pub[s])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall_ev = time.perf_counter() - t0
 
     ev_st = events(4)
     for s in range(steps):
@@ -292,7 +299,7 @@ def run_workload(cfg, steps, warmup, prewarm_s=PREWARM_S):
     def mean(evs, i):
         return sum(e[i].elapsed_time(e[i + 1]) for e in evs) / len(evs)
 
-    out = {"ms_per_step": wall * 1e3 / steps,
+    out = {"ms_per_step": wall * 1e3 / steps, "ms_per_step_with_events": wall_ev * 1e3 / steps,
            "fwd_ms": med(ev_pub, 0), "bwd_ms": med(ev_pub, 1),
            "fwd_ms_mean": mean(ev_pub, 0), "bwd_ms_mean": mean(ev_pub, 1),
            "kernels_ms": {"fwd": med(ev_st, 0), "bwd_dq_dvec": med(ev_st, 1),
@@ -329,6 +336,7 @@ def summarize(cfg, r, peak):
     s = {
         "workload": cfg.describe(),
         "ms_per_step": round(r["ms_per_step"], 4),
+        "ms_per_step_with_events": round(r["ms_per_step_with_events"], 4),
         "fwd_bwd_tflops": round((ff + bf) / (r["ms_per_step"] * 1e-3) / 1e12, 2),
         "fwd_ms": round(r["fwd_ms"], 4),
         "bwd_ms": round(r["bwd_ms"], 4),
@@ -377,6 +385,7 @@ def make_line(cfg, r, steps, warmup, prewarm, traffic, probe=None, extra=None):
         "steps": steps,
         "warmup": warmup,
         "ms_per_step": round(r["ms_per_step"], 4),
+        "ms_per_step_with_events": round(r["ms_per_step_with_events"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -391,10 +400,11 @@ def make_line(cfg, r, steps, warmup, prewarm, traffic, probe=None, extra=None):
         "fwd_ms": s["fwd_ms"],
         "bwd_ms": s["bwd_ms"],
         "timing": ("each workload: untimed steps for %.1f s (clock settling), the warmup "
-                   "steps, then the timed steps; fwd_ms / bwd_ms: medians of per-call HIP "
-                   "events on flash_attn_fwd and flash_attn_bwd over the timed steps; kernels: "
-                   "the stage entry points over a second run of as many steps, HIP events on "
-                   "the launch stream (ms: median, ms_mean: mean; achieved = work FLOP / mean)"
+                   "steps, then the timed steps (no events between the calls); fwd_ms / "
+                   "bwd_ms: medians of per-call HIP events on flash_attn_fwd and "
+                   "flash_attn_bwd over a second run of as many steps; kernels: the stage "
+                   "entry points over a third run, HIP events on the launch stream (ms: "
+                   "median, ms_mean: mean; achieved = work FLOP / mean)"
                    % prewarm),
         "fwd_ms_mean": round(r["fwd_ms_mean"], 4),
         "bwd_ms_mean": round(r["bwd_ms_mean"], 4),

@@ -47,7 +47,7 @@ def test_json_line_from_synthetic_timings():
     traffic lookup only for the headline workload."""
     from workloads import get_config, fwd_flops, bwd_flops
     cfg = get_config("C4")
-    r = {"ms_per_step": 2.0, "fwd_ms": 0.5, "bwd_ms": 1.5, "fwd_ms_mean": 0.51, "bwd_ms_mean": 1.52,
+    r = {"ms_per_step": 2.0, "ms_per_step_with_events": 2.02, "fwd_ms": 0.5, "bwd_ms": 1.5, "fwd_ms_mean": 0.51, "bwd_ms_mean": 1.52,
          "kernels_ms": {"fwd": 0.5, "bwd_dq_dvec": 0.7, "bwd_dkdv": 0.8},
          "kernels_ms_mean": {"fwd": 0.5, "bwd_dq_dvec": 0.7, "bwd_dkdv": 0.8}}
     probe = {"unit": "TFLOP/s", "normal": 1500.0, "uniform01": 1600.0, "constant": 1900.0}
@@ -55,7 +55,7 @@ def test_json_line_from_synthetic_timings():
     line = bench.make_line(cfg, r, 20, 5, 0.2, lambda k: asked.append(k) or 123, probe,
                            {"C3": {"ms_per_step": 0.35}})
     for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
-                "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+                "ms_per_step_with_events", "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
                 "roofline", "kernels", "fwd_frac_peak", "fwd_bwd_frac_peak", "workloads",
                 "mfma_probe"):
         assert key in line, key
