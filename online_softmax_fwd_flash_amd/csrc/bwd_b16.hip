@@ -24,12 +24,14 @@
 // multiply per score; the per-block class test runs only outside each wave's precomputed range
 // of FULL blocks, and the diagonal mask is a branch.
 //
-// dQ pass (32x32x16 MFMA).  Workgroup = 4 waves x 32 query rows of one (b, h), two
-// workgroups per CU, walking its key blocks of 64; K and V reach LDS by LDS-DMA (padded
-// rows, double-buffered).  S^T = K Q^T and dP^T = V dO^T keep a query per accumulator
-// column, so L and D are per-lane scalars and dS^T feeds dQ^T += K^T dS^T directly, as P^T
-// feeds O^T in the forward; the K^T operand comes from the same K tile through transpose
-// reads.
+// dQ pass (16x16x32 MFMA; on N(0, 1) operands the chip sustains about a third more FLOP/s on
+// this shape than on 32x32x16 under its power limit).  Workgroup = 4 waves x 32 query rows
+// (two 16-row tiles per wave) of one (b, h), two workgroups per CU at D = 128, walking its key
+// blocks of 64; K and V reach LDS by LDS-DMA (padded rows, double-buffered).  S^T = K Q^T and
+// dP^T = V dO^T keep a query per accumulator column, so L and D are per-lane values and each
+// lane's dS^T entries of two stacked 16-key tiles form its B operand of dQ^T += K^T dS^T
+// directly; the K^T operand comes from the same K tile through transpose reads in that key
+// order.
 #include "common.h"
 #include "kernels.h"
 #include "stage_b16.h"
@@ -451,14 +453,15 @@ struct DqCfg {
     static constexpr int NT = NW * 64;
     static constexpr int BQ = NW * 32;   // NW waves x 32 query rows
     static constexpr int BK = 64;        // keys per staged block
-    static constexpr int DC = D / 16;
-    static constexpr int NDB = D / 32;
-    // Row-major K and V tiles with padded rows of D + 24 elements (LDS-DMA fills the pad
+    static constexpr int DS = D / 32;    // 32-column k-steps of S^T and dP^T
+    static constexpr int DT = D / 16;    // 16-column tiles of dQ^T
+    // Row-major K and V tiles with padded rows of D + 16 elements (LDS-DMA fills the pad
     // slots with copies).  K and V are read 16 bytes per lane as A operands of S^T and dP^T
-    // (32 consecutive rows at one chunk per half-wave: measured conflict-free at this stride,
-    // 2-way conflicted at D + 16); K is also read through transpose reads as the A operand
-    // of dQ^T += K^T dS^T (8 rows x 32 bytes per 16 lanes).
-    using PadT = Pad<D, 3>;
+    // (16 consecutive rows at four consecutive 16-byte chunks), and K through transpose reads
+    // as the A operand of dQ^T += K^T dS^T (4 rows x 32 bytes per 16 lanes): at this stride
+    // neither has LDS bank conflicts (measured; D + 8 and D + 24 give 3 conflict cycles per
+    // LDS instruction).
+    using PadT = Pad<D, 2>;
     static constexpr int LDN = PadT::ROWB / 2;                // elements per row
     static constexpr int TPIECES = BK * PadT::ROWB / 1024;    // 1 KB pieces per tile
     static constexpr int OFF_V = TPIECES * 1024;              // bytes
@@ -496,6 +499,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_b16_kernel(
     int window, int nqt, int xcd_group, Layout lq, Layout lk, int g16) {
     using C = DqCfg<D, NW>;
     using V8 = typename E::v8;
+    using S16 = typename E::s;
     extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
     char* sm = reinterpret_cast<char*>(smem);
 
@@ -504,55 +508,66 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_b16_kernel(
     const int hk = h / (H / HKV);
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index (uniform)
-    const int n = lane & 31, g = lane >> 5;
+    const int n = lane & 15, g = lane >> 4;
     const int wr0 = qt * C::BQ + w * 32;
-    const int q = wr0 + n;
     const int64_t ldq = lq.t, ldk = lk.t;   // row strides (elements)
     const uint32_t ldk_b = (uint32_t)(ldk * 2);
     const Buf kbuf = head_buf<D>(K + b * lk.b + hk * lk.h, ldk, Tk);
     const Buf vbuf = head_buf<D>(V + b * lk.b + hk * lk.h, ldk, Tk);
-    // element offset of this lane's query row in Q, O, dO and dQ
-    const int64_t qrow = b * lq.b + (int64_t)q * ldq + h * lq.h;
     const bool cz = causal != 0;
     const float c = scale * kLog2e;
 
-    // B operands of S^T = K Q^T and dP^T = V dO^T: lane (n, g) holds Q/dO[q][16*dc + 8g ..]
-    V8 qreg[C::DC], oreg[C::DC];
-    {
-        const int64_t base = qrow + 8 * g;
+    // the wave's 32 query rows are two 16-row tiles: lane (n, g) holds query rows wr0 + n and
+    // wr0 + 16 + n, and qrow is each one's element offset in Q, O, dO and dQ
+    int qq[2];
+    int64_t qrow[2];
 #pragma unroll
-        for (int dc = 0; dc < C::DC; ++dc) {
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            qreg[dc] = __builtin_bit_cast(V8, q < T ? *reinterpret_cast<const u32x4*>(Q + base + dc * 16) : z);
-            oreg[dc] = __builtin_bit_cast(V8, q < T ? *reinterpret_cast<const u32x4*>(dO + base + dc * 16) : z);
-        }
+    for (int qh = 0; qh < 2; ++qh) {
+        qq[qh] = wr0 + 16 * qh + n;
+        qrow[qh] = b * lq.b + (int64_t)qq[qh] * ldq + h * lq.h;
     }
-    const float l2 = q < T ? L[((int64_t)b * H + h) * T + q] * kLog2e : kBigLse;
-    float dq_i;
+
+    // B operands of S^T = K Q^T and dP^T = V dO^T: lane (n, g) holds Q / dO[q][32*ds + 8g ..]
+    V8 qreg[2][C::DS], oreg[2][C::DS];
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+        for (int ds = 0; ds < C::DS; ++ds) {
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            const int64_t at = qrow[qh] + ds * 32 + 8 * g;
+            qreg[qh][ds] = __builtin_bit_cast(V8, qq[qh] < T ? *reinterpret_cast<const u32x4*>(Q + at) : z);
+            oreg[qh][ds] = __builtin_bit_cast(V8, qq[qh] < T ? *reinterpret_cast<const u32x4*>(dO + at) : z);
+        }
+    float l2[2], dq_i[2];
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh)
+        l2[qh] = qq[qh] < T ? L[((int64_t)b * H + h) * T + qq[qh]] * kLog2e : kBigLse;
     if constexpr (FUSE_D) {
-        // D_i = sum_d dO[i][d] O[i][d] from this lane's 8*DC columns plus the other half's;
-        // rows past T load zeros and give 0
-        const int64_t base = qrow + 8 * g;
-        float s = 0.f;
+        // D_i = sum_d dO[i][d] O[i][d]: this lane's 8*DS columns, then the other three 16-lane
+        // rows' (rows past T load zeros and give 0)
 #pragma unroll
-        for (int dc = 0; dc < C::DC; ++dc) {
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            const u32x4 o = q < T ? *reinterpret_cast<const u32x4*>(O + base + dc * 16) : z;
-            s = dot8<E>(o, __builtin_bit_cast(u32x4, oreg[dc]), s);
+        for (int qh = 0; qh < 2; ++qh) {
+            float s = 0.f;
+#pragma unroll
+            for (int ds = 0; ds < C::DS; ++ds) {
+                const u32x4 z = {0u, 0u, 0u, 0u};
+                const u32x4 o = qq[qh] < T ? *reinterpret_cast<const u32x4*>(O + qrow[qh] + ds * 32 + 8 * g) : z;
+                s = dot8<E>(o, __builtin_bit_cast(u32x4, oreg[qh][ds]), s);
+            }
+            dq_i[qh] = rows4_sum(s);
+            if (g == 0 && qq[qh] < T) Dv[((int64_t)b * H + h) * T + qq[qh]] = dq_i[qh];
         }
-        dq_i = halves_sum(s);
-        if (g == 0 && q < T) Dv[((int64_t)b * H + h) * T + q] = dq_i;
     } else {
-        dq_i = q < T ? Dv[((int64_t)b * H + h) * T + q] : 0.f;
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh) dq_i[qh] = qq[qh] < T ? Dv[((int64_t)b * H + h) * T + qq[qh]] : 0.f;
     }
-    // keys this query row may see: [klo, klo + kn)
-    int klo, kn;
-    row_keys(q, T, Tk, cz, window, klo, kn);
-    f32x16 dqa[C::NDB];
+    // dQ^T accumulators: tile (dt, qh), entry r of lane (n, g): column 16*dt + 4g + r of query
+    // row wr0 + 16*qh + n
+    f32x4 dqa[C::DT][2];
 #pragma unroll
-    for (int i = 0; i < C::NDB; ++i)
+    for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dqa[i][r] = 0.f;
+        for (int qh = 0; qh < 2; ++qh) dqa[dt][qh] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     int jlo, jhi;
     kv_block_range(T, Tk, qt * C::BQ, qt * C::BQ + C::BQ, C::BK, cz, window, jlo, jhi);
@@ -561,7 +576,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_b16_kernel(
     uint32_t voff[C::PMAX];
 #pragma unroll
     for (int i = 0; i < C::PMAX; ++i)
-        voff[i] = dma_src_offset_padded<D, 3>(w % C::TW + C::TW * i, lane, ldk_b);
+        voff[i] = dma_src_offset_padded<D, 2>(w % C::TW + C::TW * i, lane, ldk_b);
 
     if (jlo < jhi) dq_issue<D, NW>(sm, kbuf, vbuf, voff, w, ldk_b, jlo);
     for (int j = jlo; j < jhi; ++j) {
@@ -579,91 +594,104 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_b16_kernel(
         if (cls == kSkip) continue;
         const uint16_t* Kn = reinterpret_cast<const uint16_t*>(sm + stg * C::STAGE);
         const uint16_t* Vn = reinterpret_cast<const uint16_t*>(sm + stg * C::STAGE + C::OFF_V);
-        // NF of the two 32-key halves at a time: their S^T and dP^T MFMAs first, then each
-        // one's softmax arithmetic and dQ^T MFMAs.  With NF = 2 (D = 128) the second half's
-        // MFMAs run while the first half's exp2 and products issue (2% faster); at D = 64 the
-        // extra accumulators cost more than they hide (NF = 1).
-        constexpr int NF = D == 128 ? 2 : 1;
+        // the two 32-key halves in turn: S^T and dP^T, the softmax arithmetic, then dQ^T
 #pragma unroll
-        for (int kb0 = 0; kb0 < 2; kb0 += NF) {
-            // dP^T starts at -D of this lane's query row, so the MFMAs leave dP^T - D
-            f32x16 sk[NF], dk[NF];
+        for (int kb = 0; kb < 2; ++kb) {
+            // tiles [kt][qh] of S^T and dP^T: entry r of lane (n, g) is key
+            // j*64 + 32*kb + 16*kt + 4g + r, query row wr0 + 16*qh + n.  dP^T starts at -D of
+            // its query row, so the MFMAs leave dP^T - D.
+            f32x4 sk[2][2], dk[2][2];
 #pragma unroll
-            for (int f = 0; f < NF; ++f)
+            for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    sk[f][r] = 0.f;
-                    dk[f][r] = -dq_i;
+                for (int qh = 0; qh < 2; ++qh) {
+                    sk[kt][qh] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    dk[kt][qh] = f32x4{-dq_i[qh], -dq_i[qh], -dq_i[qh], -dq_i[qh]};
                 }
-            // A operands of S^T and dP^T for each 32-key half, four k-steps ahead
+            // A operands: 16 key rows of K / V at one 32-column k-step, 16 bytes per lane
 #pragma unroll
-            for (int f = 0; f < NF; ++f)
+            for (int ds = 0; ds < C::DS; ++ds) {
+                V8 ak[2], av[2];
 #pragma unroll
-                for (int d0 = 0; d0 < C::DC; d0 += 4) {
-                    V8 ak[4], av[4];
+                for (int kt = 0; kt < 2; ++kt) {
+                    const int off = (kb * 32 + kt * 16 + n) * C::LDN + ds * 32 + 8 * g;
+                    ak[kt] = *reinterpret_cast<const V8*>(Kn + off);
+                    av[kt] = *reinterpret_cast<const V8*>(Vn + off);
+                }
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int off = ((kb0 + f) * 32 + n) * C::LDN + (d0 + u) * 16 + 8 * g;
-                        ak[u] = *reinterpret_cast<const V8*>(Kn + off);
-                        av[u] = *reinterpret_cast<const V8*>(Vn + off);
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int qh = 0; qh < 2; ++qh) {
+                        sk[kt][qh] = mfma16x16x32(ak[kt], qreg[qh][ds], sk[kt][qh]);
+                        dk[kt][qh] = mfma16x16x32(av[kt], oreg[qh][ds], dk[kt][qh]);
                     }
+            }
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        sk[f] = mfma32x32x16(ak[u], qreg[d0 + u], sk[f]);
-                        dk[f] = mfma32x32x16(av[u], oreg[d0 + u], dk[f]);
-                    }
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sk[kt][qh][r] = fast_exp2(fmaf(sk[kt][qh][r], c, -l2[qh]));
+            if (cls == kPartial) {
+                keep_branch();
+#pragma unroll
+                for (int qh = 0; qh < 2; ++qh) {
+                    int klo, kn;   // keys the query row may see: [klo, klo + kn)
+                    row_keys(qq[qh], T, Tk, cz, window, klo, kn);
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int kk = j * C::BK + 32 * kb + 16 * kt + 4 * g + r;
+                            if ((unsigned)(kk - klo) >= (unsigned)kn) sk[kt][qh][r] = 0.f;
+                        }
                 }
+            }
+            // B operand of dQ^T += K^T dS^T for query tile qh: element e is key 32*kb + 4g + e
+            // (e < 4) or 32*kb + 16 + 4g + e - 4, the lane's own entries
+            V8 pd[2];
 #pragma unroll
-            for (int f = 0; f < NF; ++f) {
-                const int kb = kb0 + f;
-                // entry r of lane (n, g): key j*64 + 32kb + 8*(r/4) + 4g + r%4, query q
+            for (int qh = 0; qh < 2; ++qh)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sk[f][r] = fast_exp2(fmaf(sk[f][r], c, -l2));
-                if (cls == kPartial) {
-                    keep_branch();
+                for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int kk = j * C::BK + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-                        if ((unsigned)(kk - klo) >= (unsigned)kn) sk[f][r] = 0.f;
-                    }
-                }
-                V8 pd[2];
+                    for (int r = 0; r < 4; ++r) pd[qh][4 * kt + r] = (S16)(sk[kt][qh][r] * dk[kt][qh][r]);
+            // A operands K^T (16 columns of K over the same 32 keys) through transpose reads,
+            // four column tiles at a time
 #pragma unroll
-                for (int r = 0; r < 16; ++r) pd[r >> 3][r & 7] = (typename E::s)(sk[f][r] * dk[f][r]);
-                // dQ^T += K^T dS^T over this half's 32 keys, 16 per k-step
+            for (int dt0 = 0; dt0 < C::DT; dt0 += 4) {
+                V8 at[4];
 #pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    V8 at[C::NDB];
+                for (int u = 0; u < 4; ++u) at[u] = tr_operand16<E, C::LDN>(Kn, kb * 32, (dt0 + u) * 16, lane);
 #pragma unroll
-                    for (int db = 0; db < C::NDB; ++db)
-                        at[db] = tr_operand32<E, C::LDN>(Kn, kb * 32 + hf * 16, db * 32, lane);
+                for (int u = 0; u < 4; ++u)
 #pragma unroll
-                    for (int db = 0; db < C::NDB; ++db) dqa[db] = mfma32x32x16(at[db], pd[hf], dqa[db]);
-                }
+                    for (int qh = 0; qh < 2; ++qh) dqa[dt0 + u][qh] = mfma16x16x32(at[u], pd[qh], dqa[dt0 + u][qh]);
             }
         }
     }
 
-    if (q >= T) return;
-    // entry r of block db: dQ^T[db*32 + 8*(r/4) + 4g + r%4][query n]; float32, or (g16)
-    // rounded to the element type
+    // tile (dt, qh) entry r: dQ[wr0 + 16*qh + n][16*dt + 4g + r]; float32, or (g16) rounded to
+    // the element type.  One store instruction writes 64 contiguous bytes of each of 16 rows.
 #pragma unroll
-    for (int db = 0; db < C::NDB; ++db)
+    for (int qh = 0; qh < 2; ++qh) {
+        if (qq[qh] >= T) continue;
 #pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4) {
+        for (int dt = 0; dt < C::DT; ++dt) {
             f32x4 o;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) o[u] = dqa[db][4 * t4 + u] * scale;
-            const int64_t at = qrow + db * 32 + 8 * t4 + 4 * g;
+            for (int r = 0; r < 4; ++r) o[r] = dqa[dt][qh][r] * scale;
+            const int64_t at = qrow[qh] + dt * 16 + 4 * g;
             if (g16) {
-                u32x2 h;
-                h[0] = pack2<E>(opaque(o[0]), opaque(o[1]));
-                h[1] = pack2<E>(opaque(o[2]), opaque(o[3]));
-                *reinterpret_cast<u32x2*>(reinterpret_cast<typename E::s*>(dQ) + at) = h;
+                u32x2 hv;
+                hv[0] = pack2<E>(opaque(o[0]), opaque(o[1]));
+                hv[1] = pack2<E>(opaque(o[2]), opaque(o[3]));
+                *reinterpret_cast<u32x2*>(reinterpret_cast<S16*>(dQ) + at) = hv;
             } else {
                 *reinterpret_cast<f32x4*>(dQ + at) = o;
             }
         }
+    }
 }
 
 // ------------------------------------------------------------------------------ launchers

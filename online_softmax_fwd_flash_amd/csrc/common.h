@@ -86,6 +86,16 @@ __device__ __forceinline__ float halves_sum(float v) {
     return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
 }
 
+// v summed over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four 16-lane rows of the wave), in
+// VALU: halves_sum, then v_permlane16_swap_b32 pairs each lane with lane l ^ 16.  Every step
+// adds two terms, which commutes, so all four lanes get the same bits.
+__device__ __forceinline__ float rows4_sum(float v) {
+    const unsigned u = __builtin_bit_cast(unsigned, halves_sum(v));
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const unsigned r0 = r[0], r1 = r[1];
+    return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+}
+
 __device__ __forceinline__ float xor_shfl(float v, int mask) {
     return __shfl_xor(v, mask, 64);
 }

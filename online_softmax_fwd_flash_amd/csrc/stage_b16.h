@@ -105,7 +105,11 @@ __device__ __forceinline__ uint32_t dma_src_offset_swz(int p, int lane, uint32_t
 // consecutive rows at one chunk are conflict-free at D + 8 and D + 24 (an odd number of
 // 16-byte slots per row whose product with 16 rows is not a multiple of the 512-byte bank
 // line) but 2-way conflicted at D + 16 and 16-way at D; transpose reads of 8 rows x 32 bytes
-// are conflict-free at D + 16 and D + 24 but 2-way at D and D + 8.  Slot s (16 bytes) of the tile is row s / (CPR + PADC), chunk s % (CPR + PADC);
+// are conflict-free at D + 16 and D + 24 but 2-way at D and D + 8.  The 16x16x32 operand
+// pattern, 16-byte reads of 16 consecutive rows at two adjacent chunks per 32 lanes, and
+// transpose reads of 4 rows x 32 bytes per 16 lanes are both conflict-free at D + 16 (the 16
+// rows' 32-byte pieces then tile the 128 banks) and conflicted at D + 8 and D + 24.
+// Slot s (16 bytes) of the tile is row s / (CPR + PADC), chunk s % (CPR + PADC);
 // a pad slot receives a copy of the row's last chunk, so every lane loads valid bytes.
 template <int D, int PADC = 1>
 struct Pad {
@@ -171,16 +175,18 @@ __device__ __forceinline__ void decode_q_work(int id, int nqt, int B, int H, int
 // max over an accumulator tile without NaN canonicalisation (v_maximum3_f32)
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
-// A operand (M = 32 columns of a row-major tile, K = 16 rows) of a 32x32x16 MFMA whose B
-// operand comes from a 32x32 accumulator: lane l = 16c + j covers column c0 + 16*(c%2) + j,
-// half g = c/2, and element e holds row r0 + 8*(e/4) + 4g + e%4 -- the row order in which
-// accumulator lane half g holds its rows.  Two LDS transpose reads of 4 rows each.
+// A operand (M = 16 columns c0 .. c0 + 15 of a row-major tile, K = 32 rows) of a 16x16x32
+// MFMA whose B operand comes from 16x16 accumulators: lane l = 16g + j covers column c0 + j,
+// and element e holds row r0 + 4g + e (e < 4) or r0 + 16 + 4g + e - 4 -- the rows in which
+// lane row g of two stacked 16-row accumulator tiles holds its entries.  Two LDS transpose
+// reads of 4 rows each: the 16 lanes of row g address rows r0 + 4g + j/4 at columns
+// c0 + 4*(j%4) .. +3, and lane j receives column c0 + j of the four rows.
 template <class E, int LD>
-__device__ __forceinline__ typename E::v8 tr_operand32(const uint16_t* tile, int r0, int c0, int lane) {
-    const int j = lane & 15, c = lane >> 4, g = c >> 1;
-    const uint16_t* p = tile + (r0 + 4 * g + (j >> 2)) * LD + c0 + 16 * (c & 1) + 4 * (j & 3);
+__device__ __forceinline__ typename E::v8 tr_operand16(const uint16_t* tile, int r0, int c0, int lane) {
+    const int j = lane & 15, g = lane >> 4;
+    const uint16_t* p = tile + (r0 + 4 * g + (j >> 2)) * LD + c0 + 4 * (j & 3);
     const typename E::v4 lo = lds_read_tr4e<E>(p);
-    const typename E::v4 hi = lds_read_tr4e<E>(p + 8 * LD);
+    const typename E::v4 hi = lds_read_tr4e<E>(p + 16 * LD);
     typename E::v8 r;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
