@@ -64,9 +64,6 @@ __device__ __forceinline__ bf16x4 lds_read_tr4(const uint16_t* p) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Value held by lane l ^ 32 (the other half of the wave).
-__device__ __forceinline__ float swap_halves(float v) { return __shfl_xor(v, 32, 64); }
-
 // max(v[l], v[l ^ 32]) for every lane l, in VALU (v_permlane32_swap_b32 exchanges lanes 32-63
 // of one copy of v with lanes 0-31 of another: the two results hold v[l % 32] and
 // v[32 + l % 32] in some order, and max does not care which)
@@ -84,6 +81,15 @@ __device__ __forceinline__ float halves_sum(float v) {
     const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
     const unsigned r0 = r[0], r1 = r[1];
     return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+}
+
+// max of v over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four 16-lane rows of the wave), in
+// VALU: halves_max, then v_permlane16_swap_b32 pairs each lane with lane l ^ 16.
+__device__ __forceinline__ float rows4_max(float v) {
+    const unsigned u = __builtin_bit_cast(unsigned, halves_max(v));
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const unsigned r0 = r[0], r1 = r[1];
+    return __builtin_elementwise_maximum(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
 }
 
 // v summed over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four 16-lane rows of the wave), in

@@ -1,4 +1,4 @@
-// 16-bit forward attention for gfx950 (bf16 or fp16 I/O, D in {64, 128}): MFMA 32x32x16 with
+// 16-bit forward attention for gfx950 (bf16 or fp16 I/O, D in {64, 128}): MFMA 16x16x32 with
 // fp32 accumulation, online softmax in registers, O and one log-sum-exp per query row stored.
 //
 // Method (prior art, other hardware): forge "flash_attention.metal", header comment and the
@@ -13,17 +13,20 @@
 //    Key blocks of 32 go HBM -> LDS by LDS-DMA (buffer_load ... lds, 16 bytes per lane): no
 //    staging registers and no LDS write instructions.  Two stages: block j + 1 is fetched
 //    while block j is computed; one barrier per block, which does not wait for that fetch.
-//  * The K tile keeps padded rows (D + 8 elements: 16-byte operand-row reads of consecutive
-//    rows at one chunk are free of bank conflicts; each row's pad slot gets a copy of a valid
-//    chunk); the V tile is unpadded with XOR-swizzled 16-byte chunks for its transpose reads
-//    (8 rows x 4 chunks per wave).
-//  * Scores are formed transposed, S^T = K Q^T: the accumulator column (lane % 32) is a query
-//    row, so each query's max / sum are in-lane plus one exchange between wave halves.
+//  * All products are 16x16x32 MFMAs (on N(0, 1) operands the chip sustains about a third
+//    more FLOP/s on this shape than on 32x32x16 under its power limit).  A wave's 32 rows are
+//    two 16-row query tiles, so each lane holds two query rows (n and 16 + n).
+//  * K and V tiles keep padded rows (D + 16 elements; each row's pad slots get copies of a
+//    valid chunk): the 16-byte K operand reads and the V^T transpose reads are then free of
+//    bank conflicts.
+//  * Scores are formed transposed, S^T = K Q^T: the accumulator column (lane % 16) is a query
+//    row, so each query's max / sum are in-lane plus two exchanges across the four 16-lane
+//    rows.
 //  * P^T (rounded to the element type, RNE) feeds O^T += V^T P^T straight from the
-//    accumulator registers.  The
-//    accumulator gives lane half g the keys 8*(r/4) + 4g + r%4 of each 32-key group; the
-//    V^T operand in that key order comes from the row-major V tile through two LDS
-//    transpose reads (ds_read_b64_tr_b16) per MFMA, so V needs no transposed copy.
+//    accumulator registers: lane row g holds keys 4g .. 4g + 3 of each 16-key tile, so its
+//    entries of the block's two key tiles are the 8 keys it supplies for a 32-key k-step; the
+//    V^T operand in that key order comes from the row-major V tile through two LDS transpose
+//    reads (ds_read_b64_tr_b16) per MFMA, so V needs no transposed copy.
 //  * The running max is rescaled lazily: O and l are only rescaled when some row's max grew
 //    by more than 2^8 (the stale max keeps every exp2 argument below 8, so nothing overflows
 //    and the final O / l and L = m*scale + ln l are exact up to rounding).
@@ -43,46 +46,42 @@ namespace fa {
 namespace {
 
 constexpr int kBQ = 128, kBK = 32, kThreads = 256;
-constexpr int kNH = kBK / 32;   // 32-key halves of a key block
 constexpr int kWgs = 3;         // workgroups per CU
 static_assert(kBQ == kB16FwdBq && kBK == kB16FwdBk, "forward tiling differs from kernels.h");
 
 template <int D>
 struct Bf16Fwd {
-    static constexpr int DC = D / 16;          // 16-wide k-steps of S^T = K Q^T
-    static constexpr int NDB = D / 32;         // 32-row blocks of O^T
+    static constexpr int DS = D / 32;          // 32-wide k-steps of S^T = K Q^T
+    static constexpr int DT = D / 16;          // 16-row tiles of O^T
     static constexpr int NW = kThreads / 64;
-    // K tile padded (operand-row reads), V tile unpadded and swizzled (transpose reads)
-    static constexpr int KROWB = Pad<D>::ROWB;
-    static constexpr int VROWB = 2 * D;
-    // LDS-DMA pieces of 1 KB (the K tile rounded up; slots past its last row take rows of
-    // the next block, which nothing reads)
-    static constexpr int KPIECES = (kBK * KROWB + 1023) / 1024;
-    static constexpr int VPIECES = kBK * VROWB / 1024;
-    static constexpr int KMAX = (KPIECES + NW - 1) / NW;      // K pieces per wave (at most)
-    static constexpr int VPW = VPIECES / NW;                  // V pieces per wave
-    static constexpr int KTILEB = KPIECES * 1024;
-    static constexpr int STAGEB = KTILEB + VPIECES * 1024;    // K tile then V tile
-    static_assert(VPW * NW == VPIECES, "V tile must split evenly over the waves");
+    // K and V tiles with padded rows of D + 16 elements: the 16-byte K operand reads (16 rows
+    // x 2 adjacent chunks per 32 lanes) and the V^T transpose reads (4 rows x 32 bytes per
+    // 16 lanes) are then free of bank conflicts
+    using PadT = Pad<D, 2>;
+    static constexpr int ROWB = PadT::ROWB;
+    static constexpr int PIECES = kBK * ROWB / 1024;          // 1 KB LDS-DMA pieces per tile
+    static constexpr int KMAX = (PIECES + NW - 1) / NW;       // pieces per wave and tile (at most)
+    static constexpr int TILEB = PIECES * 1024;
+    static constexpr int STAGEB = 2 * TILEB;                  // K tile then V tile
+    static_assert(PIECES * 1024 == kBK * ROWB, "tile must be whole pieces");
 };
 
-// LDS-DMA of key block jb into stage buffer `stage`: wave wu fills K pieces wu, wu + NW, ...
-// and V pieces [wu*VPW, +VPW).
+// LDS-DMA of key block jb into stage buffer `stage`: wave wu fills pieces wu, wu + NW, ... of
+// the K tile and the same pieces of the V tile (same layout, so the same source offsets).
 template <int D>
-__device__ __forceinline__ void fwd_issue(const Buf& kb, const Buf& vb, const uint32_t* koff,
-                                          const uint32_t* voff, char* stage, int wu,
-                                          uint32_t ld_bytes, int jb, int klast) {
+__device__ __forceinline__ void fwd_issue(const Buf& kb, const Buf& vb, const uint32_t* off,
+                                          char* stage, int wu, uint32_t ld_bytes, int jb,
+                                          int last) {
     using C = Bf16Fwd<D>;
     const int soff = __builtin_amdgcn_readfirstlane((int)((uint32_t)jb * kBK * ld_bytes));
-    // pieces wu + i*NW exist for every wave except possibly the last one (klast: this wave's
+    // pieces wu + i*NW exist for every wave except possibly the last one (last: this wave's
     // last piece exists; a wave-uniform value)
 #pragma unroll
     for (int i = 0; i < C::KMAX; ++i)
-        if (i < C::KMAX - 1 || klast)
-            dma_piece(kb, stage + (wu + i * C::NW) * 1024, koff[i], soff);
-    char* vbase = stage + C::KTILEB + wu * C::VPW * 1024;
-#pragma unroll
-    for (int i = 0; i < C::VPW; ++i) dma_piece(vb, vbase + i * 1024, voff[i], soff);
+        if (i < C::KMAX - 1 || last) {
+            dma_piece(kb, stage + (wu + i * C::NW) * 1024, off[i], soff);
+            dma_piece(vb, stage + C::TILEB + (wu + i * C::NW) * 1024, off[i], soff);
+        }
 }
 
 }  // namespace
@@ -92,31 +91,31 @@ template <int D>
 struct FwdCtx {
     using C = Bf16Fwd<D>;
     Buf kbuf, vbuf;
-    uint32_t koff[C::KMAX], voff[C::VPW];   // LDS-DMA source offsets of this lane's pieces
+    uint32_t off[C::KMAX];                   // LDS-DMA source offsets of this lane's pieces
     uint32_t kp;                             // K operand reads: stage-0 LDS address
-    uint32_t vp[C::NDB];                     // V^T operand transpose reads: stage-0 addresses
+    uint32_t vp;                             // V^T operand transpose reads: stage-0 address
     uint32_t ldk_b;                          // key row stride (bytes)
     int wu;                                  // wave index (uniform)
-    int klast;                               // this wave fills the last K piece (uniform)
+    int last;                                // this wave fills the last piece (uniform)
     int jhi, jf0, jf1;                       // block range end; FULL blocks [jf0, jf1)
     int T, Tk, wr0, window;
     bool cz;
-    int klo, kn;                             // keys this lane's query row sees
-    int g;                                   // lane half
+    int g;                                   // lane row (lane / 16)
+    int q[2];                                // this lane's two query rows
     float c;                                 // scale * log2(e)
     float inv8c;                             // 8 / c: rescale threshold above the running max
     __device__ __forceinline__ FwdCtx(const Buf& k, const Buf& v) : kbuf(k), vbuf(v) {}
 };
 
-// Online-softmax state of one wave: Q^T operands, O^T accumulators, and per query row the
-// running max m (raw score units), the rescale threshold thr = m + 8/c, m*c (clamped finite)
-// and the running sum.
+// Online-softmax state of one wave: Q^T operands, O^T accumulators, and per query row (two
+// per lane, tile qh) the running max m (raw score units), the rescale threshold thr = m + 8/c,
+// m*c (clamped finite) and the lane's part of the running sum.
 template <class E, int D>
 struct FwdState {
     using C = Bf16Fwd<D>;
-    typename E::v8 qreg[C::DC];
-    f32x16 oacc[C::NDB];
-    float m, thr, mc, lsum;
+    typename E::v8 qreg[2][C::DS];
+    f32x4 oacc[C::DT][2];
+    float m[2], thr[2], mc[2], lsum[2];
 };
 
 // One key block j, staged in LDS stage STG (a compile-time constant, so every LDS address is
@@ -138,111 +137,100 @@ __device__ __forceinline__ void fwd_block(FwdState<E, D>& st, const FwdCtx<D>& x
     // all pieces visible; every wave is done with the other stage (block j - 1)
     lds_barrier();
     if (j + 1 < x.jhi)
-        fwd_issue<D>(x.kbuf, x.vbuf, x.koff, x.voff, sm + (STG ^ 1) * C::STAGEB, x.wu, x.ldk_b,
-                     j + 1, x.klast);
+        fwd_issue<D>(x.kbuf, x.vbuf, x.off, sm + (STG ^ 1) * C::STAGEB, x.wu, x.ldk_b, j + 1, x.last);
     if (cls == kSkip) return;
-    // S^T for the block's 32-key halves: entry r of lane (n, g) in s[hk] is key
-    // j*BK + 32*hk + 8*(r/4) + 4g + r%4 of query n
-    f32x16 s[kNH];
+    // S^T tiles [kt][qh]: entry r of lane (n, g) is key j*BK + 16*kt + 4g + r of query row
+    // wr0 + 16*qh + n
+    f32x4 s[2][2];
 #pragma unroll
-    for (int hk = 0; hk < kNH; ++hk)
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[hk][r] = 0.f;
-    V8 ka[C::DC][kNH];
+        for (int qh = 0; qh < 2; ++qh) s[kt][qh] = f32x4{0.f, 0.f, 0.f, 0.f};
+    V8 ka[C::DS][2];
 #pragma unroll
-    for (int dc = 0; dc < C::DC; ++dc)
+    for (int ds = 0; ds < C::DS; ++ds)
 #pragma unroll
-        for (int hk = 0; hk < kNH; ++hk)
-            ka[dc][hk] = lds_load<V8>(x.kp + STG * C::STAGEB + 32 * dc + 32 * hk * C::KROWB);
+        for (int kt = 0; kt < 2; ++kt)
+            ka[ds][kt] = lds_load<V8>(x.kp + STG * C::STAGEB + 16 * kt * C::ROWB + 64 * ds);
 #pragma unroll
-    for (int dc = 0; dc < C::DC; ++dc)
+    for (int ds = 0; ds < C::DS; ++ds)
 #pragma unroll
-        for (int hk = 0; hk < kNH; ++hk) s[hk] = mfma32x32x16(ka[dc][hk], st.qreg[dc], s[hk]);
-    // schedule: the first DC K reads up front, then one read per MFMA, so the LDS
-    // latency hides behind the MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, C::DC, 0);
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int i = 0; i < (kNH * C::DC) / 2; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, (kNH * C::DC) / 2, 0);
+            for (int qh = 0; qh < 2; ++qh) s[kt][qh] = mfma16x16x32(ka[ds][kt], st.qreg[qh][ds], s[kt][qh]);
     if (cls == kPartial) {
         keep_branch();
 #pragma unroll
-        for (int hk = 0; hk < kNH; ++hk)
+        for (int qh = 0; qh < 2; ++qh) {
+            int klo, kn;   // keys the query row may see: [klo, klo + kn)
+            row_keys(x.q[qh], x.T, x.Tk, x.cz, x.window, klo, kn);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int k0 = j * kBK + 32 * hk + 8 * (r >> 2) + 4 * x.g + (r & 3);
-                if ((unsigned)(k0 - x.klo) >= (unsigned)x.kn) s[hk][r] = -INFINITY;
-            }
-    }
-    // block max of each query row: three-input maxima over the lane's 16 * kNH entries, then
-    // the other wave half's
-    float mx;
-    {
-        float t[kNH];
+            for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int hk = 0; hk < kNH; ++hk) {
-            const f32x16& v = s[hk];
-            const float a0 = vmax(vmax(v[0], v[1]), v[2]), a1 = vmax(vmax(v[3], v[4]), v[5]);
-            const float a2 = vmax(vmax(v[6], v[7]), v[8]), a3 = vmax(vmax(v[9], v[10]), v[11]);
-            const float a4 = vmax(vmax(v[12], v[13]), v[14]);
-            t[hk] = vmax(vmax(vmax(a0, a1), a2), vmax(vmax(a3, a4), v[15]));
+                for (int r = 0; r < 4; ++r) {
+                    const int k0 = j * kBK + 16 * kt + 4 * x.g + r;
+                    if ((unsigned)(k0 - klo) >= (unsigned)kn) s[kt][qh][r] = -INFINITY;
+                }
         }
-        mx = t[0];
-#pragma unroll
-        for (int hk = 1; hk < kNH; ++hk) mx = vmax(mx, t[hk]);
     }
-    mx = halves_max(mx);
+    // block max of each query row: three-input maxima over the lane's 8 entries, then the
+    // other three 16-lane rows'
+    float mx[2];
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+        const f32x4 &a = s[0][qh], &b = s[1][qh];
+        const float t = vmax(vmax(vmax(a[0], a[1]), a[2]), vmax(vmax(a[3], b[0]), b[1]));
+        mx[qh] = rows4_max(vmax(vmax(b[2], b[3]), t));
+    }
     // lazy rescale: only when some row's block max passed its threshold (the first visible
     // key of a row always does: thr starts at -inf).  Otherwise the stale max keeps every
     // exp2 argument below 8.
-    if (__any(mx > st.thr)) {
-        const float mnew = vmax(st.m, mx);
-        const float corr = fast_exp2((st.m - mnew) * x.c);
-        st.m = mnew;
-        st.thr = mnew + x.inv8c;
-        st.mc = vmax(mnew * x.c, kNegMax);   // finite even while m = -FLT_MAX
-        st.lsum *= corr;
+    if (__any(mx[0] > st.thr[0] || mx[1] > st.thr[1])) {
 #pragma unroll
-        for (int i = 0; i < C::NDB; ++i) st.oacc[i] *= corr;
-    }
-    float ps[kNH];
+        for (int qh = 0; qh < 2; ++qh) {
+            const float mnew = vmax(st.m[qh], mx[qh]);
+            const float corr = fast_exp2((st.m[qh] - mnew) * x.c);
+            st.m[qh] = mnew;
+            st.thr[qh] = mnew + x.inv8c;
+            st.mc[qh] = vmax(mnew * x.c, kNegMax);   // finite even while m = -FLT_MAX
+            st.lsum[qh] *= corr;
 #pragma unroll
-    for (int hk = 0; hk < kNH; ++hk) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[hk][r] = fast_exp2(fmaf(s[hk][r], x.c, -st.mc));
-        // pairwise sum: a dependency chain of 4 adds instead of 16
-        float t4[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) t4[i] = (s[hk][i] + s[hk][4 + i]) + (s[hk][8 + i] + s[hk][12 + i]);
-        ps[hk] = (t4[0] + t4[1]) + (t4[2] + t4[3]);
-    }
-#pragma unroll
-    for (int hk = 0; hk < kNH; ++hk) st.lsum += ps[hk];
-    // P^T operand of 16-key quarter kh: element e <-> accumulator entry 8*(kh % 2) + e of
-    // s[kh / 2]
-    V8 pb[2 * kNH];
-#pragma unroll
-    for (int kh = 0; kh < 2 * kNH; ++kh)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[kh][e] = (typename E::s)s[kh >> 1][8 * (kh & 1) + e];
-#pragma unroll
-    for (int kh = 0; kh < 2 * kNH; ++kh)
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-            const uint32_t pv = x.vp[db] + STG * C::STAGEB + 16 * kh * C::VROWB;
-            const V4 lo = lds_load_tr4<E>(pv);
-            const V4 hi = lds_load_tr4<E>(pv + 8 * C::VROWB);
-            V8 av;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                av[e] = lo[e];
-                av[4 + e] = hi[e];
-            }
-            st.oacc[db] = mfma32x32x16(av, pb[kh], st.oacc[db]);
+            for (int dt = 0; dt < C::DT; ++dt) st.oacc[dt][qh] *= corr;
         }
+    }
+    // P^T operand of query tile qh: element e is key 4g + e (e < 4) or 16 + 4g + e - 4, the
+    // lane's own entries, in the key order of the V^T transpose reads
+    V8 pb[2];
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s[kt][qh][r] = fast_exp2(fmaf(s[kt][qh][r], x.c, -st.mc[qh]));
+        const f32x4 &a = s[0][qh], &b = s[1][qh];
+        st.lsum[qh] += ((a[0] + a[1]) + (a[2] + a[3])) + ((b[0] + b[1]) + (b[2] + b[3]));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            pb[qh][e] = (typename E::s)a[e];
+            pb[qh][4 + e] = (typename E::s)b[e];
+        }
+    }
+    // O^T += V^T P^T: the V^T operand of column tile dt (16 columns of V over the block's 32
+    // keys) from two transpose reads
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+        const uint32_t pv = x.vp + STG * C::STAGEB + 32 * dt;
+        const V4 lo = lds_load_tr4<E>(pv);
+        const V4 hi = lds_load_tr4<E>(pv + 16 * C::ROWB);
+        V8 av;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            av[e] = lo[e];
+            av[4 + e] = hi[e];
+        }
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh) st.oacc[dt][qh] = mfma16x16x32(av, pb[qh], st.oacc[dt][qh]);
+    }
 }
 
 template <class E, int D>
@@ -259,13 +247,12 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_b16_kernel(
     decode_q_work(blockIdx.x, nqt, B, H, HKV, xcd_group, qt, b, h);
     const int hk = h / (H / HKV);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int n = lane & 31, g = lane >> 5;
+    const int n = lane & 15, g = lane >> 4;
     const int64_t ldq = lq.t, ldk = lk.t;   // row strides (elements)
 
     FwdCtx<D> x(head_buf<D>(K + b * lk.b + hk * lk.h, ldk, Tk),
                 head_buf<D>(V + b * lk.b + hk * lk.h, ldk, Tk));
     x.wr0 = qt * kBQ + __builtin_amdgcn_readfirstlane(w) * 32;   // wave-uniform: scalar block tests
-    const int q = x.wr0 + n;
     x.ldk_b = (uint32_t)(ldk * 2);
     x.cz = causal != 0;
     x.T = T;
@@ -274,26 +261,32 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_b16_kernel(
     x.g = g;
     x.c = scale * kLog2e;
     x.inv8c = 8.0f / x.c;
-    // keys this query row may see: [klo, klo + kn)
-    row_keys(q, T, Tk, x.cz, window, x.klo, x.kn);
+    x.q[0] = x.wr0 + n;
+    x.q[1] = x.wr0 + 16 + n;
 
     FwdState<E, D> st;
-    // Q^T operand: lane (n, g) holds Q[q][16*dc + 8*g .. +7] (zero past T)
+    // Q^T operands: lane (n, g) holds Q[q][32*ds + 8g .. +7] of its two rows (zero past T)
     {
         const Buf qbuf = head_buf<D>(Q + b * lq.b + h * lq.h, ldq, T);
-        const uint32_t off = (uint32_t)q * (uint32_t)(ldq * 2) + 16 * g;
 #pragma unroll
-        for (int dc = 0; dc < C::DC; ++dc)
-            st.qreg[dc] = __builtin_bit_cast(V8, qbuf.load16(off + dc * 32));
+        for (int qh = 0; qh < 2; ++qh) {
+            const uint32_t off = (uint32_t)x.q[qh] * (uint32_t)(ldq * 2) + 16 * g;
+#pragma unroll
+            for (int ds = 0; ds < C::DS; ++ds)
+                st.qreg[qh][ds] = __builtin_bit_cast(V8, qbuf.load16(off + ds * 64));
+        }
     }
 #pragma unroll
-    for (int i = 0; i < C::NDB; ++i)
+    for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) st.oacc[i][r] = 0.f;
-    st.m = kNegMax;
-    st.thr = -INFINITY;
-    st.mc = kNegMax;
-    st.lsum = 0.f;
+        for (int qh = 0; qh < 2; ++qh) st.oacc[dt][qh] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+        st.m[qh] = kNegMax;
+        st.thr[qh] = -INFINITY;
+        st.mc[qh] = kNegMax;
+        st.lsum[qh] = 0.f;
+    }
 
     int jlo;
     kv_block_range(T, Tk, qt * kBQ, qt * kBQ + kBQ, kBK, x.cz, window, jlo, x.jhi);
@@ -303,28 +296,16 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_b16_kernel(
     // LDS-DMA source offsets of this lane in its wave's pieces of a K / V tile
     x.wu = __builtin_amdgcn_readfirstlane(w);
 #pragma unroll
-    for (int i = 0; i < C::KMAX; ++i) x.koff[i] = dma_src_offset_padded<D>(w + i * C::NW, lane, x.ldk_b);
-#pragma unroll
-    for (int i = 0; i < C::VPW; ++i) x.voff[i] = dma_src_offset_swz<D>(w * C::VPW + i, lane, x.ldk_b);
-    // LDS read offsets inside a stage.  K operand: rows n and 32 + n, chunk 2*dc + g (padded
-    // rows: consecutive k-steps are 32 bytes apart).  V^T operand via transpose reads: lane
-    // 16*cq + jj reads 8 bytes of row 16*kh + 4*(cq/2) + jj/4 (and 8 rows further) at
-    // column 32*db + 16*(cq%2) + 4*(jj%4).
+    for (int i = 0; i < C::KMAX; ++i) x.off[i] = dma_src_offset_padded<D, 2>(w + i * C::NW, lane, x.ldk_b);
+    // LDS read bases inside a stage.  K operand: row n at byte 16g (k-steps 64 bytes apart,
+    // key tiles 16 rows apart).  V^T operand: lane (j, g) addresses row 4g + j/4 at column
+    // 4*(j%4) (column tiles 32 bytes apart; the second read 16 rows further).
     char* sm = reinterpret_cast<char*>(smem);
-    x.kp = pinned_lds_addr(lds_addr(sm + n * C::KROWB + 16 * g));
-    {
-        const int jj = lane & 15, cq = lane >> 4;
-        const int vr = 4 * (cq >> 1) + (jj >> 2);
-        const int vx = Swz<D>::v(vr) >> 2;
-        const int lo2 = 2 * (cq & 1) + ((jj & 3) >> 1);
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
-            x.vp[db] = pinned_lds_addr(lds_addr(sm + C::KTILEB + vr * C::VROWB +
-                                                16 * (4 * (db ^ vx) + lo2) + 8 * (jj & 1)));
-    }
+    x.kp = pinned_lds_addr(lds_addr(sm + n * C::ROWB + 16 * g));
+    x.vp = pinned_lds_addr(lds_addr(sm + C::TILEB + (4 * g + (n >> 2)) * C::ROWB + 8 * (n & 3)));
 
-    x.klast = __builtin_amdgcn_readfirstlane((int)(x.wu + (C::KMAX - 1) * C::NW < C::KPIECES));
-    if (jlo < x.jhi) fwd_issue<D>(x.kbuf, x.vbuf, x.koff, x.voff, sm, x.wu, x.ldk_b, jlo, x.klast);
+    x.last = __builtin_amdgcn_readfirstlane((int)(x.wu + (C::KMAX - 1) * C::NW < C::PIECES));
+    if (jlo < x.jhi) fwd_issue<D>(x.kbuf, x.vbuf, x.off, sm, x.wu, x.ldk_b, jlo, x.last);
 
     // blocks alternate between the two LDS stages: two per trip, stage 0 then stage 1
     int j = jlo;
@@ -334,29 +315,34 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_b16_kernel(
     }
     if (j < x.jhi) fwd_block<E, D, 0>(st, x, sm, j);
 
-    float lsum = st.lsum + swap_halves(st.lsum);
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    if (g == 0 && q < T)
-        L[((int64_t)b * H + h) * T + q] = lsum > 0.f ? st.m * scale + fast_log2(lsum) * kLn2 : 0.f;
+    // the row sums over the four 16-lane rows; L and 1/l per query row
+    float inv[2];
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+        const float lsum = rows4_sum(st.lsum[qh]);
+        inv[qh] = lsum > 0.f ? 1.f / lsum : 0.f;
+        if (g == 0 && x.q[qh] < T)
+            L[((int64_t)b * H + h) * T + x.q[qh]] = lsum > 0.f ? st.m[qh] * scale + fast_log2(lsum) * kLn2 : 0.f;
+    }
     // O leaves through LDS, so that every store instruction writes whole rows: each wave puts
-    // its 32 x D tile, row-major, in its quarter of the two stages (free once every wave is
-    // past its last block), then reads it back 16 bytes per lane, 16 lanes per row.  Row
-    // stride D + 8 elements: the 8-byte writes of 32 rows at one column hit distinct banks.
+    // its 32 x D tile, row-major, in its part of the two stages (free once every wave is past
+    // its last block), then reads it back 16 bytes per lane, D/8 lanes per row.  Row stride
+    // D + 8 elements: the 8-byte writes of 16 rows at 4 adjacent columns hit distinct banks.
     lds_barrier();
     constexpr uint32_t OROW = 2 * D + 16;
     static_assert(kThreads / 64 * 32 * OROW <= 2 * C::STAGEB, "O tiles must fit the stages");
     const uint32_t ot = lds_addr(sm) + (uint32_t)w * 32 * OROW;
-    // lane (n, g), entry r of block db: O^T[db*32 + 8*(r/4) + 4g + r%4][query n]
+    // tile (dt, qh), entry r of lane (n, g): O^T[16*dt + 4g + r][query row 16*qh + n]
 #pragma unroll
-    for (int db = 0; db < C::NDB; ++db)
+    for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4) {
+        for (int qh = 0; qh < 2; ++qh) {
             u32x2 wv;
-            wv[0] = pack2<E>(st.oacc[db][4 * t4 + 0] * inv, st.oacc[db][4 * t4 + 1] * inv);
-            wv[1] = pack2<E>(st.oacc[db][4 * t4 + 2] * inv, st.oacc[db][4 * t4 + 3] * inv);
-            *(__attribute__((address_space(3))) u32x2*)(ot + n * OROW + 2 * (db * 32 + 8 * t4 + 4 * g)) = wv;
+            wv[0] = pack2<E>(st.oacc[dt][qh][0] * inv[qh], st.oacc[dt][qh][1] * inv[qh]);
+            wv[1] = pack2<E>(st.oacc[dt][qh][2] * inv[qh], st.oacc[dt][qh][3] * inv[qh]);
+            *(__attribute__((address_space(3))) u32x2*)(ot + (16 * qh + n) * OROW + 2 * (16 * dt + 4 * g)) = wv;
         }
-    // lane l: row 4i + l/16 of the wave's 32, elements 8*(l%16) .. +7 (rows past T not stored)
+    // lane l: row RPI*i + l/LPR of the wave's 32, elements 8*(l%LPR) .. +7 (rows past T not stored)
     constexpr int LPR = D / 8;                  // lanes per row
     constexpr int RPI = 64 / LPR;               // rows per instruction
     const int rr = lane / LPR, ch = lane % LPR;

@@ -77,29 +77,6 @@ __device__ __forceinline__ void wait_vmcnt() {
 // after the barrier once that wave has waited for those loads (wait_vmcnt).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// Unpadded row-major [rows x D] 16-bit tile in LDS whose 16-byte chunks are XOR-swizzled per
-// row, filled by LDS-DMA (buffer_load ... lds, 16 bytes per lane: a wave instruction writes
-// 1 KB of consecutive LDS bytes).  The swizzle serves tiles read with ds_read_b64_tr_b16
-// (8 consecutive rows x 4 adjacent chunks per wave): XOR with a multiple of 4 keeps the 4
-// chunks adjacent and spreads the rows over the 128 four-byte banks (512 bytes = RP rows).
-template <int D>
-struct Swz {
-    static constexpr int ROWB = 2 * D;         // bytes per row
-    static constexpr int CPR = D / 8;          // 16-byte chunks per row
-    static constexpr int RP = 512 / ROWB;      // rows per bank line
-    static __device__ __forceinline__ int v(int r) { return 4 * ((r / RP) % (CPR / 4)); }
-};
-
-// Byte offset, relative to the tile's first global row, of the 16 bytes lane `lane` moves
-// into slot `lane` of LDS-DMA piece p (tile bytes [p KB, p KB + 1 KB)) of a swizzled tile.
-template <int D>
-__device__ __forceinline__ uint32_t dma_src_offset_swz(int p, int lane, uint32_t ld_bytes) {
-    using S = Swz<D>;
-    const int byte = p * 1024 + 16 * lane;
-    const int r = byte / S::ROWB, pc = (byte % S::ROWB) / 16;
-    return (uint32_t)r * ld_bytes + 16u * (uint32_t)(pc ^ S::v(r));
-}
-
 // Padded row-major [rows x D] 16-bit tile filled by LDS-DMA: rows are D + 8*PADC elements
 // apart.  Measured on gfx950 (128 banks, 32 lanes serviced together): 16-byte reads of 32
 // consecutive rows at one chunk are conflict-free at D + 8 and D + 24 (an odd number of
