@@ -23,8 +23,9 @@ algorithmic work is FLOP per visible (query, key) pair times the visible pairs.
 window; the window one also counted by its visible pairs) unless --no-extra-workloads.
 
 `roofline.measured_peak` is the bf16 MFMA rate the chip sustains in the library's MFMA probe
-(flash_attn_mfma_rate_probe) on N(0,1) operands, the distribution of this workload's inputs;
-`mfma_probe` lists it beside the rates on uniform [0,1) and constant operands.
+(flash_attn_mfma_rate_probe: 16x16x32 MFMAs, the shape the attention kernels use) on N(0,1)
+operands, the distribution of this workload's inputs; `mfma_probe` lists it beside the rates
+on uniform [0,1) and constant operands.
 
 roofline.traffic is the HBM byte count (read + write) per launch of the dominant kernel, taken
 from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary scaled by a plain device copy of
@@ -52,8 +53,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_c4_hbm_traffic.md")
 CSRC = os.path.join(ROOT, "online_softmax_fwd_flash_amd", "csrc")
 METRIC = "causal attn TFLOP/s fwd & fwd+bwd (bf16, GQA, T=4096, D=128); % MFMA peak"
 EXTRA_WORKLOADS = ("C3", "C5")
-PROBE_GRID, PROBE_ITERS = 2048, 1000   # MFMA probe launch: grid * 4 * iters * 16 MFMAs
-MFMA_FLOP = 2 * 32 * 32 * 16           # one bf16 32x32x16 MFMA
+PROBE_GRID, PROBE_ITERS = 2048, 1000   # MFMA probe launch: grid * 4 * iters * 32 MFMAs
+MFMA_FLOP = 2 * 16 * 16 * 32           # one bf16 16x16x32 MFMA
 
 
 def visible_pairs(T, causal, window):
@@ -202,7 +203,7 @@ def mfma_probe(steps=10, warmup=3):
     }
     out = torch.empty(PROBE_GRID * 256, device=dev, dtype=torch.float32)
     stream = torch.cuda.current_stream()
-    flop = PROBE_GRID * 4 * PROBE_ITERS * 16 * MFMA_FLOP
+    flop = PROBE_GRID * 4 * PROBE_ITERS * 32 * MFMA_FLOP
     res = {}
     for name, vals in dists.items():
         ops = vals.to(torch.bfloat16).to(dev)
@@ -217,8 +218,9 @@ def mfma_probe(steps=10, warmup=3):
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1))
         res[name] = round(flop / (statistics.median(ts) * 1e-3) / 1e12, 1)
-    return {"unit": "TFLOP/s", "kernel": "mfma_probe_kernel (bf16 32x32x16, 4 independent "
-            "accumulators per wave)", "grid": PROBE_GRID, "iters": PROBE_ITERS, **res}
+    return {"unit": "TFLOP/s", "kernel": "mfma_probe_kernel (bf16 16x16x32, the attention "
+            "kernels' shape; 8 independent accumulators per wave)", "grid": PROBE_GRID,
+            "iters": PROBE_ITERS, **res}
 
 
 PREWARM_S = 0.2

@@ -291,9 +291,9 @@ fa_status_t flash_attn_check_layout(fa_layout_t layout, int B, int T, int heads,
                                     fa_dtype_t dtype);
 
 /* Measurement helper (not part of the attention path): a kernel of `grid` workgroups of 256
- * threads (four waves) in which every wave issues iters * 16 bf16 MFMA 32x32x16 operations
- * (32768 FLOP each) on fixed operands, so the launch performs grid * 4 * iters * 16 * 32768
- * FLOP.  `operands` holds 4096 bf16 values (lane l's 16-byte fragments at element offsets
+ * threads (four waves) in which every wave issues iters * 32 bf16 MFMA 16x16x32 operations
+ * (16384 FLOP each; the shape the attention kernels use) on fixed operands, so the launch
+ * performs grid * 4 * iters * 32 * 16384 FLOP.  `operands` holds 4096 bf16 values (lane l's 16-byte fragments at element offsets
  * (i*64 + l)*8, i < 8), loaded once per wave; their distribution decides the rate, since the
  * chip's power limit depends on the bits the MFMA units switch.  `out` receives grid * 256
  * floats (sums of the accumulators, so the work is not optimised away).  Device pointers,

@@ -399,7 +399,7 @@ def flash_attn_check_layout(strides, B, T, heads, D, dtype):
 
 
 def flash_attn_mfma_rate_probe(operands, out, grid, iters, stream=None):
-    """Launch the library's MFMA throughput probe (grid * 4 * iters * 16 bf16 32x32x16 MFMAs)
+    """Launch the library's MFMA throughput probe (grid * 4 * iters * 32 bf16 16x16x32 MFMAs)
     on `operands` (4096 bfloat16 values, cuda) writing grid * 256 floats to `out`."""
     _want(operands, (4096,), torch.bfloat16, "operands")
     _want(out, (grid * 256,), torch.float32, "out", operands.device)

@@ -15,7 +15,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -24,13 +23,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegMax = -3.402823466e+38f;  // running max starts here, never at -inf
 
-// D(32x32) += A(32x16) * B(16x32), bf16 inputs, fp32 accumulate.
-// Lane l supplies A row (l % 32) and B column (l % 32), each with 8 consecutive k of the
-// half (l / 32); D element r of lane l is row 8*(r/4) + 4*(l/32) + (r%4), column l % 32.
-__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
 // D(16x16) += A(16x32) * B(32x16), bf16 inputs, fp32 accumulate.  Lane l supplies A row
 // (l % 16) and B column (l % 16), each with 8 consecutive k of group l / 16; D element r of
 // lane l is row 4*(l/16) + r, column l % 16.
@@ -38,10 +30,7 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// The same two MFMA shapes with IEEE half inputs (same lane layouts).
-__device__ __forceinline__ f32x16 mfma32x32x16(f16x8 a, f16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
+// The same MFMA shape with IEEE half inputs (same lane layout).
 __device__ __forceinline__ f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }

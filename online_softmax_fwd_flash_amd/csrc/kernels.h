@@ -124,8 +124,8 @@ constexpr int64_t kNoAllocDvecFloats = int64_t(1) << 22;
 // kNoAllocDvecFloats.
 hipError_t noalloc_dvec(size_t floats, float** out);
 
-// MFMA throughput probe: grid workgroups of 256 threads, each wave running iters x 16
-// bf16 32x32x16 MFMAs on the 4096 bf16 operand values at ops; out gets grid * 256 floats.
+// MFMA throughput probe: grid workgroups of 256 threads, each wave running iters x 32
+// bf16 16x16x32 MFMAs on the 4096 bf16 operand values at ops; out gets grid * 256 floats.
 hipError_t launch_mfma_probe(const void* ops, float* out, int grid, int iters,
                              hipStream_t stream);
 
