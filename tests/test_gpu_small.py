@@ -107,3 +107,13 @@ def test_window_at_block_edges(dtype, D, causal, window):
     query block, 64 in dQ): where each wave's precomputed FULL blocks, which skip the class
     test and the mask, begin and end."""
     check_case(1, 300, 4, 2, D, dtype, causal, window, seed=150 + window)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f16", 128)])
+@pytest.mark.parametrize("window", [1, 4, 5, 15, 16, 17, 47, 48, 49])
+def test_window_at_tile_edges(dtype, D, window):
+    """Windows around the 16-key and 4-key granules of the MFMA tiles (a 16x16 accumulator tile
+    holds 16 keys, 4 per lane row) and T around the 16-row query tiles: a key index off by one
+    inside a tile moves a masked score across the window edge."""
+    for T in (47, 49):
+        check_case(1, T, 4, 2, D, dtype, True, window, seed=300 + window + T)
