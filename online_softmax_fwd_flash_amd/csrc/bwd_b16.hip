@@ -561,6 +561,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_b16_kernel(
 #pragma unroll
         for (int qh = 0; qh < 2; ++qh) dq_i[qh] = qq[qh] < T ? Dv[((int64_t)b * H + h) * T + qq[qh]] : 0.f;
     }
+    // keys each query row may see: [klo, klo + kn)
+    int klo[2], kn[2];
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) row_keys(qq[qh], T, Tk, cz, window, klo[qh], kn[qh]);
     // dQ^T accumulators: tile (dt, qh), entry r of lane (n, g): column 16*dt + 4g + r of query
     // row wr0 + 16*qh + n
     f32x4 dqa[C::DT][2];
@@ -635,17 +639,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void dq_b16_kernel(
             if (cls == kPartial) {
                 keep_branch();
 #pragma unroll
-                for (int qh = 0; qh < 2; ++qh) {
-                    int klo, kn;   // keys the query row may see: [klo, klo + kn)
-                    row_keys(qq[qh], T, Tk, cz, window, klo, kn);
+                for (int qh = 0; qh < 2; ++qh)
 #pragma unroll
                     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int kk = j * C::BK + 32 * kb + 16 * kt + 4 * g + r;
-                            if ((unsigned)(kk - klo) >= (unsigned)kn) sk[kt][qh][r] = 0.f;
+                            if ((unsigned)(kk - klo[qh]) >= (unsigned)kn[qh]) sk[kt][qh][r] = 0.f;
                         }
-                }
             }
             // B operand of dQ^T += K^T dS^T for query tile qh: element e is key 32*kb + 4g + e
             // (e < 4) or 32*kb + 16 + 4g + e - 4, the lane's own entries

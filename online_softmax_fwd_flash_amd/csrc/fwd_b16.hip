@@ -102,6 +102,7 @@ struct FwdCtx {
     bool cz;
     int g;                                   // lane row (lane / 16)
     int q[2];                                // this lane's two query rows
+    int klo[2], kn[2];                       // keys each of them may see: [klo, klo + kn)
     float c;                                 // scale * log2(e)
     float inv8c;                             // 8 / c: rescale threshold above the running max
     __device__ __forceinline__ FwdCtx(const Buf& k, const Buf& v) : kbuf(k), vbuf(v) {}
@@ -162,14 +163,12 @@ __device__ __forceinline__ void fwd_block(FwdState<E, D>& st, const FwdCtx<D>& x
         keep_branch();
 #pragma unroll
         for (int qh = 0; qh < 2; ++qh) {
-            int klo, kn;   // keys the query row may see: [klo, klo + kn)
-            row_keys(x.q[qh], x.T, x.Tk, x.cz, x.window, klo, kn);
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int k0 = j * kBK + 16 * kt + 4 * x.g + r;
-                    if ((unsigned)(k0 - klo) >= (unsigned)kn) s[kt][qh][r] = -INFINITY;
+                    if ((unsigned)(k0 - x.klo[qh]) >= (unsigned)x.kn[qh]) s[kt][qh][r] = -INFINITY;
                 }
         }
     }
@@ -267,6 +266,8 @@ __global__ __launch_bounds__(kThreads, kWgs) void fwd_b16_kernel(
     x.inv8c = 8.0f / x.c;
     x.q[0] = x.wr0 + n;
     x.q[1] = x.wr0 + 16 + n;
+    row_keys(x.q[0], T, Tk, x.cz, window, x.klo[0], x.kn[0]);
+    row_keys(x.q[1], T, Tk, x.cz, window, x.klo[1], x.kn[1]);
 
     FwdState<E, D> st;
     // Q^T operands: lane (n, g) holds Q[q][32*ds + 8g .. +7] of its two rows (zero past T)
